@@ -1,0 +1,72 @@
+"""dt / decay through the NAU, and the fixed-point selective scan.
+
+[FM] "What carries the argument": power-of-two scaling makes the SSM block's
+arithmetic shifts, adds and products; [FMV] supporting citations [14]
+(zero-order-hold discretization, giving the decay e^(dt*A)) and [15] (the
+shift-based exponential used for e^dt).  [FM] Fig. 2: per head, the state
+h[p, n] evolves as h_t = exp(dt_t * A) h_{t-1} + dt_t * x_t[p] * B_t[n] and the
+output is y_t[p] = sum_n C_t[n] h_t[p, n] + D x_t[p] (Mamba2, one group).
+
+Readings:
+* dt_in = sat32(rint((dt_raw + dt_bias) * 2^16)) (float32 add, then the exact
+  scaling); dt = SoftPlus(dt_in) in Q.16; A_q16 = sat32(rint(A * 2^16));
+  dA = e^(rshr(dt * A_q16, 16)) in Q.16 (argument <= 0, so dA in [0, 2^16]).
+* Exponents: x has p_x, B has p_B, C has p_C.  The state is int32 with
+  exponent p_h = p_x + p_B + 8 and the output y is int32 with exponent
+  p_y = p_x + 8.
+* One step, per (batch, head, p, n), in exact integers:
+    u   = dt * x_q                                   (exponent 16 + p_x)
+    h_t = sat32( floor( (dA * h_{t-1} + 2^8 * u * B_q + 2^15) / 2^16 ) )
+  i.e. the decayed state and the input term are aligned to exponent
+  16 + p_h, summed exactly and rounded half up once onto the state grid.
+    y_acc = sum_n C_q * h_t                          (exponent p_C + p_h)
+    y     = sat32( rshr(y_acc, p_B + p_C) + rshr(D_q16 * x_q, 8) )
+* The scan is sequential in t; the state starts at zero or from the cache.
+"""
+import numpy as np
+
+from .fixedpoint import f32_to_i32_sat, rshr, sat32
+from .nau import exp_q16, softplus_q16
+
+
+def dt_dA(dt_raw, dt_bias, A_q16):
+    """dt_raw [..., H] float32 -> (dt Q.16, dA Q.16) int64 arrays of the same shape."""
+    dt_raw = np.asarray(dt_raw, dtype=np.float32)
+    dt_in = f32_to_i32_sat(np.rint((dt_raw + np.asarray(dt_bias, dtype=np.float32))
+                                   * np.float32(65536.0)))
+    dt = softplus_q16(dt_in)
+    arg = sat32(rshr(dt * np.asarray(A_q16, dtype=np.int64), 16))
+    assert np.all(arg <= 0), "A must be <= 0"
+    dA = exp_q16(arg)
+    return dt, dA
+
+
+def ssm_scan_pot(x_q, B_q, C_q, dt, dA, D_q16, p_B, p_C, state_in=None):
+    """Fixed-point scan.
+
+    x_q [Bsz, L, H, P] int8; B_q, C_q [Bsz, L, N] int8; dt, dA [Bsz, L, H] Q.16;
+    D_q16 [H]; state_in [Bsz, H, P, N] int32 or None.
+    Returns (y int64 [Bsz, L, H, P], state_out int64 [Bsz, H, P, N]).
+    """
+    x = np.asarray(x_q, dtype=np.int64)
+    Bm = np.asarray(B_q, dtype=np.int64)
+    Cm = np.asarray(C_q, dtype=np.int64)
+    dt = np.asarray(dt, dtype=np.int64)
+    dA = np.asarray(dA, dtype=np.int64)
+    D = np.asarray(D_q16, dtype=np.int64)
+    Bsz, L, H, P = x.shape
+    N = Bm.shape[-1]
+    if state_in is None:
+        h = np.zeros((Bsz, H, P, N), dtype=np.int64)
+    else:
+        h = np.asarray(state_in, dtype=np.int64).copy()
+    y = np.zeros((Bsz, L, H, P), dtype=np.int64)
+    ky = int(p_B) + int(p_C)
+    for t in range(L):
+        u = dt[:, t, :, None] * x[:, t]                                  # [Bsz, H, P]
+        inc = (u[..., None] * Bm[:, t, None, None, :]) << 8              # [Bsz, H, P, N]
+        num = dA[:, t, :, None, None] * h + inc + (1 << 15)
+        h = sat32(num >> 16)
+        y_acc = np.sum(Cm[:, t, None, None, :] * h, axis=-1)            # exact int64
+        y[:, t] = sat32(rshr(y_acc, ky) + rshr(D[None, :, None] * x[:, t], 8))
+    return y, h

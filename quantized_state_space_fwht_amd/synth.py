@@ -1,0 +1,70 @@
+"""Seeded synthetic inputs and random-init parameters.
+
+The FastMamba paper evaluates trained Mamba2-130M / 2.7B checkpoints on text
+(Section V.A, Table II); neither weights nor datasets are used here.  Instead
+every tensor is drawn from numpy's PCG64 generator with a fixed seed:
+
+* activations ~ N(0, 1) with a few fixed channels scaled up (x50), the
+  outlier-channel pattern that motivates the Hadamard rotation (Fig. 3,
+  activation distributions before the transform; the Mamba-PTQ finding that
+  Mamba activations carry outlier channels);
+* projection and conv weights ~ N(0, 0.02); dt bias ~ U(-4, -2);
+  A = -exp(U(0, 2)); D = 1; gated-RMSNorm weight = 1.
+
+This module only draws numbers.  It holds no step of the method: quantizers,
+transforms and fixed-point conversions live on each side (kernels, oracle)
+separately.  Both the GPU path and the CPU oracle receive these arrays.
+"""
+import numpy as np
+
+from .configs import LayerShape, Workload
+
+
+def outlier_channels(d_model: int, seed: int = 7, count: int = 4) -> np.ndarray:
+    """Indices of the outlier channels: first `count` of a seeded permutation, sorted."""
+    perm = np.random.default_rng(seed).permutation(d_model)
+    return np.sort(perm[:count])
+
+
+def activations(shape: LayerShape, batch: int, seqlen: int, seed: int,
+                outlier_seed: int = 7, n_outliers: int = 4, scale: float = 50.0) -> np.ndarray:
+    """u [batch, seqlen, d_model] float32."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((batch, seqlen, shape.d_model), dtype=np.float32)
+    idx = outlier_channels(shape.d_model, outlier_seed, n_outliers)
+    u[..., idx] *= np.float32(scale)
+    return u
+
+
+def workload_activations(w: Workload, seed: int = None) -> np.ndarray:
+    return activations(w.shape, w.batch, w.seqlen, w.input_seed if seed is None else seed,
+                       w.outlier_seed, w.n_outliers, w.outlier_scale)
+
+
+def decode_step_input(w: Workload, step: int) -> np.ndarray:
+    """u_t [batch, d_model] for decode step `step` (seed 400 + step)."""
+    return activations(w.shape, w.batch, 1, 400 + step, w.outlier_seed,
+                       w.n_outliers, w.outlier_scale)[:, 0, :]
+
+
+def layer_params(shape: LayerShape, seed: int) -> dict:
+    """Random-init float32 parameters of one mixer layer (draw order fixed)."""
+    rng = np.random.default_rng(seed)
+    s = shape
+    p = {}
+    p["w_in"] = (rng.standard_normal((s.d_in_proj, s.d_model), dtype=np.float32)
+                 * np.float32(0.02))
+    p["w_out"] = (rng.standard_normal((s.d_model, s.d_inner), dtype=np.float32)
+                  * np.float32(0.02))
+    p["conv_w"] = (rng.standard_normal((s.conv_ch, s.d_conv), dtype=np.float32)
+                   * np.float32(0.02))
+    p["conv_b"] = (rng.standard_normal((s.conv_ch,), dtype=np.float32) * np.float32(0.02))
+    p["dt_bias"] = rng.uniform(-4.0, -2.0, size=(s.nheads,)).astype(np.float32)
+    p["A"] = (-np.exp(rng.uniform(0.0, 2.0, size=(s.nheads,)))).astype(np.float32)
+    p["D"] = np.ones((s.nheads,), dtype=np.float32)
+    p["norm_w"] = np.ones((s.d_inner,), dtype=np.float32)
+    return p
+
+
+def workload_params(w: Workload, layer: int) -> dict:
+    return layer_params(w.shape, w.param_seed_base + layer)
