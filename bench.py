@@ -1,0 +1,157 @@
+#!/usr/bin/env python3
+"""Benchmark: quantized Mamba2 mixer layer prefill tokens/s on one MI355X.
+
+One step = one full prefill pass of the mixer layer (Hadamard-quant, in_proj
+W8A8 GEMM, PoT conv1d + SiLU, NAU dt/decay + fixed-point scan, gate +
+RMSNorm + Hadamard-quant, out_proj W8A8 GEMM) over one batch of seeded
+synthetic input already resident in HBM.  Default workload: one
+Mamba2-130M-shaped layer, batch 1, L 2048, dynamic scales.
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel (the scan),
+timed live with HIP events recorded by the library around that kernel on the
+layer's stream inside the timed region.  `cpu_baseline` times the CPU oracle
+(test infrastructure, never tuned) on the same workload on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Mamba2 layer prefill tokens/s (W8A8+PoT SSM); % of i8 MFMA / HBM peak"
+# MI355X: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.32e12 vector lane-operations/s
+# (float64 FMA runs at this rate: 78.6 TFLOP/s counting an FMA as 2).
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# algorithmic integer work per state element per time step of the scan:
+# 3 multiply-adds (decay*h + input, dt*x*B, C*h accumulation), 1 rounding, 1 saturation
+SCAN_OPS_PER_ELEMENT_STEP = 5
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def scan_source_hash():
+    p = os.path.join(ROOT, "quantized_state_space_fwht_amd", "csrc", "fm_scan.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, per_launch_units):
+    """HBM bytes per scan launch from committed rocprofv3 counter runs, if still current."""
+    p = os.path.join(ROOT, "profiles", f"scan_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("scan_source_sha256_16") != scan_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, min_seconds=10.0, max_reps=3):
+    import numpy as np
+    import oracle as O
+    from quantized_state_space_fwht_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    prep = O.prepare_layer(synth.workload_params(w, 0))
+    u = synth.workload_activations(w)
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        O.layer_prefill(prep, w.shape, u)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(w.tokens * reps / dt, 1), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{reps} full oracle prefill pass(es) of the same workload "
+                      f"({w.batch}x{w.seqlen} tokens, seeds as the GPU run), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="m130m_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_state_space_fwht_amd import binding as B
+    from quantized_state_space_fwht_amd import configs, synth
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+
+    w = configs.get(args.workload)
+    if w.nlayers != 1 or w.decode_steps:
+        print("bench.py times single-layer prefill workloads", file=sys.stderr)
+        sys.exit(2)
+    s = w.shape
+    torch.cuda.set_device(0)
+    log(f"bench: building layer {w.name} ({w.description})")
+    layer = Mamba2Layer(s, synth.workload_params(w, 0))
+    u = torch.from_numpy(synth.workload_activations(w)).cuda()
+    out = torch.empty_like(u)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        layer.prefill(u, out, stream=stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    for a, b in evs:  # create the underlying HIP events
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    log(f"bench: timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        B.lib.fm_layer_set_timing_events(evs[i][0].cuda_event, evs[i][1].cuda_event)
+        layer.prefill(u, out, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    tokens_per_s = w.tokens / (ms_per_step / 1e3)
+
+    elem_steps = w.batch * w.seqlen * s.nheads * s.headdim * s.dstate
+    achieved = SCAN_OPS_PER_ELEMENT_STEP * elem_steps / (scan_ms / 1e3) / 1e12
+    roofline = {"bound": "alu", "kernel": "scan_kernel", "achieved": round(achieved, 3),
+                "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(achieved / VALU_PEAK_TOPS, 4),
+                "traffic": load_traffic(w.name, elem_steps),
+                "launch_ms": round(scan_ms, 4),
+                "work": f"{SCAN_OPS_PER_ELEMENT_STEP} ops x {elem_steps} element-steps"}
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+int32", "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
+                   "d_model": s.d_model, "d_inner": s.d_inner, "nheads": s.nheads,
+                   "headdim": s.headdim, "d_state": s.dstate, "mode": w.mode,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

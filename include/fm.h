@@ -1,0 +1,322 @@
+/*
+ * fm.h — C-ABI of the MI355X quantized Mamba2 mixer (FastMamba method).
+ *
+ * The library computes the quantized Mamba2 mixer layer described on the
+ * review page of "FastMamba: A High-Speed and Efficient Mamba Accelerator on
+ * FPGA with Accurate Quantization" (arXiv 2505.18975):
+ *   - a Hadamard rotation Y = (X H)(H^T W^T) followed by per-tensor int8
+ *     quantization ("What carries the argument"), with the scale taken from
+ *     the maximum of the rotated tensor (Algorithm 1, Section III-A) or fixed
+ *     as a multiply + shift (Fig. 6, Section IV-B; referee major comment);
+ *   - W8A8 in_proj / out_proj with int32 accumulation (abstract);
+ *   - power-of-two fixed-point causal conv1d and SSM scan (abstract);
+ *   - an 8-segment first-order approximation of 2^v serving e^x and
+ *     SoftPlus through SoftPlus(x) = x + SoftPlus(-x) ("What carries the
+ *     argument"; Eq. (5), Section III-B.2).
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
+ *     are dense row-major unless a row stride is given (strides count
+ *     elements).  The library never allocates device memory and never frees
+ *     caller memory.
+ *   - Every call is asynchronous on `stream` and never synchronizes.
+ *     Temporary memory comes from a caller-provided `workspace` of at least
+ *     the bytes returned by the matching *_workspace_size query (256-byte
+ *     aligned).  Calls sharing a workspace must be ordered on one stream.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     an error nothing is launched and the status says why
+ *     (fm_last_error() returns a thread-local message).
+ *   - Scales and exponents computed from the data stay on the device: the
+ *     dynamic mode never copies to the host.
+ *   - Fixed-point formats: int8 codes lie in [-127, 127]; "Q.16" is int32
+ *     with 16 fraction bits; power-of-two exponents p mean value = code*2^-p.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FM_ABI_VERSION 1
+#define FM_HADAMARD_BLOCK 256
+#define FM_PMIN (-24)
+#define FM_PMAX 24
+
+typedef enum fm_status {
+    FM_OK = 0,
+    FM_ERR_NULL = 1,      /* a required pointer is NULL */
+    FM_ERR_SHAPE = 2,     /* a size is negative, too large or not supported */
+    FM_ERR_MODE = 3,      /* bad mode, or static parameters out of range */
+    FM_ERR_WORKSPACE = 4, /* workspace NULL / too small / misaligned */
+    FM_ERR_HIP = 5        /* a HIP launch failed */
+} fm_status;
+
+typedef enum fm_scale_mode {
+    FM_SCALE_DYNAMIC = 0, /* scale / exponent from the maximum of this call's tensor */
+    FM_SCALE_STATIC = 1   /* scale / exponent given (calibrated offline) */
+} fm_scale_mode;
+
+int fm_abi_version(void);
+const char* fm_status_string(fm_status s);
+/* Message of the last failing call made by this thread ("" if none). */
+const char* fm_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * fm_hadamard_quant — rotate rows by H_K and quantize the tensor to int8.
+ * Definition: review page, "What carries the argument" (rotation with the
+ * Hadamard matrix normalized by sqrt(n)); referee major comment on
+ * Sections III-A / IV-B (scale from the maximum of the rotated tensor in
+ * Algorithm 1; "x scoe, >> sshift" in Fig. 6).
+ *
+ *   r = x · H_K per row, H_K = I_{K/256} ⊗ (S_256 / 16), S_256 the Sylvester
+ *       Hadamard matrix; computed as a float32 fast Walsh–Hadamard
+ *       transform with stages 1, 2, 4, ..., 128 in that order, then * 1/16.
+ *   dynamic: c = 127 / max|r| over the whole tensor (c = 1 if max|r| = 0)
+ *   static:  c = scoe * 2^-sshift  (0 < scoe < 2^24, |sshift| <= 126)
+ *   q = clamp(rint(r * c), -127, 127);  *scale_out = 1 / c  (float32).
+ *
+ * x [rows, k] float32; q [rows, k] int8; scale_out: 1 float (device).
+ * amax_stats: NULL, or 1 float (device) max-accumulated with max|r| (the
+ *   caller zeroes it before the first call of a calibration run).
+ * k must be a positive multiple of 256 and <= 65536; rows >= 0, rows*k < 2^31.
+ * Workspace: fm_hadamard_quant_workspace_size() bytes (dynamic mode; static
+ *   mode accepts NULL).
+ * ---------------------------------------------------------------------- */
+size_t fm_hadamard_quant_workspace_size(int64_t rows, int64_t k);
+fm_status fm_hadamard_quant(const float* x, int64_t rows, int64_t k, fm_scale_mode mode,
+                            int32_t scoe, int32_t sshift, int8_t* q, float* scale_out,
+                            float* amax_stats, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fm_w8a8_gemm — W8A8 linear layer (review page abstract: 8-bit linear
+ * layers; "What carries the argument": Y = (XH)(H^T W^T)).
+ *
+ *   acc[i, j] = sum_k a[i, k] * b[j, k]       (int32, exact)
+ *   out[i, j] = float(acc[i, j]) * (scale_a[0] * scale_b[0])
+ *               (the two scales multiplied first in float32; float(acc) is
+ *               round-to-nearest-even)
+ *
+ * a [m, k] int8, b [n, k] int8 (rows = output features), acc [m, n] int32
+ * (NULL to skip), out [m, n] float32 (NULL to skip; needs both scales).
+ * At least one of acc / out.  k a positive multiple of 64, k <= 131072;
+ * m, n >= 0.
+ * ---------------------------------------------------------------------- */
+fm_status fm_w8a8_gemm(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
+                       const float* scale_a, const float* scale_b, int32_t* acc, float* out,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fm_conv1d_pot — power-of-two quantized causal depthwise conv1d + SiLU +
+ * requantization of x, B, C (review page abstract and "What carries the
+ * argument": fine-grained power-of-two quantization for the convolution;
+ * Fig. 2: conv1d then SiLU in the Mamba2 block).
+ *
+ * Input xbc: the in_proj output columns x|B|C, float32 rows of ch =
+ *   d_inner + 2*dstate values, row r at xbc + r*xbc_row_stride, rows ordered
+ *   [batch, len].
+ *   p_c  = pot(max|xbc|) (dynamic) or p_fixed[0] (static); pot(a) is the
+ *          largest p in [-24, 24] with a*2^p <= 127 (0 if a = 0)
+ *   xq   = clamp(rint(xbc * 2^p_c), -127, 127)
+ *   acc  = sum_{k<4} w_q[c, k] * xq[t-3+k, c]   (t-3+k < 0 reads conv_state_in,
+ *          zeros if NULL)
+ *   a    = sat32(rshr(acc, p_c + p_w[c] - 16) + b_q16[c])        (Q.16)
+ *   s    = SiLU(a) in Q.16 through the 2^v unit (x + SiLU(-x) symmetry)
+ *   x|B|C= s split at d_inner and d_inner + dstate; each part has exponent
+ *          p = largest in [-24, 24] with max|part| * 2^(p-16) <= 127
+ *          (dynamic) or p_fixed[1..3] (static); code = clamp(rshr(s, 16-p))
+ *   rshr(v, s) = floor(v / 2^s + 1/2) (s < 0: exact left shift).
+ *
+ * w_q [ch, 4] int8, p_w [ch] int32, b_q16 [ch] int32 (see fm_prepare_layer).
+ * p_fixed: device int32[4] (p_c, p_x, p_B, p_C), required in static mode.
+ * conv_state_in / conv_state_out: [batch, ch, 3] int8, inputs at t = -3..-1
+ *   (oldest first) / the last 3 inputs after this call; either may be NULL.
+ * xbc_q [batch*len, ch] int8 (NULL to skip); x_out [batch*len, d_inner],
+ *   b_out / c_out [batch*len, dstate] int8 (required).
+ * p_out: device int32[4] written with (p_c, p_x, p_B, p_C).
+ * amax_stats: NULL or device int32[4] max-accumulated with (float bits of
+ *   max|xbc|, max|x|, max|B|, max|C| in Q.16).
+ * d_inner % 64 == 0, dstate % 64 == 0, len >= 1, batch >= 1.
+ * ---------------------------------------------------------------------- */
+size_t fm_conv1d_pot_workspace_size(int64_t batch, int64_t len, int64_t d_inner, int64_t dstate);
+fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch, int64_t len,
+                        int64_t d_inner, int64_t dstate, const int8_t* w_q, const int32_t* p_w,
+                        const int32_t* b_q16, fm_scale_mode mode, const int32_t* p_fixed,
+                        const int8_t* conv_state_in, int8_t* conv_state_out, int8_t* xbc_q,
+                        int8_t* x_out, int8_t* b_out, int8_t* c_out, int32_t* p_out,
+                        int32_t* amax_stats, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fm_ssm_scan_pot — dt / decay through the 2^v unit and the fixed-point
+ * selective scan (review page "What carries the argument"; Eq. (5) and the
+ * SoftPlus symmetry; verdict record citations [14] zero-order hold and
+ * [15] shift-based exponential for e^dt; Fig. 2 SSM block).
+ *
+ *   dt_in = sat32(rint((dt_raw + dt_bias[h]) * 2^16))        (float32)
+ *   dt    = SoftPlus_q16(dt_in) = e^(-|x|) + max(x, 0)        (Q.16)
+ *   dA    = e^(rshr(dt * a_q16[h], 16)) in Q.16, in [0, 2^16]
+ *   per (b, h, p, n), t ascending, from state_in (zeros if NULL):
+ *     u     = dt * x_q                                      (int64)
+ *     state = sat32(floor((dA*state + 2^8*u*B_q + 2^15) / 2^16))
+ *     y     = sat32(rshr(sum_n C_q*state, p_B + p_C) + rshr(d_q16[h]*x_q, 8))
+ *   State exponent p_x + p_B + 8, y exponent p_x + 8.
+ *
+ * x [batch, len, nheads, headdim] int8; bm, cm [batch, len, dstate] int8;
+ * dt_raw: float32 rows (one per token, [batch, len] order) of >= nheads
+ *   values, row r at dt_raw + r*dt_row_stride; dt_bias [nheads] float32;
+ * a_q16 [nheads] int32 (<= 0), d_q16 [nheads] int32;
+ * p: device int32[4] = (p_c, p_x, p_B, p_C) (only p_B + p_C is used);
+ * state_in / state_out [batch, nheads, headdim, dstate] int32 (NULL: zeros
+ *   / not written); y [batch, len, nheads, headdim] int32;
+ * dt_out, da_out [batch, len, nheads] int32 Q.16 (NULL to skip).
+ * headdim % 4 == 0, dstate in {64, 128, 256}, len >= 1.
+ * ---------------------------------------------------------------------- */
+fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
+                          const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
+                          const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
+                          int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
+                          int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
+                          int32_t* dt_out, int32_t* da_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fm_gate_norm_quant — output gate, gated RMSNorm and the out_proj input
+ * quantization (Fig. 2: y * SiLU(z), RMSNorm, out_proj; the out_proj input
+ * is rotated and quantized exactly as fm_hadamard_quant).
+ *
+ *   g = (float(y) * 2^-(p_x+8)) * (float(SiLU_q16(sat32(rint(z*2^16)))) * 2^-16)
+ *   ss: 64 partial sums, partial l adds g_i*g_i for i = l, l+64, ... in
+ *       ascending order (no fused multiply-add), then a[l] += a[l xor k]
+ *       for k = 32, 16, 8, 4, 2, 1; ss = a[0]
+ *   n_i = (g_i * (1 / sqrt(ss / d_inner + 1e-5))) * norm_w[i]
+ *   then rotation + per-tensor int8 of n as fm_hadamard_quant.
+ *
+ * y [rows, d_inner] int32 (exponent p_x + 8); z: float32 rows of d_inner
+ * values at z + r*z_row_stride; p: device int32[4] (p_x = p[1] is used);
+ * norm_w [d_inner]; q [rows, d_inner] int8; scale_out 1 float;
+ * amax_stats as fm_hadamard_quant; normed_out [rows, d_inner] float32 or
+ * NULL.  d_inner a positive multiple of 256.
+ * ---------------------------------------------------------------------- */
+size_t fm_gate_norm_quant_workspace_size(int64_t rows, int64_t d_inner);
+fm_status fm_gate_norm_quant(const int32_t* y, const float* z, int64_t z_row_stride,
+                             const int32_t* p, const float* norm_w, int64_t rows, int64_t d_inner,
+                             fm_scale_mode mode, int32_t scoe, int32_t sshift, int8_t* q,
+                             float* scale_out, float* amax_stats, float* normed_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Layer-level calls.
+ * ---------------------------------------------------------------------- */
+typedef struct fm_layer_desc {
+    int64_t d_model, d_inner, nheads, headdim, dstate, d_conv; /* d_conv must be 4 */
+    int32_t mode;             /* fm_scale_mode of every activation quantization point */
+    int32_t prenorm_residual; /* 1: out = u + mixer(RMSNorm(u)) (stacks), 0: out = mixer(u) */
+} fm_layer_desc;
+
+/* Static-mode parameters (host values; calibrated with fm_qparams_from_stats). */
+typedef struct fm_static_params {
+    int32_t scoe[2];   /* Hadamard points: [0] in_proj input, [1] out_proj input */
+    int32_t sshift[2];
+    int32_t p[4];      /* power-of-two points: p_c, p_x, p_B, p_C */
+} fm_static_params;
+
+/* Prepared weights (device pointers, written by fm_prepare_layer). */
+typedef struct fm_layer_weights {
+    const int8_t* w_in_q;  const float* s_w_in;   /* [2*di + 2*N + H, d_model], 1 float */
+    const int8_t* w_out_q; const float* s_w_out;  /* [d_model, d_inner], 1 float */
+    const int8_t* conv_w_q; const int32_t* conv_p_w; const int32_t* conv_b_q16; /* [ch,4],[ch],[ch] */
+    const float* dt_bias; const int32_t* a_q16; const int32_t* d_q16;        /* [H] each */
+    const float* norm_w;                                                       /* [d_inner] */
+} fm_layer_weights;
+
+/* Device-resident per-layer record of what a call used and saw. */
+typedef struct fm_qparams {
+    float scale[2];            /* dequant scales used at the two Hadamard points */
+    int32_t p[4];              /* exponents used: p_c, p_x, p_B, p_C */
+    float stat_amax[3];        /* max-accumulated: |u rotated|, |n rotated|, |xBC| */
+    int32_t stat_amax_q16[3];  /* max-accumulated: |x|, |B|, |C| in Q.16 */
+    int32_t reserved[4];
+} fm_qparams;
+
+/* Decode caches of one layer (device pointers). */
+typedef struct fm_cache {
+    int8_t* conv_state;   /* [batch, d_inner + 2*dstate, 3] int8 */
+    int32_t* ssm_state;   /* [batch, nheads, headdim, dstate] int32 */
+    int32_t* p;           /* [4] exponents frozen by the prefill: p_c, p_x, p_B, p_C */
+} fm_cache;
+
+/* Offline parameter preparation (Section III-A: weights rotated by H^T and
+ * quantized per tensor; conv weights power-of-two per channel):
+ *   w_in_q, s_w_in   = fm_hadamard_quant(w_in) dynamic
+ *   w_out_q, s_w_out = fm_hadamard_quant(w_out) dynamic
+ *   conv_p_w[c] = pot(max_k |conv_w[c,k]|); conv_w_q = clamp(rint(w*2^p_w))
+ *   conv_b_q16  = sat32(rint(conv_b * 2^16))
+ *   a_q16 = sat32(rint(A * 2^16)) (A <= 0), d_q16 = sat32(rint(D * 2^16)).
+ * Inputs are float32 device arrays of the Mamba2 parameter shapes. */
+size_t fm_prepare_layer_workspace_size(const fm_layer_desc* d);
+fm_status fm_prepare_layer(const fm_layer_desc* d, const float* w_in, const float* w_out,
+                           const float* conv_w, const float* conv_b, const float* a,
+                           const float* dvec, int8_t* w_in_q, float* s_w_in, int8_t* w_out_q,
+                           float* s_w_out, int8_t* conv_w_q, int32_t* conv_p_w,
+                           int32_t* conv_b_q16, int32_t* a_q16, int32_t* d_q16, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* fm_mamba2_layer_prefill — the whole mixer over u [batch, len, d_model]
+ * from a zero state (Fig. 2 flow: in_proj, conv1d + SiLU, SSM, gated
+ * RMSNorm, out_proj), each step as the calls above.  out [batch, len,
+ * d_model] float32 (may not alias u).  cache (nullable): receives the conv
+ * window, the final int32 state and the exponents used.  qp (device,
+ * required): receives the scales / exponents used; its stat_* fields are
+ * max-accumulated (zero them before a calibration run).  sp: required in
+ * static mode, ignored otherwise.  Workspace: fm_mamba2_layer_workspace_size. */
+size_t fm_mamba2_layer_workspace_size(const fm_layer_desc* d, int64_t batch, int64_t len);
+fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights* w,
+                                  const fm_static_params* sp, const float* u, int64_t batch,
+                                  int64_t len, float* out, const fm_cache* cache, fm_qparams* qp,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fm_mamba2_layer_decode — one token per sequence, u_t [batch, d_model],
+ * continuing from `cache` (updated in place): the conv window shifts, the
+ * state advances one step, the exponents stay frozen at cache->p, the
+ * Hadamard scales follow the layer mode.  out_t [batch, d_model]. */
+fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights* w,
+                                 const fm_static_params* sp, const float* u_t, int64_t batch,
+                                 const fm_cache* cache, float* out_t, fm_qparams* qp,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Byte offsets, inside the layer workspace, of the intermediates the last
+ * prefill / decode call on that workspace left there (for parity tests):
+ * u_q [T, d_model] i8, v [T, dip] f32 (in_proj out: z|xBC|dt), xbc_q [T, ch] i8,
+ * x_q [T, d_inner] i8, b_q / c_q [T, dstate] i8, y [T, d_inner] i32,
+ * g_q [T, d_inner] i8, normed [T, d_inner] f32 (written only if requested
+ * by fm_layer_keep_intermediates), with T = batch * len. */
+typedef struct fm_layer_taps {
+    size_t u_q, v, xbc_q, x_q, b_q, c_q, y, g_q, normed, dt, da;
+} fm_layer_taps;
+fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len,
+                               fm_layer_taps* taps);
+/* 1: later layer calls in this process also write xbc_q, normed, dt, dA into
+ * their workspace (slower; for tests).  0 (default): they do not. */
+void fm_layer_keep_intermediates(int32_t on);
+
+/* Profiling hook: the next layer call made by this thread records `start`
+ * right before and `stop` right after its scan kernel (the dominant kernel)
+ * on its stream; the hook then clears itself.  Both are hipEvent_t handles
+ * owned by the caller; NULL clears the hook. */
+void fm_layer_set_timing_events(void* start, void* stop);
+
+/* Host helper: static parameters from the max statistics of a calibration
+ * run (fm_qparams copied to the host).  Hadamard points: c = 127 / amax in
+ * double, sshift with 2^14 <= c * 2^sshift < 2^15, scoe = rint(c * 2^sshift);
+ * power-of-two points: p = pot(amax) as in fm_conv1d_pot. */
+fm_status fm_qparams_from_stats(const fm_qparams* host_stats, fm_static_params* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_H */

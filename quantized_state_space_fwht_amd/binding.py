@@ -1,0 +1,202 @@
+"""ctypes binding of libfm.so (include/fm.h): argument marshalling only.
+
+Every function here has the name of a C entry point and forwards torch
+tensors' device pointers and sizes to it; every step of the method runs in the
+library's HIP kernels.  The library is loaded from this package's directory;
+if it is missing the import fails loudly — there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfm.so")
+
+FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_MODE, FM_ERR_WORKSPACE, FM_ERR_HIP = range(6)
+DYNAMIC, STATIC = 0, 1
+
+
+class FmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"fm status {status}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_state_space_fwht_amd.build` (no fallback exists)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_c_i64, _c_i32, _c_sz, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d_model", _c_i64), ("d_inner", _c_i64), ("nheads", _c_i64),
+                ("headdim", _c_i64), ("dstate", _c_i64), ("d_conv", _c_i64),
+                ("mode", _c_i32), ("prenorm_residual", _c_i32)]
+
+
+class StaticParams(ctypes.Structure):
+    _fields_ = [("scoe", _c_i32 * 2), ("sshift", _c_i32 * 2), ("p", _c_i32 * 4)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_in_q", "s_w_in", "w_out_q", "s_w_out", "conv_w_q",
+                                   "conv_p_w", "conv_b_q16", "dt_bias", "a_q16", "d_q16",
+                                   "norm_w")]
+
+
+class QParams(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float * 2), ("p", _c_i32 * 4),
+                ("stat_amax", ctypes.c_float * 3), ("stat_amax_q16", _c_i32 * 3),
+                ("reserved", _c_i32 * 4)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("conv_state", _vp), ("ssm_state", _vp), ("p", _vp)]
+
+
+class LayerTaps(ctypes.Structure):
+    _fields_ = [(n, _c_sz) for n in ("u_q", "v", "xbc_q", "x_q", "b_q", "c_q", "y", "g_q",
+                                     "normed", "dt", "da")]
+
+
+QPARAMS_BYTES = ctypes.sizeof(QParams)
+
+_SIGS = {
+    "fm_abi_version": (ctypes.c_int, []),
+    "fm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fm_last_error": (ctypes.c_char_p, []),
+    "fm_hadamard_quant_workspace_size": (_c_sz, [_c_i64, _c_i64]),
+    "fm_hadamard_quant": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, _c_i32, _c_i32, _vp,
+                                         _vp, _vp, _vp, _c_sz, _vp]),
+    "fm_w8a8_gemm": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "fm_conv1d_pot_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fm_conv1d_pot": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp,
+                                     ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _c_sz, _vp]),
+    "fm_ssm_scan_pot": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _vp, _c_i64,
+                                       _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
+                                       _vp]),
+    "fm_gate_norm_quant_workspace_size": (_c_sz, [_c_i64, _c_i64]),
+    "fm_gate_norm_quant": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_i64, _c_i64,
+                                          ctypes.c_int, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
+                                          _c_sz, _vp]),
+    "fm_prepare_layer_workspace_size": (_c_sz, [ctypes.POINTER(LayerDesc)]),
+    "fm_prepare_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc)] + [_vp] * 15 + [_vp, _c_sz,
+                                                                                 _vp]),
+    "fm_mamba2_layer_workspace_size": (_c_sz, [ctypes.POINTER(LayerDesc), _c_i64, _c_i64]),
+    "fm_mamba2_layer_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
+                                               ctypes.POINTER(LayerWeights),
+                                               ctypes.POINTER(StaticParams), _vp, _c_i64, _c_i64,
+                                               _vp, ctypes.POINTER(Cache), _vp, _vp, _c_sz, _vp]),
+    "fm_mamba2_layer_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
+                                              ctypes.POINTER(LayerWeights),
+                                              ctypes.POINTER(StaticParams), _vp, _c_i64,
+                                              ctypes.POINTER(Cache), _vp, _vp, _vp, _c_sz, _vp]),
+    "fm_mamba2_layer_taps": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _c_i64, _c_i64,
+                                            ctypes.POINTER(LayerTaps)]),
+    "fm_layer_keep_intermediates": (None, [_c_i32]),
+    "fm_layer_set_timing_events": (None, [_vp, _vp]),
+    "fm_qparams_from_stats": (ctypes.c_int, [ctypes.POINTER(QParams),
+                                             ctypes.POINTER(StaticParams)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(status):
+    if status != FM_OK:
+        raise FmError(status, lib.fm_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous"
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace(nbytes, device="cuda"):
+    """A 256-byte aligned device buffer (torch's allocator aligns to >= 512 bytes)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- step calls
+def fm_hadamard_quant(x, mode, scoe, sshift, q, scale_out, amax_stats=None, ws=None, stream=None):
+    rows, k = x.shape
+    if ws is None and mode == DYNAMIC:
+        ws = workspace(lib.fm_hadamard_quant_workspace_size(rows, k), x.device)
+    _check(lib.fm_hadamard_quant(_ptr(x), rows, k, mode, scoe, sshift, _ptr(q), _ptr(scale_out),
+                                 _ptr(amax_stats), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)))
+
+
+def fm_w8a8_gemm(a, b, scale_a, scale_b, acc=None, out=None, stream=None):
+    m, k = a.shape
+    n = b.shape[0]
+    _check(lib.fm_w8a8_gemm(_ptr(a), _ptr(b), m, n, k, _ptr(scale_a), _ptr(scale_b), _ptr(acc),
+                            _ptr(out), _stream(stream)))
+
+
+def fm_conv1d_pot(xbc, row_stride, batch, length, d_inner, dstate, w_q, p_w, b_q16, mode,
+                  p_fixed, state_in, state_out, xbc_q, x_out, b_out, c_out, p_out,
+                  amax_stats=None, ws=None, stream=None):
+    if ws is None:
+        ws = workspace(lib.fm_conv1d_pot_workspace_size(batch, length, d_inner, dstate),
+                       xbc.device)
+    _check(lib.fm_conv1d_pot(xbc.data_ptr(), row_stride, batch, length, d_inner, dstate,
+                             _ptr(w_q), _ptr(p_w), _ptr(b_q16), mode, _ptr(p_fixed),
+                             _ptr(state_in), _ptr(state_out), _ptr(xbc_q), _ptr(x_out),
+                             _ptr(b_out), _ptr(c_out), _ptr(p_out), _ptr(amax_stats), _ptr(ws),
+                             ws.numel(), _stream(stream)))
+
+
+def fm_ssm_scan_pot(x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p, batch, length,
+                    nheads, headdim, dstate, state_in, state_out, y, dt_out=None, da_out=None,
+                    stream=None):
+    _check(lib.fm_ssm_scan_pot(_ptr(x), _ptr(bm), _ptr(cm), dt_raw.data_ptr(), dt_row_stride,
+                               _ptr(dt_bias), _ptr(a_q16), _ptr(d_q16), _ptr(p), batch, length,
+                               nheads, headdim, dstate, _ptr(state_in), _ptr(state_out), _ptr(y),
+                               _ptr(dt_out), _ptr(da_out), _stream(stream)))
+
+
+def fm_gate_norm_quant(y, z, z_row_stride, p, norm_w, rows, d_inner, mode, scoe, sshift, q,
+                       scale_out, amax_stats=None, normed_out=None, ws=None, stream=None):
+    if ws is None:
+        ws = workspace(lib.fm_gate_norm_quant_workspace_size(rows, d_inner), y.device)
+    _check(lib.fm_gate_norm_quant(_ptr(y), z.data_ptr(), z_row_stride, _ptr(p), _ptr(norm_w),
+                                  rows, d_inner, mode, scoe, sshift, _ptr(q), _ptr(scale_out),
+                                  _ptr(amax_stats), _ptr(normed_out), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+
+
+def fm_qparams_from_stats(qp_host: QParams) -> StaticParams:
+    sp = StaticParams()
+    _check(lib.fm_qparams_from_stats(ctypes.byref(qp_host), ctypes.byref(sp)))
+    return sp
+
+
+def qparams_from_device(qp_dev) -> QParams:
+    """Copy a device fm_qparams block to a host QParams (synchronizes)."""
+    raw = qp_dev.cpu().numpy().tobytes()
+    return QParams.from_buffer_copy(raw)
+
+
+def keep_intermediates(on: bool):
+    lib.fm_layer_keep_intermediates(1 if on else 0)

@@ -1,0 +1,169 @@
+// Hadamard rotation (fast Walsh–Hadamard transform over 256-wide blocks) fused
+// with the per-tensor int8 quantization.
+//
+// Review page of FastMamba, "What carries the argument": Y = (X H)(H^T W^T)
+// with H normalized by sqrt(n); referee major comment on Sections III-A / IV-B:
+// the scale comes from the maximum of the rotated tensor (Algorithm 1) or is a
+// fixed multiply + shift (Fig. 6).
+//
+// Layout: one wave per 256-block of a row; lane l holds elements 4l..4l+3
+// (one 16-byte load).  Butterfly stages h = 1, 2 run inside the lane, stages
+// h = 4..128 pair lane l with lane l ^ (h/4).  The stage order is fixed
+// (h = 1, 2, ..., 128) because float32 rounding depends on it.
+#include "fm_internal.hpp"
+
+namespace fm {
+
+constexpr int kHqThreads = 256;  // 4 waves, one 256-block each per iteration
+
+// Rotate the 4 values of this lane (lane = threadIdx % 64) through the block.
+__device__ __forceinline__ float4 fwht256_lane(float4 v, int lane) {
+    float t0 = v.x + v.y, t1 = v.x - v.y, t2 = v.z + v.w, t3 = v.z - v.w;  // h = 1
+    v.x = t0 + t2;                                                         // h = 2
+    v.z = t0 - t2;
+    v.y = t1 + t3;
+    v.w = t1 - t3;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {  // h = 4m: partner lane ^ m
+        float px = __shfl_xor(v.x, m, 64);
+        float py = __shfl_xor(v.y, m, 64);
+        float pz = __shfl_xor(v.z, m, 64);
+        float pw = __shfl_xor(v.w, m, 64);
+        if (lane & m) {  // this lane holds the upper element b of (a, b): a - b
+            v.x = px - v.x;
+            v.y = py - v.y;
+            v.z = pz - v.z;
+            v.w = pw - v.w;
+        } else {  // lower element a: a + b
+            v.x = v.x + px;
+            v.y = v.y + py;
+            v.z = v.z + pz;
+            v.w = v.w + pw;
+        }
+    }
+    v.x *= 0.0625f;
+    v.y *= 0.0625f;
+    v.z *= 0.0625f;
+    v.w *= 0.0625f;
+    return v;
+}
+
+__device__ __forceinline__ float absmax4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ void block_max_to(float m, float* a0, float* a1) {
+    __shared__ float red[kHqThreads / 64];
+    m = wave_max_f32(m);
+    int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+        for (int i = 1; i < kHqThreads / 64; ++i) r = fmaxf(r, red[i]);
+        if (a0) atomic_max_nonneg_f32(a0, r);
+        if (a1) atomic_max_nonneg_f32(a1, r);
+    }
+}
+
+// pass 1 (dynamic): grid maximum of |x H| into amax_ws (and amax_stats)
+__global__ __launch_bounds__(kHqThreads) void hq_amax_kernel(const float* __restrict__ x,
+                                                             int64_t nblk_total, float* amax_ws,
+                                                             float* amax_stats) {
+    int lane = threadIdx.x & 63;
+    int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
+    int64_t stride = (int64_t)gridDim.x * (kHqThreads / 64);
+    float m = 0.0f;
+    for (int64_t b = wv; b < nblk_total; b += stride) {
+        float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
+        m = fmaxf(m, absmax4(fwht256_lane(v, lane)));
+    }
+    block_max_to(m, amax_ws, amax_stats);
+}
+
+__device__ __forceinline__ float scale_coef(fm_scale_mode mode, int32_t scoe, int32_t sshift,
+                                            const float* amax_ws) {
+    if (mode == FM_SCALE_DYNAMIC) {
+        float amax = *amax_ws;
+        return amax == 0.0f ? 1.0f : 127.0f / amax;
+    }
+    return ldexpf((float)scoe, -sshift);
+}
+
+__device__ __forceinline__ char4 quant4(float4 v, float c) {
+    char4 q;
+    q.x = (signed char)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f);
+    q.y = (signed char)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f);
+    q.z = (signed char)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f);
+    q.w = (signed char)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f);
+    return q;
+}
+
+// pass 2 (or the only pass in static mode): rotate again and quantize
+__global__ __launch_bounds__(kHqThreads) void hq_quant_kernel(
+    const float* __restrict__ x, int64_t nblk_total, fm_scale_mode mode, int32_t scoe,
+    int32_t sshift, const float* amax_ws, char4* __restrict__ q, float* scale_out,
+    float* amax_stats, int rotated_input) {
+    int lane = threadIdx.x & 63;
+    float c = scale_coef(mode, scoe, sshift, amax_ws);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = 1.0f / c;
+    int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
+    int64_t stride = (int64_t)gridDim.x * (kHqThreads / 64);
+    float m = 0.0f;
+    for (int64_t b = wv; b < nblk_total; b += stride) {
+        float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
+        if (!rotated_input) v = fwht256_lane(v, lane);
+        m = fmaxf(m, absmax4(v));
+        q[b * 64 + lane] = quant4(v, c);
+    }
+    if (amax_stats) block_max_to(m, amax_stats, nullptr);
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+static int hq_grid(int64_t nblk_total) {
+    int64_t g = (nblk_total + 3) / 4;
+    if (g > 4096) g = 4096;
+    return (int)(g < 1 ? 1 : g);
+}
+
+fm_status zero_words(void* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return FM_OK;
+    int g = (int)((n + 255) / 256);
+    if (g > 1024) g = 1024;
+    zero_words_kernel<<<g, 256, 0, s>>>((uint32_t*)p, n);
+    return check_launch("zero_words");
+}
+
+fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
+                 int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
+                 hipStream_t s) {
+    int64_t nb = rows * (k / 256);
+    int g = hq_grid(nb);
+    fm_status st;
+    if (mode == FM_SCALE_DYNAMIC) {  // amax_ws must hold 0 (zeroed by the caller)
+        hq_amax_kernel<<<g, kHqThreads, 0, s>>>(x, nb, amax_ws, amax_stats);
+        if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
+        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, (char4*)q,
+                                                 scale_out, nullptr, 0);
+    } else {
+        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, nullptr, (char4*)q,
+                                                 scale_out, amax_stats, 0);
+    }
+    return check_launch("hq_quant_kernel");
+}
+
+fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
+                           int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
+                           float* scale_out, hipStream_t s) {
+    int64_t nb = rows * (k / 256);
+    hq_quant_kernel<<<hq_grid(nb), kHqThreads, 0, s>>>(r, nb, mode, scoe, sshift, amax_ws,
+                                                       (char4*)q, scale_out, nullptr, 1);
+    return check_launch("hq_quant_kernel(rotated)");
+}
+
+}  // namespace fm

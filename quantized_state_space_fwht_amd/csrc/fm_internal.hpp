@@ -1,0 +1,143 @@
+// Internal host-side declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fm.h"
+#include "fm_device.hpp"
+
+namespace fm {
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+fm_status fail(fm_status s, const char* fmt, ...);
+// hipGetLastError after a launch; FM_ERR_HIP with the kernel name on failure
+fm_status check_launch(const char* what);
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Bump allocator over a caller workspace.  With a null base it only measures:
+// the returned "pointers" are then byte offsets from the start of the workspace.
+struct Arena {
+    uintptr_t base;
+    size_t used;
+    explicit Arena(void* b) : base((uintptr_t)b), used(0) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = (T*)(base + used);
+        used += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+// ---------------------------------------------------------------- launchers
+// Zero `n` 32-bit words (a kernel, so it can sit inside captured graphs).
+fm_status zero_words(void* p, int64_t n, hipStream_t s);
+
+// Hadamard rotation + per-tensor int8.  In dynamic mode `amax_ws` (one float,
+// holding 0 on entry: the caller zeroes it) receives the grid maximum between
+// the two passes.
+fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
+                 int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
+                 hipStream_t s);
+// second pass only: quantize already-rotated rows r (dynamic: amax_ws holds the max)
+fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
+                           int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
+                           float* scale_out, hipStream_t s);
+
+struct GemmEpilogue {
+    int32_t* acc = nullptr;
+    int64_t ld_acc = 0;
+    float* out = nullptr;
+    int64_t ld_out = 0;
+    const float* s_a = nullptr;
+    const float* s_b = nullptr;
+    const float* resid = nullptr;  // out = resid + acc * s (pre-norm residual stacks)
+    int64_t ld_resid = 0;
+    float* amax = nullptr;         // max |out| over columns [amax_c0, amax_c1)
+    int64_t amax_c0 = 0, amax_c1 = 0;
+};
+fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
+                   const GemmEpilogue& ep, hipStream_t s);
+
+// conv: quantize xBC, conv, SiLU.  Dynamic: writes Q.16 activations to s16 and
+// accumulates part maxima into amax_q16[3]; static (p given): writes codes directly.
+struct ConvArgs {
+    const float* xbc;
+    int64_t xbc_stride;
+    int64_t batch, len, d_inner, dstate;
+    const int8_t* w_q;
+    const int32_t* p_w;
+    const int32_t* b_q16;
+    const float* xbc_amax;     // dynamic: device max |xBC| (from the GEMM epilogue or a pass)
+    const int32_t* p_fixed;    // static: device int32[4]
+    const int8_t* state_in;
+    int8_t* state_out;
+    int8_t* xbc_q;
+    int32_t* s16;              // dynamic: [T, ch] Q.16 SiLU outputs
+    int32_t* amax_q16;         // dynamic: [3] zeroed before
+    int8_t* x_out;
+    int8_t* b_out;
+    int8_t* c_out;
+    int32_t* p_out;            // [4]
+    int32_t* amax_stats;       // nullable [4]
+};
+fm_status conv_run(const ConvArgs& a, hipStream_t s);
+fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t stride,
+                           float* amax, hipStream_t s);
+
+struct ScanArgs {
+    const int8_t* x;
+    const int8_t* bm;
+    const int8_t* cm;
+    const float* dt_raw;
+    int64_t dt_stride;
+    const float* dt_bias;
+    const int32_t* a_q16;
+    const int32_t* d_q16;
+    const int32_t* p;
+    int64_t batch, len, nheads, headdim, dstate;
+    const int32_t* state_in;
+    int32_t* state_out;
+    int32_t* y;
+    int32_t* dt_out;
+    int32_t* da_out;
+};
+fm_status scan_run(const ScanArgs& a, hipStream_t s);
+
+struct GateArgs {
+    const int32_t* y;
+    const float* z;
+    int64_t z_stride;
+    const int32_t* p;
+    const float* norm_w;
+    int64_t rows, d_inner;
+    fm_scale_mode mode;
+    int32_t scoe, sshift;
+    int8_t* q;
+    float* scale_out;
+    float* amax_stats;
+    float* normed_out;
+    float* rot_ws;     // dynamic: [rows, d_inner] rotated values between passes
+    float* amax_ws;    // dynamic: 1 float
+};
+fm_status gate_run(const GateArgs& a, hipStream_t s);
+
+// layer pipeline (fm_layer.hip)
+size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);
+void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t);
+void set_keep_intermediates(bool on);
+void set_timing_events(void* start, void* stop);
+fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
+                    const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
+                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s);
+fm_status prepare_run(const fm_layer_desc* d, const float* w_in, const float* w_out,
+                      const float* conv_w, const float* conv_b, const float* a, const float* dv,
+                      int8_t* w_in_q, float* s_w_in, int8_t* w_out_q, float* s_w_out,
+                      int8_t* conv_w_q, int32_t* conv_p_w, int32_t* conv_b_q16, int32_t* a_q16,
+                      int32_t* d_q16, void* ws, hipStream_t s);
+
+// pre-norm of the residual stream: n = RMSNorm(h) (weight 1, fixed order)
+fm_status rmsnorm_rows_run(const float* h, int64_t rows, int64_t d, float* out, hipStream_t s);
+
+}  // namespace fm

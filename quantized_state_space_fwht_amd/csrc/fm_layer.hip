@@ -1,0 +1,321 @@
+// The quantized Mamba2 mixer layer (Fig. 2 flow of the FastMamba paper:
+// in_proj -> conv1d + SiLU -> SSM -> gated RMSNorm -> out_proj) assembled from
+// the step kernels, plus the offline parameter preparation.
+//
+// Every step runs on the device; the dynamic scales and exponents flow from
+// kernel to kernel through a small block at the head of the workspace and
+// are never copied to the host.
+#include "fm_internal.hpp"
+
+namespace fm {
+
+// small per-call block at the head of the layer workspace (32-bit words)
+enum SmallSlot {
+    kAmaxU = 0,    // float: max |u H|
+    kAmaxG = 1,    // float: max |n H|
+    kAmaxXbc = 2,  // float: max |xBC|
+    kAmaxQ = 3,    // int[3]: max |x|, |B|, |C| in Q.16
+    kScaleU = 6,   // float: in_proj input dequant scale
+    kScaleG = 7,   // float: out_proj input dequant scale
+    kP = 8,        // int[4]: p_c, p_x, p_B, p_C
+    kSmallWords = 16
+};
+
+struct LayerWs {
+    uint32_t* small;
+    float* un;       // pre-norm output [T, dm]
+    int8_t* u_q;     // [T, dm]
+    float* v;        // [T, dip]
+    int8_t* xbc_q;   // [T, ch]
+    int32_t* s16;    // [T, ch]
+    int8_t* x_q;     // [T, di]
+    int8_t* b_q;     // [T, N]
+    int8_t* c_q;     // [T, N]
+    int32_t* y;      // [T, di]
+    float* rot;      // [T, di]
+    float* normed;   // [T, di]
+    int8_t* g_q;     // [T, di]
+    int32_t* dt;     // [T, H]
+    int32_t* da;     // [T, H]
+    size_t bytes;
+};
+
+static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void* base) {
+    const int64_t T = batch * len;
+    const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads;
+    const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
+    Arena ar(base);
+    LayerWs w;
+    w.small = ar.take<uint32_t>(kSmallWords);
+    w.un = ar.take<float>((size_t)T * dm);
+    w.u_q = ar.take<int8_t>((size_t)T * dm);
+    w.v = ar.take<float>((size_t)T * dip);
+    w.xbc_q = ar.take<int8_t>((size_t)T * ch);
+    w.s16 = ar.take<int32_t>((size_t)T * ch);
+    w.x_q = ar.take<int8_t>((size_t)T * di);
+    w.b_q = ar.take<int8_t>((size_t)T * N);
+    w.c_q = ar.take<int8_t>((size_t)T * N);
+    w.y = ar.take<int32_t>((size_t)T * di);
+    w.rot = ar.take<float>((size_t)T * di);
+    w.normed = ar.take<float>((size_t)T * di);
+    w.g_q = ar.take<int8_t>((size_t)T * di);
+    w.dt = ar.take<int32_t>((size_t)T * H);
+    w.da = ar.take<int32_t>((size_t)T * H);
+    w.bytes = ar.used;
+    return w;
+}
+
+size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len) {
+    return layer_ws(d, batch, len, nullptr).bytes;
+}
+
+void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t) {
+    LayerWs w = layer_ws(d, batch, len, nullptr);
+    auto off = [](const void* p) { return (size_t)(uintptr_t)p; };
+    t->u_q = off(w.u_q);
+    t->v = off(w.v);
+    t->xbc_q = off(w.xbc_q);
+    t->x_q = off(w.x_q);
+    t->b_q = off(w.b_q);
+    t->c_q = off(w.c_q);
+    t->y = off(w.y);
+    t->g_q = off(w.g_q);
+    t->normed = off(w.normed);
+    t->dt = off(w.dt);
+    t->da = off(w.da);
+}
+
+static bool g_keep = false;
+void set_keep_intermediates(bool on) { g_keep = on; }
+
+static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+void set_timing_events(void* start, void* stop) {
+    g_ev_start = (hipEvent_t)start;
+    g_ev_stop = (hipEvent_t)stop;
+}
+
+// zero the small block; optionally load the exponents (static values or a device copy)
+__global__ void layer_setup_kernel(uint32_t* small, const int32_t* p_src, int p0, int p1, int p2,
+                                   int p3, int how) {
+    const int i = threadIdx.x;
+    if (i < kSmallWords) small[i] = 0u;
+    __syncthreads();
+    if (i == 0 && how != 0) {
+        int32_t* p = (int32_t*)(small + kP);
+        if (how == 1) {
+            p[0] = p0;
+            p[1] = p1;
+            p[2] = p2;
+            p[3] = p3;
+        } else {
+            for (int k = 0; k < 4; ++k) p[k] = p_src[k];
+        }
+    }
+}
+
+// publish what the call used into qp (and the frozen exponents into the cache)
+__global__ void layer_finalize_kernel(const uint32_t* small, fm_qparams* qp, int32_t* cache_p) {
+    if (threadIdx.x != 0) return;
+    const int32_t* p = (const int32_t*)(small + kP);
+    qp->scale[0] = __uint_as_float(small[kScaleU]);
+    qp->scale[1] = __uint_as_float(small[kScaleG]);
+    for (int k = 0; k < 4; ++k) qp->p[k] = p[k];
+    if (cache_p)
+        for (int k = 0; k < 4; ++k) cache_p[k] = p[k];
+    atomicMax((unsigned int*)&qp->stat_amax[0], small[kAmaxU]);
+    atomicMax((unsigned int*)&qp->stat_amax[1], small[kAmaxG]);
+    atomicMax((unsigned int*)&qp->stat_amax[2], small[kAmaxXbc]);
+    for (int k = 0; k < 3; ++k) atomicMax(&qp->stat_amax_q16[k], (int32_t)small[kAmaxQ + k]);
+}
+
+// Shared body of prefill (len tokens, fresh state) and decode (len = 1, cache).
+fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
+                    const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
+                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s) {
+    const int64_t T = batch * len;
+    const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads, P = d->headdim;
+    const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
+    const fm_scale_mode mode = (fm_scale_mode)d->mode;
+    const bool stat = mode == FM_SCALE_STATIC;
+    LayerWs w = layer_ws(d, batch, len, workspace);
+    fm_status st;
+    float* small_f = (float*)w.small;
+    int32_t* small_i = (int32_t*)w.small;
+    int32_t* pdev = small_i + kP;
+
+    // 0. setup: zero the per-call block, load exponents (static values or the cache's)
+    if (decode)
+        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, cache->p, 0, 0, 0, 0, 2);
+    else if (stat)
+        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, sp->p[0], sp->p[1], sp->p[2],
+                                            sp->p[3], 1);
+    else
+        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, 0, 0, 0, 0, 0);
+    if ((st = check_launch("layer_setup_kernel")) != FM_OK) return st;
+
+    // 1. (stacks) pre-norm of the residual stream
+    const float* xin = u;
+    if (d->prenorm_residual) {
+        if ((st = rmsnorm_rows_run(u, T, dm, w.un, s)) != FM_OK) return st;
+        xin = w.un;
+    }
+    // 2. rotate + quantize the in_proj input
+    if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0, w.u_q,
+                     small_f + kScaleU, stat ? small_f + kAmaxU : nullptr, small_f + kAmaxU, s)) !=
+        FM_OK)
+        return st;
+    // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
+    {
+        GemmEpilogue ep;
+        ep.out = w.v;
+        ep.ld_out = dip;
+        ep.s_a = small_f + kScaleU;
+        ep.s_b = W->s_w_in;
+        ep.amax = small_f + kAmaxXbc;
+        ep.amax_c0 = di;
+        ep.amax_c1 = di + ch;
+        if ((st = gemm_run(w.u_q, W->w_in_q, T, dip, dm, ep, s)) != FM_OK) return st;
+    }
+    // 4-5. conv1d + SiLU + requant of x / B / C
+    {
+        ConvArgs a{};
+        a.xbc = w.v + di;
+        a.xbc_stride = dip;
+        a.batch = batch;
+        a.len = len;
+        a.d_inner = di;
+        a.dstate = N;
+        a.w_q = W->conv_w_q;
+        a.p_w = W->conv_p_w;
+        a.b_q16 = W->conv_b_q16;
+        a.xbc_amax = small_f + kAmaxXbc;
+        const bool fixed_p = stat || decode;
+        a.p_fixed = fixed_p ? pdev : nullptr;
+        a.state_in = decode ? cache->conv_state : nullptr;
+        a.state_out = cache ? cache->conv_state : nullptr;
+        a.xbc_q = g_keep ? w.xbc_q : nullptr;
+        a.s16 = w.s16;
+        a.amax_q16 = small_i + kAmaxQ;
+        a.x_out = w.x_q;
+        a.b_out = w.b_q;
+        a.c_out = w.c_q;
+        a.p_out = pdev;
+        // with fixed exponents the conv kernel records the maxima itself (calibration stats)
+        a.amax_stats = fixed_p ? small_i + kAmaxXbc : nullptr;
+        if ((st = conv_run(a, s)) != FM_OK) return st;
+    }
+    // 6-7. dt / decay and the scan
+    {
+        ScanArgs a{};
+        a.x = w.x_q;
+        a.bm = w.b_q;
+        a.cm = w.c_q;
+        a.dt_raw = w.v + di + ch;
+        a.dt_stride = dip;
+        a.dt_bias = W->dt_bias;
+        a.a_q16 = W->a_q16;
+        a.d_q16 = W->d_q16;
+        a.p = pdev;
+        a.batch = batch;
+        a.len = len;
+        a.nheads = H;
+        a.headdim = P;
+        a.dstate = N;
+        a.state_in = decode ? cache->ssm_state : nullptr;
+        a.state_out = cache ? cache->ssm_state : nullptr;
+        a.y = w.y;
+        a.dt_out = g_keep ? w.dt : nullptr;
+        a.da_out = g_keep ? w.da : nullptr;
+        hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+        g_ev_start = g_ev_stop = nullptr;
+        if (ev0 && hipEventRecord(ev0, s) != hipSuccess)
+            return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
+        if ((st = scan_run(a, s)) != FM_OK) return st;
+        if (ev1 && hipEventRecord(ev1, s) != hipSuccess)
+            return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
+    }
+    // 8. gate + RMSNorm + rotate + quantize the out_proj input
+    {
+        GateArgs g{};
+        g.y = w.y;
+        g.z = w.v;
+        g.z_stride = dip;
+        g.p = pdev;
+        g.norm_w = W->norm_w;
+        g.rows = T;
+        g.d_inner = di;
+        g.mode = mode;
+        g.scoe = stat ? sp->scoe[1] : 0;
+        g.sshift = stat ? sp->sshift[1] : 0;
+        g.q = w.g_q;
+        g.scale_out = small_f + kScaleG;
+        g.amax_stats = stat ? small_f + kAmaxG : nullptr;
+        g.normed_out = g_keep ? w.normed : nullptr;
+        g.rot_ws = w.rot;
+        g.amax_ws = small_f + kAmaxG;
+        if ((st = gate_run(g, s)) != FM_OK) return st;
+    }
+    // 9. out_proj W8A8 (+ residual for stacks)
+    {
+        GemmEpilogue ep;
+        ep.out = out;
+        ep.ld_out = dm;
+        ep.s_a = small_f + kScaleG;
+        ep.s_b = W->s_w_out;
+        if (d->prenorm_residual) {
+            ep.resid = u;
+            ep.ld_resid = dm;
+        }
+        if ((st = gemm_run(w.g_q, W->w_out_q, T, dm, di, ep, s)) != FM_OK) return st;
+    }
+    layer_finalize_kernel<<<1, 64, 0, s>>>(w.small, qp, (cache && !decode) ? cache->p : nullptr);
+    return check_launch("layer_finalize_kernel");
+}
+
+// ---------------------------------------------------------------- preparation
+__global__ void prep_conv_kernel(const float* __restrict__ w, const float* __restrict__ b,
+                                 int64_t ch, int8_t* w_q, int32_t* p_w, int32_t* b_q16) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= ch) return;
+    float m = 0.0f;
+    for (int k = 0; k < 4; ++k) m = fmaxf(m, fabsf(w[c * 4 + k]));
+    const int p = pot_from_f32(m);
+    const float sc = ldexpf(1.0f, p);
+    for (int k = 0; k < 4; ++k)
+        w_q[c * 4 + k] = (int8_t)fminf(fmaxf(rintf(w[c * 4 + k] * sc), -127.0f), 127.0f);
+    p_w[c] = p;
+    b_q16[c] = f2i_sat(rintf(b[c] * 65536.0f));
+}
+
+__global__ void prep_q16_kernel(const float* __restrict__ a, const float* __restrict__ dv,
+                                int64_t h, int32_t* a_q16, int32_t* d_q16) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= h) return;
+    a_q16[i] = f2i_sat(rintf(a[i] * 65536.0f));
+    d_q16[i] = f2i_sat(rintf(dv[i] * 65536.0f));
+}
+
+fm_status prepare_run(const fm_layer_desc* d, const float* w_in, const float* w_out,
+                      const float* conv_w, const float* conv_b, const float* a, const float* dv,
+                      int8_t* w_in_q, float* s_w_in, int8_t* w_out_q, float* s_w_out,
+                      int8_t* conv_w_q, int32_t* conv_p_w, int32_t* conv_b_q16, int32_t* a_q16,
+                      int32_t* d_q16, void* ws, hipStream_t s) {
+    const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads;
+    const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
+    float* amax = (float*)ws;
+    fm_status st;
+    if ((st = zero_words(amax, 2, s)) != FM_OK) return st;
+    if ((st = hq_run(w_in, dip, dm, FM_SCALE_DYNAMIC, 0, 0, w_in_q, s_w_in, nullptr, amax, s)) !=
+        FM_OK)
+        return st;
+    if ((st = hq_run(w_out, dm, di, FM_SCALE_DYNAMIC, 0, 0, w_out_q, s_w_out, nullptr, amax + 1,
+                     s)) != FM_OK)
+        return st;
+    prep_conv_kernel<<<(unsigned)((ch + 255) / 256), 256, 0, s>>>(conv_w, conv_b, ch, conv_w_q,
+                                                                 conv_p_w, conv_b_q16);
+    if ((st = check_launch("prep_conv_kernel")) != FM_OK) return st;
+    prep_q16_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(a, dv, H, a_q16, d_q16);
+    return check_launch("prep_q16_kernel");
+}
+
+}  // namespace fm

@@ -1,0 +1,187 @@
+"""Device-memory owners around the C-ABI: one mixer layer, and pre-norm stacks.
+
+These classes allocate torch device tensors (weights, caches, workspaces) and
+call libfm.so; they compute nothing themselves.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .configs import LayerShape
+
+
+def _dev(a, dtype=None, device="cuda"):
+    t = torch.as_tensor(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device).contiguous()
+
+
+class Mamba2Layer:
+    """One quantized mixer layer with prepared weights, a workspace and a cache."""
+
+    def __init__(self, shape: LayerShape, params: dict, mode: str = "dynamic",
+                 prenorm_residual: bool = False, device="cuda", stream=None):
+        s = shape
+        self.shape = s
+        self.device = device
+        self.desc = B.LayerDesc(s.d_model, s.d_inner, s.nheads, s.headdim, s.dstate, s.d_conv,
+                                B.STATIC if mode == "static" else B.DYNAMIC,
+                                1 if prenorm_residual else 0)
+        self.static = None
+        f32 = torch.float32
+        w_in = _dev(params["w_in"], f32, device)
+        w_out = _dev(params["w_out"], f32, device)
+        conv_w = _dev(params["conv_w"], f32, device)
+        conv_b = _dev(params["conv_b"], f32, device)
+        A = _dev(params["A"], f32, device)
+        D = _dev(params["D"], f32, device)
+        ch, dip, H = s.conv_ch, s.d_in_proj, s.nheads
+        t = {}
+        t["w_in_q"] = torch.empty((dip, s.d_model), dtype=torch.int8, device=device)
+        t["s_w_in"] = torch.empty(1, dtype=f32, device=device)
+        t["w_out_q"] = torch.empty((s.d_model, s.d_inner), dtype=torch.int8, device=device)
+        t["s_w_out"] = torch.empty(1, dtype=f32, device=device)
+        t["conv_w_q"] = torch.empty((ch, 4), dtype=torch.int8, device=device)
+        t["conv_p_w"] = torch.empty(ch, dtype=torch.int32, device=device)
+        t["conv_b_q16"] = torch.empty(ch, dtype=torch.int32, device=device)
+        t["a_q16"] = torch.empty(H, dtype=torch.int32, device=device)
+        t["d_q16"] = torch.empty(H, dtype=torch.int32, device=device)
+        t["dt_bias"] = _dev(params["dt_bias"], f32, device)
+        t["norm_w"] = _dev(params["norm_w"], f32, device)
+        ws = B.workspace(B.lib.fm_prepare_layer_workspace_size(ctypes.byref(self.desc)), device)
+        B._check(B.lib.fm_prepare_layer(
+            ctypes.byref(self.desc), w_in.data_ptr(), w_out.data_ptr(), conv_w.data_ptr(),
+            conv_b.data_ptr(), A.data_ptr(), D.data_ptr(), t["w_in_q"].data_ptr(),
+            t["s_w_in"].data_ptr(), t["w_out_q"].data_ptr(), t["s_w_out"].data_ptr(),
+            t["conv_w_q"].data_ptr(), t["conv_p_w"].data_ptr(), t["conv_b_q16"].data_ptr(),
+            t["a_q16"].data_ptr(), t["d_q16"].data_ptr(), ws.data_ptr(), ws.numel(),
+            B._stream(stream)))
+        self.t = t
+        self.weights = B.LayerWeights(*(t[n].data_ptr() for n in (
+            "w_in_q", "s_w_in", "w_out_q", "s_w_out", "conv_w_q", "conv_p_w", "conv_b_q16",
+            "dt_bias", "a_q16", "d_q16", "norm_w")))
+        self.qp = torch.zeros(B.QPARAMS_BYTES, dtype=torch.uint8, device=device)
+        self._ws = None
+        self._ws_key = None
+        self.cache = None
+
+    # ------------------------------------------------------------ memory
+    def workspace_for(self, batch, length):
+        need = B.lib.fm_mamba2_layer_workspace_size(ctypes.byref(self.desc), batch, length)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = B.workspace(need, self.device)
+        self._ws_key = (batch, length)
+        return self._ws
+
+    def alloc_cache(self, batch):
+        s = self.shape
+        self.cache_t = {
+            "conv_state": torch.zeros((batch, s.conv_ch, 3), dtype=torch.int8, device=self.device),
+            "ssm_state": torch.zeros((batch, s.nheads, s.headdim, s.dstate), dtype=torch.int32,
+                                     device=self.device),
+            "p": torch.zeros(4, dtype=torch.int32, device=self.device),
+        }
+        self.cache = B.Cache(self.cache_t["conv_state"].data_ptr(),
+                             self.cache_t["ssm_state"].data_ptr(), self.cache_t["p"].data_ptr())
+        return self.cache
+
+    def set_static(self, sp: "B.StaticParams"):
+        self.static = sp
+        self.desc.mode = B.STATIC
+
+    def set_dynamic(self):
+        self.desc.mode = B.DYNAMIC
+
+    def reset_stats(self):
+        self.qp.zero_()
+
+    def qparams(self) -> "B.QParams":
+        return B.qparams_from_device(self.qp)
+
+    # ------------------------------------------------------------ calls
+    def prefill(self, u, out=None, with_cache=True, stream=None):
+        """u [batch, len, d_model] float32 device tensor -> out (same shape)."""
+        batch, length, dm = u.shape
+        if out is None:
+            out = torch.empty_like(u)
+        ws = self.workspace_for(batch, length)
+        cache = None
+        if with_cache:
+            if self.cache is None or self.cache_t["ssm_state"].shape[0] != batch:
+                self.alloc_cache(batch)
+            cache = ctypes.byref(self.cache)
+        sp = ctypes.byref(self.static) if self.static is not None else None
+        B._check(B.lib.fm_mamba2_layer_prefill(
+            ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u.data_ptr(), batch, length,
+            out.data_ptr(), cache, self.qp.data_ptr(), ws.data_ptr(), ws.numel(),
+            B._stream(stream)))
+        return out
+
+    def decode(self, u_t, out=None, stream=None):
+        """u_t [batch, d_model] -> out_t, advancing the cache by one token."""
+        batch, dm = u_t.shape
+        if out is None:
+            out = torch.empty_like(u_t)
+        ws = self.workspace_for(batch, 1)
+        sp = ctypes.byref(self.static) if self.static is not None else None
+        B._check(B.lib.fm_mamba2_layer_decode(
+            ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u_t.data_ptr(), batch,
+            ctypes.byref(self.cache), out.data_ptr(), self.qp.data_ptr(), ws.data_ptr(),
+            ws.numel(), B._stream(stream)))
+        return out
+
+    def taps(self, batch, length):
+        t = B.LayerTaps()
+        B._check(B.lib.fm_mamba2_layer_taps(ctypes.byref(self.desc), batch, length,
+                                            ctypes.byref(t)))
+        return t
+
+    def tap(self, name, dtype, shape):
+        """View of an intermediate the last call left in the workspace."""
+        batch, length = self._ws_key
+        off = getattr(self.taps(batch, length), name)
+        n = int(np.prod(shape))
+        itemsize = torch.tensor([], dtype=dtype).element_size()
+        raw = self._ws[off:off + n * itemsize]
+        return raw.view(dtype).view(*shape)
+
+
+class Mamba2Stack:
+    """Pre-norm residual stack: h <- h + layer(RMSNorm(h)) per layer."""
+
+    def __init__(self, shape: LayerShape, params_list, mode="dynamic", device="cuda"):
+        self.layers = [Mamba2Layer(shape, p, mode, prenorm_residual=True, device=device)
+                       for p in params_list]
+        self.shape = shape
+
+    def prefill(self, u, with_cache=True, stream=None):
+        h = u.contiguous()
+        bufs = [torch.empty_like(h), torch.empty_like(h)]
+        for i, layer in enumerate(self.layers):
+            nxt = bufs[i % 2]
+            layer.prefill(h, out=nxt, with_cache=with_cache, stream=stream)
+            h = nxt
+        return h
+
+    def decode(self, u_t, stream=None):
+        h = u_t.contiguous()
+        bufs = [torch.empty_like(h), torch.empty_like(h)]
+        for i, layer in enumerate(self.layers):
+            nxt = bufs[i % 2]
+            layer.decode(h, out=nxt, stream=stream)
+            h = nxt
+        return h
+
+    def calibrate(self, inputs):
+        """Dynamic passes over `inputs` (list of [B, L, dm] device tensors), then static."""
+        for layer in self.layers:
+            layer.set_dynamic()
+            layer.static = None
+            layer.reset_stats()
+        for u in inputs:
+            self.prefill(u, with_cache=False)
+        for layer in self.layers:
+            layer.set_static(B.fm_qparams_from_stats(layer.qparams()))
