@@ -174,15 +174,39 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
  * p: device int32[4] = (p_c, p_x, p_B, p_C) (only p_B + p_C is used);
  * state_in / state_out [batch, nheads, headdim, dstate] int32 (NULL: zeros
  *   / not written); y [batch, len, nheads, headdim] int32;
- * dt_out, da_out [batch, len, nheads] int32 Q.16 (NULL to skip).
- * headdim % 4 == 0, dstate in {64, 128, 256}, len >= 1.
+ * dt_out, da_out [batch, len, nheads] int32 Q.16 (required: dt and the decay
+ *   are computed for every token first, then read by the scan).
+ * headdim % 8 == 0, dstate in {64, 128}, len >= 1; y 16-byte and bm / cm
+ * 4-byte aligned.  Workspace: fm_ssm_scan_pot_workspace_size() bytes (the
+ * per-step float64 scalars of the prologue).
  * ---------------------------------------------------------------------- */
+size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t nheads,
+                                      int64_t headdim);
 fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
                           const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
                           const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
                           int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
                           int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
-                          int32_t* dt_out, int32_t* da_out, hipStream_t stream);
+                          int32_t* dt_out, int32_t* da_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fm_nau_eval — the nonlinear approximation unit elementwise, Q.16 in and
+ * out (review page "What carries the argument": an 8-segment first-order
+ * approximation of 2^v, e^x = 2^(x log2 e), SoftPlus(x) = x + SoftPlus(-x);
+ * Eq. (5), Section III-B.2):
+ *   2^(v/2^16), v <= 0: n = v >> 16, f = v & 0xFFFF, i = f >> 13, r = f & 0x1FFF,
+ *       m = Y[i] + rshr((Y[i+1] - Y[i]) * r, 13), result rshr(m, 14 - n),
+ *       Y[i] = rint(2^(i/8) * 2^30)
+ *   FM_NAU_EXP:      e^x = 2^(rshr(x * rint(log2(e) * 2^30), 30)), x <= 0
+ *                    (inputs > 0 are treated as 0)
+ *   FM_NAU_SOFTPLUS: e^(-|x|) + max(x, 0), saturated to int32
+ *   FM_NAU_SILU:     x <= 0: rshr(x * floor(E*2^16 / (2^16 + E)), 16), E = e^x;
+ *                    x > 0: x + SiLU(-x)
+ * x, y [n] int32 (y may alias x); n >= 0.
+ * ---------------------------------------------------------------------- */
+typedef enum fm_nau_fn { FM_NAU_EXP = 0, FM_NAU_SOFTPLUS = 1, FM_NAU_SILU = 2 } fm_nau_fn;
+fm_status fm_nau_eval(fm_nau_fn fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fm_gate_norm_quant — output gate, gated RMSNorm and the out_proj input

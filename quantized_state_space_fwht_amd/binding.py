@@ -80,9 +80,11 @@ _SIGS = {
     "fm_conv1d_pot": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp,
                                      ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _c_sz, _vp]),
+    "fm_ssm_scan_pot_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fm_ssm_scan_pot": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _vp, _c_i64,
                                        _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
-                                       _vp]),
+                                       _vp, _c_sz, _vp]),
+    "fm_nau_eval": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _c_i64, _vp]),
     "fm_gate_norm_quant_workspace_size": (_c_sz, [_c_i64, _c_i64]),
     "fm_gate_norm_quant": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, _vp, _c_i64, _c_i64,
                                           ctypes.c_int, _c_i32, _c_i32, _vp, _vp, _vp, _vp, _vp,
@@ -169,11 +171,15 @@ def fm_conv1d_pot(xbc, row_stride, batch, length, d_inner, dstate, w_q, p_w, b_q
 
 def fm_ssm_scan_pot(x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p, batch, length,
                     nheads, headdim, dstate, state_in, state_out, y, dt_out=None, da_out=None,
-                    stream=None):
+                    ws=None, stream=None):
+    if ws is None:
+        ws = workspace(lib.fm_ssm_scan_pot_workspace_size(batch, length, nheads, headdim),
+                       y.device)
     _check(lib.fm_ssm_scan_pot(_ptr(x), _ptr(bm), _ptr(cm), dt_raw.data_ptr(), dt_row_stride,
                                _ptr(dt_bias), _ptr(a_q16), _ptr(d_q16), _ptr(p), batch, length,
                                nheads, headdim, dstate, _ptr(state_in), _ptr(state_out), _ptr(y),
-                               _ptr(dt_out), _ptr(da_out), _stream(stream)))
+                               _ptr(dt_out), _ptr(da_out), _ptr(ws), ws.numel(),
+                               _stream(stream)))
 
 
 def fm_gate_norm_quant(y, z, z_row_stride, p, norm_w, rows, d_inner, mode, scoe, sshift, q,
@@ -184,6 +190,13 @@ def fm_gate_norm_quant(y, z, z_row_stride, p, norm_w, rows, d_inner, mode, scoe,
                                   rows, d_inner, mode, scoe, sshift, _ptr(q), _ptr(scale_out),
                                   _ptr(amax_stats), _ptr(normed_out), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+NAU_EXP, NAU_SOFTPLUS, NAU_SILU = 0, 1, 2
+
+
+def fm_nau_eval(fn, x, y, stream=None):
+    _check(lib.fm_nau_eval(fn, _ptr(x), _ptr(y), x.numel(), _stream(stream)))
 
 
 def fm_qparams_from_stats(qp_host: QParams) -> StaticParams:

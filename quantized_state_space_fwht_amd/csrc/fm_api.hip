@@ -238,22 +238,31 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
 }
 
 // ---------------------------------------------------------------- fm_ssm_scan_pot
+size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t nheads,
+                                      int64_t headdim) {
+    if (batch < 0 || len < 0 || nheads < 0 || headdim < 0) return 0;
+    return scan_ws_bytes(batch, len, nheads, headdim);
+}
+
 fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
                           const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
                           const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
                           int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
                           int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
-                          int32_t* dt_out, int32_t* da_out, hipStream_t stream) {
+                          int32_t* dt_out, int32_t* da_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
     const char* who = "fm_ssm_scan_pot";
     g_err[0] = 0;
-    if (!x || !bm || !cm || !dt_raw || !dt_bias || !a_q16 || !d_q16 || !p || !y)
+    if (!x || !bm || !cm || !dt_raw || !dt_bias || !a_q16 || !d_q16 || !p || !y || !dt_out ||
+        !da_out)
         return fail(FM_ERR_NULL, "%s: a required pointer is NULL", who);
-    if (batch < 1 || len < 1 || nheads < 1 || headdim < 4 || headdim % 4 ||
-        (dstate != 64 && dstate != 128 && dstate != 256) || batch > 65535 || nheads > 65535 ||
-        headdim / 4 > 65535)
-        return fail(FM_ERR_SHAPE, "%s: need headdim %% 4 == 0, dstate in {64,128,256}", who);
+    if (batch < 1 || len < 1 || nheads < 1 || headdim < 8 || headdim % 8 ||
+        (dstate != 64 && dstate != 128) || batch > 65535 || nheads > 65535 ||
+        batch * len * nheads >= ((int64_t)1 << 31) || batch * len * nheads * headdim >= ((int64_t)1 << 40))
+        return fail(FM_ERR_SHAPE, "%s: need headdim %% 8 == 0, dstate in {64, 128}", who);
     if (dt_row_stride < nheads) return fail(FM_ERR_SHAPE, "%s: dt row stride < nheads", who);
-    if (!aligned(y, 16)) return fail(FM_ERR_SHAPE, "%s: y must be 16-byte aligned", who);
+    if (!aligned(y, 16) || !aligned(bm, 4) || !aligned(cm, 4))
+        return fail(FM_ERR_SHAPE, "%s: y must be 16-byte, bm / cm 4-byte aligned", who);
     ScanArgs a{};
     a.x = x;
     a.bm = bm;
@@ -274,7 +283,21 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
     a.y = y;
     a.dt_out = dt_out;
     a.da_out = da_out;
-    return scan_run(a, stream);
+    fm_status st = check_ws(workspace, workspace_bytes,
+                            scan_ws_bytes(batch, len, nheads, headdim), who);
+    if (st != FM_OK) return st;
+    return scan_run(a, workspace, stream);
+}
+
+// ---------------------------------------------------------------- fm_nau_eval
+fm_status fm_nau_eval(fm_nau_fn fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t stream) {
+    const char* who = "fm_nau_eval";
+    g_err[0] = 0;
+    if (fn != FM_NAU_EXP && fn != FM_NAU_SOFTPLUS && fn != FM_NAU_SILU)
+        return fail(FM_ERR_MODE, "%s: bad function %d", who, (int)fn);
+    if (n < 0) return fail(FM_ERR_SHAPE, "%s: n < 0", who);
+    if (n > 0 && (!x || !y)) return fail(FM_ERR_NULL, "%s: x or y is NULL", who);
+    return nau_run((int)fn, x, y, n, stream);
 }
 
 // ---------------------------------------------------------------- fm_gate_norm_quant

@@ -29,19 +29,13 @@ __device__ __forceinline__ int8_t quant_xbc(float v, float scale) {
 // Dynamic: writes Q.16 SiLU outputs + per-part maxima.  Static: writes codes.
 __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
-    __shared__ int sp[4];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) {
-        if (K.dynamic) {
-            sp[0] = pot_from_f32(*A.xbc_amax);
-            sp[1] = sp[2] = sp[3] = 0;
-        } else {
-            for (int i = 0; i < 4; ++i) sp[i] = A.p_fixed[i];
-        }
-        if (!K.dynamic && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
-            for (int i = 0; i < 4; ++i) A.p_out[i] = sp[i];
-    }
+    __shared__ NauLds tab;
+    nau_lds_init(tab);
     __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p_c = K.dynamic ? pot_from_f32(*A.xbc_amax) : A.p_fixed[0];
+    if (!K.dynamic && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 4)
+        A.p_out[threadIdx.x] = A.p_fixed[threadIdx.x];
     const int c = blockIdx.x * 64 + lane;
     const int64_t b = blockIdx.z;
     const int64_t L = A.len;
@@ -51,15 +45,22 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     int32_t amax = 0;
     float xmax = 0.0f;
     if (t0 < L) {
-        const int p_c = sp[0];
         const float qscale = ldexpf(1.0f, p_c);
         const int32_t w0 = A.w_q[c * 4 + 0], w1 = A.w_q[c * 4 + 1], w2 = A.w_q[c * 4 + 2],
                       w3 = A.w_q[c * 4 + 3];
         const int sh = p_c + A.p_w[c] - 16;
         const int64_t bias = A.b_q16[c];
-        const int p_part = sp[1 + part];
+        const int p_part = K.dynamic ? 0 : A.p_fixed[1 + part];
         const float* xrow = A.xbc + (b * L) * A.xbc_stride + c;
-        int32_t xm3, xm2, xm1;  // inputs at t-3, t-2, t-1
+        const int n = (int)(t0 + kConvTL < L ? kConvTL : L - t0);
+        // issue every load of this run (3 window inputs + kConvTL new ones) up front
+        float win[3];
+        float xv[kConvTL];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) win[j] = t0 > 0 ? xrow[(t0 - 3 + j) * A.xbc_stride] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kConvTL; ++i) xv[i] = i < n ? xrow[(t0 + i) * A.xbc_stride] : 0.0f;
+        int32_t xm3, xm2, xm1;  // codes at t-3, t-2, t-1
         if (t0 == 0) {
             if (A.state_in) {
                 const int8_t* st = A.state_in + (b * K.ch + c) * 3;
@@ -70,35 +71,37 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
                 xm3 = xm2 = xm1 = 0;
             }
         } else {  // t0 >= kConvTL >= 3: the window lies inside this call's input
-            xm3 = quant_xbc(xrow[(t0 - 3) * A.xbc_stride], qscale);
-            xm2 = quant_xbc(xrow[(t0 - 2) * A.xbc_stride], qscale);
-            xm1 = quant_xbc(xrow[(t0 - 1) * A.xbc_stride], qscale);
+            xm3 = quant_xbc(win[0], qscale);
+            xm2 = quant_xbc(win[1], qscale);
+            xm1 = quant_xbc(win[2], qscale);
         }
-        const int64_t t1 = t0 + kConvTL < L ? t0 + kConvTL : L;
-        for (int64_t t = t0; t < t1; ++t) {
-            const float xv = xrow[t * A.xbc_stride];
-            xmax = fmaxf(xmax, fabsf(xv));
-            const int32_t xq = quant_xbc(xv, qscale);
-            const int64_t row = b * L + t;
-            if (A.xbc_q) A.xbc_q[row * K.ch + c] = (int8_t)xq;
-            const int64_t acc = (int64_t)(w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq);
-            const int32_t a = sat32(rshr(acc, sh) + bias);
-            const int32_t s = nau_silu(a);
-            const int32_t sa = s < 0 ? -s : s;
-            amax = sa > amax ? sa : amax;
-            if (K.dynamic) {
-                A.s16[row * K.ch + c] = s;
-            } else {
-                const int8_t code = sat8(rshr((int64_t)s, 16 - p_part));
-                if (part == 0) A.x_out[row * di + c] = code;
-                else if (part == 1) A.b_out[row * N + (c - di)] = code;
-                else A.c_out[row * N + (c - di - N)] = code;
+#pragma unroll
+        for (int i = 0; i < kConvTL; ++i) {
+            if (i < n) {
+                const float xv_i = xv[i];
+                xmax = fmaxf(xmax, fabsf(xv_i));
+                const int32_t xq = quant_xbc(xv_i, qscale);
+                const int64_t row = b * L + t0 + i;
+                if (A.xbc_q) A.xbc_q[row * K.ch + c] = (int8_t)xq;
+                const int32_t acc = w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq;
+                const int32_t a = sat32(rshr((int64_t)acc, sh) + bias);
+                const int32_t sv = nau_silu_f(a, tab);
+                const int32_t sa = sv < 0 ? -sv : sv;
+                amax = sa > amax ? sa : amax;
+                if (K.dynamic) {
+                    A.s16[row * K.ch + c] = sv;
+                } else {
+                    const int8_t code = sat8(rshr((int64_t)sv, 16 - p_part));
+                    if (part == 0) A.x_out[row * di + c] = code;
+                    else if (part == 1) A.b_out[row * N + (c - di)] = code;
+                    else A.c_out[row * N + (c - di - N)] = code;
+                }
+                xm3 = xm2;
+                xm2 = xm1;
+                xm1 = xq;
             }
-            xm3 = xm2;
-            xm2 = xm1;
-            xm1 = xq;
         }
-        if (A.state_out && t1 == L) {
+        if (A.state_out && t0 + n == L) {
             int8_t* st = A.state_out + (b * K.ch + c) * 3;
             st[0] = (int8_t)xm3;
             st[1] = (int8_t)xm2;
@@ -119,32 +122,25 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
 }
 
 // Dynamic second pass: exponents from the maxima, Q.16 -> int8 codes.
-__global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K, int64_t total) {
+// grid.y = token row, threads over groups of 4 channels.
+__global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
-    __shared__ int sp[4];
-    if (threadIdx.x == 0) {
-        sp[0] = pot_from_f32(*A.xbc_amax);
-        for (int i = 0; i < 3; ++i) sp[1 + i] = pot_from_q16(A.amax_q16[i]);
-        if (blockIdx.x == 0) {
-            for (int i = 0; i < 4; ++i) A.p_out[i] = sp[i];
-            if (A.amax_stats) {
-                atomicMax((unsigned int*)&A.amax_stats[0], __float_as_uint(*A.xbc_amax));
-                for (int i = 0; i < 3; ++i) atomicMax(&A.amax_stats[1 + i], A.amax_q16[i]);
-            }
+    const int di = (int)A.d_inner, N = (int)A.dstate;
+    const int c = (blockIdx.x * kConvThreads + threadIdx.x) * 4;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        A.p_out[0] = pot_from_f32(*A.xbc_amax);
+        for (int i = 0; i < 3; ++i) A.p_out[1 + i] = pot_from_q16(A.amax_q16[i]);
+        if (A.amax_stats) {
+            atomicMax((unsigned int*)&A.amax_stats[0], __float_as_uint(*A.xbc_amax));
+            for (int i = 0; i < 3; ++i) atomicMax(&A.amax_stats[1 + i], A.amax_q16[i]);
         }
     }
-    __syncthreads();
-    const int di = (int)A.d_inner, N = (int)A.dstate;
-    // 4 channels per thread (ch % 64 == 0)
-    const int64_t nq = total / 4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nq;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t e = i * 4;
-        const int64_t row = e / K.ch;
-        const int c = (int)(e - row * K.ch);
-        const int4 s = *reinterpret_cast<const int4*>(A.s16 + e);
-        const int part = c < di ? 0 : (c < di + N ? 1 : 2);
-        const int sh = 16 - sp[1 + part];
+    if (c >= K.ch) return;
+    const int part = c < di ? 0 : (c < di + N ? 1 : 2);
+    const int sh = 16 - pot_from_q16(A.amax_q16[part]);
+    const int64_t rows = A.batch * A.len;
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const int4 s = *reinterpret_cast<const int4*>(A.s16 + row * K.ch + c);
         char4 q;
         q.x = sat8(rshr((int64_t)s.x, sh));
         q.y = sat8(rshr((int64_t)s.y, sh));
@@ -188,11 +184,10 @@ fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     conv_silu_kernel<<<grid, kConvThreads, 0, s>>>(K);
     fm_status st = check_launch("conv_silu_kernel");
     if (st != FM_OK || !K.dynamic) return st;
-    const int64_t total = a.batch * a.len * K.ch;
-    int g = (int)((total / 4 + kConvThreads - 1) / kConvThreads);
-    if (g > 4096) g = 4096;
-    if (g < 1) g = 1;
-    requant_kernel<<<g, kConvThreads, 0, s>>>(K, total);
+    const int64_t rows = a.batch * a.len;
+    dim3 rgrid((unsigned)((K.ch / 4 + kConvThreads - 1) / kConvThreads),
+               (unsigned)(rows < 65535 ? rows : 65535));
+    requant_kernel<<<rgrid, kConvThreads, 0, s>>>(K);
     return check_launch("requant_kernel");
 }
 

@@ -46,20 +46,25 @@ __device__ __forceinline__ int32_t f2i_sat(float f) {
 }
 
 // Largest p in [kPMin, kPMax] with a * 2^p <= 127 (a >= 0 float32); 0 for a == 0.
+// With a = m * 2^e, m in [0.5, 1): p = 7 - e when m * 128 <= 127, else 6 - e.
 __device__ __forceinline__ int pot_from_f32(float a) {
     if (!(a > 0.0f)) return 0;
-    double ad = (double)a;
-    for (int p = kPMax; p > kPMin; --p)
-        if (ad * __builtin_ldexp(1.0, p) <= 127.0) return p;
-    return kPMin;
+    int e;
+    const float m = frexpf(a, &e);
+    int p = (m <= 0.9921875f) ? 7 - e : 6 - e;
+    return p > kPMax ? kPMax : (p < kPMin ? kPMin : p);
 }
 
 // Largest p in [kPMin, kPMax] with (m / 2^16) * 2^p <= 127 for a Q.16 maximum m >= 0.
+// For m in [2^(k-1), 2^k) every p >= 24 - k fails, so the search starts there.
 __device__ __forceinline__ int pot_from_q16(int64_t m) {
     if (m <= 0) return 0;
+    const int k = 64 - __clzll((unsigned long long)m);
     const int64_t lim = (int64_t)127 << 16;
-    for (int p = kPMax; p > kPMin; --p) {
-        bool ok = p >= 0 ? ((m << p) <= lim) : (m <= (lim << (-p)));
+    int p0 = 24 - k;
+    if (p0 > kPMax) p0 = kPMax;
+    for (int p = p0; p > kPMin; --p) {
+        const bool ok = p >= 0 ? ((m << p) <= lim) : (m <= (lim << (-p)));
         if (ok) return p;
     }
     return kPMin;
@@ -82,38 +87,72 @@ __device__ __forceinline__ int64_t exp2_knot(uint32_t i) {
 }
 constexpr int64_t kLog2eQ30 = 1549082005LL;  // rint(log2(e) * 2^30)
 
-// 2^(v/2^16) in Q.16 for v <= 0 (result in [0, 2^16]).
-__device__ __forceinline__ int32_t nau_exp2(int64_t v) {
-    if (v < -((int64_t)32 << 16)) return 0;
-    int64_t n = v >> 16;                       // floor of the integer part
-    uint32_t f = (uint32_t)(v - (n << 16));    // [0, 2^16)
-    uint32_t seg = f >> 13;                    // chord 0..7
-    int64_t r = (int64_t)(f & 0x1FFFu);        // 13-bit position on the chord
-    int64_t y0 = exp2_knot(seg), y1 = exp2_knot(seg + 1);
-    int64_t m = y0 + rshr((y1 - y0) * r, 13);  // Q.30 mantissa
-    return (int32_t)rshr(m, (int)(14 - n));
+// ---------------------------------------------------------------- NAU evaluation
+// Integer definitions (Q.16 in and out):
+//   2^(v/2^16), v <= 0:  n = v >> 16, f = v & 0xFFFF, seg = f >> 13, r = f & 0x1FFF,
+//                        m = Y[seg] + rshr((Y[seg+1] - Y[seg]) * r, 13),  result rshr(m, 14 - n)
+//   e^(x/2^16), x <= 0:  2^(rshr(x * kLog2eQ30, 30) / 2^16)
+// They are evaluated with float64 operations on integer-valued operands (full
+// vector rate on MI355X, where 64-bit integer multiplies and shifts are not).
+// Every product below stays under 2^53 wherever the result is not already
+// known to be 0, so each floor() sees the exact rational value and the results
+// equal the integer definitions.  The 9 chord endpoints live in LDS
+// (nau_lds_init, then a barrier before first use).
+struct NauLds {
+    double y[9];
+};
+
+__device__ __forceinline__ void nau_lds_init(NauLds& t) {
+    if (threadIdx.x < 9) t.y[threadIdx.x] = (double)exp2_knot(threadIdx.x);
 }
 
 // e^(x/2^16) in Q.16 for -2^31 <= x <= 0.
-__device__ __forceinline__ int32_t nau_exp(int64_t x) {
-    return nau_exp2(rshr(x * kLog2eQ30, 30));
+__device__ __forceinline__ int32_t nau_exp_f(int32_t x, const NauLds& t) {
+    // v = rshr(x * log2e_q30, 30): exact while v >= -17*2^16 (|x * log2e| < 2^51)
+    const double vf =
+        __builtin_floor(__builtin_fma((double)x, (double)kLog2eQ30, 0x1p29) * 0x1p-30);
+    // integer part n <= -18: the Q.30 mantissa shifted right by >= 32 rounds to 0
+    if (vf < -1114112.0) return 0;
+    const int v = (int)vf;
+    const int n = v >> 16;  // -17..0
+    const int f = v & 0xFFFF;
+    const int seg = f >> 13;
+    const double r = (double)(f & 0x1FFF);
+    const double y0 = t.y[seg], y1 = t.y[seg + 1];
+    // m = Y[seg] + rshr((Y[seg+1] - Y[seg]) * r, 13): the product is below 2^41
+    const double m = y0 + __builtin_floor(__builtin_fma(y1 - y0, r, 0x1p12) * 0x1p-13);
+    // rshr(m, 14 - n): m * 2^(n-14) + 1/2 spans at most 50 bits
+    return (int)__builtin_floor(__builtin_fma(m, __builtin_ldexp(1.0, n - 14), 0.5));
 }
 
 // SoftPlus in Q.16: e^-|x| + max(x, 0) (Eq. (5) for x <= 0, the symmetry above).
-__device__ __forceinline__ int32_t nau_softplus(int32_t x) {
-    int64_t xa = x < 0 ? -(int64_t)x : (int64_t)x;
-    int64_t e = nau_exp(-xa);
+__device__ __forceinline__ int32_t nau_softplus_f(int32_t x, const NauLds& t) {
+    const int32_t xn = x < 0 ? x : -x;  // -|x| (no overflow for INT32_MIN)
+    const int64_t e = nau_exp_f(xn, t);
     return sat32(e + (x > 0 ? (int64_t)x : 0));
 }
 
 // SiLU in Q.16: for x <= 0, sigma = floor(E*2^16 / (2^16 + E)), E = e^x,
 // SiLU = rshr(x * sigma, 16); for x > 0, x + SiLU(-x).
-__device__ __forceinline__ int32_t nau_silu(int32_t x) {
-    int64_t xn = x < 0 ? (int64_t)x : -(int64_t)x;   // -|x|
-    uint32_t e = (uint32_t)nau_exp(xn);             // [0, 2^16]
-    uint32_t sig = (e >= 65536u) ? 32768u : ((e << 16) / (65536u + e));
-    int64_t sn = rshr(xn * (int64_t)sig, 16);
-    return (int32_t)(x > 0 ? (int64_t)x + sn : sn);
+__device__ __forceinline__ int32_t nau_silu_f(int32_t x, const NauLds& t) {
+    const int32_t xn = x < 0 ? x : -x;
+    const int32_t e = nau_exp_f(xn, t);  // [0, 2^16]
+    int32_t sig;
+    if (e >= 65536) {
+        sig = 32768;
+    } else {
+        // quotient < 2^15: a float32 reciprocal puts floor() within 1 of it, and
+        // the exact remainder a - q*b (integers below 2^34) corrects it
+        const double a = (double)e * 65536.0, b = 65536.0 + (double)e;
+        double q = __builtin_floor(a * (double)__builtin_amdgcn_rcpf((float)b));
+        const double rem = __builtin_fma(-q, b, a);
+        q = rem < 0.0 ? q - 1.0 : (rem >= b ? q + 1.0 : q);
+        sig = (int32_t)q;
+    }
+    // rshr(xn * sig, 16): |xn * sig| < 2^46
+    const int32_t sn =
+        (int32_t)__builtin_floor(__builtin_fma((double)xn, (double)sig * 0x1p-16, 0.5));
+    return x > 0 ? x + sn : sn;
 }
 
 // ---------------------------------------------------------------- wave helpers

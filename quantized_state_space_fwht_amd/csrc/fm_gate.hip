@@ -54,6 +54,9 @@ constexpr int kGateMaxD = 8192;
 
 __global__ __launch_bounds__(64) void gate_norm_kernel(GateArgs G) {
     extern __shared__ __attribute__((aligned(16))) float row_buf[];  // d_inner floats
+    __shared__ NauLds tab;
+    nau_lds_init(tab);
+    __syncthreads();
     const int lane = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int D = (int)G.d_inner;
@@ -61,14 +64,29 @@ __global__ __launch_bounds__(64) void gate_norm_kernel(GateArgs G) {
     const int32_t* yr = G.y + row * D;
     const float* zr = G.z + row * G.z_stride;
     float a = 0.0f;
-    for (int i = lane; i < D; i += 64) {
-        const float yf = (float)yr[i] * ysc;
-        const int32_t zq = f2i_sat(rintf(zr[i] * 65536.0f));
-        const float sz = (float)nau_silu(zq) * 0x1p-16f;
-        const float g = yf * sz;
-        row_buf[i] = g;
-        const float g2 = g * g;
-        a = a + g2;
+    // four elements per lane per round: their loads are issued together
+    for (int i0 = lane; i0 < D; i0 += 4 * 64) {
+        int32_t yv[4];
+        float zv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 64 * k;
+            yv[k] = i < D ? yr[i] : 0;
+            zv[k] = i < D ? zr[i] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 64 * k;
+            if (i < D) {
+                const float yf = (float)yv[k] * ysc;
+                const int32_t zq = f2i_sat(rintf(zv[k] * 65536.0f));
+                const float sz = (float)nau_silu_f(zq, tab) * 0x1p-16f;
+                const float g = yf * sz;
+                row_buf[i] = g;
+                const float g2 = g * g;
+                a = a + g2;  // ascending i within this lane: the fixed order
+            }
+        }
     }
     const float ss = row_sumsq(a);
     const float ms = ss / (float)D;

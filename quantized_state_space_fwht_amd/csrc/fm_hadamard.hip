@@ -125,9 +125,9 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
         p[i] = 0u;
 }
 
-static int hq_grid(int64_t nblk_total) {
+static int hq_grid(int64_t nblk_total, int64_t cap = 4096) {
     int64_t g = (nblk_total + 3) / 4;
-    if (g > 4096) g = 4096;
+    if (g > cap) g = cap;
     return (int)(g < 1 ? 1 : g);
 }
 
@@ -146,7 +146,8 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
     int g = hq_grid(nb);
     fm_status st;
     if (mode == FM_SCALE_DYNAMIC) {  // amax_ws must hold 0 (zeroed by the caller)
-        hq_amax_kernel<<<g, kHqThreads, 0, s>>>(x, nb, amax_ws, amax_stats);
+        // few workgroups (grid-stride): one same-address atomic per workgroup
+        hq_amax_kernel<<<hq_grid(nb, 512), kHqThreads, 0, s>>>(x, nb, amax_ws, amax_stats);
         if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
         hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, (char4*)q,
                                                  scale_out, nullptr, 0);

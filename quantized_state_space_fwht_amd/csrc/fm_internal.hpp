@@ -100,10 +100,14 @@ struct ScanArgs {
     const int32_t* state_in;
     int32_t* state_out;
     int32_t* y;
-    int32_t* dt_out;
+    int32_t* dt_out;           // [T, H] written by the dt / decay prologue (required)
     int32_t* da_out;
+    const double* dak;         // set by scan_run: per (token, head) dA*2^-16 and K_t
+    const double* us;          // set by scan_run: per (token, head, p) dt*x*2^-8
 };
-fm_status scan_run(const ScanArgs& a, hipStream_t s);
+// workspace of the scan prologue (float64 per-step scalars)
+size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t nheads, int64_t headdim);
+fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s);
 
 struct GateArgs {
     const int32_t* y;
@@ -122,6 +126,8 @@ struct GateArgs {
     float* amax_ws;    // dynamic: 1 float
 };
 fm_status gate_run(const GateArgs& a, hipStream_t s);
+
+fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s);
 
 // layer pipeline (fm_layer.hip)
 size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);

@@ -37,6 +37,7 @@ struct LayerWs {
     int8_t* g_q;     // [T, di]
     int32_t* dt;     // [T, H]
     int32_t* da;     // [T, H]
+    void* scan_ws;   // scan prologue scalars
     size_t bytes;
 };
 
@@ -61,6 +62,7 @@ static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void
     w.g_q = ar.take<int8_t>((size_t)T * di);
     w.dt = ar.take<int32_t>((size_t)T * H);
     w.da = ar.take<int32_t>((size_t)T * H);
+    w.scan_ws = ar.take<char>(scan_ws_bytes(batch, len, H, d->headdim));
     w.bytes = ar.used;
     return w;
 }
@@ -224,13 +226,13 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.state_in = decode ? cache->ssm_state : nullptr;
         a.state_out = cache ? cache->ssm_state : nullptr;
         a.y = w.y;
-        a.dt_out = g_keep ? w.dt : nullptr;
-        a.da_out = g_keep ? w.da : nullptr;
+        a.dt_out = w.dt;
+        a.da_out = w.da;
         hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
         g_ev_start = g_ev_stop = nullptr;
         if (ev0 && hipEventRecord(ev0, s) != hipSuccess)
             return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
-        if ((st = scan_run(a, s)) != FM_OK) return st;
+        if ((st = scan_run(a, w.scan_ws, s)) != FM_OK) return st;
         if (ev1 && hipEventRecord(ev1, s) != hipSuccess)
             return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
     }

@@ -7,136 +7,286 @@
 //
 // The integer recurrence, per (b, head, p, n):
 //     state = sat32(floor((dA*state + 2^8*dt*x*B + 2^15) / 2^16))
-// runs in float64 on integer-valued operands: dA*2^-16 * state and
-// dt*x*2^-8 * B + 1/2 are exact (<= 49 and 46 significant bits), their fused
-// sum is exact whenever the result fits int32 (a larger sum saturates either
-// way), and floor / clamp are exact.  So one step is two FMAs, a floor and a
-// clamp — MI355X runs float64 FMA at full vector rate, while 32x32->64-bit
-// integer multiplies run at a quarter of it.
+// runs in float64 on integer-valued operands, on the biased state
+// hb = state + 2^31 in [0, 2^32):
+//     hb' = clamp(floor(dA*2^-16 * hb + (u * B + K_t)), 0, 2^32 - 1)
+//     u = dt*x*2^-8,  K_t = 2^31 * (1 - dA*2^-16) + 1/2
+// Both products are exact (<= 49 and 46 significant bits) and the fused sum
+// is exact whenever it lies within 2^33 of the int32 range (further out the
+// result saturates either way).  floor + clamp is one saturating
+// v_cvt_u32_f64.  So a step is two FMAs and two conversions — MI355X runs
+// float64 at full vector rate, while 32x32->64-bit integer multiplies run at a
+// quarter of it.  y uses sum_n C*state = sum_n C*hb - 2^31 * sum_n C.
 //
-// Work split: a workgroup of 4 waves owns (b, head, 4 consecutive p); wave w
-// owns one p, lane l owns n = l*NL .. l*NL+NL-1 (d_state = 64*NL).  Time runs
-// in chunks of kTC steps: B, C (as float64), the decay and dt*x for the chunk
-// are staged in LDS, each lane then advances its NL states through the chunk
-// keeping partial sums of C*state per step, and the partials are reduced
-// across lanes once per chunk.
+// scan_prep_kernel runs first, over every (token, head): dt, the decay, and
+// the per-step float64 scalars (dA*2^-16, K_t) and u for every p, so that the
+// sequential scan reads them with wave-uniform scalar loads (SGPR operands,
+// no LDS traffic) and never waits on the exponential unit.
+//
+// scan_kernel: a workgroup of 4 waves owns (b, head, 8 consecutive p).  Lane l
+// of wave w owns the states (p, n) for p in {2w, 2w+1} and n = NN*l .. NN*l+NN-1
+// (d_state = 64*NN), so a wave reads each B/C value once for two p.  Time runs
+// in chunks of kTC steps: B and C of the chunk are staged in LDS as float32
+// (exact for int8 codes) while the next chunk's global loads are in flight;
+// per step each lane writes its partial sums of C*state (one per p) and after
+// the chunk the 64 partials of each (step, p) are added (exact: integers below
+// 2^46) and y is written.
 #include "fm_internal.hpp"
 
 namespace fm {
 
-constexpr int kTC = 16;
 constexpr int kScanWaves = 4;
 constexpr int kScanThreads = 64 * kScanWaves;
+constexpr int kScanP = 2 * kScanWaves;  // p per workgroup
+constexpr int kTC = 16;                 // steps per chunk
 
-template <int NL>
+// ---------------------------------------------------------------- prologue
+// 4 (token, head) pairs per block of 256 threads; lane i of pair q handles
+// p = i, i + 64, ...
+__global__ __launch_bounds__(256) void scan_prep_kernel(
+    const float* __restrict__ dt_raw, int64_t dt_stride, const float* __restrict__ bias,
+    const int32_t* __restrict__ a_q16, const int8_t* __restrict__ x, int64_t pairs, int H, int P,
+    int32_t* __restrict__ dt_out, int32_t* __restrict__ da_out, double* __restrict__ dak,
+    double* __restrict__ us) {
+    __shared__ NauLds tab;
+    __shared__ int32_t dts[4];
+    nau_lds_init(tab);
+    __syncthreads();
+    const int grp = threadIdx.x >> 6, i = threadIdx.x & 63;
+    const int64_t q = (int64_t)blockIdx.x * 4 + grp;  // (row, head) pair = row*H + h
+    if (q < pairs && i == 0) {
+        const int64_t row = q / H;
+        const int h = (int)(q - row * H);
+        const float raw = dt_raw[row * dt_stride + h];
+        const int32_t dt_in = f2i_sat(rintf((raw + bias[h]) * 65536.0f));
+        const int32_t dt = nau_softplus_f(dt_in, tab);
+        const int32_t arg = sat32(rshr((int64_t)dt * (int64_t)a_q16[h], 16));
+        const int32_t da = nau_exp_f(arg, tab);
+        dt_out[q] = dt;
+        da_out[q] = da;
+        dak[2 * q] = (double)da * 0x1p-16;
+        dak[2 * q + 1] = 2147483648.0 - (double)da * 32768.0 + 0.5;
+        dts[grp] = dt;
+    }
+    __syncthreads();
+    if (q < pairs) {
+        const double dtd = (double)dts[grp] * 0x1p-8;  // exact: power-of-two scaling
+        for (int p = i; p < P; p += 64) us[q * P + p] = dtd * (double)x[q * P + p];
+    }
+}
+
+// ---------------------------------------------------------------- scan
+// ypart layout: a row of kTC+1 doubles per lane; lanes 32..63 start 4 doubles
+// later and each (wave, p) plane is padded by 8 doubles, so that the writes
+// (one double per lane per step) and the reduction's reads (consecutive steps
+// across lanes, planes r = 0/1 and halves side by side) spread over the banks.
+constexpr int kYRow = kTC + 1;
+constexpr int kYPlane = 64 * kYRow + 4 + 8;
+__device__ __forceinline__ int ypart_at(int w, int r, int lane, int t) {
+    return (w * 2 + r) * kYPlane + lane * kYRow + (lane >= 32 ? 4 : 0) + t;
+}
+
+template <int NN>
+struct alignas(16) ScanSmem {
+    float Bf[kTC][64 * NN];
+    float Cf[kTC][64 * NN];
+    // partial sums, [wave][p of the wave][lane][step] (see ypart_at)
+    double ypart[kScanWaves * 2 * kYPlane];
+    int32_t sumC[kTC];
+    int32_t ystage[kTC][kScanP];
+    int8_t xs[kTC][kScanP];
+};
+
+template <int NN>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
-    constexpr int N = 64 * NL;
-    __shared__ double Bf[kTC][N];
-    __shared__ double Cf[kTC][N];
-    __shared__ double ypart[kScanWaves][kTC][64];
-    __shared__ double dAs[kTC];
-    __shared__ double us[kTC][kScanWaves];
-    __shared__ int64_t dterm[kTC][kScanWaves];
-    __shared__ int32_t dt_sh[kTC];
-    __shared__ int32_t ystage[kTC][kScanWaves];
+    constexpr int N = 64 * NN;
+    constexpr int kBytes = kTC * N / kScanThreads;  // B (and C) bytes staged per thread
+    constexpr int kThreadsPerRow = N / kBytes;
+    static_assert(kBytes == 4 || kBytes == 8, "staging split");
+    __shared__ ScanSmem<NN> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t H = A.nheads, P = A.headdim, L = A.len;
-    const int64_t pg = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-    const int64_t p = pg * kScanWaves + w;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = (int)A.nheads, P = (int)A.headdim;
+    const int64_t L = A.len;
+    const int pg = blockIdx.x, head = blockIdx.y;
+    const int64_t b = blockIdx.z;
     const int ky = A.p[2] + A.p[3];
-    const int32_t a_h = A.a_q16[head];
     const int64_t d_h = A.d_q16[head];
-    const float bias = A.dt_bias[head];
+    const int64_t p0 = (int64_t)pg * kScanP + 2 * w;  // this wave's two p: p0, p0 + 1
 
-    double h[NL];
-    const int64_t sbase = ((b * H + head) * P + p) * N + lane * NL;
+    // biased states hb = state + 2^31 of (p0 + r, NN*lane + j)
+    double hb[2][NN];
+    const int64_t sbase = ((b * H + head) * P + p0) * N + NN * lane;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) h[j] = A.state_in ? (double)A.state_in[sbase + j] : 0.0;
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int j = 0; j < NN; ++j)
+            hb[r][j] = (A.state_in ? (double)A.state_in[sbase + r * N + j] : 0.0) + 2147483648.0;
 
+    // per-step scalars: (dA*2^-16, K_t) and (u of p0, u of p0+1), wave-uniform
+    const double* __restrict__ dak = A.dak + (b * L * H + head) * 2;
+    const double* __restrict__ usp = A.us + (b * L * H + head) * P + p0;
+    const int64_t dak_step = 2 * (int64_t)H, us_step = (int64_t)H * P;
+
+    // staging roles
+    const int st_t = tid / kThreadsPerRow, st_n = (tid % kThreadsPerRow) * kBytes;
+    int32_t rb[kBytes / 4] = {}, rc[kBytes / 4] = {};
+    int32_t rx = 0;
+    auto prefetch = [&](int64_t t0) {
+        if (t0 + st_t < L) {
+            const int32_t* pb = (const int32_t*)(A.bm + (b * L + t0 + st_t) * N + st_n);
+            const int32_t* pc = (const int32_t*)(A.cm + (b * L + t0 + st_t) * N + st_n);
+#pragma unroll
+            for (int k = 0; k < kBytes / 4; ++k) {
+                rb[k] = pb[k];
+                rc[k] = pc[k];
+            }
+        }
+        if (tid < kTC * kScanP && t0 + tid / kScanP < L)
+            rx = A.x[((b * L + t0 + tid / kScanP) * H + head) * P + (int64_t)pg * kScanP +
+                     tid % kScanP];
+    };
+    auto stage = [&]() {
+        int32_t csum = 0;
+#pragma unroll
+        for (int k = 0; k < kBytes / 4; ++k) {
+            float bv[4], cv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int32_t bi = (int8_t)(rb[k] >> (8 * e)), ci = (int8_t)(rc[k] >> (8 * e));
+                bv[e] = (float)bi;
+                cv[e] = (float)ci;
+                csum += ci;
+            }
+            *reinterpret_cast<float4*>(&sm.Bf[st_t][st_n + 4 * k]) =
+                make_float4(bv[0], bv[1], bv[2], bv[3]);
+            *reinterpret_cast<float4*>(&sm.Cf[st_t][st_n + 4 * k]) =
+                make_float4(cv[0], cv[1], cv[2], cv[3]);
+        }
+#pragma unroll
+        for (int m = 1; m < kThreadsPerRow; m <<= 1) csum += __shfl_xor(csum, m, kThreadsPerRow);
+        if (tid % kThreadsPerRow == 0) sm.sumC[st_t] = csum;
+        if (tid < kTC * kScanP) sm.xs[tid / kScanP][tid % kScanP] = (int8_t)rx;
+    };
+
+    // one step of the recurrence for this lane's 2*NN states; writes the two partials
+    auto step = [&](int t, int64_t tg) {
+        const double da = dak[tg * dak_step], kt = dak[tg * dak_step + 1];
+        const double u0 = usp[tg * us_step], u1 = usp[tg * us_step + 1];
+        double bv[NN], cv[NN];
+        if constexpr (NN == 2) {
+            const float2 bb = *reinterpret_cast<const float2*>(&sm.Bf[t][2 * lane]);
+            const float2 cc = *reinterpret_cast<const float2*>(&sm.Cf[t][2 * lane]);
+            bv[0] = bb.x;
+            bv[1] = bb.y;
+            cv[0] = cc.x;
+            cv[1] = cc.y;
+        } else {
+            bv[0] = sm.Bf[t][lane];
+            cv[0] = sm.Cf[t][lane];
+        }
+        double y[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const double u = r ? u1 : u0;
+#pragma unroll
+            for (int j = 0; j < NN; ++j) {
+                const double sv = __builtin_fma(da, hb[r][j], __builtin_fma(u, bv[j], kt));
+                uint32_t hu;
+                // floor + clamp to [0, 2^32-1] in one instruction (saturating conversion)
+                asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
+                hb[r][j] = (double)hu;
+            }
+            y[r] = cv[0] * hb[r][0];
+#pragma unroll
+            for (int j = 1; j < NN; ++j) y[r] = __builtin_fma(cv[j], hb[r][j], y[r]);
+        }
+        sm.ypart[ypart_at(w, 0, lane, t)] = y[0];  // exact: integers below 2^40
+        sm.ypart[ypart_at(w, 1, lane, t)] = y[1];
+    };
+
+    prefetch(0);
+    stage();
+    __syncthreads();
     for (int64_t t0 = 0; t0 < L; t0 += kTC) {
-        const int tc = (int)(L - t0 < kTC ? L - t0 : kTC);
-        // ---- stage B, C and the per-step scalars of this chunk
-        for (int i = tid; i < tc * N; i += kScanThreads) {
-            const int t = i / N, n = i - t * N;
-            const int64_t src = (b * L + t0 + t) * N + n;
-            Bf[t][n] = (double)A.bm[src];
-            Cf[t][n] = (double)A.cm[src];
-        }
-        if (tid < tc) {
-            const int64_t row = b * L + t0 + tid;
-            const float raw = A.dt_raw[row * A.dt_stride + head];
-            const int32_t dt_in = f2i_sat(rintf((raw + bias) * 65536.0f));
-            const int32_t dt = nau_softplus(dt_in);
-            const int32_t arg = sat32(rshr((int64_t)dt * (int64_t)a_h, 16));
-            const int32_t da = nau_exp((int64_t)arg);
-            dt_sh[tid] = dt;
-            dAs[tid] = (double)da * 0x1p-16;
-            if (pg == 0) {
-                if (A.dt_out) A.dt_out[row * H + head] = dt;
-                if (A.da_out) A.da_out[row * H + head] = da;
-            }
-        }
-        __syncthreads();
-        if (tid < tc * kScanWaves) {
-            const int t = tid / kScanWaves, pp = tid - t * kScanWaves;
-            const int64_t xi = ((b * L + t0 + t) * H + head) * P + pg * kScanWaves + pp;
-            const int64_t x = A.x[xi];
-            us[t][pp] = (double)((int64_t)dt_sh[t] * x) * 0x1p-8;
-            dterm[t][pp] = rshr(d_h * x, 8);
-        }
-        __syncthreads();
-        // ---- the recurrence
-        for (int t = 0; t < tc; ++t) {
-            const double da = dAs[t];
-            const double u = us[t][w];
-            double yp = 0.0;
+        const bool more = t0 + kTC < L;
+        if (more) prefetch(t0 + kTC);
+        int tc;
+        if (t0 + kTC <= L) {
+            tc = kTC;
 #pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const double inc = __builtin_fma(u, Bf[t][lane * NL + j], 0.5);
-                double s = __builtin_floor(__builtin_fma(da, h[j], inc));
-                s = __builtin_fmin(__builtin_fmax(s, -2147483648.0), 2147483647.0);
-                h[j] = s;
-                yp = __builtin_fma(Cf[t][lane * NL + j], s, yp);
-            }
-            ypart[w][t][lane] = yp;
+            for (int t = 0; t < kTC; ++t) step(t, t0 + t);
+        } else {
+            tc = (int)(L - t0);
+            for (int t = 0; t < tc; ++t) step(t, t0 + t);
         }
         __syncthreads();
-        // ---- y for this wave's p: lane (t = lane/4, quarter = lane%4) sums 16 partials
+        // ---- y: lane l adds 32 of the 64 partials of output (r, t) = ((l%32)/16, l%16);
+        //      lanes l and l+32 then combine their halves
         {
-            const int t = lane >> 2, qtr = lane & 3;
-            double s = 0.0;
+            const int o = lane & 31, half = lane >> 5;
+            const int r = o >> 4, t = o & 15;
+            double v[32];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) s += ypart[w][t][qtr * 16 + k];
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            if (qtr == 0 && t < tc) {
-                const int64_t yacc = (int64_t)s;  // integer below 2^46: exact
-                ystage[t][w] = sat32(rshr(yacc, ky) + dterm[t][w]);
+            for (int k = 0; k < 32; ++k) v[k] = sm.ypart[ypart_at(w, r, half * 32 + k, t)];
+#pragma unroll
+            for (int k = 16; k >= 1; k >>= 1)
+#pragma unroll
+                for (int i = 0; i < k; ++i) v[i] += v[i + k];
+            const double tot = v[0] + __shfl_xor(v[0], 32, 64);
+            if (half == 0 && t < tc) {
+                // sum_n C*state = sum_n C*hb - 2^31 * sum_n C (exact integers)
+                const int64_t yacc = (int64_t)tot - ((int64_t)sm.sumC[t] << 31);
+                const int pl = 2 * w + r;
+                const int64_t dterm = rshr(d_h * (int64_t)sm.xs[t][pl], 8);
+                sm.ystage[t][pl] = sat32(rshr(yacc, ky) + dterm);
             }
         }
         __syncthreads();
-        if (tid < tc) {
-            const int64_t yi = ((b * L + t0 + tid) * H + head) * P + pg * kScanWaves;
+        // ---- write y rows (8 consecutive p per step) and stage the next chunk
+        if (tid < 2 * tc) {
+            const int t = tid >> 1, hf = tid & 1;
+            const int64_t yi = ((b * L + t0 + t) * H + head) * P + (int64_t)pg * kScanP + 4 * hf;
             *reinterpret_cast<int4*>(A.y + yi) =
-                make_int4(ystage[tid][0], ystage[tid][1], ystage[tid][2], ystage[tid][3]);
+                *reinterpret_cast<const int4*>(&sm.ystage[t][4 * hf]);
         }
-        // the next chunk's staging overwrites LDS read above
+        if (more) stage();
         __syncthreads();
     }
     if (A.state_out) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) A.state_out[sbase + j] = (int32_t)h[j];
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int j = 0; j < NN; ++j)
+                A.state_out[sbase + r * N + j] = (int32_t)((uint32_t)hb[r][j] ^ 0x80000000u);
     }
 }
 
-fm_status scan_run(const ScanArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)(a.headdim / kScanWaves), (unsigned)a.nheads, (unsigned)a.batch);
+size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t nheads, int64_t headdim) {
+    const int64_t pairs = batch * len * nheads;
+    return align256((size_t)pairs * 2 * sizeof(double)) +
+           align256((size_t)(pairs * headdim) * sizeof(double));
+}
+
+fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s) {
+    const int64_t pairs = a.batch * a.len * a.nheads;
+    Arena ar(ws);
+    double* dak = ar.take<double>((size_t)pairs * 2);
+    double* us = ar.take<double>((size_t)(pairs * a.headdim));
+    ScanArgs k = a;
+    k.dak = dak;
+    k.us = us;
+    scan_prep_kernel<<<(unsigned)((pairs + 3) / 4), 256, 0, s>>>(
+        a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, a.x, pairs, (int)a.nheads, (int)a.headdim,
+        a.dt_out, a.da_out, dak, us);
+    fm_status st = check_launch("scan_prep_kernel");
+    if (st != FM_OK) return st;
+    dim3 grid((unsigned)(a.headdim / kScanP), (unsigned)a.nheads, (unsigned)a.batch);
     switch (a.dstate) {
-        case 64: scan_kernel<1><<<grid, kScanThreads, 0, s>>>(a); break;
-        case 128: scan_kernel<2><<<grid, kScanThreads, 0, s>>>(a); break;
-        case 256: scan_kernel<4><<<grid, kScanThreads, 0, s>>>(a); break;
-        default: return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64,128,256}", (long long)a.dstate);
+        case 64: scan_kernel<1><<<grid, kScanThreads, 0, s>>>(k); break;
+        case 128: scan_kernel<2><<<grid, kScanThreads, 0, s>>>(k); break;
+        default: return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
     }
     return check_launch("scan_kernel");
 }

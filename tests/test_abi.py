@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "quantized_state_space_fwht_amd", "libfm.so")
+HEADER = os.path.join(ROOT, "include", "fm.h")
+
+FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_MODE, FM_ERR_WORKSPACE = 0, 1, 2, 3, 4
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfm.so is not built: run `python -m quantized_state_space_fwht_amd.build`")
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_entry_point(lib):
+    names = declared()
+    assert len(names) >= 19
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    lib.fm_abi_version.restype = ctypes.c_int
+    assert lib.fm_abi_version() == 1
+
+
+def _last_error(lib):
+    lib.fm_last_error.restype = ctypes.c_char_p
+    return lib.fm_last_error().decode()
+
+
+def test_hadamard_quant_validation(lib):
+    f = lib.fm_hadamard_quant
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    f.argtypes = [vp, i64, i64, ctypes.c_int, i32, i32, vp, vp, vp, vp, sz, vp]
+    fake = 0x10000  # never dereferenced: every case fails validation before a launch
+    assert f(fake, 4, 100, 0, 0, 0, fake, fake, None, fake, 256, None) == FM_ERR_SHAPE
+    assert "multiple of 256" in _last_error(lib)
+    assert f(fake, 4, 256, 0, 0, 0, fake, None, None, fake, 256, None) == FM_ERR_NULL
+    assert f(fake, 4, 256, 0, 0, 0, fake, fake, None, None, 0, None) == FM_ERR_WORKSPACE
+    assert f(fake, 4, 256, 0, 0, 0, fake, fake, None, fake + 1, 256, None) == FM_ERR_WORKSPACE
+    assert f(fake, 4, 256, 1, 0, 3, fake, fake, None, None, 0, None) == FM_ERR_MODE  # scoe 0
+    assert f(fake, 4, 256, 1, 1 << 24, 3, fake, fake, None, None, 0, None) == FM_ERR_MODE
+    assert f(fake, 4, 256, 7, 1000, 3, fake, fake, None, fake, 256, None) == FM_ERR_MODE
+    assert f(fake, -1, 256, 0, 0, 0, fake, fake, None, fake, 256, None) == FM_ERR_SHAPE
+
+
+def test_gemm_validation(lib):
+    f = lib.fm_w8a8_gemm
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    fake = 0x10000
+    assert f(fake, fake, 4, 4, 64, None, None, None, None, None) == FM_ERR_NULL   # no output
+    assert f(fake, fake, 4, 4, 64, None, None, None, fake, None) == FM_ERR_NULL   # out w/o scales
+    assert f(fake, fake, 4, 4, 100, None, None, fake, None, None) == FM_ERR_SHAPE  # k % 64
+    assert f(fake + 1, fake, 4, 4, 64, None, None, fake, None, None) == FM_ERR_SHAPE  # alignment
+
+
+def test_scan_validation(lib):
+    f = lib.fm_ssm_scan_pot
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                  vp, vp, ctypes.c_size_t, vp]
+    fake = 0x10000
+    ok = [fake, fake, fake, fake, 24, fake, fake, fake, fake, 1, 16, 24, 64, 128, None, None,
+          fake, fake, fake, fake, 1 << 30, None]
+    bad = list(ok); bad[13] = 96          # dstate
+    assert f(*bad) == FM_ERR_SHAPE
+    bad = list(ok); bad[12] = 12          # headdim % 8
+    assert f(*bad) == FM_ERR_SHAPE
+    bad = list(ok); bad[4] = 8            # dt row stride < nheads
+    assert f(*bad) == FM_ERR_SHAPE
+    bad = list(ok); bad[17] = None        # dt_out required
+    assert f(*bad) == FM_ERR_NULL
+    bad = list(ok); bad[19] = None        # workspace required
+    assert f(*bad) == FM_ERR_WORKSPACE
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("d_conv", ctypes.c_int64),
+                ("mode", ctypes.c_int32), ("prenorm_residual", ctypes.c_int32)]
+
+
+def test_layer_validation_and_workspace_query(lib):
+    lib.fm_mamba2_layer_workspace_size.restype = ctypes.c_size_t
+    lib.fm_mamba2_layer_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int64,
+                                                   ctypes.c_int64]
+    d = Desc(768, 1536, 24, 64, 128, 4, 0, 0)
+    ws = lib.fm_mamba2_layer_workspace_size(ctypes.byref(d), 1, 2048)
+    assert ws > 2048 * (768 + 3352 * 4)
+    f = lib.fm_mamba2_layer_prefill
+    f.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    bad = Desc(768, 1536, 24, 64, 128, 3, 0, 0)  # d_conv != 4
+    assert f(ctypes.byref(bad), None, None, None, 1, 16, None, None, None, None, 0, None) \
+        == FM_ERR_SHAPE
+    assert f(ctypes.byref(d), None, None, None, 1, 16, None, None, None, None, 0, None) \
+        == FM_ERR_NULL
+
+
+def test_qparams_from_stats_on_host(lib):
+    class QP(ctypes.Structure):
+        _fields_ = [("scale", ctypes.c_float * 2), ("p", ctypes.c_int32 * 4),
+                    ("stat_amax", ctypes.c_float * 3), ("stat_amax_q16", ctypes.c_int32 * 3),
+                    ("reserved", ctypes.c_int32 * 4)]
+
+    class SP(ctypes.Structure):
+        _fields_ = [("scoe", ctypes.c_int32 * 2), ("sshift", ctypes.c_int32 * 2),
+                    ("p", ctypes.c_int32 * 4)]
+    import oracle as O
+    st = O.layer.Stats(amax_u=21.7, amax_g=0.013, amax_xbc=9.5, amax_q16=[1000, 70000, 5])
+    qp = QP()
+    qp.stat_amax[0], qp.stat_amax[1], qp.stat_amax[2] = 21.7, 0.013, 9.5
+    qp.stat_amax_q16[0], qp.stat_amax_q16[1], qp.stat_amax_q16[2] = 1000, 70000, 5
+    sp = SP()
+    assert lib.fm_qparams_from_stats(ctypes.byref(qp), ctypes.byref(sp)) == FM_OK
+    # the oracle reads the same float32 statistics
+    st.amax_u, st.amax_g, st.amax_xbc = (float(qp.stat_amax[i]) for i in range(3))
+    want = O.qparams_from_stats(st)
+    assert tuple(sp.scoe) == want.scoe and tuple(sp.sshift) == want.sshift
+    assert tuple(sp.p) == want.p

@@ -90,6 +90,23 @@ def test_w8a8_gemm(B, m, n, k):
     assert np.array_equal(host(out), oout)
 
 
+# --------------------------------------------------------------------------- a6 (NAU)
+@pytest.mark.parametrize("fn", ["exp", "softplus", "silu"])
+def test_nau_elementwise(B, fn):
+    """Every Q.16 input in [-2^23, 2^23] plus 2^20 random int32 values."""
+    rng = np.random.default_rng(17)
+    x = np.concatenate([np.arange(-(1 << 23), (1 << 23) + 1, dtype=np.int64),
+                        rng.integers(-(1 << 31), (1 << 31), size=1 << 20),
+                        np.array([-(1 << 31), (1 << 31) - 1, -1, 0, 1])]).astype(np.int32)
+    code = {"exp": B.NAU_EXP, "softplus": B.NAU_SOFTPLUS, "silu": B.NAU_SILU}[fn]
+    t_y = torch.empty(x.shape, dtype=torch.int32, device="cuda")
+    B.fm_nau_eval(code, dev(x), t_y)
+    xi = x.astype(np.int64)
+    want = {"exp": lambda: O.exp_q16(np.minimum(xi, 0)), "softplus": lambda: O.softplus_q16(xi),
+            "silu": lambda: O.silu_q16(xi)}[fn]()
+    assert_exact(host(t_y), want, fn)
+
+
 # --------------------------------------------------------------------------- a4 / a5
 def _conv_case(shape, batch, length, seed):
     rng = np.random.default_rng(seed)
@@ -211,7 +228,7 @@ def test_ssm_scan_pot(B, wname, batch, length, heads, with_state):
 
 def test_ssm_scan_saturates_like_the_oracle(B):
     """Extreme inputs: the int32 clamp of the state and of y must agree."""
-    batch, length, H, P, N = 1, 40, 2, 4, 64
+    batch, length, H, P, N = 1, 40, 2, 8, 64
     x = np.full((batch, length, H, P), 127, np.int8)
     x[..., 1] = -127
     bm = np.full((batch, length, N), 127, np.int8)
@@ -226,9 +243,12 @@ def test_ssm_scan_saturates_like_the_oracle(B):
     assert np.any(np.abs(st) == 2 ** 31 - 1) or np.any(st == -2 ** 31)
     t_y = torch.empty((batch, length, H, P), dtype=torch.int32, device="cuda")
     t_st = torch.empty((batch, H, P, N), dtype=torch.int32, device="cuda")
+    t_dt = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+    t_da = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
     B.fm_ssm_scan_pot(dev(x), dev(bm), dev(cm), dev(dt_raw), H, dev(dt_bias),
                       dev(a_q16, torch.int32), dev(d_q16, torch.int32), dev(p), batch, length, H,
-                      P, N, None, t_st, t_y)
+                      P, N, None, t_st, t_y, t_dt, t_da)
+    assert_exact(host(t_dt), dt, "dt (saturating)")
     assert_exact(host(t_y), y, "y (saturating)")
     assert_exact(host(t_st), st, "state (saturating)")
 
