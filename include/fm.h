@@ -176,12 +176,12 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
  *   / not written); y [batch, len, nheads, headdim] int32;
  * dt_out, da_out [batch, len, nheads] int32 Q.16 (required: dt and the decay
  *   are computed for every token first, then read by the scan).
- * headdim % 8 == 0, dstate in {64, 128}, len >= 1; y 16-byte and bm / cm
- * 4-byte aligned.  Workspace: fm_ssm_scan_pot_workspace_size() bytes (the
- * per-step float64 scalars of the prologue).
+ * headdim % 8 == 0, dstate in {64, 128}, len >= 1; y 8-byte and x 2-byte
+ * aligned.  Workspace: fm_ssm_scan_pot_workspace_size(batch, len, dstate)
+ * bytes (B and C widened to float64 by the prologue, 16*dstate bytes per
+ * token), caller-owned, contents undefined on entry and exit.
  * ---------------------------------------------------------------------- */
-size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t nheads,
-                                      int64_t headdim);
+size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t dstate);
 fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
                           const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
                           const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,

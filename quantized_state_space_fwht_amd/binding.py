@@ -80,7 +80,7 @@ _SIGS = {
     "fm_conv1d_pot": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp,
                                      ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _c_sz, _vp]),
-    "fm_ssm_scan_pot_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fm_ssm_scan_pot_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "fm_ssm_scan_pot": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _vp, _c_i64,
                                        _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _c_sz, _vp]),
@@ -173,8 +173,7 @@ def fm_ssm_scan_pot(x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p, 
                     nheads, headdim, dstate, state_in, state_out, y, dt_out=None, da_out=None,
                     ws=None, stream=None):
     if ws is None:
-        ws = workspace(lib.fm_ssm_scan_pot_workspace_size(batch, length, nheads, headdim),
-                       y.device)
+        ws = workspace(lib.fm_ssm_scan_pot_workspace_size(batch, length, dstate), y.device)
     _check(lib.fm_ssm_scan_pot(_ptr(x), _ptr(bm), _ptr(cm), dt_raw.data_ptr(), dt_row_stride,
                                _ptr(dt_bias), _ptr(a_q16), _ptr(d_q16), _ptr(p), batch, length,
                                nheads, headdim, dstate, _ptr(state_in), _ptr(state_out), _ptr(y),

@@ -238,10 +238,9 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
 }
 
 // ---------------------------------------------------------------- fm_ssm_scan_pot
-size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t nheads,
-                                      int64_t headdim) {
-    if (batch < 0 || len < 0 || nheads < 0 || headdim < 0) return 0;
-    return scan_ws_bytes(batch, len, nheads, headdim);
+size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t dstate) {
+    if (batch < 0 || len < 0 || dstate < 0) return 0;
+    return scan_ws_bytes(batch, len, dstate);
 }
 
 fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
@@ -261,8 +260,8 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
         batch * len * nheads >= ((int64_t)1 << 31) || batch * len * nheads * headdim >= ((int64_t)1 << 40))
         return fail(FM_ERR_SHAPE, "%s: need headdim %% 8 == 0, dstate in {64, 128}", who);
     if (dt_row_stride < nheads) return fail(FM_ERR_SHAPE, "%s: dt row stride < nheads", who);
-    if (!aligned(y, 16) || !aligned(bm, 4) || !aligned(cm, 4))
-        return fail(FM_ERR_SHAPE, "%s: y must be 16-byte, bm / cm 4-byte aligned", who);
+    if (!aligned(y, 8) || !aligned(x, 2))
+        return fail(FM_ERR_SHAPE, "%s: y must be 8-byte, x 2-byte aligned", who);
     ScanArgs a{};
     a.x = x;
     a.bm = bm;
@@ -284,7 +283,7 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
     a.dt_out = dt_out;
     a.da_out = da_out;
     fm_status st = check_ws(workspace, workspace_bytes,
-                            scan_ws_bytes(batch, len, nheads, headdim), who);
+                            scan_ws_bytes(batch, len, dstate), who);
     if (st != FM_OK) return st;
     return scan_run(a, workspace, stream);
 }

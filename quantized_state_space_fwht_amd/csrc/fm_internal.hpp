@@ -102,11 +102,10 @@ struct ScanArgs {
     int32_t* y;
     int32_t* dt_out;           // [T, H] written by the dt / decay prologue (required)
     int32_t* da_out;
-    const double* dak;         // set by scan_run: per (token, head) dA*2^-16 and K_t
-    const double* us;          // set by scan_run: per (token, head, p) dt*x*2^-8
+    const double* bc64;        // set by scan_run: B and C codes widened to float64
 };
-// workspace of the scan prologue (float64 per-step scalars)
-size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t nheads, int64_t headdim);
+// workspace of the scan prologue (B and C as float64 in the scan's layout)
+size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);
 fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s);
 
 struct GateArgs {

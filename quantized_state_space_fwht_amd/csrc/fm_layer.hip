@@ -62,7 +62,7 @@ static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void
     w.g_q = ar.take<int8_t>((size_t)T * di);
     w.dt = ar.take<int32_t>((size_t)T * H);
     w.da = ar.take<int32_t>((size_t)T * H);
-    w.scan_ws = ar.take<char>(scan_ws_bytes(batch, len, H, d->headdim));
+    w.scan_ws = ar.take<char>(scan_ws_bytes(batch, len, d->dstate));
     w.bytes = ar.used;
     return w;
 }

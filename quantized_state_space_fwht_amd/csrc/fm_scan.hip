@@ -6,31 +6,37 @@
 // (shift-based exponential for e^dt); Fig. 2 (the SSM recurrence and output).
 //
 // The integer recurrence, per (b, head, p, n):
-//     state = sat32(floor((dA*state + 2^8*dt*x*B + 2^15) / 2^16))
-// runs in float64 on integer-valued operands, on the biased state
-// hb = state + 2^31 in [0, 2^32):
-//     hb' = clamp(floor(dA*2^-16 * hb + (u * B + K_t)), 0, 2^32 - 1)
-//     u = dt*x*2^-8,  K_t = 2^31 * (1 - dA*2^-16) + 1/2
-// Both products are exact (<= 49 and 46 significant bits) and the fused sum
-// is exact whenever it lies within 2^33 of the int32 range (further out the
-// result saturates either way).  floor + clamp is one saturating
-// v_cvt_u32_f64.  So a step is two FMAs and two conversions — MI355X runs
-// float64 at full vector rate, while 32x32->64-bit integer multiplies run at a
-// quarter of it.  y uses sum_n C*state = sum_n C*hb - 2^31 * sum_n C.
+//     h' = sat32(floor((dA*h + 2^8*dt*x*B + 2^15) / 2^16))
+//        = sat32(floor(da*h + u*B + 1/2)),   da = dA*2^-16 <= 1,  u = dt*x*2^-8
+// runs in float64 on integer-valued operands: both products are exact and so
+// is the fused sum while it lies within 2^37 of zero (further out the result
+// saturates either way).  y = sum_n C*h stays an exact integer below 2^46.
 //
-// scan_prep_kernel runs first, over every (token, head): dt, the decay, and
-// the per-step float64 scalars (dA*2^-16, K_t) and u for every p, so that the
-// sequential scan reads them with wave-uniform scalar loads (SGPR operands,
-// no LDS traffic) and never waits on the exponential unit.
+// Fast and exact paths.  With da <= 1 and |B| <= 127, one step moves |h| by
+// at most |u|*127 + 1/2 (plus the floor's 1), so before a chunk of steps the
+// kernel bounds max|h| + sum_t (max_p |u_t| * 127 + 3/2) for the whole wave.
+// When that bound stays inside int32 the clamp cannot fire and a step is
+// fma, fma, floor; otherwise the chunk runs the clamped form (biased by 2^31
+// into a saturating unsigned conversion).  Both give the integer definition.
+//
+// scan_prep_kernel (one wave per token row): dt and the decay for every head
+// through the 2^v unit, and B, C widened to float64 in the layout the scan
+// reads ([token][lane][B pair, C pair] for d_state 128).
 //
 // scan_kernel: a workgroup of 4 waves owns (b, head, 8 consecutive p).  Lane l
-// of wave w owns the states (p, n) for p in {2w, 2w+1} and n = NN*l .. NN*l+NN-1
-// (d_state = 64*NN), so a wave reads each B/C value once for two p.  Time runs
-// in chunks of kTC steps: B and C of the chunk are staged in LDS as float32
-// (exact for int8 codes) while the next chunk's global loads are in flight;
-// per step each lane writes its partial sums of C*state (one per p) and after
-// the chunk the 64 partials of each (step, p) are added (exact: integers below
-// 2^46) and y is written.
+// of wave w owns the states (p, n) for p in {p0, p0+1} = {8g + 2w, 8g + 2w + 1}
+// and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time runs in chunks of 16 steps:
+//  - B/C of the next chunk are loaded into registers while the current chunk
+//    computes and written to the other LDS buffer after it (one barrier per
+//    chunk);
+//  - the per-step wave-uniform scalars (da, u of p0, u of p0+1) of a chunk sit
+//    one step per lane in each 16-lane row and are broadcast with DPP
+//    row_newbcast, so they cost no memory traffic inside the step loop;
+//  - the two partial sums of C*h (one per p) of each lane are paired across
+//    the wave halves by a lane swap, stored one per lane per step, and summed
+//    per (step, p) after the chunk.
+#include <utility>
+
 #include "fm_internal.hpp"
 
 namespace fm {
@@ -38,71 +44,97 @@ namespace fm {
 constexpr int kScanWaves = 4;
 constexpr int kScanThreads = 64 * kScanWaves;
 constexpr int kScanP = 2 * kScanWaves;  // p per workgroup
-constexpr int kTC = 16;                 // steps per chunk
+constexpr int kTC = 16;                 // steps per chunk (= lanes per DPP row)
+constexpr int kYRow = 66;               // doubles per partial-sum row (64 + pad)
 
 // ---------------------------------------------------------------- prologue
-// 4 (token, head) pairs per block of 256 threads; lane i of pair q handles
-// p = i, i + 64, ...
+// One wave per token row (4 rows per block).  Lane l widens B/C codes of its
+// n-group to float64; lanes also compute dt and dA for heads h = l, l + 64, ...
+template <int NN>
 __global__ __launch_bounds__(256) void scan_prep_kernel(
     const float* __restrict__ dt_raw, int64_t dt_stride, const float* __restrict__ bias,
-    const int32_t* __restrict__ a_q16, const int8_t* __restrict__ x, int64_t pairs, int H, int P,
-    int32_t* __restrict__ dt_out, int32_t* __restrict__ da_out, double* __restrict__ dak,
-    double* __restrict__ us) {
+    const int32_t* __restrict__ a_q16, const int8_t* __restrict__ bm,
+    const int8_t* __restrict__ cm, int64_t rows, int H, int32_t* __restrict__ dt_out,
+    int32_t* __restrict__ da_out, double* __restrict__ bc64) {
+    constexpr int N = 64 * NN;
     __shared__ NauLds tab;
-    __shared__ int32_t dts[4];
     nau_lds_init(tab);
     __syncthreads();
-    const int grp = threadIdx.x >> 6, i = threadIdx.x & 63;
-    const int64_t q = (int64_t)blockIdx.x * 4 + grp;  // (row, head) pair = row*H + h
-    if (q < pairs && i == 0) {
-        const int64_t row = q / H;
-        const int h = (int)(q - row * H);
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    double v[2 * NN];
+#pragma unroll
+    for (int j = 0; j < NN; ++j) {
+        v[j] = (double)bm[row * N + NN * lane + j];
+        v[NN + j] = (double)cm[row * N + NN * lane + j];
+    }
+    double* dst = bc64 + (row * 64 + lane) * (2 * NN);
+#pragma unroll
+    for (int j = 0; j < NN; ++j)
+        *reinterpret_cast<double2*>(dst + 2 * j) = make_double2(v[2 * j], v[2 * j + 1]);
+    for (int h = lane; h < H; h += 64) {
         const float raw = dt_raw[row * dt_stride + h];
         const int32_t dt_in = f2i_sat(rintf((raw + bias[h]) * 65536.0f));
         const int32_t dt = nau_softplus_f(dt_in, tab);
         const int32_t arg = sat32(rshr((int64_t)dt * (int64_t)a_q16[h], 16));
-        const int32_t da = nau_exp_f(arg, tab);
-        dt_out[q] = dt;
-        da_out[q] = da;
-        dak[2 * q] = (double)da * 0x1p-16;
-        dak[2 * q + 1] = 2147483648.0 - (double)da * 32768.0 + 0.5;
-        dts[grp] = dt;
-    }
-    __syncthreads();
-    if (q < pairs) {
-        const double dtd = (double)dts[grp] * 0x1p-8;  // exact: power-of-two scaling
-        for (int p = i; p < P; p += 64) us[q * P + p] = dtd * (double)x[q * P + p];
+        dt_out[row * H + h] = dt;
+        da_out[row * H + h] = nau_exp_f(arg, tab);
     }
 }
 
-// ---------------------------------------------------------------- scan
-// ypart layout: a row of kTC+1 doubles per lane; lanes 32..63 start 4 doubles
-// later and each (wave, p) plane is padded by 8 doubles, so that the writes
-// (one double per lane per step) and the reduction's reads (consecutive steps
-// across lanes, planes r = 0/1 and halves side by side) spread over the banks.
-constexpr int kYRow = kTC + 1;
-constexpr int kYPlane = 64 * kYRow + 4 + 8;
-__device__ __forceinline__ int ypart_at(int w, int r, int lane, int t) {
-    return (w * 2 + r) * kYPlane + lane * kYRow + (lane >= 32 ? 4 : 0) + t;
+// ---------------------------------------------------------------- lane helpers
+// value of lane T of this lane's 16-lane row (DPP row_newbcast)
+template <int T>
+__device__ __forceinline__ double row_bcast(double v) {
+    const long long r = __builtin_amdgcn_update_dpp(0LL, __builtin_bit_cast(long long, v),
+                                                    0x150 + T, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, r);
 }
+
+// lane l < 32 returns a(l) + a(l + 32); lane l >= 32 returns b(l - 32) + b(l)
+__device__ __forceinline__ double swap32_add(double a, double b) {
+    const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+    const auto lo = __builtin_amdgcn_permlane32_swap(ua.x, ub.x, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(ua.y, ub.y, false, false);
+    return __builtin_bit_cast(double, make_uint2(lo[0], hi[0])) +
+           __builtin_bit_cast(double, make_uint2(lo[1], hi[1]));
+}
+
+// float rotated within the 16-lane row by R lanes (DPP row_ror)
+template <int R>
+__device__ __forceinline__ float row_ror(float v) {
+    const int r = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + R, 0xF, 0xF,
+                                              false);
+    return __builtin_bit_cast(float, r);
+}
+
+// sum of a float over the 16 lanes of each row (every lane gets it)
+__device__ __forceinline__ float row_sum16(float v) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    v += row_ror<1>(v);
+    return v;
+}
+
+typedef double dpair __attribute__((ext_vector_type(2)));
 
 template <int NN>
 struct alignas(16) ScanSmem {
-    float Bf[kTC][64 * NN];
-    float Cf[kTC][64 * NN];
-    // partial sums, [wave][p of the wave][lane][step] (see ypart_at)
-    double ypart[kScanWaves * 2 * kYPlane];
-    int32_t sumC[kTC];
-    int32_t ystage[kTC][kScanP];
-    int8_t xs[kTC][kScanP];
+    double bc[2][kTC][64][2 * NN];         // [buffer][step][lane][B.., C..]
+    double ypart[kScanWaves][kTC][kYRow];  // [wave][step][lane]
 };
 
+template <int... Ts, class F>
+__device__ __forceinline__ void unroll_steps(std::integer_sequence<int, Ts...>, F&& f) {
+    (f(std::integral_constant<int, Ts>{}), ...);
+}
+
+// ---------------------------------------------------------------- scan
 template <int NN>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     constexpr int N = 64 * NN;
-    constexpr int kBytes = kTC * N / kScanThreads;  // B (and C) bytes staged per thread
-    constexpr int kThreadsPerRow = N / kBytes;
-    static_assert(kBytes == 4 || kBytes == 8, "staging split");
     __shared__ ScanSmem<NN> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -111,183 +143,238 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     const int64_t L = A.len;
     const int pg = blockIdx.x, head = blockIdx.y;
     const int64_t b = blockIdx.z;
+    const int p0 = pg * kScanP + 2 * w;  // this wave's two p: p0, p0 + 1
     const int ky = A.p[2] + A.p[3];
-    const int64_t d_h = A.d_q16[head];
-    const int64_t p0 = (int64_t)pg * kScanP + 2 * w;  // this wave's two p: p0, p0 + 1
+    const double dq = (double)A.d_q16[head];
+    const int i16 = lane & 15;
 
-    // biased states hb = state + 2^31 of (p0 + r, NN*lane + j)
-    double hb[2][NN];
+    // states h of (p0 + r, NN*lane + j)
+    double h[2][NN];
     const int64_t sbase = ((b * H + head) * P + p0) * N + NN * lane;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int j = 0; j < NN; ++j)
-            hb[r][j] = (A.state_in ? (double)A.state_in[sbase + r * N + j] : 0.0) + 2147483648.0;
+            h[r][j] = A.state_in ? (double)A.state_in[sbase + r * N + j] : 0.0;
 
-    // per-step scalars: (dA*2^-16, K_t) and (u of p0, u of p0+1), wave-uniform
-    const double* __restrict__ dak = A.dak + (b * L * H + head) * 2;
-    const double* __restrict__ usp = A.us + (b * L * H + head) * P + p0;
-    const int64_t dak_step = 2 * (int64_t)H, us_step = (int64_t)H * P;
-
-    // staging roles
-    const int st_t = tid / kThreadsPerRow, st_n = (tid % kThreadsPerRow) * kBytes;
-    int32_t rb[kBytes / 4] = {}, rc[kBytes / 4] = {};
-    int32_t rx = 0;
-    auto prefetch = [&](int64_t t0) {
-        if (t0 + st_t < L) {
-            const int32_t* pb = (const int32_t*)(A.bm + (b * L + t0 + st_t) * N + st_n);
-            const int32_t* pc = (const int32_t*)(A.cm + (b * L + t0 + st_t) * N + st_n);
-#pragma unroll
-            for (int k = 0; k < kBytes / 4; ++k) {
-                rb[k] = pb[k];
-                rc[k] = pc[k];
-            }
-        }
-        if (tid < kTC * kScanP && t0 + tid / kScanP < L)
-            rx = A.x[((b * L + t0 + tid / kScanP) * H + head) * P + (int64_t)pg * kScanP +
-                     tid % kScanP];
+    // ---- B/C staging: global -> registers at the top of a chunk, registers ->
+    //      LDS (the other buffer) at its end; thread k moves 16-byte pieces
+    //      k, k + 256, ... of the next chunk
+    constexpr int kPieces = kTC * 64 * 2 * NN * 8 / 16;  // 16-byte pieces per chunk
+    constexpr int kPer = kPieces / kScanThreads;
+    constexpr int kPiecesPerStep = 64 * 2 * NN * 8 / 16;
+    const double* __restrict__ bc_g = A.bc64 + b * L * (64 * 2 * NN);
+    dpair stg[kPer];
+    const auto pieces = std::make_integer_sequence<int, kPer>{};
+    auto stage_load = [&](int64_t t0) __attribute__((always_inline)) {
+        unroll_steps(pieces, [&](auto Mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(Mc)::value;
+            const int k = tid + kScanThreads * m;
+            const int64_t t = t0 + k / kPiecesPerStep;
+            if (t < L)
+                stg[m] = *reinterpret_cast<const dpair*>(bc_g + t * (64 * 2 * NN) +
+                                                         2 * (k % kPiecesPerStep));
+        });
     };
-    auto stage = [&]() {
-        int32_t csum = 0;
-#pragma unroll
-        for (int k = 0; k < kBytes / 4; ++k) {
-            float bv[4], cv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int32_t bi = (int8_t)(rb[k] >> (8 * e)), ci = (int8_t)(rc[k] >> (8 * e));
-                bv[e] = (float)bi;
-                cv[e] = (float)ci;
-                csum += ci;
-            }
-            *reinterpret_cast<float4*>(&sm.Bf[st_t][st_n + 4 * k]) =
-                make_float4(bv[0], bv[1], bv[2], bv[3]);
-            *reinterpret_cast<float4*>(&sm.Cf[st_t][st_n + 4 * k]) =
-                make_float4(cv[0], cv[1], cv[2], cv[3]);
-        }
-#pragma unroll
-        for (int m = 1; m < kThreadsPerRow; m <<= 1) csum += __shfl_xor(csum, m, kThreadsPerRow);
-        if (tid % kThreadsPerRow == 0) sm.sumC[st_t] = csum;
-        if (tid < kTC * kScanP) sm.xs[tid / kScanP][tid % kScanP] = (int8_t)rx;
+    auto stage_store = [&](int buf) __attribute__((always_inline)) {
+        dpair* dst = reinterpret_cast<dpair*>(&sm.bc[buf][0][0][0]);
+        unroll_steps(pieces, [&](auto Mc) __attribute__((always_inline)) {
+            constexpr int m = decltype(Mc)::value;
+            dst[tid + kScanThreads * m] = stg[m];
+        });
     };
 
-    // one step of the recurrence for this lane's 2*NN states; writes the two partials
-    auto step = [&](int t, int64_t tg) {
-        const double da = dak[tg * dak_step], kt = dak[tg * dak_step + 1];
-        const double u0 = usp[tg * us_step], u1 = usp[tg * us_step + 1];
-        double bv[NN], cv[NN];
-        if constexpr (NN == 2) {
-            const float2 bb = *reinterpret_cast<const float2*>(&sm.Bf[t][2 * lane]);
-            const float2 cc = *reinterpret_cast<const float2*>(&sm.Cf[t][2 * lane]);
-            bv[0] = bb.x;
-            bv[1] = bb.y;
-            cv[0] = cc.x;
-            cv[1] = cc.y;
-        } else {
-            bv[0] = sm.Bf[t][lane];
-            cv[0] = sm.Cf[t][lane];
+    // ---- per-step scalars: lane i of every row holds step t0 + i
+    int32_t pf_dt = 0, pf_da = 0;
+    uint32_t pf_x = 0;
+    auto prefetch = [&](int64_t t0) __attribute__((always_inline)) {
+        const int64_t t = t0 + i16;
+        if (t < L) {
+            const int64_t q = (b * L + t) * H + head;
+            pf_dt = A.dt_out[q];
+            pf_da = A.da_out[q];
+            pf_x = *reinterpret_cast<const uint16_t*>(A.x + q * P + p0);
         }
-        double y[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const double u = r ? u1 : u0;
-#pragma unroll
-            for (int j = 0; j < NN; ++j) {
-                const double sv = __builtin_fma(da, hb[r][j], __builtin_fma(u, bv[j], kt));
-                uint32_t hu;
-                // floor + clamp to [0, 2^32-1] in one instruction (saturating conversion)
-                asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
-                hb[r][j] = (double)hu;
-            }
-            y[r] = cv[0] * hb[r][0];
-#pragma unroll
-            for (int j = 1; j < NN; ++j) y[r] = __builtin_fma(cv[j], hb[r][j], y[r]);
-        }
-        sm.ypart[ypart_at(w, 0, lane, t)] = y[0];  // exact: integers below 2^40
-        sm.ypart[ypart_at(w, 1, lane, t)] = y[1];
     };
 
+    stage_load(0);
     prefetch(0);
-    stage();
+    stage_store(0);
     __syncthreads();
+
+    int buf = 0;
     for (int64_t t0 = 0; t0 < L; t0 += kTC) {
+        const int tc = (int)(L - t0 < kTC ? L - t0 : kTC);
+        // this chunk's scalars
+        const double uda = (double)pf_da * 0x1p-16;
+        const double dtd = (double)pf_dt * 0x1p-8;
+        const int32_t x0i = (int8_t)(pf_x & 0xFF), x1i = (int8_t)((pf_x >> 8) & 0xFF);
+        const double uu0 = dtd * (double)x0i, uu1 = dtd * (double)x1i;
+        // next chunk in flight
         const bool more = t0 + kTC < L;
-        if (more) prefetch(t0 + kTC);
-        int tc;
-        if (t0 + kTC <= L) {
-            tc = kTC;
-#pragma unroll
-            for (int t = 0; t < kTC; ++t) step(t, t0 + t);
-        } else {
-            tc = (int)(L - t0);
-            for (int t = 0; t < tc; ++t) step(t, t0 + t);
+        if (more) {
+            stage_load(t0 + kTC);
+            prefetch(t0 + kTC);
         }
-        __syncthreads();
-        // ---- y: lane l adds 32 of the 64 partials of output (r, t) = ((l%32)/16, l%16);
-        //      lanes l and l+32 then combine their halves
+
+        // ---- bound: can any state of this wave leave int32 within the chunk?
+        const float e = (float)__builtin_fma(
+            __builtin_fmax(__builtin_fabs(uu0), __builtin_fabs(uu1)), 127.0, 1.5);
+        const double S = (double)row_sum16(e) * (1.0 + 0x1p-16) + 16.0;
+        double hm = 0.0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int j = 0; j < NN; ++j) hm = __builtin_fmax(hm, __builtin_fabs(h[r][j]));
+        const bool exact_path = __any(hm + S > 2147483646.0);
+
+        const double(*bcs)[64][2 * NN] = sm.bc[buf];
+        double* yp = &sm.ypart[w][0][0];
+
+        // B/C of step T, read kAhead steps before use (program order keeps the
+        // read ahead of the partial-sum stores, which could alias it)
+        constexpr int kAhead = 2;
+        dpair ring[kAhead + 1][NN];
+        auto load_bc = [&](auto Tc) __attribute__((always_inline)) {
+            constexpr int T = decltype(Tc)::value;
+            if constexpr (T < kTC) {
+#pragma unroll
+                for (int q = 0; q < NN; ++q)
+                    ring[T % (kAhead + 1)][q] =
+                        *reinterpret_cast<const dpair*>(&bcs[T][lane][2 * q]);
+            }
+        };
+        auto step = [&](auto Tc, auto clamp, auto guard) __attribute__((always_inline)) {
+            constexpr int T = decltype(Tc)::value;
+            constexpr bool kClamp = decltype(clamp)::value;
+            load_bc(std::integral_constant<int, T + kAhead>{});
+            if constexpr (decltype(guard)::value)
+                if (T >= tc) return;
+            const double da = row_bcast<T>(uda);
+            const double u0 = row_bcast<T>(uu0), u1 = row_bcast<T>(uu1);
+            double bv[NN], cv[NN];
+            if constexpr (NN == 2) {
+                bv[0] = ring[T % (kAhead + 1)][0].x;
+                bv[1] = ring[T % (kAhead + 1)][0].y;
+                cv[0] = ring[T % (kAhead + 1)][1].x;
+                cv[1] = ring[T % (kAhead + 1)][1].y;
+            } else {
+                bv[0] = ring[T % (kAhead + 1)][0].x;
+                cv[0] = ring[T % (kAhead + 1)][0].y;
+            }
+            double y[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const double u = r ? u1 : u0;
+#pragma unroll
+                for (int j = 0; j < NN; ++j) {
+                    if constexpr (kClamp) {
+                        // h + 2^31 floored and clamped to [0, 2^32 - 1] by the conversion
+                        const double sv =
+                            __builtin_fma(da, h[r][j], __builtin_fma(u, bv[j], 2147483648.5));
+                        uint32_t hu;
+                        asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
+                        h[r][j] = (double)hu - 2147483648.0;
+                    } else {
+                        h[r][j] = __builtin_floor(
+                            __builtin_fma(da, h[r][j], __builtin_fma(u, bv[j], 0.5)));
+                    }
+                }
+                y[r] = cv[0] * h[r][0];
+#pragma unroll
+                for (int j = 1; j < NN; ++j) y[r] = __builtin_fma(cv[j], h[r][j], y[r]);
+            }
+            // lanes 0..31: p0 partial of lanes (l, l+32); lanes 32..63: p0+1
+            yp[T * kYRow + lane] = swap32_add(y[0], y[1]);
+        };
+        unroll_steps(std::make_integer_sequence<int, kAhead>{}, load_bc);
+        const auto steps = std::make_integer_sequence<int, kTC>{};
+        if (tc == kTC) {
+            if (exact_path)
+                unroll_steps(steps, [&](auto Tc) { step(Tc, std::true_type{}, std::false_type{}); });
+            else
+                unroll_steps(steps, [&](auto Tc) { step(Tc, std::false_type{}, std::false_type{}); });
+        } else {
+            if (exact_path)
+                unroll_steps(steps, [&](auto Tc) { step(Tc, std::true_type{}, std::true_type{}); });
+            else
+                unroll_steps(steps, [&](auto Tc) { step(Tc, std::false_type{}, std::true_type{}); });
+        }
+
+        // ---- y of the chunk: lane (t, r, half) adds 16 of the 32 partials of (t, p0 + r)
         {
-            const int o = lane & 31, half = lane >> 5;
-            const int r = o >> 4, t = o & 15;
-            double v[32];
+            const int t = lane & 15, r = (lane >> 4) & 1, half = lane >> 5;
+            const double* src = yp + t * kYRow + r * 32 + half * 16;
+            double v[8];
 #pragma unroll
-            for (int k = 0; k < 32; ++k) v[k] = sm.ypart[ypart_at(w, r, half * 32 + k, t)];
-#pragma unroll
-            for (int k = 16; k >= 1; k >>= 1)
-#pragma unroll
-                for (int i = 0; i < k; ++i) v[i] += v[i + k];
-            const double tot = v[0] + __shfl_xor(v[0], 32, 64);
-            if (half == 0 && t < tc) {
-                // sum_n C*state = sum_n C*hb - 2^31 * sum_n C (exact integers)
-                const int64_t yacc = (int64_t)tot - ((int64_t)sm.sumC[t] << 31);
-                const int pl = 2 * w + r;
-                const int64_t dterm = rshr(d_h * (int64_t)sm.xs[t][pl], 8);
-                sm.ystage[t][pl] = sat32(rshr(yacc, ky) + dterm);
+            for (int k = 0; k < 8; ++k) {
+                const double2 d2 = *reinterpret_cast<const double2*>(src + 2 * k);
+                v[k] = d2.x + d2.y;
+            }
+            const double part =
+                ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+            const double tot = swap32_add(part, part);  // lanes < 32: both halves
+            // y = sat32(rshr(tot, ky) + rshr(D*x, 8)) in exact float64 steps
+            const double xr = (double)(r ? x1i : x0i);
+            const double ya =
+                __builtin_floor(__builtin_fma(tot, __builtin_ldexp(1.0, -ky), 0.5));
+            const double yd = __builtin_floor(__builtin_fma(dq * xr, 0x1p-8, 0.5));
+            const double yv =
+                __builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
+            const int32_t yi = (int32_t)yv;
+            // lanes 0..15 take p0 + 1 from lanes 16..31 and store both p of step t
+            const auto sw =
+                __builtin_amdgcn_permlane16_swap((uint32_t)yi, (uint32_t)yi, false, false);
+            if (lane < 16 && t < tc) {
+                int32_t* dst = A.y + ((b * L + t0 + t) * H + head) * P + p0;
+                *reinterpret_cast<int2*>(dst) = make_int2(yi, (int32_t)sw[1]);
             }
         }
+
+        // the next chunk's B/C go to the other buffer (last read a chunk ago,
+        // before the previous barrier) and must be visible before anyone reads them
+        if (more) stage_store(buf ^ 1);
         __syncthreads();
-        // ---- write y rows (8 consecutive p per step) and stage the next chunk
-        if (tid < 2 * tc) {
-            const int t = tid >> 1, hf = tid & 1;
-            const int64_t yi = ((b * L + t0 + t) * H + head) * P + (int64_t)pg * kScanP + 4 * hf;
-            *reinterpret_cast<int4*>(A.y + yi) =
-                *reinterpret_cast<const int4*>(&sm.ystage[t][4 * hf]);
-        }
-        if (more) stage();
-        __syncthreads();
+        buf ^= 1;
     }
     if (A.state_out) {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int j = 0; j < NN; ++j)
-                A.state_out[sbase + r * N + j] = (int32_t)((uint32_t)hb[r][j] ^ 0x80000000u);
+            for (int j = 0; j < NN; ++j) A.state_out[sbase + r * N + j] = (int32_t)h[r][j];
     }
 }
 
-size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t nheads, int64_t headdim) {
-    const int64_t pairs = batch * len * nheads;
-    return align256((size_t)pairs * 2 * sizeof(double)) +
-           align256((size_t)(pairs * headdim) * sizeof(double));
+size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate) {
+    return align256((size_t)(batch * len) * (size_t)dstate * 2 * sizeof(double));
 }
 
 fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s) {
-    const int64_t pairs = a.batch * a.len * a.nheads;
+    const int64_t rows = a.batch * a.len;
     Arena ar(ws);
-    double* dak = ar.take<double>((size_t)pairs * 2);
-    double* us = ar.take<double>((size_t)(pairs * a.headdim));
+    double* bc64 = ar.take<double>((size_t)(rows * a.dstate * 2));
     ScanArgs k = a;
-    k.dak = dak;
-    k.us = us;
-    scan_prep_kernel<<<(unsigned)((pairs + 3) / 4), 256, 0, s>>>(
-        a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, a.x, pairs, (int)a.nheads, (int)a.headdim,
-        a.dt_out, a.da_out, dak, us);
-    fm_status st = check_launch("scan_prep_kernel");
-    if (st != FM_OK) return st;
+    k.bc64 = bc64;
+    const unsigned pgrid = (unsigned)((rows + 3) / 4);
     dim3 grid((unsigned)(a.headdim / kScanP), (unsigned)a.nheads, (unsigned)a.batch);
     switch (a.dstate) {
-        case 64: scan_kernel<1><<<grid, kScanThreads, 0, s>>>(k); break;
-        case 128: scan_kernel<2><<<grid, kScanThreads, 0, s>>>(k); break;
-        default: return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
+        case 64:
+            scan_prep_kernel<1><<<pgrid, 256, 0, s>>>(a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16,
+                                                       a.bm, a.cm, rows, (int)a.nheads, a.dt_out,
+                                                       a.da_out, bc64);
+            break;
+        case 128:
+            scan_prep_kernel<2><<<pgrid, 256, 0, s>>>(a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16,
+                                                       a.bm, a.cm, rows, (int)a.nheads, a.dt_out,
+                                                       a.da_out, bc64);
+            break;
+        default:
+            return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
     }
+    fm_status st = check_launch("scan_prep_kernel");
+    if (st != FM_OK) return st;
+    if (a.dstate == 64) scan_kernel<1><<<grid, kScanThreads, 0, s>>>(k);
+    else scan_kernel<2><<<grid, kScanThreads, 0, s>>>(k);
     return check_launch("scan_kernel");
 }
 

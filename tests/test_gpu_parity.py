@@ -191,6 +191,9 @@ def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
 @pytest.mark.parametrize("wname,batch,length,heads", [("tiny_layer", 1, 256, None),
                                                       ("tiny_layer", 2, 19, None),
                                                       ("m130m_layer", 1, 2048, None),
+                                                      ("m130m_layer", 3, 5, 2),
+                                                      ("m130m_layer", 1, 16, 2),
+                                                      ("m130m_layer", 2, 33, 3),
                                                       ("m2p7b_stack", 1, 300, 4)])
 @pytest.mark.parametrize("with_state", [False, True])
 def test_ssm_scan_pot(B, wname, batch, length, heads, with_state):
@@ -251,6 +254,41 @@ def test_ssm_scan_saturates_like_the_oracle(B):
     assert_exact(host(t_dt), dt, "dt (saturating)")
     assert_exact(host(t_y), y, "y (saturating)")
     assert_exact(host(t_st), st, "state (saturating)")
+
+
+def test_ssm_scan_mixed_saturation(B):
+    """Some states reach the int32 clamp part-way through a long sequence (decay
+    exactly 1, B and x of one sign) while others stay small: chunks before and
+    after the crossing, and workgroups that never get near it, must all agree."""
+    batch, length, H, P, N = 1, 181, 2, 16, 128
+    rng = np.random.default_rng(11)
+    x = rng.integers(-127, 128, size=(batch, length, H, P)).astype(np.int8)
+    x[:, :, 1, :8] = 127                        # head 1, first 8 p: one sign
+    bm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    bm[:, :, :64] = 127                         # n < 64: one sign
+    cm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    dt_raw = np.empty((batch * length, H), np.float32)
+    dt_raw[:, 0] = rng.uniform(-3, 0, batch * length)
+    dt_raw[:, 1] = rng.uniform(8.5, 9.5, batch * length)   # dt near 9 in Q.16
+    dt_bias = np.zeros(H, np.float32)
+    a_q16 = np.array([-3 * 65536, 0], np.int64)            # head 1: decay exactly 1
+    d_q16 = np.array([65536, 3 << 16], np.int64)
+    p = np.array([0, 7, 0, 0], np.int32)
+    state = rng.integers(-(1 << 20), 1 << 20, size=(batch, H, P, N)).astype(np.int32)
+    state[0, 0, 8:] = 2 ** 31 - 5                          # one workgroup starts at the edge
+    dt, dA = O.dt_dA(dt_raw.reshape(batch, length, H), dt_bias, a_q16)
+    y, st = O.ssm_scan_pot(x, bm, cm, dt, dA, d_q16, p[2], p[3], state)
+    assert np.any(st[0, 1, :8, :64] == 2 ** 31 - 1)
+    assert np.all(np.abs(st[0, 1, 8:]) < 2 ** 31 - 1)
+    t_y = torch.empty((batch, length, H, P), dtype=torch.int32, device="cuda")
+    t_st = torch.empty((batch, H, P, N), dtype=torch.int32, device="cuda")
+    t_dt = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+    t_da = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+    B.fm_ssm_scan_pot(dev(x), dev(bm), dev(cm), dev(dt_raw), H, dev(dt_bias),
+                      dev(a_q16, torch.int32), dev(d_q16, torch.int32), dev(p), batch, length, H,
+                      P, N, dev(state), t_st, t_y, t_dt, t_da)
+    assert_exact(host(t_y), y, "y (mixed)")
+    assert_exact(host(t_st), st, "state (mixed)")
 
 
 # --------------------------------------------------------------------------- a8
