@@ -176,10 +176,11 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
  *   / not written); y [batch, len, nheads, headdim] int32;
  * dt_out, da_out [batch, len, nheads] int32 Q.16 (required: dt and the decay
  *   are computed for every token first, then read by the scan).
- * headdim % 8 == 0, dstate in {64, 128}, len >= 1; y 8-byte and x 2-byte
+ * headdim % 8 == 0, dstate in {64, 128}, len >= 1, batch*len*nheads*headdim
+ * and batch*len*dstate below 2^31; y 8-byte, x 2-byte and bm / cm 16-byte
  * aligned.  Workspace: fm_ssm_scan_pot_workspace_size(batch, len, dstate)
- * bytes (B and C widened to float64 by the prologue, 16*dstate bytes per
- * token), caller-owned, contents undefined on entry and exit.
+ * bytes (currently 0: B and C are staged through on-chip memory; the
+ * workspace arguments are kept so that callers need not change if that does).
  * ---------------------------------------------------------------------- */
 size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t dstate);
 fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,

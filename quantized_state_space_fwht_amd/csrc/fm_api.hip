@@ -257,11 +257,14 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
         return fail(FM_ERR_NULL, "%s: a required pointer is NULL", who);
     if (batch < 1 || len < 1 || nheads < 1 || headdim < 8 || headdim % 8 ||
         (dstate != 64 && dstate != 128) || batch > 65535 || nheads > 65535 ||
-        batch * len * nheads >= ((int64_t)1 << 31) || batch * len * nheads * headdim >= ((int64_t)1 << 40))
-        return fail(FM_ERR_SHAPE, "%s: need headdim %% 8 == 0, dstate in {64, 128}", who);
+        batch * len * nheads * headdim >= ((int64_t)1 << 31) ||
+        batch * len * dstate >= ((int64_t)1 << 31))
+        return fail(FM_ERR_SHAPE,
+                    "%s: need headdim %% 8 == 0, dstate in {64, 128}, batch*len*nheads*headdim "
+                    "and batch*len*dstate below 2^31", who);
     if (dt_row_stride < nheads) return fail(FM_ERR_SHAPE, "%s: dt row stride < nheads", who);
-    if (!aligned(y, 8) || !aligned(x, 2))
-        return fail(FM_ERR_SHAPE, "%s: y must be 8-byte, x 2-byte aligned", who);
+    if (!aligned(y, 8) || !aligned(x, 2) || !aligned(bm, 16) || !aligned(cm, 16))
+        return fail(FM_ERR_SHAPE, "%s: y must be 8-byte, x 2-byte, bm / cm 16-byte aligned", who);
     ScanArgs a{};
     a.x = x;
     a.bm = bm;

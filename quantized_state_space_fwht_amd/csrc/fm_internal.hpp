@@ -102,9 +102,8 @@ struct ScanArgs {
     int32_t* y;
     int32_t* dt_out;           // [T, H] written by the dt / decay prologue (required)
     int32_t* da_out;
-    const double* bc64;        // set by scan_run: B and C codes widened to float64
 };
-// workspace of the scan prologue (B and C as float64 in the scan's layout)
+// workspace of the scan (none: B and C are staged through LDS)
 size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);
 fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s);
 

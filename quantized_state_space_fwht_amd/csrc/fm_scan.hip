@@ -19,22 +19,21 @@
 // fma, fma, floor; otherwise the chunk runs the clamped form (biased by 2^31
 // into a saturating unsigned conversion).  Both give the integer definition.
 //
-// scan_prep_kernel (one wave per token row): dt and the decay for every head
-// through the 2^v unit, and B, C widened to float64 in the layout the scan
-// reads ([token][lane][B pair, C pair] for d_state 128).
+// scan_prep_kernel: dt and the decay for every (token, head) through the 2^v
+// unit, before the scan reads them.
 //
 // scan_kernel: a workgroup of 4 waves owns (b, head, 8 consecutive p).  Lane l
 // of wave w owns the states (p, n) for p in {p0, p0+1} = {8g + 2w, 8g + 2w + 1}
-// and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time runs in chunks of 16 steps:
-//  - B/C of the next chunk are loaded into registers while the current chunk
-//    computes and written to the other LDS buffer after it (one barrier per
-//    chunk);
+// and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time runs in chunks of 16
+// steps, one barrier per chunk:
 //  - the per-step wave-uniform scalars (da, u of p0, u of p0+1) of a chunk sit
 //    one step per lane in each 16-lane row and are broadcast with DPP
 //    row_newbcast, so they cost no memory traffic inside the step loop;
-//  - the two partial sums of C*h (one per p) of each lane are paired across
-//    the wave halves by a lane swap, stored one per lane per step, and summed
-//    per (step, p) after the chunk.
+//  - B/C codes (int8) of the next chunk are loaded while a chunk runs and
+//    written to the other LDS buffer, widened to float64, after it;
+//  - the two partial sums of C*h of each lane (one per p) are paired across
+//    the wave halves by a lane swap and stored, one per lane per step; after
+//    the chunk they are added per (step, p) and y is written.
 #include <utility>
 
 #include "fm_internal.hpp"
@@ -48,39 +47,24 @@ constexpr int kTC = 16;                 // steps per chunk (= lanes per DPP row)
 constexpr int kYRow = 66;               // doubles per partial-sum row (64 + pad)
 
 // ---------------------------------------------------------------- prologue
-// One wave per token row (4 rows per block).  Lane l widens B/C codes of its
-// n-group to float64; lanes also compute dt and dA for heads h = l, l + 64, ...
-template <int NN>
+// One thread per (token, head): dt and the decay through the 2^v unit.
 __global__ __launch_bounds__(256) void scan_prep_kernel(
     const float* __restrict__ dt_raw, int64_t dt_stride, const float* __restrict__ bias,
-    const int32_t* __restrict__ a_q16, const int8_t* __restrict__ bm,
-    const int8_t* __restrict__ cm, int64_t rows, int H, int32_t* __restrict__ dt_out,
-    int32_t* __restrict__ da_out, double* __restrict__ bc64) {
-    constexpr int N = 64 * NN;
+    const int32_t* __restrict__ a_q16, int64_t pairs, int H, int32_t* __restrict__ dt_out,
+    int32_t* __restrict__ da_out) {
     __shared__ NauLds tab;
     nau_lds_init(tab);
     __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    double v[2 * NN];
-#pragma unroll
-    for (int j = 0; j < NN; ++j) {
-        v[j] = (double)bm[row * N + NN * lane + j];
-        v[NN + j] = (double)cm[row * N + NN * lane + j];
-    }
-    double* dst = bc64 + (row * 64 + lane) * (2 * NN);
-#pragma unroll
-    for (int j = 0; j < NN; ++j)
-        *reinterpret_cast<double2*>(dst + 2 * j) = make_double2(v[2 * j], v[2 * j + 1]);
-    for (int h = lane; h < H; h += 64) {
-        const float raw = dt_raw[row * dt_stride + h];
-        const int32_t dt_in = f2i_sat(rintf((raw + bias[h]) * 65536.0f));
-        const int32_t dt = nau_softplus_f(dt_in, tab);
-        const int32_t arg = sat32(rshr((int64_t)dt * (int64_t)a_q16[h], 16));
-        dt_out[row * H + h] = dt;
-        da_out[row * H + h] = nau_exp_f(arg, tab);
-    }
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // = row * H + h
+    if (q >= pairs) return;
+    const int64_t row = q / H;
+    const int h = (int)(q - row * H);
+    const float raw = dt_raw[row * dt_stride + h];
+    const int32_t dt_in = f2i_sat(rintf((raw + bias[h]) * 65536.0f));
+    const int32_t dt = nau_softplus_f(dt_in, tab);
+    const int32_t arg = sat32(rshr((int64_t)dt * (int64_t)a_q16[h], 16));
+    dt_out[q] = dt;
+    da_out[q] = nau_exp_f(arg, tab);
 }
 
 // ---------------------------------------------------------------- lane helpers
@@ -122,8 +106,8 @@ typedef double dpair __attribute__((ext_vector_type(2)));
 
 template <int NN>
 struct alignas(16) ScanSmem {
-    double bc[2][kTC][64][2 * NN];         // [buffer][step][lane][B.., C..]
-    double ypart[kScanWaves][kTC][kYRow];  // [wave][step][lane]
+    double bc[2][kTC][2 * 64 * NN];           // [chunk parity][step][B row, C row]
+    double ypart[kScanWaves][kTC][kYRow];     // [wave][step][lane]
 };
 
 template <int... Ts, class F>
@@ -147,6 +131,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     const int ky = A.p[2] + A.p[3];
     const double dq = (double)A.d_q16[head];
     const int i16 = lane & 15;
+    const int64_t nchunks = (L + kTC - 1) / kTC;
 
     // states h of (p0 + r, NN*lane + j)
     double h[2][NN];
@@ -157,67 +142,67 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
         for (int j = 0; j < NN; ++j)
             h[r][j] = A.state_in ? (double)A.state_in[sbase + r * N + j] : 0.0;
 
-    // ---- B/C staging: global -> registers at the top of a chunk, registers ->
-    //      LDS (the other buffer) at its end; thread k moves 16-byte pieces
-    //      k, k + 256, ... of the next chunk
-    constexpr int kPieces = kTC * 64 * 2 * NN * 8 / 16;  // 16-byte pieces per chunk
-    constexpr int kPer = kPieces / kScanThreads;
-    constexpr int kPiecesPerStep = 64 * 2 * NN * 8 / 16;
-    const double* __restrict__ bc_g = A.bc64 + b * L * (64 * 2 * NN);
-    dpair stg[kPer];
-    const auto pieces = std::make_integer_sequence<int, kPer>{};
-    auto stage_load = [&](int64_t t0) __attribute__((always_inline)) {
-        unroll_steps(pieces, [&](auto Mc) __attribute__((always_inline)) {
-            constexpr int m = decltype(Mc)::value;
-            const int k = tid + kScanThreads * m;
-            const int64_t t = t0 + k / kPiecesPerStep;
-            if (t < L)
-                stg[m] = *reinterpret_cast<const dpair*>(bc_g + t * (64 * 2 * NN) +
-                                                         2 * (k % kPiecesPerStep));
-        });
+    // ---- B/C staging.  Thread k < kLoaders owns 16 consecutive codes (B or C,
+    //      one step of a chunk, n = 16g .. 16g+15): a 16-byte load while the
+    //      previous chunk runs, eight 16-byte LDS stores of float64 pairs after it.
+    //      d_state 128: the pair of lane l sits in slot bc_slot(l) of its row,
+    //      which keeps both the stores (writers of one step hit 8 different
+    //      16-byte columns per instruction) and the step reads conflict-free.
+    constexpr int kGroups = N / 16;              // 16-code groups per row
+    constexpr int kLoaders = 2 * kTC * kGroups;  // 256 (d_state 128) or 128
+    const int ld_which = tid / (kTC * kGroups);  // 0: B, 1: C
+    const int ld_step = (tid / kGroups) % kTC;
+    const int ld_g = tid % kGroups;
+    const int8_t* __restrict__ ld_src = (ld_which ? A.cm : A.bm) + (int64_t)b * L * N + ld_g * 16;
+    int4 stg = make_int4(0, 0, 0, 0);
+    // chunk c's codes into stg (rows past the end repeat the last row: unused)
+    auto stage_load = [&](int64_t c) __attribute__((always_inline)) {
+        if (tid < kLoaders) {
+            const int64_t t = c * kTC + ld_step < L ? c * kTC + ld_step : L - 1;
+            stg = *reinterpret_cast<const int4*>(ld_src + (uint32_t)t * (uint32_t)N);
+        }
     };
-    auto stage_store = [&](int buf) __attribute__((always_inline)) {
-        dpair* dst = reinterpret_cast<dpair*>(&sm.bc[buf][0][0][0]);
-        unroll_steps(pieces, [&](auto Mc) __attribute__((always_inline)) {
-            constexpr int m = decltype(Mc)::value;
-            dst[tid + kScanThreads * m] = stg[m];
-        });
+    // stg into LDS buffer `par`
+    auto stage_store = [&](int par) __attribute__((always_inline)) {
+        if (tid < kLoaders) {
+            double* row = &sm.bc[par][ld_step][ld_which * N];
+            const int32_t wv[4] = {stg.x, stg.y, stg.z, stg.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int32_t word = wv[q >> 1];
+                const int sh = (q & 1) * 16;
+                const dpair v = {(double)(int8_t)(word >> sh), (double)(int8_t)(word >> (sh + 8))};
+                // codes 16g + 2q, +1: the pair of lane 8g + q (d_state 128)
+                const int slot = NN == 2 ? 8 * ld_g + ((q + ld_g) & 7) : 8 * ld_g + q;
+                *reinterpret_cast<dpair*>(row + 2 * slot) = v;
+            }
+        }
     };
+    const int bc_slot = NN == 2 ? (lane & ~7) + (((lane & 7) + (lane >> 3)) & 7) : 0;
 
-    // ---- per-step scalars: lane i of every row holds step t0 + i
+    // ---- per-step scalars: lane i of every row holds step 16c + i of chunk c
     int32_t pf_dt = 0, pf_da = 0;
     uint32_t pf_x = 0;
-    auto prefetch = [&](int64_t t0) __attribute__((always_inline)) {
-        const int64_t t = t0 + i16;
-        if (t < L) {
-            const int64_t q = (b * L + t) * H + head;
-            pf_dt = A.dt_out[q];
-            pf_da = A.da_out[q];
-            pf_x = *reinterpret_cast<const uint16_t*>(A.x + q * P + p0);
-        }
+    auto prefetch = [&](int64_t c) __attribute__((always_inline)) {
+        const int64_t t = c * kTC + i16 < L ? c * kTC + i16 : L - 1;  // past the end: unused
+        const uint32_t q = ((uint32_t)b * (uint32_t)L + (uint32_t)t) * (uint32_t)H + head;
+        pf_dt = A.dt_out[q];
+        pf_da = A.da_out[q];
+        pf_x = *reinterpret_cast<const uint16_t*>(A.x + (q * (uint32_t)P + p0));
     };
-
-    stage_load(0);
-    prefetch(0);
-    stage_store(0);
-    __syncthreads();
-
-    int buf = 0;
-    for (int64_t t0 = 0; t0 < L; t0 += kTC) {
-        const int tc = (int)(L - t0 < kTC ? L - t0 : kTC);
-        // this chunk's scalars
-        const double uda = (double)pf_da * 0x1p-16;
+    // scalars of the chunk about to run
+    double uda = 0.0, uu0 = 0.0, uu1 = 0.0;
+    int32_t x0i = 0, x1i = 0;
+    auto setup = [&]() __attribute__((always_inline)) {
+        uda = (double)pf_da * 0x1p-16;
         const double dtd = (double)pf_dt * 0x1p-8;
-        const int32_t x0i = (int8_t)(pf_x & 0xFF), x1i = (int8_t)((pf_x >> 8) & 0xFF);
-        const double uu0 = dtd * (double)x0i, uu1 = dtd * (double)x1i;
-        // next chunk in flight
-        const bool more = t0 + kTC < L;
-        if (more) {
-            stage_load(t0 + kTC);
-            prefetch(t0 + kTC);
-        }
-
-        // ---- bound: can any state of this wave leave int32 within the chunk?
+        x0i = (int8_t)(pf_x & 0xFF);
+        x1i = (int8_t)((pf_x >> 8) & 0xFF);
+        uu0 = dtd * (double)x0i;  // exact: dt * x < 2^38
+        uu1 = dtd * (double)x1i;
+    };
+    // bound: can any state of this wave leave int32 within the chunk?
+    auto needs_clamp = [&]() __attribute__((always_inline)) {
         const float e = (float)__builtin_fma(
             __builtin_fmax(__builtin_fabs(uu0), __builtin_fabs(uu1)), 127.0, 1.5);
         const double S = (double)row_sum16(e) * (1.0 + 0x1p-16) + 16.0;
@@ -226,42 +211,90 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int j = 0; j < NN; ++j) hm = __builtin_fmax(hm, __builtin_fabs(h[r][j]));
-        const bool exact_path = __any(hm + S > 2147483646.0);
+        return __any(hm + S > 2147483646.0);
+    };
+    // partial sums of the chunk just run -> y codes; lane l < 16 returns (y of
+    // p0, y of p0 + 1) of step l
+    auto reduce = [&]() __attribute__((always_inline)) {
+        const int t = lane & 15, r = (lane >> 4) & 1, half = lane >> 5;
+        const double* src = &sm.ypart[w][t][r * 32 + half * 16];
+        double v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const dpair d2 = *reinterpret_cast<const dpair*>(src + 2 * k);
+            v[k] = d2.x + d2.y;
+        }
+        const double part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        const double tot = swap32_add(part, part);  // every lane: both halves of (t, r)
+        // y = sat32(rshr(tot, ky) + rshr(D*x, 8)) in exact float64 steps
+        const double xr = (double)(r ? x1i : x0i);
+        const double ya = __builtin_floor(__builtin_fma(tot, __builtin_ldexp(1.0, -ky), 0.5));
+        const double yd = __builtin_floor(__builtin_fma(dq * xr, 0x1p-8, 0.5));
+        const double yv = __builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
+        const int32_t yi = (int32_t)yv;
+        // lanes 0..15 take p0 + 1 from lanes 16..31
+        const auto sw = __builtin_amdgcn_permlane16_swap((uint32_t)yi, (uint32_t)yi, false, false);
+        return make_int2(yi, (int32_t)sw[1]);
+    };
+    // y of chunk c from reduce(): lanes 0..15, one step each
+    auto write_y = [&](int64_t c, int2 yy) __attribute__((always_inline)) {
+        const int tcc = (int)(L - c * kTC < kTC ? L - c * kTC : kTC);
+        if (lane < tcc) {
+            int32_t* dst = A.y + (((uint32_t)b * (uint32_t)L + (uint32_t)(c * kTC + lane)) *
+                                      (uint32_t)H + head) * (uint32_t)P + p0;
+            *reinterpret_cast<int2*>(dst) = yy;
+        }
+    };
 
-        const double(*bcs)[64][2 * NN] = sm.bc[buf];
+    stage_load(0);
+    prefetch(0);
+    stage_store(0);
+    __syncthreads();
+
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int par = (int)(c & 1);
+        const int tc = (int)(L - c * kTC < kTC ? L - c * kTC : kTC);
+        setup();  // this chunk's scalars
+        const bool more = c + 1 < nchunks;
+        if (more) {  // next chunk in flight
+            stage_load(c + 1);
+            prefetch(c + 1);
+        }
+        const bool clamp = needs_clamp();
+        const double(*bcs)[2 * N] = sm.bc[par];
         double* yp = &sm.ypart[w][0][0];
 
         // B/C of step T, read kAhead steps before use (program order keeps the
         // read ahead of the partial-sum stores, which could alias it)
         constexpr int kAhead = 2;
-        dpair ring[kAhead + 1][NN];
+        double ring[kAhead + 1][2 * NN];  // B of n = NN*lane.., then C
         auto load_bc = [&](auto Tc) __attribute__((always_inline)) {
             constexpr int T = decltype(Tc)::value;
             if constexpr (T < kTC) {
-#pragma unroll
-                for (int q = 0; q < NN; ++q)
-                    ring[T % (kAhead + 1)][q] =
-                        *reinterpret_cast<const dpair*>(&bcs[T][lane][2 * q]);
+                double* o = ring[T % (kAhead + 1)];
+                if constexpr (NN == 2) {
+                    const dpair bb = *reinterpret_cast<const dpair*>(&bcs[T][2 * bc_slot]);
+                    const dpair cc = *reinterpret_cast<const dpair*>(&bcs[T][N + 2 * bc_slot]);
+                    o[0] = bb.x;
+                    o[1] = bb.y;
+                    o[2] = cc.x;
+                    o[3] = cc.y;
+                } else {
+                    o[0] = bcs[T][lane];
+                    o[1] = bcs[T][N + lane];
+                }
             }
         };
-        auto step = [&](auto Tc, auto clamp, auto guard) __attribute__((always_inline)) {
+        auto step = [&](auto Tc, auto clampc, auto guard) __attribute__((always_inline)) {
             constexpr int T = decltype(Tc)::value;
-            constexpr bool kClamp = decltype(clamp)::value;
+            constexpr bool kClamp = decltype(clampc)::value;
             load_bc(std::integral_constant<int, T + kAhead>{});
             if constexpr (decltype(guard)::value)
                 if (T >= tc) return;
             const double da = row_bcast<T>(uda);
             const double u0 = row_bcast<T>(uu0), u1 = row_bcast<T>(uu1);
-            double bv[NN], cv[NN];
-            if constexpr (NN == 2) {
-                bv[0] = ring[T % (kAhead + 1)][0].x;
-                bv[1] = ring[T % (kAhead + 1)][0].y;
-                cv[0] = ring[T % (kAhead + 1)][1].x;
-                cv[1] = ring[T % (kAhead + 1)][1].y;
-            } else {
-                bv[0] = ring[T % (kAhead + 1)][0].x;
-                cv[0] = ring[T % (kAhead + 1)][0].y;
-            }
+            const double* bv = ring[T % (kAhead + 1)];
+            const double* cv = bv + NN;
             double y[2];
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -290,52 +323,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
         unroll_steps(std::make_integer_sequence<int, kAhead>{}, load_bc);
         const auto steps = std::make_integer_sequence<int, kTC>{};
         if (tc == kTC) {
-            if (exact_path)
+            if (clamp)
                 unroll_steps(steps, [&](auto Tc) { step(Tc, std::true_type{}, std::false_type{}); });
             else
                 unroll_steps(steps, [&](auto Tc) { step(Tc, std::false_type{}, std::false_type{}); });
         } else {
-            if (exact_path)
+            if (clamp)
                 unroll_steps(steps, [&](auto Tc) { step(Tc, std::true_type{}, std::true_type{}); });
             else
                 unroll_steps(steps, [&](auto Tc) { step(Tc, std::false_type{}, std::true_type{}); });
         }
-
-        // ---- y of the chunk: lane (t, r, half) adds 16 of the 32 partials of (t, p0 + r)
-        {
-            const int t = lane & 15, r = (lane >> 4) & 1, half = lane >> 5;
-            const double* src = yp + t * kYRow + r * 32 + half * 16;
-            double v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const double2 d2 = *reinterpret_cast<const double2*>(src + 2 * k);
-                v[k] = d2.x + d2.y;
-            }
-            const double part =
-                ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-            const double tot = swap32_add(part, part);  // lanes < 32: both halves
-            // y = sat32(rshr(tot, ky) + rshr(D*x, 8)) in exact float64 steps
-            const double xr = (double)(r ? x1i : x0i);
-            const double ya =
-                __builtin_floor(__builtin_fma(tot, __builtin_ldexp(1.0, -ky), 0.5));
-            const double yd = __builtin_floor(__builtin_fma(dq * xr, 0x1p-8, 0.5));
-            const double yv =
-                __builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
-            const int32_t yi = (int32_t)yv;
-            // lanes 0..15 take p0 + 1 from lanes 16..31 and store both p of step t
-            const auto sw =
-                __builtin_amdgcn_permlane16_swap((uint32_t)yi, (uint32_t)yi, false, false);
-            if (lane < 16 && t < tc) {
-                int32_t* dst = A.y + ((b * L + t0 + t) * H + head) * P + p0;
-                *reinterpret_cast<int2*>(dst) = make_int2(yi, (int32_t)sw[1]);
-            }
-        }
-
+        write_y(c, reduce());
         // the next chunk's B/C go to the other buffer (last read a chunk ago,
         // before the previous barrier) and must be visible before anyone reads them
-        if (more) stage_store(buf ^ 1);
+        if (more) stage_store(par ^ 1);
         __syncthreads();
-        buf ^= 1;
     }
     if (A.state_out) {
 #pragma unroll
@@ -345,36 +347,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     }
 }
 
-size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate) {
-    return align256((size_t)(batch * len) * (size_t)dstate * 2 * sizeof(double));
-}
+size_t scan_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s) {
-    const int64_t rows = a.batch * a.len;
-    Arena ar(ws);
-    double* bc64 = ar.take<double>((size_t)(rows * a.dstate * 2));
-    ScanArgs k = a;
-    k.bc64 = bc64;
-    const unsigned pgrid = (unsigned)((rows + 3) / 4);
-    dim3 grid((unsigned)(a.headdim / kScanP), (unsigned)a.nheads, (unsigned)a.batch);
-    switch (a.dstate) {
-        case 64:
-            scan_prep_kernel<1><<<pgrid, 256, 0, s>>>(a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16,
-                                                       a.bm, a.cm, rows, (int)a.nheads, a.dt_out,
-                                                       a.da_out, bc64);
-            break;
-        case 128:
-            scan_prep_kernel<2><<<pgrid, 256, 0, s>>>(a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16,
-                                                       a.bm, a.cm, rows, (int)a.nheads, a.dt_out,
-                                                       a.da_out, bc64);
-            break;
-        default:
-            return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
-    }
+fm_status scan_run(const ScanArgs& a, void*, hipStream_t s) {
+    const int64_t pairs = a.batch * a.len * a.nheads;
+    scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
+        a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
     fm_status st = check_launch("scan_prep_kernel");
     if (st != FM_OK) return st;
-    if (a.dstate == 64) scan_kernel<1><<<grid, kScanThreads, 0, s>>>(k);
-    else scan_kernel<2><<<grid, kScanThreads, 0, s>>>(k);
+    dim3 grid((unsigned)(a.headdim / kScanP), (unsigned)a.nheads, (unsigned)a.batch);
+    switch (a.dstate) {
+        case 64: scan_kernel<1><<<grid, kScanThreads, 0, s>>>(a); break;
+        case 128: scan_kernel<2><<<grid, kScanThreads, 0, s>>>(a); break;
+        default: return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
+    }
     return check_launch("scan_kernel");
 }
 

@@ -83,8 +83,8 @@ def test_scan_validation(lib):
     assert f(*bad) == FM_ERR_SHAPE
     bad = list(ok); bad[17] = None        # dt_out required
     assert f(*bad) == FM_ERR_NULL
-    bad = list(ok); bad[19] = None        # workspace required
-    assert f(*bad) == FM_ERR_WORKSPACE
+    bad = list(ok); bad[1] = fake + 4     # B codes must be 16-byte aligned
+    assert f(*bad) == FM_ERR_SHAPE
 
 
 class Desc(ctypes.Structure):
