@@ -22,101 +22,135 @@ struct ConvKParams {
     int dynamic;
 };
 
-__device__ __forceinline__ int8_t quant_xbc(float v, float scale) {
-    return (int8_t)fminf(fmaxf(rintf(v * scale), -127.0f), 127.0f);
+__device__ __forceinline__ int32_t quant_xbc(float v, float scale) {
+    return (int32_t)fminf(fmaxf(rintf(v * scale), -127.0f), 127.0f);
 }
 
+// clamp(floor(v + 1/2)) to int32 for an integer-valued or half-step v
+__device__ __forceinline__ int32_t round_sat32(double v) {
+    return (int32_t)__builtin_fmin(__builtin_fmax(__builtin_floor(v + 0.5), -2147483648.0),
+                                   2147483647.0);
+}
+
+// One thread: channel c, steps t0 .. t0+n-1 (n = kConvTL unless kTail).
 // Dynamic: writes Q.16 SiLU outputs + per-part maxima.  Static: writes codes.
+template <bool kTail, bool kDyn, bool kXq>
+__device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLds& tab, int c,
+                                               int64_t row0, int64_t t0, int n, int p_c,
+                                               int part, int32_t& amax, float& xmax) {
+    const ConvArgs& A = K.a;
+    const int di = (int)A.d_inner, N = (int)A.dstate;
+    const float qscale = ldexpf(1.0f, p_c);
+    const int32_t w0 = A.w_q[c * 4 + 0], w1 = A.w_q[c * 4 + 1], w2 = A.w_q[c * 4 + 2],
+                  w3 = A.w_q[c * 4 + 3];
+    // a = sat32(rshr(acc, sh) + bias): acc * 2^-sh is exact in float64 (|acc| < 2^17)
+    const double ascale = __builtin_ldexp(1.0, 16 - p_c - A.p_w[c]);
+    const double bias = (double)A.b_q16[c];
+    const float* xrow = A.xbc + row0 * A.xbc_stride + c;  // step t0
+    const uint32_t xs = (uint32_t)A.xbc_stride;
+    // every load of the run issued up front (3 window inputs + the new ones)
+    float win[3];
+    float xv[kConvTL];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) win[j] = t0 > 0 ? xrow[-(int64_t)(3 - j) * A.xbc_stride] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kConvTL; ++i) xv[i] = (!kTail || i < n) ? xrow[(uint32_t)i * xs] : 0.0f;
+    int32_t xm3, xm2, xm1;  // codes at t-3, t-2, t-1
+    if (t0 == 0) {
+        if (A.state_in) {
+            const int8_t* st = A.state_in + (row0 / A.len * K.ch + c) * 3;
+            xm3 = st[0];
+            xm2 = st[1];
+            xm1 = st[2];
+        } else {
+            xm3 = xm2 = xm1 = 0;
+        }
+    } else {  // t0 >= kConvTL >= 3: the window lies inside this call's input
+        xm3 = quant_xbc(win[0], qscale);
+        xm2 = quant_xbc(win[1], qscale);
+        xm1 = quant_xbc(win[2], qscale);
+    }
+    // outputs of this thread: element (row0 + i, c) of [rows, ch] / of the part
+    const int p_part = kDyn ? 0 : A.p_fixed[1 + part];
+    const double oscale = __builtin_ldexp(1.0, p_part - 16);
+    int32_t* s16 = kDyn ? A.s16 + row0 * K.ch + c : nullptr;
+    int8_t* code = nullptr;
+    uint32_t cstride = 0;
+    if (!kDyn) {
+        if (part == 0) code = A.x_out + row0 * di + c, cstride = (uint32_t)di;
+        else if (part == 1) code = A.b_out + row0 * N + (c - di), cstride = (uint32_t)N;
+        else code = A.c_out + row0 * N + (c - di - N), cstride = (uint32_t)N;
+    }
+    int8_t* xq_out = kXq ? A.xbc_q + row0 * K.ch + c : nullptr;
+#pragma unroll
+    for (int i = 0; i < kConvTL; ++i) {
+        if (kTail && i >= n) continue;
+        const float xv_i = xv[i];
+        xmax = fmaxf(xmax, fabsf(xv_i));
+        const int32_t xq = quant_xbc(xv_i, qscale);
+        if constexpr (kXq) xq_out[(uint32_t)i * (uint32_t)K.ch] = (int8_t)xq;
+        const int32_t acc = w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq;
+        const int32_t a = round_sat32(__builtin_fma((double)acc, ascale, bias));
+        const int32_t sv = nau_silu_f(a, tab);
+        const int32_t sa = sv < 0 ? -sv : sv;
+        amax = sa > amax ? sa : amax;
+        if constexpr (kDyn) {
+            s16[(uint32_t)i * (uint32_t)K.ch] = sv;
+        } else {
+            // sat8(rshr(sv, 16 - p_part)): sv * 2^(p_part-16) is exact in float64
+            const double q = __builtin_floor(__builtin_fma((double)sv, oscale, 0.5));
+            code[(uint32_t)i * cstride] = (int8_t)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
+        }
+        xm3 = xm2;
+        xm2 = xm1;
+        xm1 = xq;
+    }
+    if (A.state_out && t0 + n == A.len) {
+        int8_t* st = A.state_out + (row0 / A.len * K.ch + c) * 3;
+        st[0] = (int8_t)xm3;
+        st[1] = (int8_t)xm2;
+        st[2] = (int8_t)xm1;
+    }
+}
+
+template <bool kDyn>
 __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
     __shared__ NauLds tab;
     nau_lds_init(tab);
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int p_c = K.dynamic ? pot_from_f32(*A.xbc_amax) : A.p_fixed[0];
-    if (!K.dynamic && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 4)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int p_c = kDyn ? pot_from_f32(*A.xbc_amax) : A.p_fixed[0];
+    if (!kDyn && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 4)
         A.p_out[threadIdx.x] = A.p_fixed[threadIdx.x];
-    const int c = blockIdx.x * 64 + lane;
-    const int64_t b = blockIdx.z;
+    const int c0 = blockIdx.x * 64;  // a wave covers 64 channels of one part
+    const int c = c0 + lane;
+    const int di = (int)A.d_inner, N = (int)A.dstate;
+    const int part = c0 < di ? 0 : (c0 < di + N ? 1 : 2);
     const int64_t L = A.len;
     const int64_t t0 = ((int64_t)blockIdx.y * (kConvThreads / 64) + wave) * kConvTL;
-    const int di = (int)A.d_inner, N = (int)A.dstate;
-    const int part = c < di ? 0 : (c < di + N ? 1 : 2);
+    if (t0 >= L) return;  // whole wave: no barrier follows
+    const int64_t row0 = (int64_t)blockIdx.z * L + t0;
+    const int n = (int)(t0 + kConvTL < L ? kConvTL : L - t0);
     int32_t amax = 0;
     float xmax = 0.0f;
-    if (t0 < L) {
-        const float qscale = ldexpf(1.0f, p_c);
-        const int32_t w0 = A.w_q[c * 4 + 0], w1 = A.w_q[c * 4 + 1], w2 = A.w_q[c * 4 + 2],
-                      w3 = A.w_q[c * 4 + 3];
-        const int sh = p_c + A.p_w[c] - 16;
-        const int64_t bias = A.b_q16[c];
-        const int p_part = K.dynamic ? 0 : A.p_fixed[1 + part];
-        const float* xrow = A.xbc + (b * L) * A.xbc_stride + c;
-        const int n = (int)(t0 + kConvTL < L ? kConvTL : L - t0);
-        // issue every load of this run (3 window inputs + kConvTL new ones) up front
-        float win[3];
-        float xv[kConvTL];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) win[j] = t0 > 0 ? xrow[(t0 - 3 + j) * A.xbc_stride] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < kConvTL; ++i) xv[i] = i < n ? xrow[(t0 + i) * A.xbc_stride] : 0.0f;
-        int32_t xm3, xm2, xm1;  // codes at t-3, t-2, t-1
-        if (t0 == 0) {
-            if (A.state_in) {
-                const int8_t* st = A.state_in + (b * K.ch + c) * 3;
-                xm3 = st[0];
-                xm2 = st[1];
-                xm1 = st[2];
-            } else {
-                xm3 = xm2 = xm1 = 0;
-            }
-        } else {  // t0 >= kConvTL >= 3: the window lies inside this call's input
-            xm3 = quant_xbc(win[0], qscale);
-            xm2 = quant_xbc(win[1], qscale);
-            xm1 = quant_xbc(win[2], qscale);
-        }
-#pragma unroll
-        for (int i = 0; i < kConvTL; ++i) {
-            if (i < n) {
-                const float xv_i = xv[i];
-                xmax = fmaxf(xmax, fabsf(xv_i));
-                const int32_t xq = quant_xbc(xv_i, qscale);
-                const int64_t row = b * L + t0 + i;
-                if (A.xbc_q) A.xbc_q[row * K.ch + c] = (int8_t)xq;
-                const int32_t acc = w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq;
-                const int32_t a = sat32(rshr((int64_t)acc, sh) + bias);
-                const int32_t sv = nau_silu_f(a, tab);
-                const int32_t sa = sv < 0 ? -sv : sv;
-                amax = sa > amax ? sa : amax;
-                if (K.dynamic) {
-                    A.s16[row * K.ch + c] = sv;
-                } else {
-                    const int8_t code = sat8(rshr((int64_t)sv, 16 - p_part));
-                    if (part == 0) A.x_out[row * di + c] = code;
-                    else if (part == 1) A.b_out[row * N + (c - di)] = code;
-                    else A.c_out[row * N + (c - di - N)] = code;
-                }
-                xm3 = xm2;
-                xm2 = xm1;
-                xm1 = xq;
-            }
-        }
-        if (A.state_out && t0 + n == L) {
-            int8_t* st = A.state_out + (b * K.ch + c) * 3;
-            st[0] = (int8_t)xm3;
-            st[1] = (int8_t)xm2;
-            st[2] = (int8_t)xm1;
-        }
+    if (A.xbc_q) {
+        if (n == kConvTL) conv_run_steps<false, kDyn, true>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
+        else conv_run_steps<true, kDyn, true>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
+    } else {
+        if (n == kConvTL) conv_run_steps<false, kDyn, false>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
+        else conv_run_steps<true, kDyn, false>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
     }
     // per-wave maxima (all lanes of a wave are in one part)
     amax = wave_max_i32(amax);
     xmax = wave_max_f32(xmax);
     if (lane == 0) {
-        if (K.dynamic) {
-            if (amax > 0) atomicMax(&A.amax_q16[part], amax);
+        if (kDyn) {
+            if (amax > 0) atomic_max_i32(&A.amax_q16[part], amax);
         } else if (A.amax_stats) {
-            if (amax > 0) atomicMax(&A.amax_stats[1 + part], amax);
-            if (xmax > 0.0f) atomicMax((unsigned int*)&A.amax_stats[0], __float_as_uint(xmax));
+            if (amax > 0) atomic_max_i32(&A.amax_stats[1 + part], amax);
+            if (xmax > 0.0f) atomic_max_nonneg_f32((float*)&A.amax_stats[0], xmax);
         }
     }
 }
@@ -181,7 +215,8 @@ fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     const int64_t per_block = (kConvThreads / 64) * kConvTL;
     dim3 grid((unsigned)(K.ch / 64), (unsigned)((a.len + per_block - 1) / per_block),
               (unsigned)a.batch);
-    conv_silu_kernel<<<grid, kConvThreads, 0, s>>>(K);
+    if (K.dynamic) conv_silu_kernel<true><<<grid, kConvThreads, 0, s>>>(K);
+    else conv_silu_kernel<false><<<grid, kConvThreads, 0, s>>>(K);
     fm_status st = check_launch("conv_silu_kernel");
     if (st != FM_OK || !K.dynamic) return st;
     const int64_t rows = a.batch * a.len;

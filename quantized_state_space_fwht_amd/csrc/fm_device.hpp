@@ -106,15 +106,14 @@ __device__ __forceinline__ void nau_lds_init(NauLds& t) {
     if (threadIdx.x < 9) t.y[threadIdx.x] = (double)exp2_knot(threadIdx.x);
 }
 
-// e^(x/2^16) in Q.16 for -2^31 <= x <= 0.
+// e^(x/2^16) in Q.16 for -2^31 <= x <= 0.  Branch-free: below v = -18*2^16
+// the Q.30 mantissa is shifted right by >= 32 and rounds to 0, so v is clamped
+// there (the product is exact wherever v >= -17*2^16, |x * log2e| < 2^51).
 __device__ __forceinline__ int32_t nau_exp_f(int32_t x, const NauLds& t) {
-    // v = rshr(x * log2e_q30, 30): exact while v >= -17*2^16 (|x * log2e| < 2^51)
-    const double vf =
-        __builtin_floor(__builtin_fma((double)x, (double)kLog2eQ30, 0x1p29) * 0x1p-30);
-    // integer part n <= -18: the Q.30 mantissa shifted right by >= 32 rounds to 0
-    if (vf < -1114112.0) return 0;
+    double vf = __builtin_floor(__builtin_fma((double)x, (double)kLog2eQ30, 0x1p29) * 0x1p-30);
+    vf = __builtin_fmax(vf, -1179648.0);
     const int v = (int)vf;
-    const int n = v >> 16;  // -17..0
+    const int n = v >> 16;  // -18..0
     const int f = v & 0xFFFF;
     const int seg = f >> 13;
     const double r = (double)(f & 0x1FFF);
@@ -133,25 +132,19 @@ __device__ __forceinline__ int32_t nau_softplus_f(int32_t x, const NauLds& t) {
 }
 
 // SiLU in Q.16: for x <= 0, sigma = floor(E*2^16 / (2^16 + E)), E = e^x,
-// SiLU = rshr(x * sigma, 16); for x > 0, x + SiLU(-x).
+// SiLU = rshr(x * sigma, 16); for x > 0, x + SiLU(-x).  Branch-free (E = 2^16
+// gives sigma = 2^15 through the same division).
 __device__ __forceinline__ int32_t nau_silu_f(int32_t x, const NauLds& t) {
     const int32_t xn = x < 0 ? x : -x;
     const int32_t e = nau_exp_f(xn, t);  // [0, 2^16]
-    int32_t sig;
-    if (e >= 65536) {
-        sig = 32768;
-    } else {
-        // quotient < 2^15: a float32 reciprocal puts floor() within 1 of it, and
-        // the exact remainder a - q*b (integers below 2^34) corrects it
-        const double a = (double)e * 65536.0, b = 65536.0 + (double)e;
-        double q = __builtin_floor(a * (double)__builtin_amdgcn_rcpf((float)b));
-        const double rem = __builtin_fma(-q, b, a);
-        q = rem < 0.0 ? q - 1.0 : (rem >= b ? q + 1.0 : q);
-        sig = (int32_t)q;
-    }
-    // rshr(xn * sig, 16): |xn * sig| < 2^46
-    const int32_t sn =
-        (int32_t)__builtin_floor(__builtin_fma((double)xn, (double)sig * 0x1p-16, 0.5));
+    // quotient <= 2^15: a float32 reciprocal puts floor() within 1 of it, and
+    // the exact remainder a - q*b (integers below 2^34) corrects it
+    const double a = (double)e * 65536.0, b = 65536.0 + (double)e;
+    double q = __builtin_floor(a * (double)__builtin_amdgcn_rcpf((float)b));
+    const double rem = __builtin_fma(-q, b, a);
+    q = rem < 0.0 ? q - 1.0 : (rem >= b ? q + 1.0 : q);
+    // rshr(xn * sigma, 16): |xn * sigma| < 2^46
+    const int32_t sn = (int32_t)__builtin_floor(__builtin_fma((double)xn, q * 0x1p-16, 0.5));
     return x > 0 ? x + sn : sn;
 }
 
@@ -168,9 +161,18 @@ __device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
     return v;
 }
 
+// Maxima shared by a whole grid.  The stored value only grows, so the atomic
+// is skipped when a plain (device-coherent) read already covers v: a stale
+// read can only cost an extra atomic, never lose one.  Thousands of waves
+// updating one word would otherwise serialize on it.
+__device__ __forceinline__ void atomic_max_i32(int32_t* addr, int32_t v) {
+    if (__hip_atomic_load(addr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v) atomicMax(addr, v);
+}
 // non-negative float maxima accumulate as their bit patterns (order-preserving)
 __device__ __forceinline__ void atomic_max_nonneg_f32(float* addr, float v) {
-    atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+    unsigned int* a = reinterpret_cast<unsigned int*>(addr);
+    const unsigned int u = __float_as_uint(v);
+    if (__hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < u) atomicMax(a, u);
 }
 
 }  // namespace fm

@@ -18,23 +18,19 @@ __device__ __forceinline__ float4 fwht256_lane_g(float4 v, int lane) {
     v.z = t0 - t2;
     v.y = t1 + t3;
     v.w = t1 - t3;
+    // stage m: the lane with bit m clear keeps a + b, its partner b' = a - b;
+    // fma(+-1, v, p) rounds p + v / p - v exactly as the plain sums do
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
-        float px = __shfl_xor(v.x, m, 64);
-        float py = __shfl_xor(v.y, m, 64);
-        float pz = __shfl_xor(v.z, m, 64);
-        float pw = __shfl_xor(v.w, m, 64);
-        if (lane & m) {
-            v.x = px - v.x;
-            v.y = py - v.y;
-            v.z = pz - v.z;
-            v.w = pw - v.w;
-        } else {
-            v.x = v.x + px;
-            v.y = v.y + py;
-            v.z = v.z + pz;
-            v.w = v.w + pw;
-        }
+        const float px = __shfl_xor(v.x, m, 64);
+        const float py = __shfl_xor(v.y, m, 64);
+        const float pz = __shfl_xor(v.z, m, 64);
+        const float pw = __shfl_xor(v.w, m, 64);
+        const float sg = (lane & m) ? -1.0f : 1.0f;
+        v.x = __builtin_fmaf(sg, v.x, px);
+        v.y = __builtin_fmaf(sg, v.y, py);
+        v.z = __builtin_fmaf(sg, v.z, pz);
+        v.w = __builtin_fmaf(sg, v.w, pw);
     }
     v.x *= 0.0625f;
     v.y *= 0.0625f;
@@ -64,28 +60,41 @@ __global__ __launch_bounds__(64) void gate_norm_kernel(GateArgs G) {
     const int32_t* yr = G.y + row * D;
     const float* zr = G.z + row * G.z_stride;
     float a = 0.0f;
-    // four elements per lane per round: their loads are issued together
-    for (int i0 = lane; i0 < D; i0 += 4 * 64) {
-        int32_t yv[4];
-        float zv[4];
+    // four elements per lane per round (i = lane + 64*(4k + j)); the loads of
+    // round k + 1 are issued before round k is computed
+    const int rounds = D / 256;
+    int32_t yc[4];
+    float zc[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = i0 + 64 * k;
-            yv[k] = i < D ? yr[i] : 0;
-            zv[k] = i < D ? zr[i] : 0.0f;
+    for (int j = 0; j < 4; ++j) {
+        yc[j] = yr[lane + 64 * j];
+        zc[j] = zr[lane + 64 * j];
+    }
+    for (int k = 0; k < rounds; ++k) {
+        int32_t yn[4] = {0, 0, 0, 0};
+        float zn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (k + 1 < rounds) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                yn[j] = yr[lane + 64 * (4 * k + 4 + j)];
+                zn[j] = zr[lane + 64 * (4 * k + 4 + j)];
+            }
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = i0 + 64 * k;
-            if (i < D) {
-                const float yf = (float)yv[k] * ysc;
-                const int32_t zq = f2i_sat(rintf(zv[k] * 65536.0f));
-                const float sz = (float)nau_silu_f(zq, tab) * 0x1p-16f;
-                const float g = yf * sz;
-                row_buf[i] = g;
-                const float g2 = g * g;
-                a = a + g2;  // ascending i within this lane: the fixed order
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int i = lane + 64 * (4 * k + j);
+            const float yf = (float)yc[j] * ysc;
+            const int32_t zq = f2i_sat(rintf(zc[j] * 65536.0f));
+            const float sz = (float)nau_silu_f(zq, tab) * 0x1p-16f;
+            const float g = yf * sz;
+            row_buf[i] = g;
+            const float g2 = g * g;
+            a = a + g2;  // ascending i within this lane: the fixed order
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            yc[j] = yn[j];
+            zc[j] = zn[j];
         }
     }
     const float ss = row_sumsq(a);
