@@ -27,9 +27,11 @@ METRIC = "Mamba2 layer prefill tokens/s (W8A8+PoT SSM); % of i8 MFMA / HBM peak"
 # MI355X: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.32e12 vector lane-operations/s
 # (float64 FMA runs at this rate: 78.6 TFLOP/s counting an FMA as 2).
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
-# algorithmic integer work per state element per time step of the scan:
-# 3 multiply-adds (decay*h + input, dt*x*B, C*h accumulation), 1 rounding, 1 saturation
-SCAN_OPS_PER_ELEMENT_STEP = 5
+# algorithmic integer work per state element (b, head, p, n) per time step of
+# the scan: 3 multiplies (dA*h, (dt*x)*B, C*h), 3 additions (the two rounded
+# terms, the y accumulation) and 2 rounding shifts
+SCAN_OPS_PER_ELEMENT_STEP = 8
+COPY_PROBE_BYTES = 256 << 20
 
 
 def log(msg):
@@ -85,10 +87,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="m130m_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, copy 256 MiB device-to-device three times "
+                         "(a reference kernel of known traffic for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the layer would "
+              "shard over the batch); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -147,6 +152,13 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
     }
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(w)

@@ -105,7 +105,9 @@ struct ScanArgs {
 };
 // workspace of the scan (none: B and C are staged through LDS)
 size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);
-fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s);
+// ev_start / ev_stop (nullable): recorded on s right around the scan kernel
+fm_status scan_run(const ScanArgs& a, void* ws, hipStream_t s, hipEvent_t ev_start = nullptr,
+                   hipEvent_t ev_stop = nullptr);
 
 struct GateArgs {
     const int32_t* y;

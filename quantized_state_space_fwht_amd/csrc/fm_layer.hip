@@ -230,11 +230,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.da_out = w.da;
         hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
         g_ev_start = g_ev_stop = nullptr;
-        if (ev0 && hipEventRecord(ev0, s) != hipSuccess)
-            return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
-        if ((st = scan_run(a, w.scan_ws, s)) != FM_OK) return st;
-        if (ev1 && hipEventRecord(ev1, s) != hipSuccess)
-            return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
+        if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) return st;
     }
     // 8. gate + RMSNorm + rotate + quantize the out_proj input
     {

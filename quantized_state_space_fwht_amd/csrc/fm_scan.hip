@@ -125,8 +125,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = (int)A.nheads, P = (int)A.headdim;
     const int64_t L = A.len;
-    const int pg = blockIdx.x, head = blockIdx.y;
-    const int64_t b = blockIdx.z;
+    // Workgroups go to the 8 XCDs round-robin by launch index; the launch index
+    // is remapped so that the p-groups of one (b, head), which read the same x
+    // cache lines, land on one XCD (and its L2) instead of on eight.
+    const int npg = P / kScanP;
+    const uint32_t nwg = gridDim.x, id = blockIdx.x;
+    const uint32_t lam = nwg % 8 == 0 ? (id % 8) * (nwg / 8) + id / 8 : id;
+    const int pg = (int)(lam % (uint32_t)npg);
+    const int head = (int)((lam / (uint32_t)npg) % (uint32_t)H);
+    const int64_t b = lam / ((uint32_t)npg * (uint32_t)H);
     const int p0 = pg * kScanP + 2 * w;  // this wave's two p: p0, p0 + 1
     const int ky = A.p[2] + A.p[3];
     const double dq = (double)A.d_q16[head];
@@ -349,19 +356,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
 
 size_t scan_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-fm_status scan_run(const ScanArgs& a, void*, hipStream_t s) {
+fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
+                   hipEvent_t ev_stop) {
+    if (a.dstate != 64 && a.dstate != 128)
+        return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
     const int64_t pairs = a.batch * a.len * a.nheads;
     scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
         a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
     fm_status st = check_launch("scan_prep_kernel");
     if (st != FM_OK) return st;
-    dim3 grid((unsigned)(a.headdim / kScanP), (unsigned)a.nheads, (unsigned)a.batch);
-    switch (a.dstate) {
-        case 64: scan_kernel<1><<<grid, kScanThreads, 0, s>>>(a); break;
-        case 128: scan_kernel<2><<<grid, kScanThreads, 0, s>>>(a); break;
-        default: return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
-    }
-    return check_launch("scan_kernel");
+    if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
+        return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
+    const unsigned grid = (unsigned)(a.headdim / kScanP * a.nheads * a.batch);
+    if (a.dstate == 64) scan_kernel<1><<<grid, kScanThreads, 0, s>>>(a);
+    else scan_kernel<2><<<grid, kScanThreads, 0, s>>>(a);
+    if ((st = check_launch("scan_kernel")) != FM_OK) return st;
+    if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess)
+        return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
+    return FM_OK;
 }
 
 }  // namespace fm
