@@ -35,11 +35,11 @@ mathematics the pages fix or a library routine (see each test's docstring).
 """
 from .fixedpoint import (I32_MAX, I32_MIN, PMAX, PMIN, f32_to_i32_sat, pot_f32, pot_q16, rshr,
                          sat8, sat32)
-from .hadamard import fwht256_f32, hadamard_quant
+from .hadamard import fwht256_f32, hadamard_quant, hadamard_scale, quantize_codes
 from .linear import quantize_weight, w8a8_gemm
 from .nau import (EXP2_TABLE_Q30, LOG2E_Q30, exp2_q16, exp_q16, silu_q16, softplus_q16)
 from .conv import conv1d_pot, conv_weight_prep, silu_requant, xbc_pot_quant
 from .scan import dt_dA, ssm_scan_pot
 from .gate_norm import gate, gate_norm_quant, rmsnorm_fixed_order
-from .layer import (QParams, calibrate_stack, layer_decode, layer_prefill, prepare_layer,
+from .layer import (QParams, Stats, calibrate_stack, layer_decode, layer_prefill, prepare_layer,
                     qparams_from_stats, stack_decode, stack_prefill)

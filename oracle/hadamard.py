@@ -44,14 +44,9 @@ def fwht256_f32(x):
     return v.reshape(x.shape) * np.float32(0.0625)
 
 
-def hadamard_quant(x, mode="dynamic", scoe=None, sshift=None):
-    """Rotate the rows of ``x`` by H_K and quantize the whole tensor to int8.
-
-    Returns (q int8, s float32 dequant scale, amax float32 of the rotated
-    tensor, r float32 rotated tensor).
-    """
-    r = fwht256_f32(x)
-    amax = np.float32(np.max(np.abs(r))) if r.size else np.float32(0.0)
+def hadamard_scale(amax, mode="dynamic", scoe=None, sshift=None):
+    """The float32 multiplier c of the quantizer (dynamic: from the tensor max)."""
+    amax = np.float32(amax)
     if mode == "dynamic":
         c = np.float32(1.0) if amax == 0 else np.float32(127.0) / amax
     elif mode == "static":
@@ -60,8 +55,25 @@ def hadamard_quant(x, mode="dynamic", scoe=None, sshift=None):
         c = np.float32(scoe) * np.float32(2.0 ** (-sshift))
     else:
         raise ValueError(mode)
+    return np.float32(c)
+
+
+def quantize_codes(r, c):
+    """int8 codes of the rotated values ``r`` under multiplier ``c``, and s = 1/c."""
     c = np.float32(c)
     # clamp while still float (static scales can send r*c far outside int range)
-    q = np.clip(np.rint(r * c), np.float32(-127), np.float32(127)).astype(np.int8)
-    s = np.float32(1.0) / c
-    return q, np.float32(s), amax, r
+    q = np.clip(np.rint(np.asarray(r, np.float32) * c), np.float32(-127),
+                np.float32(127)).astype(np.int8)
+    return q, np.float32(np.float32(1.0) / c)
+
+
+def hadamard_quant(x, mode="dynamic", scoe=None, sshift=None):
+    """Rotate the rows of ``x`` by H_K and quantize the whole tensor to int8.
+
+    Returns (q int8, s float32 dequant scale, amax float32 of the rotated
+    tensor, r float32 rotated tensor).
+    """
+    r = fwht256_f32(x)
+    amax = np.float32(np.max(np.abs(r))) if r.size else np.float32(0.0)
+    q, s = quantize_codes(r, hadamard_scale(amax, mode, scoe, sshift))
+    return q, s, amax, r

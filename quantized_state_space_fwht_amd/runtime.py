@@ -19,11 +19,25 @@ def _dev(a, dtype=None, device="cuda"):
     return t.to(device).contiguous()
 
 
+class WorkspacePool:
+    """One device workspace shared by layers that run one call at a time."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.t = None
+
+    def get(self, need):
+        if self.t is None or self.t.numel() < need:
+            self.t = None  # release before growing
+            self.t = B.workspace(need, self.device)
+        return self.t
+
+
 class Mamba2Layer:
     """One quantized mixer layer with prepared weights, a workspace and a cache."""
 
     def __init__(self, shape: LayerShape, params: dict, mode: str = "dynamic",
-                 prenorm_residual: bool = False, device="cuda", stream=None):
+                 prenorm_residual: bool = False, device="cuda", stream=None, ws_pool=None):
         s = shape
         self.shape = s
         self.device = device
@@ -64,6 +78,7 @@ class Mamba2Layer:
             "w_in_q", "s_w_in", "w_out_q", "s_w_out", "conv_w_q", "conv_p_w", "conv_b_q16",
             "dt_bias", "a_q16", "d_q16", "norm_w")))
         self.qp = torch.zeros(B.QPARAMS_BYTES, dtype=torch.uint8, device=device)
+        self._pool = ws_pool
         self._ws = None
         self._ws_key = None
         self.cache = None
@@ -71,7 +86,9 @@ class Mamba2Layer:
     # ------------------------------------------------------------ memory
     def workspace_for(self, batch, length):
         need = B.lib.fm_mamba2_layer_workspace_size(ctypes.byref(self.desc), batch, length)
-        if self._ws is None or self._ws.numel() < need:
+        if self._pool is not None:
+            self._ws = self._pool.get(need)
+        elif self._ws is None or self._ws.numel() < need:
             self._ws = B.workspace(need, self.device)
         self._ws_key = (batch, length)
         return self._ws
@@ -153,7 +170,11 @@ class Mamba2Stack:
     """Pre-norm residual stack: h <- h + layer(RMSNorm(h)) per layer."""
 
     def __init__(self, shape: LayerShape, params_list, mode="dynamic", device="cuda"):
-        self.layers = [Mamba2Layer(shape, p, mode, prenorm_residual=True, device=device)
+        """``params_list``: any iterable of parameter dicts (a generator keeps only one
+        layer's float32 weights on the host at a time)."""
+        self.pool = WorkspacePool(device)
+        self.layers = [Mamba2Layer(shape, p, mode, prenorm_residual=True, device=device,
+                                   ws_pool=self.pool)
                        for p in params_list]
         self.shape = shape
 

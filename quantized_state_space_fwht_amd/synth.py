@@ -41,6 +41,18 @@ def workload_activations(w: Workload, seed: int = None) -> np.ndarray:
                        w.outlier_seed, w.n_outliers, w.outlier_scale)
 
 
+def calibration_sequences(w: Workload):
+    """Static mode: one [1, L, d_model] sequence per calibration seed."""
+    return [activations(w.shape, 1, w.seqlen, sd, w.outlier_seed, w.n_outliers, w.outlier_scale)
+            for sd in w.calib_seeds]
+
+
+def eval_batch(w: Workload) -> np.ndarray:
+    """Static mode: the evaluation sequences (one per seed) as one [B, L, d_model] batch."""
+    return np.concatenate([activations(w.shape, 1, w.seqlen, sd, w.outlier_seed, w.n_outliers,
+                                       w.outlier_scale) for sd in w.eval_seeds], axis=0)
+
+
 def decode_step_input(w: Workload, step: int) -> np.ndarray:
     """u_t [batch, d_model] for decode step `step` (seed 400 + step)."""
     return activations(w.shape, w.batch, 1, 400 + step, w.outlier_seed,
