@@ -32,6 +32,8 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # terms, the y accumulation) and 2 rounding shifts
 SCAN_OPS_PER_ELEMENT_STEP = 8
 COPY_PROBE_BYTES = 256 << 20
+HBM_PEAK_GBS = 8000.0
+DECODE_WORKLOAD = "m2p7b_decode"
 
 
 def log(msg):
@@ -80,6 +82,49 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=3):
                       f"({w.batch}x{w.seqlen} tokens, seeds as the GPU run), {dt:.1f} s"}
 
 
+def decode_bench(torch, configs, synth, warmup=8, max_steps=None):
+    """Decode tokens/s of the 64-layer 2.7B-shaped stack, batch 16.
+
+    A 1024-token seeding prefill fills the caches; then the workload's 512 one-token
+    steps run as replays of one captured graph (every layer of a step): `warmup`
+    untimed, the rest timed with HIP events.  Roofline: HBM, with the algorithmic
+    bytes of a layer step = SSM state read + written (int32) + both int8 weight
+    matrices + the conv window read + written."""
+    import numpy as np
+    from quantized_state_space_fwht_amd.runtime import DecodeGraph, Mamba2Stack
+    w = configs.get(DECODE_WORKLOAD)
+    s = w.shape
+    log(f"bench: building decode stack {w.name} ({w.description})")
+    stack = Mamba2Stack(s, (synth.workload_params(w, l) for l in range(w.nlayers)))
+    stack.prefill(torch.from_numpy(synth.workload_activations(w)).cuda(), with_cache=True)
+    g = DecodeGraph(stack, w.batch)
+    nsteps = w.decode_steps if max_steps is None else min(w.decode_steps, warmup + max_steps)
+    inputs = torch.from_numpy(np.stack([synth.decode_step_input(w, t)
+                                        for t in range(nsteps)])).cuda()
+    for t in range(warmup):
+        g.step(inputs[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warmup, nsteps):
+        g.step(inputs[t])
+    e1.record()
+    torch.cuda.synchronize()
+    timed = nsteps - warmup
+    ms = e0.elapsed_time(e1) / timed
+    state_b = 2 * w.batch * s.nheads * s.headdim * s.dstate * 4
+    weight_b = s.d_in_proj * s.d_model + s.d_model * s.d_inner
+    conv_b = 2 * w.batch * s.conv_ch * 3
+    step_bytes = w.nlayers * (state_b + weight_b + conv_b)
+    gbs = step_bytes / (ms / 1e3) / 1e9
+    return {"workload": w.name, "value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s",
+            "ms_per_token_step": round(ms, 4), "batch": w.batch, "layers": w.nlayers,
+            "steps_timed": timed, "steps_warmup": warmup, "seeding_prefill": w.seqlen,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_token_step": step_bytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +132,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="m130m_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode measurement (64-layer 2.7B-shaped stack)")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="time only this many decode steps (default: the workload's)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device three times "
                          "(a reference kernel of known traffic for counter runs)")
@@ -152,6 +201,10 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
     }
+    if not args.no_decode:
+        del layer
+        torch.cuda.empty_cache()
+        line["decode"] = decode_bench(torch, configs, synth, max_steps=args.decode_steps)
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

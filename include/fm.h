@@ -237,6 +237,9 @@ fm_status fm_gate_norm_quant(const int32_t* y, const float* z, int64_t z_row_str
 /* ------------------------------------------------------------------------
  * Layer-level calls.
  * ---------------------------------------------------------------------- */
+/* Limits (FM_ERR_SHAPE otherwise): d_model and d_inner multiples of 256,
+ * d_model <= 16384, d_inner <= 8192, nheads * headdim == d_inner,
+ * headdim % 8 == 0, dstate in {64, 128}, d_conv == 4. */
 typedef struct fm_layer_desc {
     int64_t d_model, d_inner, nheads, headdim, dstate, d_conv; /* d_conv must be 4 */
     int32_t mode;             /* fm_scale_mode of every activation quantization point */

@@ -46,12 +46,12 @@ static fm_status check_ws(void* ws, size_t have, size_t need, const char* who) {
 static fm_status check_layer_desc(const fm_layer_desc* d, const char* who) {
     if (!d) return fail(FM_ERR_NULL, "%s: desc is NULL", who);
     if (d->d_conv != 4) return fail(FM_ERR_SHAPE, "%s: d_conv must be 4", who);
-    if (d->d_model <= 0 || d->d_model % 256 || d->d_model > 65536)
-        return fail(FM_ERR_SHAPE, "%s: d_model must be a positive multiple of 256", who);
+    if (d->d_model <= 0 || d->d_model % 256 || d->d_model > 16384)
+        return fail(FM_ERR_SHAPE, "%s: d_model must be a multiple of 256 in (0, 16384]", who);
     if (d->d_inner <= 0 || d->d_inner % 256 || d->d_inner > 8192)
         return fail(FM_ERR_SHAPE, "%s: d_inner must be a multiple of 256 in (0, 8192]", who);
-    if (d->headdim <= 0 || d->headdim % 4 || d->nheads * d->headdim != d->d_inner)
-        return fail(FM_ERR_SHAPE, "%s: nheads * headdim must equal d_inner, headdim %% 4 == 0", who);
+    if (d->headdim <= 0 || d->headdim % 8 || d->nheads * d->headdim != d->d_inner)
+        return fail(FM_ERR_SHAPE, "%s: nheads * headdim must equal d_inner, headdim %% 8 == 0", who);
     if (d->dstate != 64 && d->dstate != 128)
         return fail(FM_ERR_SHAPE, "%s: dstate must be 64 or 128", who);
     if (d->mode != FM_SCALE_DYNAMIC && d->mode != FM_SCALE_STATIC)

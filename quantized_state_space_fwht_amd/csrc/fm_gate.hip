@@ -3,7 +3,7 @@
 // paper: gate, RMSNorm and out_proj; the out_proj input is rotated and
 // quantized like the in_proj input, "What carries the argument").
 //
-// One wave per row.  The sum of squares follows one fixed float32 order
+// One workgroup per row.  The sum of squares follows one fixed float32 order
 // (lane l adds g_i^2 for i = l, l+64, ... ascending; then a[l] += a[l^k] for
 // k = 32..1), because the normed values become int8 codes and a different
 // rounding could flip one.  The row is staged in LDS and re-read in the
@@ -47,64 +47,65 @@ __device__ __forceinline__ float row_sumsq(float a) {
 }
 
 constexpr int kGateMaxD = 8192;
+constexpr int kGateWaves = 4;
 
-__global__ __launch_bounds__(64) void gate_norm_kernel(GateArgs G) {
+// One workgroup of 4 waves per row.  Phase 1: every thread computes gate
+// values g_i (any split: each is independent) into LDS.  Phase 2: wave 0
+// forms the sum of squares in the fixed order (lane l adds g_i^2 for
+// i = l, l+64, ... ascending, then the xor tree).  Phase 3: the 256-blocks
+// are normalized, rotated and quantized, block b by wave b % 4.
+__global__ __launch_bounds__(64 * kGateWaves) void gate_norm_kernel(GateArgs G) {
     extern __shared__ __attribute__((aligned(16))) float row_buf[];  // d_inner floats
     __shared__ NauLds tab;
+    __shared__ float rs_r;
+    __shared__ float wmax[kGateWaves];
     nau_lds_init(tab);
     __syncthreads();
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row = blockIdx.x;
     const int D = (int)G.d_inner;
     const float ysc = ldexpf(1.0f, -(G.p[1] + 8));
     const int32_t* yr = G.y + row * D;
     const float* zr = G.z + row * G.z_stride;
-    float a = 0.0f;
-    // four elements per lane per round (i = lane + 64*(4k + j)); the loads of
-    // round k + 1 are issued before round k is computed
-    const int rounds = D / 256;
-    int32_t yc[4];
-    float zc[4];
+    // phase 1: four elements per thread per round, loads of a round issued together
+    for (int i0 = tid; i0 < D; i0 += 4 * 64 * kGateWaves) {
+        int32_t yv[4];
+        float zv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        yc[j] = yr[lane + 64 * j];
-        zc[j] = zr[lane + 64 * j];
-    }
-    for (int k = 0; k < rounds; ++k) {
-        int32_t yn[4] = {0, 0, 0, 0};
-        float zn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (k + 1 < rounds) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                yn[j] = yr[lane + 64 * (4 * k + 4 + j)];
-                zn[j] = zr[lane + 64 * (4 * k + 4 + j)];
-            }
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 64 * kGateWaves * k;
+            yv[k] = i < D ? yr[i] : 0;
+            zv[k] = i < D ? zr[i] : 0.0f;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = lane + 64 * (4 * k + j);
-            const float yf = (float)yc[j] * ysc;
-            const int32_t zq = f2i_sat(rintf(zc[j] * 65536.0f));
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 64 * kGateWaves * k;
+            const float yf = (float)yv[k] * ysc;
+            const int32_t zq = f2i_sat(rintf(zv[k] * 65536.0f));
             const float sz = (float)nau_silu_f(zq, tab) * 0x1p-16f;
-            const float g = yf * sz;
-            row_buf[i] = g;
+            if (i < D) row_buf[i] = yf * sz;
+        }
+    }
+    __syncthreads();
+    // phase 2: the fixed-order sum of squares
+    if (wave == 0) {
+        float a = 0.0f;
+        for (int i = lane; i < D; i += 64) {
+            const float g = row_buf[i];
             const float g2 = g * g;
             a = a + g2;  // ascending i within this lane: the fixed order
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            yc[j] = yn[j];
-            zc[j] = zn[j];
-        }
+        const float ss = row_sumsq(a);
+        const float ms = ss / (float)D;
+        if (lane == 0) rs_r = 1.0f / sqrtf(ms + 1e-5f);
     }
-    const float ss = row_sumsq(a);
-    const float ms = ss / (float)D;
-    const float r = 1.0f / sqrtf(ms + 1e-5f);
     __syncthreads();
+    const float r = rs_r;
     float c = 0.0f;
     if (G.mode == FM_SCALE_STATIC) c = ldexpf((float)G.scoe, -G.sshift);
     float m = 0.0f;
-    for (int blk = 0; blk < D / 256; ++blk) {
+    for (int blk = wave; blk < D / 256; blk += kGateWaves) {
         const int base = blk * 256 + lane * 4;
         float4 g = *reinterpret_cast<const float4*>(&row_buf[base]);
         const float4 w = *reinterpret_cast<const float4*>(&G.norm_w[base]);
@@ -128,7 +129,10 @@ __global__ __launch_bounds__(64) void gate_norm_kernel(GateArgs G) {
         }
     }
     m = wave_max_f32(m);
-    if (lane == 0) {
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         if (G.mode == FM_SCALE_DYNAMIC) atomic_max_nonneg_f32(G.amax_ws, m);
         if (G.amax_stats) atomic_max_nonneg_f32(G.amax_stats, m);
         if (G.mode == FM_SCALE_STATIC && row == 0) *G.scale_out = 1.0f / c;
@@ -139,7 +143,8 @@ fm_status gate_run(const GateArgs& g, hipStream_t s) {
     if (g.d_inner > kGateMaxD)
         return fail(FM_ERR_SHAPE, "gate: d_inner %lld > %d", (long long)g.d_inner, kGateMaxD);
     if (g.rows > 0) {
-        gate_norm_kernel<<<(unsigned)g.rows, 64, (size_t)g.d_inner * sizeof(float), s>>>(g);
+        gate_norm_kernel<<<(unsigned)g.rows, 64 * kGateWaves, (size_t)g.d_inner * sizeof(float),
+                           s>>>(g);
         fm_status st = check_launch("gate_norm_kernel");
         if (st != FM_OK) return st;
     }
@@ -151,26 +156,37 @@ fm_status gate_run(const GateArgs& g, hipStream_t s) {
     return FM_OK;
 }
 
-// RMSNorm of the residual stream with unit weight (pre-norm stacks).
-__global__ __launch_bounds__(64) void rmsnorm_rows_kernel(const float* __restrict__ h, int d,
-                                                          float* __restrict__ out) {
-    const int lane = threadIdx.x;
+// RMSNorm of the residual stream with unit weight (pre-norm stacks): one
+// workgroup of 4 waves per row; the row is staged in LDS by all waves, wave 0
+// forms the fixed-order sum of squares, all waves write the normed row.
+__global__ __launch_bounds__(64 * kGateWaves) void rmsnorm_rows_kernel(
+    const float* __restrict__ h, int d, float* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) float hrow[];  // d floats
+    __shared__ float rs_r;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int64_t row = blockIdx.x;
     const float* hr = h + row * d;
-    float a = 0.0f;
-    for (int i = lane; i < d; i += 64) {
-        const float v = hr[i];
-        const float v2 = v * v;
-        a = a + v2;
+    for (int i = tid; i < d; i += 64 * kGateWaves) hrow[i] = hr[i];
+    __syncthreads();
+    if (tid < 64) {
+        float a = 0.0f;
+        for (int i = lane; i < d; i += 64) {
+            const float v = hrow[i];
+            const float v2 = v * v;
+            a = a + v2;
+        }
+        const float ss = row_sumsq(a);
+        if (lane == 0) rs_r = 1.0f / sqrtf(ss / (float)d + 1e-5f);
     }
-    const float ss = row_sumsq(a);
-    const float r = 1.0f / sqrtf(ss / (float)d + 1e-5f);
-    for (int i = lane; i < d; i += 64) out[row * d + i] = (hr[i] * r) * 1.0f;
+    __syncthreads();
+    const float r = rs_r;
+    for (int i = tid; i < d; i += 64 * kGateWaves) out[row * d + i] = (hrow[i] * r) * 1.0f;
 }
 
 fm_status rmsnorm_rows_run(const float* h, int64_t rows, int64_t d, float* out, hipStream_t s) {
     if (rows == 0) return FM_OK;
-    rmsnorm_rows_kernel<<<(unsigned)rows, 64, 0, s>>>(h, (int)d, out);
+    rmsnorm_rows_kernel<<<(unsigned)rows, 64 * kGateWaves, (size_t)d * sizeof(float), s>>>(
+        h, (int)d, out);
     return check_launch("rmsnorm_rows_kernel");
 }
 

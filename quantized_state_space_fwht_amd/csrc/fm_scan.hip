@@ -354,12 +354,115 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- one step (decode)
+// len == 1: the work is reading and writing the state once, so the kernel is
+// laid out for coalesced state traffic.  A wave owns (b, head, p0, p0 + 1):
+// lanes 0..31 the row p0, lanes 32..63 the row p0 + 1, lane l the NN2 = N/32
+// consecutive n = NN2*(l % 32) .. (16 or 8 contiguous bytes of state).  dt and
+// the decay of (b, head) are computed by every lane (wave-uniform); the wave
+// with p0 = 0 stores them.  The update takes the clamped form always.
+template <int NN2>
+__global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
+    __shared__ NauLds tab;
+    nau_lds_init(tab);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int H = (int)A.nheads, P = (int)A.headdim;
+    constexpr int N = 32 * NN2;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, head, p-pair)
+    const int npp = P / 2;
+    if (wid >= A.batch * H * npp) return;
+    const int pp = (int)(wid % npp);
+    const int head = (int)((wid / npp) % H);
+    const int64_t b = wid / ((int64_t)npp * H);
+    const int r = lane >> 5, l32 = lane & 31;
+    const int p = 2 * pp + r;
+    const int n0 = NN2 * l32;
+    // dt and the decay of (b, head)
+    const int64_t q = b * H + head;  // token row b (len 1)
+    const float raw = A.dt_raw[b * A.dt_stride + head];
+    const int32_t dt_in = f2i_sat(rintf((raw + A.dt_bias[head]) * 65536.0f));
+    const int32_t dt = nau_softplus_f(dt_in, tab);
+    const int32_t da = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)A.a_q16[head], 16)), tab);
+    if (pp == 0 && lane == 0) {
+        A.dt_out[q] = dt;
+        A.da_out[q] = da;
+    }
+    const int32_t xi = A.x[q * P + p];
+    const double dd = (double)da * 0x1p-16;
+    const double u = (double)dt * 0x1p-8 * (double)xi;
+    // state row (b, head, p), n0 .. n0 + NN2 - 1
+    const int64_t sidx = (q * P + p) * N + n0;
+    int32_t hs[NN2];
+    if (A.state_in) {
+        if constexpr (NN2 == 4) {
+            const int4 v = *reinterpret_cast<const int4*>(A.state_in + sidx);
+            hs[0] = v.x, hs[1] = v.y, hs[2] = v.z, hs[3] = v.w;
+        } else {
+            const int2 v = *reinterpret_cast<const int2*>(A.state_in + sidx);
+            hs[0] = v.x, hs[1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NN2; ++j) hs[j] = 0;
+    }
+    int32_t bw, cw;  // NN2 int8 codes each
+    if constexpr (NN2 == 4) {
+        bw = *reinterpret_cast<const int32_t*>(A.bm + b * N + n0);
+        cw = *reinterpret_cast<const int32_t*>(A.cm + b * N + n0);
+    } else {
+        bw = *reinterpret_cast<const int16_t*>(A.bm + b * N + n0);
+        cw = *reinterpret_cast<const int16_t*>(A.cm + b * N + n0);
+    }
+    double y = 0.0;
+#pragma unroll
+    for (int j = 0; j < NN2; ++j) {
+        const double bj = (double)(int8_t)(bw >> (8 * j)), cj = (double)(int8_t)(cw >> (8 * j));
+        // h + 2^31 floored and clamped to [0, 2^32 - 1] by the conversion
+        const double sv = __builtin_fma(dd, (double)hs[j], __builtin_fma(u, bj, 2147483648.5));
+        uint32_t hu;
+        asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
+        hs[j] = (int32_t)(hu ^ 0x80000000u);
+        y = __builtin_fma(cj, (double)hs[j], y);  // exact: integers below 2^46
+    }
+    if (A.state_out) {
+        if constexpr (NN2 == 4)
+            *reinterpret_cast<int4*>(A.state_out + sidx) = make_int4(hs[0], hs[1], hs[2], hs[3]);
+        else
+            *reinterpret_cast<int2*>(A.state_out + sidx) = make_int2(hs[0], hs[1]);
+    }
+    // sum over the 32 lanes of this half-wave
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) y += __shfl_xor(y, m, 64);
+    if (l32 == 0) {
+        const int ky = A.p[2] + A.p[3];
+        const double ya = __builtin_floor(__builtin_fma(y, __builtin_ldexp(1.0, -ky), 0.5));
+        const double yd =
+            __builtin_floor(__builtin_fma((double)A.d_q16[head] * (double)xi, 0x1p-8, 0.5));
+        A.y[q * P + p] =
+            (int32_t)__builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
+    }
+}
+
 size_t scan_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
                    hipEvent_t ev_stop) {
     if (a.dstate != 64 && a.dstate != 128)
         return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
+    if (a.len == 1) {  // one step: state traffic only
+        const int64_t waves = a.batch * a.nheads * (a.headdim / 2);
+        const unsigned g1 = (unsigned)((waves + 3) / 4);
+        if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
+            return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
+        if (a.dstate == 128) scan_step_kernel<4><<<g1, 256, 0, s>>>(a);
+        else scan_step_kernel<2><<<g1, 256, 0, s>>>(a);
+        fm_status st1 = check_launch("scan_step_kernel");
+        if (st1 != FM_OK) return st1;
+        if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess)
+            return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
+        return FM_OK;
+    }
     const int64_t pairs = a.batch * a.len * a.nheads;
     scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
         a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);

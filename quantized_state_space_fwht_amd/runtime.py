@@ -206,3 +206,29 @@ class Mamba2Stack:
             self.prefill(u, with_cache=False)
         for layer in self.layers:
             layer.set_static(B.fm_qparams_from_stats(layer.qparams()))
+
+
+class DecodeGraph:
+    """One decode step of a stack (every layer's launches) captured as a HIP graph.
+
+    The library neither allocates nor synchronizes inside a call and clears its
+    scratch words with a kernel, so the whole step is capturable.  ``step``
+    copies the input into the graph's fixed input buffer and replays; the
+    returned tensor is the graph's output buffer (the next replay overwrites
+    it).  Capture records work without running it, so the caches are not
+    advanced by building the graph; the stack's workspace must already be
+    sized (any earlier prefill or decode call on it does that)."""
+
+    def __init__(self, stack: Mamba2Stack, batch: int, device="cuda"):
+        self.stack = stack
+        self.x = torch.zeros((batch, stack.shape.d_model), dtype=torch.float32, device=device)
+        for layer in stack.layers:  # size the shared workspace outside the capture
+            layer.workspace_for(batch, 1)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = stack.decode(self.x)
+
+    def step(self, x):
+        self.x.copy_(x)
+        self.graph.replay()
+        return self.out

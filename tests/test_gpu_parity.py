@@ -75,7 +75,10 @@ def test_hadamard_quant(B, rows, k, mode):
 
 # --------------------------------------------------------------------------- a3 / a9
 @pytest.mark.parametrize("m,n,k", [(1, 1, 64), (17, 40, 64), (300, 1160, 256), (2048, 3352, 768),
-                                   (2048, 768, 1536), (129, 257, 512)])
+                                   (2048, 768, 1536), (129, 257, 512),
+                                   # few-row path (m <= 64, k % 256 == 0): decode shapes, ragged n
+                                   (16, 10576, 2560), (16, 2560, 5120), (1, 33, 256),
+                                   (3, 1160, 256), (40, 300, 768), (64, 777, 1536)])
 def test_w8a8_gemm(B, m, n, k):
     rng = np.random.default_rng(m + n + k)
     a = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
@@ -194,6 +197,8 @@ def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
                                                       ("m130m_layer", 3, 5, 2),
                                                       ("m130m_layer", 1, 16, 2),
                                                       ("m130m_layer", 2, 33, 3),
+                                                      ("m130m_layer", 3, 1, 4),
+                                                      ("tiny_layer", 2, 1, None),
                                                       ("m2p7b_stack", 1, 300, 4)])
 @pytest.mark.parametrize("with_state", [False, True])
 def test_ssm_scan_pot(B, wname, batch, length, heads, with_state):
