@@ -22,16 +22,6 @@ struct ConvKParams {
     int dynamic;
 };
 
-__device__ __forceinline__ int32_t quant_xbc(float v, float scale) {
-    return (int32_t)fminf(fmaxf(rintf(v * scale), -127.0f), 127.0f);
-}
-
-// clamp(floor(v + 1/2)) to int32 for an integer-valued or half-step v
-__device__ __forceinline__ int32_t round_sat32(double v) {
-    return (int32_t)__builtin_fmin(__builtin_fmax(__builtin_floor(v + 0.5), -2147483648.0),
-                                   2147483647.0);
-}
-
 // One thread: channel c, steps t0 .. t0+n-1 (n = kConvTL unless kTail).
 // Dynamic: writes Q.16 SiLU outputs + per-part maxima.  Static: writes codes.
 template <bool kTail, bool kDyn, bool kXq>

@@ -70,6 +70,17 @@ __device__ __forceinline__ int pot_from_q16(int64_t m) {
     return kPMin;
 }
 
+// xBC -> int8 code with its power-of-two scale 2^p_c: sat8(rint(v * 2^p_c))
+__device__ __forceinline__ int32_t quant_xbc(float v, float scale) {
+    return (int32_t)fminf(fmaxf(rintf(v * scale), -127.0f), 127.0f);
+}
+
+// clamp(floor(v + 1/2)) to int32 for an integer-valued or half-step v
+__device__ __forceinline__ int32_t round_sat32(double v) {
+    return (int32_t)__builtin_fmin(__builtin_fmax(__builtin_floor(v + 0.5), -2147483648.0),
+                                   2147483647.0);
+}
+
 // ---------------------------------------------------------------- NAU
 // Chord endpoints Y_i = rint(2^(i/8) * 2^30), i = 0..8.
 __device__ __forceinline__ int64_t exp2_knot(uint32_t i) {
@@ -146,6 +157,58 @@ __device__ __forceinline__ int32_t nau_silu_f(int32_t x, const NauLds& t) {
     // rshr(xn * sigma, 16): |xn * sigma| < 2^46
     const int32_t sn = (int32_t)__builtin_floor(__builtin_fma((double)xn, q * 0x1p-16, 0.5));
     return x > 0 ? x + sn : sn;
+}
+
+// ---------------------------------------------------------------- 256-point FWHT
+// H_256 / 16 of one 256-block held 4 values per lane (lane l: elements 4l..4l+3).
+// Stages h = 1, 2 inside the lane, then h = 4m with the partner lane l ^ m: the
+// lane with bit m clear keeps a + b, its partner a - b.  fma(+-1, v, p) rounds
+// exactly like the plain sum or difference, so every lane runs one instruction
+// stream.  The final 1/16 is exact.
+__device__ __forceinline__ float4 fwht256_lane(float4 v, int lane) {
+    float t0 = v.x + v.y, t1 = v.x - v.y, t2 = v.z + v.w, t3 = v.z - v.w;
+    v.x = t0 + t2;
+    v.z = t0 - t2;
+    v.y = t1 + t3;
+    v.w = t1 - t3;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float px = __shfl_xor(v.x, m, 64);
+        const float py = __shfl_xor(v.y, m, 64);
+        const float pz = __shfl_xor(v.z, m, 64);
+        const float pw = __shfl_xor(v.w, m, 64);
+        const float sg = (lane & m) ? -1.0f : 1.0f;
+        v.x = __builtin_fmaf(sg, v.x, px);
+        v.y = __builtin_fmaf(sg, v.y, py);
+        v.z = __builtin_fmaf(sg, v.z, pz);
+        v.w = __builtin_fmaf(sg, v.w, pw);
+    }
+    v.x *= 0.0625f;
+    v.y *= 0.0625f;
+    v.z *= 0.0625f;
+    v.w *= 0.0625f;
+    return v;
+}
+
+__device__ __forceinline__ float absmax4(float4 v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// q = sat8(rint(v * c)) per element
+__device__ __forceinline__ char4 quant4(float4 v, float c) {
+    char4 q;
+    q.x = (signed char)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f);
+    q.y = (signed char)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f);
+    q.z = (signed char)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f);
+    q.w = (signed char)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f);
+    return q;
+}
+
+// sum of a per-lane partial over the wave in the fixed xor order k = 32, 16, .., 1
+__device__ __forceinline__ float wave_sum_fixed(float a) {
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) a = a + __shfl_xor(a, k, 64);
+    return a;
 }
 
 // ---------------------------------------------------------------- wave helpers

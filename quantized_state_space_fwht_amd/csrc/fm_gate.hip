@@ -12,53 +12,24 @@
 
 namespace fm {
 
-__device__ __forceinline__ float4 fwht256_lane_g(float4 v, int lane) {
-    float t0 = v.x + v.y, t1 = v.x - v.y, t2 = v.z + v.w, t3 = v.z - v.w;
-    v.x = t0 + t2;
-    v.z = t0 - t2;
-    v.y = t1 + t3;
-    v.w = t1 - t3;
-    // stage m: the lane with bit m clear keeps a + b, its partner b' = a - b;
-    // fma(+-1, v, p) rounds p + v / p - v exactly as the plain sums do
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float px = __shfl_xor(v.x, m, 64);
-        const float py = __shfl_xor(v.y, m, 64);
-        const float pz = __shfl_xor(v.z, m, 64);
-        const float pw = __shfl_xor(v.w, m, 64);
-        const float sg = (lane & m) ? -1.0f : 1.0f;
-        v.x = __builtin_fmaf(sg, v.x, px);
-        v.y = __builtin_fmaf(sg, v.y, py);
-        v.z = __builtin_fmaf(sg, v.z, pz);
-        v.w = __builtin_fmaf(sg, v.w, pw);
-    }
-    v.x *= 0.0625f;
-    v.y *= 0.0625f;
-    v.z *= 0.0625f;
-    v.w *= 0.0625f;
-    return v;
-}
-
-// sum of squares in the fixed order, identical in every lane
-__device__ __forceinline__ float row_sumsq(float a) {
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) a = a + __shfl_xor(a, k, 64);
-    return a;
-}
-
 constexpr int kGateMaxD = 8192;
-constexpr int kGateWaves = 4;
+constexpr int kGateWaves = 4;     // many rows: a workgroup of 4 waves per row
+constexpr int kGateStepWaves = 16;  // one-token step (few rows): 16 waves per row
+constexpr int kGatePer = 8;       // gate values per thread whose loads go out together
 
-// One workgroup of 4 waves per row.  Phase 1: every thread computes gate
+// One workgroup of W waves per row.  Phase 1: every thread computes gate
 // values g_i (any split: each is independent) into LDS.  Phase 2: wave 0
 // forms the sum of squares in the fixed order (lane l adds g_i^2 for
 // i = l, l+64, ... ascending, then the xor tree).  Phase 3: the 256-blocks
-// are normalized, rotated and quantized, block b by wave b % 4.
-__global__ __launch_bounds__(64 * kGateWaves) void gate_norm_kernel(GateArgs G) {
+// are normalized, rotated and quantized, block b by wave b % W.  With
+// `rowmax` set (one-token step), the rotated row goes to rot_ws and its
+// maximum to rowmax[row]; the out_proj product quantizes.
+template <int W>
+__global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     extern __shared__ __attribute__((aligned(16))) float row_buf[];  // d_inner floats
     __shared__ NauLds tab;
     __shared__ float rs_r;
-    __shared__ float wmax[kGateWaves];
+    __shared__ float wmax[W];
     nau_lds_init(tab);
     __syncthreads();
     const int tid = threadIdx.x, lane = tid & 63;
@@ -67,45 +38,55 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_norm_kernel(GateArgs G) 
     const int D = (int)G.d_inner;
     const float ysc = ldexpf(1.0f, -(G.p[1] + 8));
     const int32_t* yr = G.y + row * D;
-    const float* zr = G.z + row * G.z_stride;
-    // phase 1: four elements per thread per round, loads of a round issued together
-    for (int i0 = tid; i0 < D; i0 += 4 * 64 * kGateWaves) {
-        int32_t yv[4];
-        float zv[4];
+    const float* zr = G.sz ? G.sz + row * D : G.z + row * G.z_stride;
+    // phase 1: kGatePer elements per thread per round, loads of a round issued together
+    for (int i0 = tid; i0 < D; i0 += kGatePer * 64 * W) {
+        int32_t yv[kGatePer];
+        float zv[kGatePer];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = i0 + 64 * kGateWaves * k;
+        for (int k = 0; k < kGatePer; ++k) {
+            const int i = i0 + 64 * W * k;
             yv[k] = i < D ? yr[i] : 0;
             zv[k] = i < D ? zr[i] : 0.0f;
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = i0 + 64 * kGateWaves * k;
-            const float yf = (float)yv[k] * ysc;
-            const int32_t zq = f2i_sat(rintf(zv[k] * 65536.0f));
-            const float sz = (float)nau_silu_f(zq, tab) * 0x1p-16f;
-            if (i < D) row_buf[i] = yf * sz;
+        for (int k = 0; k < kGatePer; ++k) {
+            const int i = i0 + 64 * W * k;
+            if (i < D) {
+                const float yf = (float)yv[k] * ysc;
+                float sz = zv[k];
+                if (!G.sz) sz = (float)nau_silu_f(f2i_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
+                row_buf[i] = yf * sz;
+            }
         }
     }
     __syncthreads();
     // phase 2: the fixed-order sum of squares
     if (wave == 0) {
         float a = 0.0f;
-        for (int i = lane; i < D; i += 64) {
-            const float g = row_buf[i];
-            const float g2 = g * g;
-            a = a + g2;  // ascending i within this lane: the fixed order
+        for (int i0 = lane; i0 < D; i0 += 16 * 64) {  // D % 256 == 0: 4 steps at least
+            float g[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) g[k] = i0 + 64 * k < D ? row_buf[i0 + 64 * k] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (i0 + 64 * k < D) {
+                    const float g2 = g[k] * g[k];
+                    a = a + g2;  // ascending i within this lane: the fixed order
+                }
+            }
         }
-        const float ss = row_sumsq(a);
+        const float ss = wave_sum_fixed(a);
         const float ms = ss / (float)D;
         if (lane == 0) rs_r = 1.0f / sqrtf(ms + 1e-5f);
     }
     __syncthreads();
     const float r = rs_r;
+    const bool dyn = G.mode == FM_SCALE_DYNAMIC;
     float c = 0.0f;
-    if (G.mode == FM_SCALE_STATIC) c = ldexpf((float)G.scoe, -G.sshift);
+    if (!dyn) c = ldexpf((float)G.scoe, -G.sshift);
     float m = 0.0f;
-    for (int blk = wave; blk < D / 256; blk += kGateWaves) {
+    for (int blk = wave; blk < D / 256; blk += W) {
         const int base = blk * 256 + lane * 4;
         float4 g = *reinterpret_cast<const float4*>(&row_buf[base]);
         const float4 w = *reinterpret_cast<const float4*>(&G.norm_w[base]);
@@ -115,36 +96,38 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_norm_kernel(GateArgs G) 
         n.z = (g.z * r) * w.z;
         n.w = (g.w * r) * w.w;
         if (G.normed_out) *reinterpret_cast<float4*>(&G.normed_out[row * D + base]) = n;
-        const float4 v = fwht256_lane_g(n, lane);
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        if (G.mode == FM_SCALE_DYNAMIC) {
-            *reinterpret_cast<float4*>(&G.rot_ws[row * D + base]) = v;
-        } else {
-            char4 q;
-            q.x = (signed char)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f);
-            q.y = (signed char)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f);
-            q.z = (signed char)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f);
-            q.w = (signed char)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f);
-            *reinterpret_cast<char4*>(&G.q[row * D + base]) = q;
-        }
+        const float4 v = fwht256_lane(n, lane);
+        m = fmaxf(m, absmax4(v));
+        if (dyn || G.rowmax) *reinterpret_cast<float4*>(&G.rot_ws[row * D + base]) = v;
+        else *reinterpret_cast<char4*>(&G.q[row * D + base]) = quant4(v, c);
     }
     m = wave_max_f32(m);
     if (lane == 0) wmax[wave] = m;
     __syncthreads();
     if (tid == 0) {
-        m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        if (G.mode == FM_SCALE_DYNAMIC) atomic_max_nonneg_f32(G.amax_ws, m);
+        m = wmax[0];
+        for (int k = 1; k < W; ++k) m = fmaxf(m, wmax[k]);
+        if (G.rowmax) {
+            G.rowmax[row] = m;
+            return;
+        }
+        if (dyn) atomic_max_nonneg_f32(G.amax_ws, m);
         if (G.amax_stats) atomic_max_nonneg_f32(G.amax_stats, m);
-        if (G.mode == FM_SCALE_STATIC && row == 0) *G.scale_out = 1.0f / c;
+        if (!dyn && row == 0) *G.scale_out = 1.0f / c;
     }
 }
 
 fm_status gate_run(const GateArgs& g, hipStream_t s) {
     if (g.d_inner > kGateMaxD)
         return fail(FM_ERR_SHAPE, "gate: d_inner %lld > %d", (long long)g.d_inner, kGateMaxD);
+    const size_t lds = (size_t)g.d_inner * sizeof(float);
+    if (g.rowmax) {  // one-token step: rotated rows and row maxima only
+        if (g.rows > 0)
+            gate_norm_kernel<kGateStepWaves><<<(unsigned)g.rows, 64 * kGateStepWaves, lds, s>>>(g);
+        return check_launch("gate_norm_kernel");
+    }
     if (g.rows > 0) {
-        gate_norm_kernel<<<(unsigned)g.rows, 64 * kGateWaves, (size_t)g.d_inner * sizeof(float),
-                           s>>>(g);
+        gate_norm_kernel<kGateWaves><<<(unsigned)g.rows, 64 * kGateWaves, lds, s>>>(g);
         fm_status st = check_launch("gate_norm_kernel");
         if (st != FM_OK) return st;
     }
@@ -175,7 +158,7 @@ __global__ __launch_bounds__(64 * kGateWaves) void rmsnorm_rows_kernel(
             const float v2 = v * v;
             a = a + v2;
         }
-        const float ss = row_sumsq(a);
+        const float ss = wave_sum_fixed(a);
         if (lane == 0) rs_r = 1.0f / sqrtf(ss / (float)d + 1e-5f);
     }
     __syncthreads();

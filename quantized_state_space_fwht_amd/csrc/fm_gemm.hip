@@ -34,6 +34,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_i8_kernel(GemmParams P) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    if (P.ep.pub_small && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+        layer_publish(P.ep.pub_small, P.ep.pub_qp, P.ep.pub_cache_p);
     const int64_t m0 = (int64_t)blockIdx.y * kBM;
     const int64_t n0 = (int64_t)blockIdx.x * kBN;
     const int64_t K = P.k;
@@ -137,88 +139,309 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_i8_kernel(GemmParams P) {
 
 // ---------------------------------------------------------------- few rows (decode)
 // M <= 64: weight traffic is the whole cost, so every workgroup streams its own
-// 16 columns of B over the full K exactly once.  The 4 waves split K in four;
-// each wave keeps MT (= ceil(M/16)) 16 x 16 accumulator tiles, and the
-// partial tiles are added through LDS before the same epilogue as above.
-constexpr int kSkU = 4;  // k-slices of 64 whose loads are issued together
+// 16*NT columns of B over the full K exactly once.  KW waves split K evenly;
+// each keeps MT x NT (MT = ceil(M/16)) 16 x 16 accumulator tiles and issues up
+// to kU 64-wide k-slices of loads at once.  The partial tiles are added through
+// LDS (int32, exact in any order) and the epilogue is spread over all waves (each
+// loads the residual of its share before the product).
+constexpr int kSkU = 8;
 
-template <int MT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_i8_few_rows_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(16))) int32_t part[4][MT][64][4];
+// A operand of the one-token step: 16 rotated floats of a row -> 16 int8 codes
+// sat8(rint(v * c)), packed in memory order (byte i of the vector = element i)
+__device__ __forceinline__ uint32_t quant_pack4(float4 v, float c) {
+    const uint32_t b0 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f) & 0xFFu;
+    const uint32_t b1 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f) & 0xFFu;
+    const uint32_t b2 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f) & 0xFFu;
+    const uint32_t b3 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f) & 0xFFu;
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+// kMode 0: int8 A.  1: float A quantized on load; the columns hold z | xBC | dt
+// of a one-token step: SiLU(z) in Q.16 goes to sz_out, xBC runs the conv step
+// (power-of-two code, the 4-tap window from the conv cache shifted in place,
+// SiLU, code of x / B / C, in the arithmetic of the conv kernel), dt is
+// stored.  2: float A quantized on load, plain epilogue.
+template <int MT, int NT, int KW, int kMode>
+__global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P) {
+    constexpr bool kAf = kMode != 0, kConv = kMode == 1;
+    // float A: 4x the bytes per slice, held raw until the whole batch is issued
+    constexpr int kU = kAf ? (MT == 1 ? 5 : (MT == 2 ? 2 : 1)) : kSkU;
+    __shared__ __attribute__((aligned(16))) int32_t part[KW][MT][NT][64][4];
+    __shared__ float wg_max[KW][2];      // per wave: max |out| (amax columns), max |xBC|
+    __shared__ int32_t wg_pmax[KW][3];   // per wave: max |SiLU| of x, B, C
+    __shared__ NauLds tab;
+    if constexpr (kConv) nau_lds_init(tab);
+    const GemmEpilogue& ep = P.ep;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t K = P.k, kq = K / 4;  // k range of this wave: [wave*kq, wave*kq + kq)
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * NT);
+    const int di = (int)ep.d_inner, N = (int)ep.dstate, ch = di + 2 * N;
+
+    // Epilogue units: (row tile t, column tile nt, row r of the lane's four),
+    // one element per lane each; wave w takes units w, w + KW, ...
+    constexpr int kUnits = MT * NT * 4, kUpw = (kUnits + KW - 1) / KW;
+    // ---- the residual of this wave's units, loaded ahead of the product (rows
+    // and columns past the edge read a valid element that is never used)
+    float res[kUpw];
+    if (!kConv && ep.resid) {
+#pragma unroll
+        for (int k = 0; k < kUpw; ++k) {
+            const int un = wave + k * KW;
+            const int t = un / (NT * 4), nt = (un / 4) % NT, r = un % 4;
+            int64_t col = n0 + 16 * nt + (lane & 15);
+            col = col < P.n ? col : P.n - 1;
+            int64_t row = t * 16 + (lane >> 4) * 4 + r;
+            row = row < P.m ? row : P.m - 1;
+            res[k] = un < kUnits ? ep.resid[row * ep.ld_resid + col] : 0.0f;
+        }
+    }
+
+    // ---- float A: the tensor scale from the row maxima (the same float ops everywhere)
+    float c = 0.0f, s_a = 0.0f;
+    if constexpr (kAf) {
+        // m <= 64 row maxima: one per lane, one load round trip (max is exact)
+        const float amax = wave_max_f32(lane < P.m ? ep.a_rowmax[lane] : 0.0f);
+        if (ep.a_mode == FM_SCALE_DYNAMIC) c = amax == 0.0f ? 1.0f : 127.0f / amax;
+        else c = ldexpf((float)ep.a_scoe, -ep.a_sshift);
+        s_a = 1.0f / c;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            *ep.a_amax_out = amax;
+            *ep.a_scale_out = s_a;
+        }
+    }
+    if (ep.pub_small && blockIdx.x == 0 && threadIdx.x == 0)
+        layer_publish(ep.pub_small, ep.pub_qp, ep.pub_cache_p);
+
+    // ---- product
+    // k range of this wave: slice ks = (wave + block) % KW, [ks*kq, ks*kq + kq): the
+    // rotation spreads the workgroups' simultaneous reads of A over the slices
+    const int64_t K = P.k, kq = K / KW;
+    const int ks = (int)((wave + blockIdx.x) % KW);
     const int frag_row = lane & 15, frag_k = (lane >> 4) * 16;
-    int64_t rb = n0 + frag_row;
-    rb = rb < P.n ? rb : P.n - 1;  // columns past the edge: computed, never stored
-    const int8_t* pb = P.b + rb * K + wave * kq + frag_k;
-    const int8_t* pa[MT];
+    const int8_t* pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        int64_t rb = n0 + 16 * nt + frag_row;
+        rb = rb < P.n ? rb : P.n - 1;  // columns past the edge: computed, never stored
+        pb[nt] = P.b + rb * K + ks * kq + frag_k;
+    }
+    int64_t aoff[MT];
+    bool tap[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        int64_t ra = t * 16 + frag_row;
-        ra = ra < P.m ? ra : P.m - 1;
-        pa[t] = P.a + ra * K + wave * kq + frag_k;
+        const int64_t ra0 = t * 16 + frag_row;
+        tap[t] = kAf && ep.a_q_tap && blockIdx.x == 0 && ra0 < P.m;
+        const int64_t ra = ra0 < P.m ? ra0 : P.m - 1;
+        aoff[t] = ra * K + ks * kq + frag_k;
     }
-    v4i acc[MT];
+    v4i acc[MT][NT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = v4i{0, 0, 0, 0};
-    const int64_t steps = kq / kBK;
-    int64_t s0 = 0;
-    for (; s0 + kSkU <= steps; s0 += kSkU) {
-        v4i bf[kSkU], af[kSkU][MT];
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int u = 0; u < kSkU; ++u) {
-            bf[u] = *reinterpret_cast<const v4i*>(pb + (s0 + u) * kBK);
+        for (int nt = 0; nt < NT; ++nt) acc[t][nt] = v4i{0, 0, 0, 0};
+    // cnt <= kU slices: every load of the batch is issued before any use (the
+    // optional code store may alias B, so no load may sit behind it)
+    auto slices = [&](int64_t s0, int cnt) {
+        v4i bf[kU][NT], af[kU][MT];
+        float4 araw[kU][MT][4];
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                af[u][t] = *reinterpret_cast<const v4i*>(pa[t] + (s0 + u) * kBK);
-        }
+        for (int u = 0; u < kU; ++u) {
+            if (u < cnt) {
 #pragma unroll
-        for (int u = 0; u < kSkU; ++u)
+                for (int nt = 0; nt < NT; ++nt)
+                    bf[u][nt] = *reinterpret_cast<const v4i*>(pb[nt] + (s0 + u) * kBK);
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[u][t], bf[u], acc[t], 0, 0, 0);
-    }
-    for (; s0 < steps; ++s0) {
-        const v4i bf = *reinterpret_cast<const v4i*>(pb + s0 * kBK);
+                for (int t = 0; t < MT; ++t) {
+                    if constexpr (kAf) {
+                        const float4* pa4 =
+                            reinterpret_cast<const float4*>(ep.a_f + aoff[t] + (s0 + u) * kBK);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const v4i af = *reinterpret_cast<const v4i*>(pa[t] + s0 * kBK);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf, acc[t], 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) *reinterpret_cast<v4i*>(&part[wave][t][lane][0]) = acc[t];
-    __syncthreads();
-    if (wave != 0) return;
-    const GemmEpilogue& ep = P.ep;
-    float sab = 0.0f;
-    if (ep.out) sab = (*ep.s_a) * (*ep.s_b);
-    float amax = 0.0f;
-    const int64_t col = n0 + (lane & 15);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t row = t * 16 + (lane >> 4) * 4 + r;
-            // int32 sum of the four k quarters (exact: |acc| < 2^31 for any order)
-            const int32_t v = part[0][t][lane][r] + part[1][t][lane][r] + part[2][t][lane][r] +
-                              part[3][t][lane][r];
-            if (row < P.m && col < P.n) {
-                if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
-                if (ep.out) {
-                    float o = (float)v * sab;
-                    if (ep.resid) o = ep.resid[row * ep.ld_resid + col] + o;
-                    ep.out[row * ep.ld_out + col] = o;
-                    if (col >= ep.amax_c0 && col < ep.amax_c1) amax = fmaxf(amax, fabsf(o));
+                        for (int e = 0; e < 4; ++e) araw[u][t][e] = pa4[e];
+                    } else {
+                        af[u][t] = *reinterpret_cast<const v4i*>(P.a + aoff[t] + (s0 + u) * kBK);
+                    }
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of its uses
+        if constexpr (kAf) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (u < cnt)
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) {
+                        af[u][t] = v4i{(int)quant_pack4(araw[u][t][0], c),
+                                       (int)quant_pack4(araw[u][t][1], c),
+                                       (int)quant_pack4(araw[u][t][2], c),
+                                       (int)quant_pack4(araw[u][t][3], c)};
+                        if (tap[t])
+                            *reinterpret_cast<v4i*>(ep.a_q_tap + aoff[t] + (s0 + u) * kBK) =
+                                af[u][t];
+                    }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (u < cnt)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        acc[t][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[u][t], bf[u][nt],
+                                                                           acc[t][nt], 0, 0, 0);
+    };
+    const int64_t steps = kq / kBK;
+    int64_t s0 = 0;
+    for (; s0 + kU <= steps; s0 += kU) slices(s0, kU);
+    if (s0 < steps) slices(s0, (int)(steps - s0));
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            *reinterpret_cast<v4i*>(&part[wave][t][nt][lane][0]) = acc[t][nt];
+    __syncthreads();
+
+    // ---- epilogue: every wave, its units.  Phase 1 issues every load of the
+    // wave's units (the conv window and weights with clamped, valid indices for
+    // the units that do not use them); phase 2 computes and stores.
+    float sab = 0.0f;
+    if (ep.out) sab = (kAf ? s_a : *ep.s_a) * (*ep.s_b);
+    int32_t uv[kUpw];
+    int32_t xw[kUpw], xs0[kUpw], xs1[kUpw], xs2[kUpw], xpw[kUpw], xb[kUpw];
+#pragma unroll
+    for (int k = 0; k < kUpw; ++k) {
+        const int un = wave + k * KW < kUnits ? wave + k * KW : kUnits - 1;
+        const int t = un / (NT * 4), nt = (un / 4) % NT, r = un % 4;
+        int32_t v = part[0][t][nt][lane][r];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += part[w][t][nt][lane][r];
+        uv[k] = v;
+        if constexpr (kConv) {
+            int64_t cx = n0 + 16 * nt + (lane & 15) - ep.amax_c0;
+            cx = cx < 0 ? 0 : (cx >= ch ? ch - 1 : cx);
+            int64_t row = t * 16 + (lane >> 4) * 4 + r;
+            row = row < P.m ? row : P.m - 1;
+            const int8_t* st = ep.conv_state + (row * ch + cx) * 3;
+            xs0[k] = st[0];
+            xs1[k] = st[1];
+            xs2[k] = st[2];
+            xw[k] = *reinterpret_cast<const int32_t*>(ep.conv_w_q + cx * 4);
+            xpw[k] = ep.conv_p_w[cx];
+            xb[k] = ep.conv_b_q16[cx];
+        }
     }
-    if (ep.amax) {
-        amax = wave_max_f32(amax);
-        if (lane == 0 && amax > 0.0f) atomic_max_nonneg_f32(ep.amax, amax);
+    float amax = 0.0f, xmax = 0.0f;
+    int32_t pmax[3] = {0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kUpw; ++k) {
+        const int un = wave + k * KW;
+        if (un >= kUnits) break;
+        const int t = un / (NT * 4), nt = (un / 4) % NT, r = un % 4;
+        const int64_t col0 = n0 + 16 * nt, col = col0 + (lane & 15);
+        const int64_t row = t * 16 + (lane >> 4) * 4 + r;
+        const int32_t v = uv[k];
+        const bool ok = row < P.m && col < P.n;
+        // column groups of 16 never straddle the z | xBC | dt boundaries
+        if (kConv && col0 >= ep.amax_c0 && col0 < ep.amax_c1) {
+            if (ok) {
+                const int cx = (int)(col - ep.amax_c0);
+                const int part_i = cx < di ? 0 : (cx < di + N ? 1 : 2);
+                const int p_c = ep.conv_p[0];
+                const int32_t w0 = (int8_t)(xw[k] & 0xFF), w1 = (int8_t)((xw[k] >> 8) & 0xFF),
+                              w2 = (int8_t)((xw[k] >> 16) & 0xFF), w3 = (int8_t)(xw[k] >> 24);
+                const double ascale = __builtin_ldexp(1.0, 16 - p_c - xpw[k]);
+                const double oscale = __builtin_ldexp(1.0, ep.conv_p[1 + part_i] - 16);
+                const int32_t xm3 = xs0[k], xm2 = xs1[k], xm1 = xs2[k];
+                const float o = (float)v * sab;
+                if (ep.write_xbc) ep.out[row * ep.ld_out + col] = o;
+                xmax = fmaxf(xmax, fabsf(o));
+                const int32_t xq = quant_xbc(o, ldexpf(1.0f, p_c));
+                if (ep.xbc_q) ep.xbc_q[row * ch + cx] = (int8_t)xq;
+                const int32_t a = round_sat32(__builtin_fma(
+                    (double)(w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq), ascale, (double)xb[k]));
+                const int32_t sv = nau_silu_f(a, tab);
+                const int32_t sa = sv < 0 ? -sv : sv;
+                pmax[part_i] = sa > pmax[part_i] ? sa : pmax[part_i];
+                // sat8(rshr(sv, 16 - p_part)): sv * 2^(p_part-16) is exact in float64
+                const double q = __builtin_floor(__builtin_fma((double)sv, oscale, 0.5));
+                int8_t* code = part_i == 0 ? ep.x_out + row * di + cx
+                                           : (part_i == 1 ? ep.b_out + row * N + (cx - di)
+                                                          : ep.c_out + row * N + (cx - di - N));
+                *code = (int8_t)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
+                int8_t* st = ep.conv_state + (row * ch + cx) * 3;
+                st[0] = (int8_t)xm2;
+                st[1] = (int8_t)xm1;
+                st[2] = (int8_t)xq;
+            }
+            continue;
+        }
+        if (kConv && col0 < ep.amax_c0) {  // z: SiLU(z) for the gate (Q.16 through the unit)
+            if (ok) {
+                const float o = (float)v * sab;
+                if (ep.write_xbc) ep.out[row * ep.ld_out + col] = o;
+                const int32_t zq = f2i_sat(rintf(o * 65536.0f));
+                ep.sz_out[row * di + col] = (float)nau_silu_f(zq, tab) * 0x1p-16f;
+            }
+            continue;
+        }
+        if (ok) {
+            if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
+            if (ep.out) {
+                float o = (float)v * sab;
+                if (ep.resid) o = res[k] + o;
+                ep.out[row * ep.ld_out + col] = o;
+                if (col >= ep.amax_c0 && col < ep.amax_c1) amax = fmaxf(amax, fabsf(o));
+            }
+        }
+    }
+    // the workgroup's maxima, then one atomic per quantity
+    if (!kConv && !ep.amax) return;
+    amax = wave_max_f32(amax);
+    xmax = wave_max_f32(xmax);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) pmax[i] = wave_max_i32(pmax[i]);
+    if (lane == 0) {
+        wg_max[wave][0] = amax;
+        wg_max[wave][1] = xmax;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) wg_pmax[wave][i] = pmax[i];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < KW; ++w) {
+            amax = fmaxf(amax, wg_max[w][0]);
+            xmax = fmaxf(xmax, wg_max[w][1]);
+            for (int i = 0; i < 3; ++i) pmax[i] = wg_pmax[w][i] > pmax[i] ? wg_pmax[w][i] : pmax[i];
+        }
+        if (kConv) {
+            if (xmax > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(ep.amax), __float_as_uint(xmax));
+            for (int i = 0; i < 3; ++i)
+                if (pmax[i] > 0) atomicMax(&ep.conv_amax_q16[i], pmax[i]);
+        } else if (amax > 0.0f) {
+            atomicMax(reinterpret_cast<unsigned int*>(ep.amax), __float_as_uint(amax));
+        }
+    }
+}
+
+template <int NT, int KW, int kMode>
+static void launch_few_rows(const GemmParams& P, unsigned g, int mt, hipStream_t s) {
+    switch (mt) {
+        case 1: gemm_i8_few_rows_kernel<1, NT, KW, kMode><<<g, 64 * KW, 0, s>>>(P); break;
+        case 2: gemm_i8_few_rows_kernel<2, NT, KW, kMode><<<g, 64 * KW, 0, s>>>(P); break;
+        case 3: gemm_i8_few_rows_kernel<3, NT, KW, kMode><<<g, 64 * KW, 0, s>>>(P); break;
+        default: gemm_i8_few_rows_kernel<4, NT, KW, kMode><<<g, 64 * KW, 0, s>>>(P); break;
+    }
+}
+
+template <int kMode>
+static void launch_few_rows_kw(const GemmParams& P, int64_t n, int mt, int kw, bool wide,
+                               hipStream_t s) {
+    const unsigned g1 = (unsigned)((n + 15) / 16), g4 = (unsigned)((n + 63) / 64);
+    if (kw == 16) {  // mt == 1
+        gemm_i8_few_rows_kernel<1, 1, 16, kMode><<<g1, 64 * 16, 0, s>>>(P);
+    } else if (kw == 8) {
+        if (wide) gemm_i8_few_rows_kernel<1, 4, 8, kMode><<<g4, 64 * 8, 0, s>>>(P);  // mt == 1
+        else launch_few_rows<1, 8, kMode>(P, g1, mt, s);
+    } else {
+        launch_few_rows<1, 4, kMode>(P, g1, mt, s);
     }
 }
 
@@ -226,16 +449,24 @@ fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64
                    const GemmEpilogue& ep, hipStream_t s) {
     if (m == 0 || n == 0) return FM_OK;
     GemmParams P{a, b, m, n, k, ep};
+    const bool conv = ep.conv_state != nullptr, af = ep.a_f != nullptr;
+    if (conv && !af) return fail(FM_ERR_SHAPE, "gemm: the conv epilogue comes with float A");
     if (m <= 64 && k % (4 * kBK) == 0) {
-        const unsigned g = (unsigned)((n + 15) / 16);
-        switch ((m + 15) / 16) {
-            case 1: gemm_i8_few_rows_kernel<1><<<g, kGemmThreads, 0, s>>>(P); break;
-            case 2: gemm_i8_few_rows_kernel<2><<<g, kGemmThreads, 0, s>>>(P); break;
-            case 3: gemm_i8_few_rows_kernel<3><<<g, kGemmThreads, 0, s>>>(P); break;
-            default: gemm_i8_few_rows_kernel<4><<<g, kGemmThreads, 0, s>>>(P); break;
-        }
+        const int mt = (int)((m + 15) / 16);
+        // as many k-splitting waves as keep at least 4 slices per wave (16 waves
+        // only for one row tile: 1024 threads leave 128 registers per lane)
+        int kw = 4;
+        if (k % (16 * kBK) == 0 && k / (16 * kBK) >= 4 && mt == 1) kw = 16;
+        else if (k % (8 * kBK) == 0 && k / (8 * kBK) >= 4) kw = 8;
+        // float A is quantized again by every workgroup: with one row tile and
+        // enough columns, 64 columns per workgroup cut that work by four
+        const bool wide = af && mt == 1 && kw == 8 && (n + 63) / 64 >= 128;
+        if (conv) launch_few_rows_kw<1>(P, n, mt, kw, wide, s);
+        else if (af) launch_few_rows_kw<2>(P, n, mt, kw, wide, s);
+        else launch_few_rows_kw<0>(P, n, mt, kw, false, s);
         return check_launch("gemm_i8_few_rows_kernel");
     }
+    if (af) return fail(FM_ERR_SHAPE, "gemm: float A needs m <= 64, k %% 256 == 0");
     dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
     gemm_i8_kernel<<<grid, kGemmThreads, 0, s>>>(P);
     return check_launch("gemm_i8_kernel");

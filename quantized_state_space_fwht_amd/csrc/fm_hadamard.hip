@@ -16,42 +16,6 @@ namespace fm {
 
 constexpr int kHqThreads = 256;  // 4 waves, one 256-block each per iteration
 
-// Rotate the 4 values of this lane (lane = threadIdx % 64) through the block.
-__device__ __forceinline__ float4 fwht256_lane(float4 v, int lane) {
-    float t0 = v.x + v.y, t1 = v.x - v.y, t2 = v.z + v.w, t3 = v.z - v.w;  // h = 1
-    v.x = t0 + t2;                                                         // h = 2
-    v.z = t0 - t2;
-    v.y = t1 + t3;
-    v.w = t1 - t3;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {  // h = 4m: partner lane ^ m
-        float px = __shfl_xor(v.x, m, 64);
-        float py = __shfl_xor(v.y, m, 64);
-        float pz = __shfl_xor(v.z, m, 64);
-        float pw = __shfl_xor(v.w, m, 64);
-        if (lane & m) {  // this lane holds the upper element b of (a, b): a - b
-            v.x = px - v.x;
-            v.y = py - v.y;
-            v.z = pz - v.z;
-            v.w = pw - v.w;
-        } else {  // lower element a: a + b
-            v.x = v.x + px;
-            v.y = v.y + py;
-            v.z = v.z + pz;
-            v.w = v.w + pw;
-        }
-    }
-    v.x *= 0.0625f;
-    v.y *= 0.0625f;
-    v.z *= 0.0625f;
-    v.w *= 0.0625f;
-    return v;
-}
-
-__device__ __forceinline__ float absmax4(float4 v) {
-    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
-
 __device__ __forceinline__ void block_max_to(float m, float* a0, float* a1) {
     __shared__ float red[kHqThreads / 64];
     m = wave_max_f32(m);
@@ -88,15 +52,6 @@ __device__ __forceinline__ float scale_coef(fm_scale_mode mode, int32_t scoe, in
         return amax == 0.0f ? 1.0f : 127.0f / amax;
     }
     return ldexpf((float)scoe, -sshift);
-}
-
-__device__ __forceinline__ char4 quant4(float4 v, float c) {
-    char4 q;
-    q.x = (signed char)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f);
-    q.y = (signed char)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f);
-    q.z = (signed char)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f);
-    q.w = (signed char)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f);
-    return q;
 }
 
 // pass 2 (or the only pass in static mode): rotate again and quantize

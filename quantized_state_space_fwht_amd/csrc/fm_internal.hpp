@@ -30,6 +30,42 @@ struct Arena {
     }
 };
 
+// ---------------------------------------------------------------- layer scalars
+// Small per-call block at the head of a layer workspace (32-bit words).  The
+// dynamic scales and exponents flow from kernel to kernel through it and are
+// never copied to the host.
+enum SmallSlot {
+    kAmaxU = 0,     // float: max |u H|
+    kAmaxG = 1,     // float: max |n H|
+    kAmaxXbc = 2,   // float: max |xBC|
+    kAmaxQ = 3,     // int[3]: max |x|, |B|, |C| in Q.16
+    kScaleU = 6,    // float: in_proj input dequant scale
+    kScaleG = 7,    // float: out_proj input dequant scale
+    kP = 8,         // int[4]: p_c, p_x, p_B, p_C
+    kSmallWords = 16
+};
+
+// Publish what a layer call used into qp (scales, exponents, statistics) and,
+// when given, the exponents into the cache.  One thread, after every kernel
+// that writes the block has completed.
+__device__ inline void layer_publish(const uint32_t* small, fm_qparams* qp, int32_t* cache_p) {
+    uint32_t v[kP + 4];  // every load before the first store: one round trip
+#pragma unroll
+    for (int k = 0; k < kP + 4; ++k) v[k] = small[k];
+    qp->scale[0] = __uint_as_float(v[kScaleU]);
+    qp->scale[1] = __uint_as_float(v[kScaleG]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qp->p[k] = (int32_t)v[kP + k];
+    if (cache_p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cache_p[k] = (int32_t)v[kP + k];
+    atomicMax((unsigned int*)&qp->stat_amax[0], v[kAmaxU]);
+    atomicMax((unsigned int*)&qp->stat_amax[1], v[kAmaxG]);
+    atomicMax((unsigned int*)&qp->stat_amax[2], v[kAmaxXbc]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) atomicMax(&qp->stat_amax_q16[k], (int32_t)v[kAmaxQ + k]);
+}
+
 // ---------------------------------------------------------------- launchers
 // Zero `n` 32-bit words (a kernel, so it can sit inside captured graphs).
 fm_status zero_words(void* p, int64_t n, hipStream_t s);
@@ -56,6 +92,39 @@ struct GemmEpilogue {
     int64_t ld_resid = 0;
     float* amax = nullptr;         // max |out| over columns [amax_c0, amax_c1)
     int64_t amax_c0 = 0, amax_c1 = 0;
+    // one-token step (few-rows kernel only): the columns [amax_c0, amax_c1) are
+    // xBC and go through its power-of-two quantization, the conv window held in
+    // conv_state, SiLU and the requantization to x / B / C codes
+    const int8_t* conv_w_q = nullptr;   // [ch, 4]
+    const int32_t* conv_p_w = nullptr;  // [ch]
+    const int32_t* conv_b_q16 = nullptr;
+    const int32_t* conv_p = nullptr;    // device int32[4]: p_c, p_x, p_B, p_C
+    int8_t* conv_state = nullptr;       // [rows, ch, 3] in/out
+    int8_t* x_out = nullptr;            // [rows, d_inner]
+    int8_t* b_out = nullptr;            // [rows, dstate]
+    int8_t* c_out = nullptr;
+    int8_t* xbc_q = nullptr;            // nullable: [rows, ch] quantized conv input
+    int32_t* conv_amax_q16 = nullptr;   // int[3]: max |SiLU| of x, B, C (Q.16)
+    int64_t d_inner = 0, dstate = 0;
+    float* sz_out = nullptr;            // [rows, d_inner]: SiLU(z) of the z columns [0, amax_c0)
+    bool write_xbc = false;             // also write the float z and xBC columns to out
+    // one-token step (few-rows kernel only): A comes as rotated float rows with
+    // their row maxima; every workgroup forms the tensor scale c from them
+    // (dynamic: 127 / max, static: scoe * 2^-sshift) and quantizes its A slices
+    // while loading them, so no pass over A separates the row kernel from the
+    // product.  Workgroup 0 stores the maximum, the dequant scale 1 / c and,
+    // when a_q_tap is set, the codes.
+    const float* a_f = nullptr;         // [m, k] rotated rows
+    const float* a_rowmax = nullptr;    // [m] max |row|
+    fm_scale_mode a_mode = FM_SCALE_DYNAMIC;
+    int32_t a_scoe = 0, a_sshift = 0;
+    float* a_amax_out = nullptr;
+    float* a_scale_out = nullptr;
+    int8_t* a_q_tap = nullptr;
+    // after the product: one thread publishes the layer's block (layer_publish)
+    const uint32_t* pub_small = nullptr;
+    fm_qparams* pub_qp = nullptr;
+    int32_t* pub_cache_p = nullptr;
 };
 fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
                    const GemmEpilogue& ep, hipStream_t s);
@@ -124,6 +193,9 @@ struct GateArgs {
     float* normed_out;
     float* rot_ws;     // dynamic: [rows, d_inner] rotated values between passes
     float* amax_ws;    // dynamic: 1 float
+    const float* sz;   // nullable: SiLU(z) already formed ([rows, d_inner], Q.16 as float)
+    float* rowmax;     // nullable: one-token form, rotated rows to rot_ws and their maxima
+                       // here (the out_proj product quantizes them); q, scale_out unused
 };
 fm_status gate_run(const GateArgs& a, hipStream_t s);
 

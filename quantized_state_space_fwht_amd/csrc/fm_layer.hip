@@ -9,18 +9,6 @@
 
 namespace fm {
 
-// small per-call block at the head of the layer workspace (32-bit words)
-enum SmallSlot {
-    kAmaxU = 0,    // float: max |u H|
-    kAmaxG = 1,    // float: max |n H|
-    kAmaxXbc = 2,  // float: max |xBC|
-    kAmaxQ = 3,    // int[3]: max |x|, |B|, |C| in Q.16
-    kScaleU = 6,   // float: in_proj input dequant scale
-    kScaleG = 7,   // float: out_proj input dequant scale
-    kP = 8,        // int[4]: p_c, p_x, p_B, p_C
-    kSmallWords = 16
-};
-
 struct LayerWs {
     uint32_t* small;
     float* un;       // pre-norm output [T, dm]
@@ -38,6 +26,8 @@ struct LayerWs {
     int32_t* dt;     // [T, H]
     int32_t* da;     // [T, H]
     void* scan_ws;   // scan prologue scalars
+    float* rowmax;   // one-token step: [2, 64] row maxima (in_proj input, out_proj input)
+    float* sz;       // one-token step: [T, di] SiLU(z) from the in_proj epilogue
     size_t bytes;
 };
 
@@ -63,6 +53,8 @@ static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void
     w.dt = ar.take<int32_t>((size_t)T * H);
     w.da = ar.take<int32_t>((size_t)T * H);
     w.scan_ws = ar.take<char>(scan_ws_bytes(batch, len, d->dstate));
+    w.rowmax = ar.take<float>(T <= 64 ? 128 : 0);
+    w.sz = ar.take<float>(T <= 64 ? (size_t)T * di : 0);
     w.bytes = ar.used;
     return w;
 }
@@ -115,19 +107,92 @@ __global__ void layer_setup_kernel(uint32_t* small, const int32_t* p_src, int p0
     }
 }
 
-// publish what the call used into qp (and the frozen exponents into the cache)
-__global__ void layer_finalize_kernel(const uint32_t* small, fm_qparams* qp, int32_t* cache_p) {
-    if (threadIdx.x != 0) return;
-    const int32_t* p = (const int32_t*)(small + kP);
-    qp->scale[0] = __uint_as_float(small[kScaleU]);
-    qp->scale[1] = __uint_as_float(small[kScaleG]);
-    for (int k = 0; k < 4; ++k) qp->p[k] = p[k];
-    if (cache_p)
-        for (int k = 0; k < 4; ++k) cache_p[k] = p[k];
-    atomicMax((unsigned int*)&qp->stat_amax[0], small[kAmaxU]);
-    atomicMax((unsigned int*)&qp->stat_amax[1], small[kAmaxG]);
-    atomicMax((unsigned int*)&qp->stat_amax[2], small[kAmaxXbc]);
-    for (int k = 0; k < 3; ++k) atomicMax(&qp->stat_amax_q16[k], (int32_t)small[kAmaxQ + k]);
+// ---------------------------------------------------------------- one-token step input
+// A decode step has few rows (T = batch <= 64).  One workgroup per row stages
+// the row in LDS, forms the pre-norm (wave 0: the fixed-order sum of squares as
+// in rmsnorm_rows_kernel), rotates the 256-blocks and stores the rotated row
+// and its maximum; the in_proj product turns them into codes with the tensor
+// scale.  Workgroup 0 also zeroes the call's small block and loads the frozen
+// exponents (nothing in this kernel reads the block).
+constexpr int kStepRowThreads = 256;
+
+struct StepRowsArgs {
+    const float* u;
+    int dm;
+    int prenorm;
+    const int32_t* p_src;  // frozen exponents [4]
+    uint32_t* small;
+    float* rot;            // [rows, dm]
+    float* rowmax;         // [rows]
+};
+
+__global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs A) {
+    extern __shared__ __attribute__((aligned(16))) float row[];  // dm floats
+    __shared__ float rs_s;
+    __shared__ float wmax[kStepRowThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0 && tid < kSmallWords)
+        A.small[tid] = (tid >= kP && tid < kP + 4) ? (uint32_t)A.p_src[tid - kP] : 0u;
+    const int dm = A.dm;
+    const int64_t r = blockIdx.x;
+    const float* ur = A.u + r * dm;
+    for (int i0 = tid * 4; i0 < dm; i0 += 4 * 4 * kStepRowThreads) {  // 4 loads in flight
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * 4 * kStepRowThreads;
+            v[k] = i < dm ? *reinterpret_cast<const float4*>(ur + i) : make_float4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * 4 * kStepRowThreads;
+            if (i < dm) *reinterpret_cast<float4*>(row + i) = v[k];
+        }
+    }
+    __syncthreads();
+    float rs = 1.0f;
+    if (A.prenorm) {
+        if (wave == 0) {
+            float a = 0.0f;
+            for (int i0 = lane; i0 < dm; i0 += 16 * 64) {
+                float v[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) v[k] = i0 + 64 * k < dm ? row[i0 + 64 * k] : 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    if (i0 + 64 * k < dm) {
+                        const float v2 = v[k] * v[k];
+                        a = a + v2;  // ascending i within this lane: the fixed order
+                    }
+                }
+            }
+            const float ss = wave_sum_fixed(a);
+            if (lane == 0) rs_s = 1.0f / sqrtf(ss / (float)dm + 1e-5f);
+        }
+        __syncthreads();
+        rs = rs_s;
+    }
+    float m = 0.0f;
+    for (int blk = wave; blk < dm / 256; blk += kStepRowThreads / 64) {
+        float4 v = *reinterpret_cast<const float4*>(row + blk * 256 + lane * 4);
+        if (A.prenorm) {
+            v.x = (v.x * rs) * 1.0f;
+            v.y = (v.y * rs) * 1.0f;
+            v.z = (v.z * rs) * 1.0f;
+            v.w = (v.w * rs) * 1.0f;
+        }
+        v = fwht256_lane(v, lane);
+        m = fmaxf(m, absmax4(v));
+        reinterpret_cast<float4*>(A.rot + r * dm + blk * 256)[lane] = v;
+    }
+    m = wave_max_f32(m);
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        for (int k = 1; k < kStepRowThreads / 64; ++k) m = fmaxf(m, wmax[k]);
+        A.rowmax[r] = fmaxf(m, wmax[0]);
+    }
 }
 
 // Shared body of prefill (len tokens, fresh state) and decode (len = 1, cache).
@@ -145,27 +210,45 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
     int32_t* small_i = (int32_t*)w.small;
     int32_t* pdev = small_i + kP;
 
-    // 0. setup: zero the per-call block, load exponents (static values or the cache's)
-    if (decode)
-        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, cache->p, 0, 0, 0, 0, 2);
-    else if (stat)
-        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, sp->p[0], sp->p[1], sp->p[2],
-                                            sp->p[3], 1);
-    else
-        layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, 0, 0, 0, 0, 0);
-    if ((st = check_launch("layer_setup_kernel")) != FM_OK) return st;
+    // A decode step with few rows takes the fused form, five kernels: rotated
+    // input rows; in_proj quantizing them on load, with the conv step in its
+    // epilogue; the scan step; rotated gate rows; out_proj quantizing them on
+    // load, adding the residual and publishing the call's scalars.
+    const bool step = decode && T <= 64;
+    if (step) {
+        StepRowsArgs a{};
+        a.u = u;
+        a.dm = (int)dm;
+        a.prenorm = d->prenorm_residual ? 1 : 0;
+        a.p_src = cache->p;
+        a.small = w.small;
+        a.rot = w.un;
+        a.rowmax = w.rowmax;
+        step_rows_kernel<<<(unsigned)T, kStepRowThreads, (size_t)dm * sizeof(float), s>>>(a);
+        if ((st = check_launch("step_rows_kernel")) != FM_OK) return st;
+    } else {
+        // 0. setup: zero the per-call block, load exponents (static values or the cache's)
+        if (decode)
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, cache->p, 0, 0, 0, 0, 2);
+        else if (stat)
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, sp->p[0], sp->p[1], sp->p[2],
+                                                sp->p[3], 1);
+        else
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, 0, 0, 0, 0, 0);
+        if ((st = check_launch("layer_setup_kernel")) != FM_OK) return st;
 
-    // 1. (stacks) pre-norm of the residual stream
-    const float* xin = u;
-    if (d->prenorm_residual) {
-        if ((st = rmsnorm_rows_run(u, T, dm, w.un, s)) != FM_OK) return st;
-        xin = w.un;
+        // 1. (stacks) pre-norm of the residual stream
+        const float* xin = u;
+        if (d->prenorm_residual) {
+            if ((st = rmsnorm_rows_run(u, T, dm, w.un, s)) != FM_OK) return st;
+            xin = w.un;
+        }
+        // 2. rotate + quantize the in_proj input
+        if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0,
+                         w.u_q, small_f + kScaleU, stat ? small_f + kAmaxU : nullptr,
+                         small_f + kAmaxU, s)) != FM_OK)
+            return st;
     }
-    // 2. rotate + quantize the in_proj input
-    if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0, w.u_q,
-                     small_f + kScaleU, stat ? small_f + kAmaxU : nullptr, small_f + kAmaxU, s)) !=
-        FM_OK)
-        return st;
     // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
     {
         GemmEpilogue ep;
@@ -176,10 +259,36 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         ep.amax = small_f + kAmaxXbc;
         ep.amax_c0 = di;
         ep.amax_c1 = di + ch;
+        if (step) {  // 2 fused: codes of the rotated rows with the tensor scale
+            ep.a_f = w.un;
+            ep.a_rowmax = w.rowmax;
+            ep.a_mode = mode;
+            ep.a_scoe = stat ? sp->scoe[0] : 0;
+            ep.a_sshift = stat ? sp->sshift[0] : 0;
+            ep.a_amax_out = small_f + kAmaxU;
+            ep.a_scale_out = small_f + kScaleU;
+            ep.a_q_tap = g_keep ? w.u_q : nullptr;
+        }
+        if (step) {  // 4-5 fused: conv step + SiLU + requant with the frozen exponents
+            ep.conv_w_q = W->conv_w_q;
+            ep.conv_p_w = W->conv_p_w;
+            ep.conv_b_q16 = W->conv_b_q16;
+            ep.conv_p = pdev;
+            ep.conv_state = cache->conv_state;
+            ep.x_out = w.x_q;
+            ep.b_out = w.b_q;
+            ep.c_out = w.c_q;
+            ep.xbc_q = g_keep ? w.xbc_q : nullptr;
+            ep.conv_amax_q16 = small_i + kAmaxQ;
+            ep.d_inner = di;
+            ep.dstate = N;
+            ep.sz_out = w.sz;
+            ep.write_xbc = g_keep;
+        }
         if ((st = gemm_run(w.u_q, W->w_in_q, T, dip, dm, ep, s)) != FM_OK) return st;
     }
     // 4-5. conv1d + SiLU + requant of x / B / C
-    {
+    if (!step) {
         ConvArgs a{};
         a.xbc = w.v + di;
         a.xbc_stride = dip;
@@ -251,6 +360,8 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         g.normed_out = g_keep ? w.normed : nullptr;
         g.rot_ws = w.rot;
         g.amax_ws = small_f + kAmaxG;
+        g.rowmax = step ? w.rowmax + 64 : nullptr;
+        g.sz = step ? w.sz : nullptr;
         if ((st = gate_run(g, s)) != FM_OK) return st;
     }
     // 9. out_proj W8A8 (+ residual for stacks)
@@ -264,10 +375,22 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.resid = u;
             ep.ld_resid = dm;
         }
-        if ((st = gemm_run(w.g_q, W->w_out_q, T, dm, di, ep, s)) != FM_OK) return st;
+        if (step) {  // 8 fused: codes of the rotated gate rows with the tensor scale
+            ep.a_f = w.rot;
+            ep.a_rowmax = w.rowmax + 64;
+            ep.a_mode = mode;
+            ep.a_scoe = stat ? sp->scoe[1] : 0;
+            ep.a_sshift = stat ? sp->sshift[1] : 0;
+            ep.a_amax_out = small_f + kAmaxG;
+            ep.a_scale_out = small_f + kScaleG;
+            ep.a_q_tap = g_keep ? w.g_q : nullptr;
+        }
+        // the call's scales, exponents and statistics go out with this last kernel
+        ep.pub_small = w.small;
+        ep.pub_qp = qp;
+        ep.pub_cache_p = (cache && !decode) ? cache->p : nullptr;
+        return gemm_run(w.g_q, W->w_out_q, T, dm, di, ep, s);
     }
-    layer_finalize_kernel<<<1, 64, 0, s>>>(w.small, qp, (cache && !decode) ? cache->p : nullptr);
-    return check_launch("layer_finalize_kernel");
 }
 
 // ---------------------------------------------------------------- preparation

@@ -356,56 +356,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
 
 // ---------------------------------------------------------------- one step (decode)
 // len == 1: the work is reading and writing the state once, so the kernel is
-// laid out for coalesced state traffic.  A wave owns (b, head, p0, p0 + 1):
-// lanes 0..31 the row p0, lanes 32..63 the row p0 + 1, lane l the NN2 = N/32
-// consecutive n = NN2*(l % 32) .. (16 or 8 contiguous bytes of state).  dt and
-// the decay of (b, head) are computed by every lane (wave-uniform); the wave
-// with p0 = 0 stores them.  The update takes the clamped form always.
+// laid out for coalesced state traffic with many bytes in flight.  A wave owns
+// (b, head) and kStepPairs pairs of rows p: in each pair lanes 0..31 hold the
+// row p0, lanes 32..63 the row p0 + 1, lane l the NN2 = N/32 consecutive
+// n = NN2*(l % 32) .. (16 or 8 contiguous bytes of state).  Every load of the
+// wave (state rows, x, B, C, dt) is issued before any arithmetic.  dt and the
+// decay of (b, head) are computed by every lane (wave-uniform); the wave with
+// p0 = 0 stores them.  The update takes the clamped form always.
+constexpr int kStepPairs = 2;
+
 template <int NN2>
 __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
     __shared__ NauLds tab;
     nau_lds_init(tab);
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int H = (int)A.nheads, P = (int)A.headdim;
     constexpr int N = 32 * NN2;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, head, p-pair)
-    const int npp = P / 2;
-    if (wid >= A.batch * H * npp) return;
-    const int pp = (int)(wid % npp);
-    const int head = (int)((wid / npp) % H);
-    const int64_t b = wid / ((int64_t)npp * H);
+    constexpr int G = kStepPairs;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, head, pair group)
+    const int ngrp = P / (2 * G);
+    const bool live = wid < A.batch * H * ngrp;  // the tail of the last workgroup idles
+    const int64_t wq = live ? wid : 0;
+    const int grp = (int)(wq % ngrp);
+    const int head = (int)((wq / ngrp) % H);
+    const int64_t b = wq / ((int64_t)ngrp * H);
     const int r = lane >> 5, l32 = lane & 31;
-    const int p = 2 * pp + r;
     const int n0 = NN2 * l32;
-    // dt and the decay of (b, head)
     const int64_t q = b * H + head;  // token row b (len 1)
+    // every load first
     const float raw = A.dt_raw[b * A.dt_stride + head];
-    const int32_t dt_in = f2i_sat(rintf((raw + A.dt_bias[head]) * 65536.0f));
-    const int32_t dt = nau_softplus_f(dt_in, tab);
-    const int32_t da = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)A.a_q16[head], 16)), tab);
-    if (pp == 0 && lane == 0) {
-        A.dt_out[q] = dt;
-        A.da_out[q] = da;
-    }
-    const int32_t xi = A.x[q * P + p];
-    const double dd = (double)da * 0x1p-16;
-    const double u = (double)dt * 0x1p-8 * (double)xi;
-    // state row (b, head, p), n0 .. n0 + NN2 - 1
-    const int64_t sidx = (q * P + p) * N + n0;
-    int32_t hs[NN2];
-    if (A.state_in) {
-        if constexpr (NN2 == 4) {
-            const int4 v = *reinterpret_cast<const int4*>(A.state_in + sidx);
-            hs[0] = v.x, hs[1] = v.y, hs[2] = v.z, hs[3] = v.w;
-        } else {
-            const int2 v = *reinterpret_cast<const int2*>(A.state_in + sidx);
-            hs[0] = v.x, hs[1] = v.y;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < NN2; ++j) hs[j] = 0;
-    }
+    const float bias = A.dt_bias[head];
+    const int32_t aq = A.a_q16[head];
     int32_t bw, cw;  // NN2 int8 codes each
     if constexpr (NN2 == 4) {
         bw = *reinterpret_cast<const int32_t*>(A.bm + b * N + n0);
@@ -414,33 +395,81 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
         bw = *reinterpret_cast<const int16_t*>(A.bm + b * N + n0);
         cw = *reinterpret_cast<const int16_t*>(A.cm + b * N + n0);
     }
-    double y = 0.0;
+    int32_t xi[G];
+    int32_t hs[G][NN2];
 #pragma unroll
-    for (int j = 0; j < NN2; ++j) {
-        const double bj = (double)(int8_t)(bw >> (8 * j)), cj = (double)(int8_t)(cw >> (8 * j));
-        // h + 2^31 floored and clamped to [0, 2^32 - 1] by the conversion
-        const double sv = __builtin_fma(dd, (double)hs[j], __builtin_fma(u, bj, 2147483648.5));
-        uint32_t hu;
-        asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
-        hs[j] = (int32_t)(hu ^ 0x80000000u);
-        y = __builtin_fma(cj, (double)hs[j], y);  // exact: integers below 2^46
-    }
-    if (A.state_out) {
-        if constexpr (NN2 == 4)
-            *reinterpret_cast<int4*>(A.state_out + sidx) = make_int4(hs[0], hs[1], hs[2], hs[3]);
-        else
-            *reinterpret_cast<int2*>(A.state_out + sidx) = make_int2(hs[0], hs[1]);
-    }
-    // sum over the 32 lanes of this half-wave
+    for (int g = 0; g < G; ++g) {
+        const int p = 2 * (grp * G + g) + r;
+        xi[g] = A.x[q * P + p];
+        const int64_t sidx = (q * P + p) * N + n0;
+        if (A.state_in) {
+            if constexpr (NN2 == 4) {
+                const int4 v = *reinterpret_cast<const int4*>(A.state_in + sidx);
+                hs[g][0] = v.x, hs[g][1] = v.y, hs[g][2] = v.z, hs[g][3] = v.w;
+            } else {
+                const int2 v = *reinterpret_cast<const int2*>(A.state_in + sidx);
+                hs[g][0] = v.x, hs[g][1] = v.y;
+            }
+        } else {
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) y += __shfl_xor(y, m, 64);
-    if (l32 == 0) {
-        const int ky = A.p[2] + A.p[3];
-        const double ya = __builtin_floor(__builtin_fma(y, __builtin_ldexp(1.0, -ky), 0.5));
-        const double yd =
-            __builtin_floor(__builtin_fma((double)A.d_q16[head] * (double)xi, 0x1p-8, 0.5));
-        A.y[q * P + p] =
-            (int32_t)__builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
+            for (int j = 0; j < NN2; ++j) hs[g][j] = 0;
+        }
+    }
+    const int ky = A.p[2] + A.p[3];
+    const int32_t dq = A.d_q16[head];
+    __syncthreads();  // the chord table
+    // dt and the decay of (b, head)
+    const int32_t dt_in = f2i_sat(rintf((raw + bias) * 65536.0f));
+    const int32_t dt = nau_softplus_f(dt_in, tab);
+    const int32_t da = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)aq, 16)), tab);
+    const double dd = (double)da * 0x1p-16;
+    double bj[NN2], cj[NN2];
+#pragma unroll
+    for (int j = 0; j < NN2; ++j)
+        bj[j] = (double)(int8_t)(bw >> (8 * j)), cj[j] = (double)(int8_t)(cw >> (8 * j));
+    double y[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const double u = (double)dt * 0x1p-8 * (double)xi[g];
+        y[g] = 0.0;
+#pragma unroll
+        for (int j = 0; j < NN2; ++j) {
+            // h + 2^31 floored and clamped to [0, 2^32 - 1] by the conversion
+            const double sv =
+                __builtin_fma(dd, (double)hs[g][j], __builtin_fma(u, bj[j], 2147483648.5));
+            uint32_t hu;
+            asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
+            hs[g][j] = (int32_t)(hu ^ 0x80000000u);
+            y[g] = __builtin_fma(cj[j], (double)hs[g][j], y[g]);  // exact: integers below 2^46
+        }
+    }
+    if (!live) return;
+    if (grp == 0 && lane == 0) {
+        A.dt_out[q] = dt;
+        A.da_out[q] = da;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int p = 2 * (grp * G + g) + r;
+        const int64_t sidx = (q * P + p) * N + n0;
+        if (A.state_out) {
+            if constexpr (NN2 == 4)
+                *reinterpret_cast<int4*>(A.state_out + sidx) =
+                    make_int4(hs[g][0], hs[g][1], hs[g][2], hs[g][3]);
+            else
+                *reinterpret_cast<int2*>(A.state_out + sidx) = make_int2(hs[g][0], hs[g][1]);
+        }
+        // sum over the 32 lanes of this half-wave
+        double yy = y[g];
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) yy += __shfl_xor(yy, m, 64);
+        if (l32 == 0) {
+            const double ya = __builtin_floor(__builtin_fma(yy, __builtin_ldexp(1.0, -ky), 0.5));
+            const double yd =
+                __builtin_floor(__builtin_fma((double)dq * (double)xi[g], 0x1p-8, 0.5));
+            A.y[q * P + p] =
+                (int32_t)__builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
+        }
     }
 }
 
@@ -451,7 +480,10 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
     if (a.dstate != 64 && a.dstate != 128)
         return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
     if (a.len == 1) {  // one step: state traffic only
-        const int64_t waves = a.batch * a.nheads * (a.headdim / 2);
+        if (a.headdim % (2 * kStepPairs))
+            return fail(FM_ERR_SHAPE, "scan: headdim %lld not a multiple of %d", (long long)a.headdim,
+                        2 * kStepPairs);
+        const int64_t waves = a.batch * a.nheads * (a.headdim / (2 * kStepPairs));
         const unsigned g1 = (unsigned)((waves + 3) / 4);
         if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
             return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
