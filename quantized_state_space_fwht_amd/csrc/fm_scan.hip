@@ -93,6 +93,14 @@ __device__ __forceinline__ float row_ror(float v) {
     return __builtin_bit_cast(float, r);
 }
 
+// double rotated within the 16-lane row by R lanes (64-bit DPP row_ror)
+template <int R>
+__device__ __forceinline__ double row_ror_d(double v) {
+    const long long r = __builtin_amdgcn_update_dpp(0LL, __builtin_bit_cast(long long, v),
+                                                    0x120 + R, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, r);
+}
+
 // sum of a float over the 16 lanes of each row (every lane gets it)
 __device__ __forceinline__ float row_sum16(float v) {
     v += row_ror<8>(v);
@@ -403,13 +411,9 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
         xi[g] = A.x[q * P + p];
         const int64_t sidx = (q * P + p) * N + n0;
         if (A.state_in) {
-            if constexpr (NN2 == 4) {
-                const int4 v = *reinterpret_cast<const int4*>(A.state_in + sidx);
-                hs[g][0] = v.x, hs[g][1] = v.y, hs[g][2] = v.z, hs[g][3] = v.w;
-            } else {
-                const int2 v = *reinterpret_cast<const int2*>(A.state_in + sidx);
-                hs[g][0] = v.x, hs[g][1] = v.y;
-            }
+            // the state streams through once: non-temporal loads and stores
+#pragma unroll
+            for (int j = 0; j < NN2; ++j) hs[g][j] = __builtin_nontemporal_load(A.state_in + sidx + j);
         } else {
 #pragma unroll
             for (int j = 0; j < NN2; ++j) hs[g][j] = 0;
@@ -453,16 +457,18 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
         const int p = 2 * (grp * G + g) + r;
         const int64_t sidx = (q * P + p) * N + n0;
         if (A.state_out) {
-            if constexpr (NN2 == 4)
-                *reinterpret_cast<int4*>(A.state_out + sidx) =
-                    make_int4(hs[g][0], hs[g][1], hs[g][2], hs[g][3]);
-            else
-                *reinterpret_cast<int2*>(A.state_out + sidx) = make_int2(hs[g][0], hs[g][1]);
-        }
-        // sum over the 32 lanes of this half-wave
-        double yy = y[g];
 #pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) yy += __shfl_xor(yy, m, 64);
+            for (int j = 0; j < NN2; ++j) __builtin_nontemporal_store(hs[g][j], A.state_out + sidx + j);
+        }
+        // sum over the 32 lanes of this half-wave: DPP rotations inside each
+        // 16-lane row, then one swap of the row pair (the terms are integers
+        // below 2^46, so any order gives the exact sum)
+        double yy = y[g];
+        yy += row_ror_d<8>(yy);
+        yy += row_ror_d<4>(yy);
+        yy += row_ror_d<2>(yy);
+        yy += row_ror_d<1>(yy);
+        yy += __shfl_xor(yy, 16, 64);
         if (l32 == 0) {
             const double ya = __builtin_floor(__builtin_fma(yy, __builtin_ldexp(1.0, -ky), 0.5));
             const double yd =
