@@ -9,15 +9,18 @@
 // 16 k-values [16*(l/16), 16*(l/16)+16) of its 64-wide k slice, for A and B
 // alike, so every k pairs with itself whatever byte order the instruction
 // uses inside a lane.  Result lane l holds rows 4*(l/16)+i, column l % 16.
+#include <utility>
+
 #include "fm_internal.hpp"
 
 namespace fm {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kLdsRow = kBK + 16;  // bytes per staged row (padding against bank conflicts)
 constexpr int kGemmThreads = 256;
+constexpr int kDepth = 3;          // k-steps whose global loads are in flight ahead of use
 
 struct GemmParams {
     const int8_t* a;
@@ -26,9 +29,21 @@ struct GemmParams {
     GemmEpilogue ep;
 };
 
-__global__ __launch_bounds__(kGemmThreads) void gemm_i8_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(16))) int8_t As[2][kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][kBN * kLdsRow];
+template <class F, int... Ss>
+__device__ __forceinline__ void for_slots(std::integer_sequence<int, Ss...>, F&& f) {
+    (f(std::integral_constant<int, Ss>{}), ...);
+}
+
+// BM x BN x 64 tiles, 4 waves as 2 x 2, each (BM/2) x (BN/2) = TM x TN tiles of
+// 16 x 16.  The global loads of k-steps kt+1 .. kt+kDepth are in flight (in a
+// register ring) while step kt is multiplied from LDS.
+template <int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void gemm_i8_kernel(GemmParams P) {
+    constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave
+    constexpr int RA = BM / 64, RB = BN / 64;  // 64-row load passes per operand
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLdsRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -36,73 +51,92 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_i8_kernel(GemmParams P) {
     const int wm = wave >> 1, wn = wave & 1;
     if (P.ep.pub_small && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
         layer_publish(P.ep.pub_small, P.ep.pub_qp, P.ep.pub_cache_p);
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
+    const int64_t m0 = (int64_t)blockIdx.y * BM;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t K = P.k;
 
-    // global -> register staging: each thread moves 2 x 16 bytes of A and of B
-    const int ld_row = tid >> 2;          // 0..63 (+64 for the second half)
+    // global -> register staging: each thread moves RA + RB pieces of 16 bytes
+    const int ld_row = tid >> 2;          // 0..63 (+64 per further pass)
     const int ld_col = (tid & 3) * 16;    // byte offset inside the 64-wide k slice
-    int64_t ra0 = m0 + ld_row, ra1 = m0 + ld_row + 64;
-    int64_t rb0 = n0 + ld_row, rb1 = n0 + ld_row + 64;
-    // rows past the edge read the last valid row; their results are never stored
-    ra0 = ra0 < P.m ? ra0 : P.m - 1;
-    ra1 = ra1 < P.m ? ra1 : P.m - 1;
-    rb0 = rb0 < P.n ? rb0 : P.n - 1;
-    rb1 = rb1 < P.n ? rb1 : P.n - 1;
-    const int8_t* pa0 = P.a + ra0 * K + ld_col;
-    const int8_t* pa1 = P.a + ra1 * K + ld_col;
-    const int8_t* pb0 = P.b + rb0 * K + ld_col;
-    const int8_t* pb1 = P.b + rb1 * K + ld_col;
-
-    v4i ga0, ga1, gb0, gb1;
-    auto gload = [&](int64_t k0) {
-        ga0 = *reinterpret_cast<const v4i*>(pa0 + k0);
-        ga1 = *reinterpret_cast<const v4i*>(pa1 + k0);
-        gb0 = *reinterpret_cast<const v4i*>(pb0 + k0);
-        gb1 = *reinterpret_cast<const v4i*>(pb1 + k0);
-    };
-    auto lstore = [&](int buf) {
-        *reinterpret_cast<v4i*>(&As[buf][ld_row * kLdsRow + ld_col]) = ga0;
-        *reinterpret_cast<v4i*>(&As[buf][(ld_row + 64) * kLdsRow + ld_col]) = ga1;
-        *reinterpret_cast<v4i*>(&Bs[buf][ld_row * kLdsRow + ld_col]) = gb0;
-        *reinterpret_cast<v4i*>(&Bs[buf][(ld_row + 64) * kLdsRow + ld_col]) = gb1;
-    };
-
-    v4i acc[4][4];
+    const int8_t* pa[RA];
+    const int8_t* pb[RB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RA; ++i) {
+        int64_t r = m0 + ld_row + 64 * i;
+        r = r < P.m ? r : P.m - 1;  // rows past the edge: computed, never stored
+        pa[i] = P.a + r * K + ld_col;
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < RB; ++i) {
+        int64_t r = n0 + ld_row + 64 * i;
+        r = r < P.n ? r : P.n - 1;
+        pb[i] = P.b + r * K + ld_col;
+    }
+    v4i ring[kDepth][RA + RB];
+    auto gload = [&](v4i* g, int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < RA; ++i) g[i] = *reinterpret_cast<const v4i*>(pa[i] + k0);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) g[RA + i] = *reinterpret_cast<const v4i*>(pb[i] + k0);
+    };
+    auto lstore = [&](const v4i* g, int buf) {
+#pragma unroll
+        for (int i = 0; i < RA; ++i)
+            *reinterpret_cast<v4i*>(&As[buf][(ld_row + 64 * i) * kLdsRow + ld_col]) = g[i];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+            *reinterpret_cast<v4i*>(&Bs[buf][(ld_row + 64 * i) * kLdsRow + ld_col]) = g[RA + i];
+    };
+
+    v4i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     const int64_t KT = K / kBK;
-    if (P.m > 0 && P.n > 0) {
-        gload(0);
-        lstore(0);
+    const bool live = P.m > 0 && P.n > 0;
+    if (live) {
+        gload(ring[0], 0);
+        lstore(ring[0], 0);
+        // steps 1 .. kDepth into slots 1 .. kDepth (mod kDepth)
+        for_slots(std::make_integer_sequence<int, kDepth>{}, [&](auto S) {
+            constexpr int s = decltype(S)::value + 1;
+            if (s < KT) gload(ring[s % kDepth], (int64_t)s * kBK);
+        });
     }
     __syncthreads();
     const int frag_row = lane & 15;
     const int frag_k = (lane >> 4) * 16;
-    int buf = 0;
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
-        if (more) gload((kt + 1) * kBK);
-        v4i af[4], bf[4];
+    // step kt: multiply buffer kt & 1; store step kt + 1 (slot (kt+1) % kDepth)
+    // into the other buffer; refill that slot with step kt + 1 + kDepth
+    auto step = [&](int64_t kt, auto S) {
+        constexpr int slot = (decltype(S)::value + 1) % kDepth;
+        const int buf = (int)(kt & 1);
+        v4i af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TM; ++i)
             af[i] = *reinterpret_cast<const v4i*>(
-                &As[buf][(wm * 64 + i * 16 + frag_row) * kLdsRow + frag_k]);
-            bf[i] = *reinterpret_cast<const v4i*>(
-                &Bs[buf][(wn * 64 + i * 16 + frag_row) * kLdsRow + frag_k]);
-        }
+                &As[buf][(wm * (BM / 2) + i * 16 + frag_row) * kLdsRow + frag_k]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < TN; ++j)
+            bf[j] = *reinterpret_cast<const v4i*>(
+                &Bs[buf][(wn * (BN / 2) + j * 16 + frag_row) * kLdsRow + frag_k]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        if (more) lstore(buf ^ 1);
+        if (kt + 1 < KT) {
+            lstore(ring[slot], buf ^ 1);
+            if (kt + 1 + kDepth < KT) gload(ring[slot], (kt + 1 + kDepth) * kBK);
+        }
         __syncthreads();
-        buf ^= 1;
+    };
+    for (int64_t kt = 0; kt < KT; kt += kDepth) {
+        for_slots(std::make_integer_sequence<int, kDepth>{}, [&](auto S) {
+            if (kt + decltype(S)::value < KT) step(kt + decltype(S)::value, S);
+        });
     }
 
     // epilogue
@@ -111,13 +145,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_i8_kernel(GemmParams P) {
     if (ep.out) sab = (*ep.s_a) * (*ep.s_b);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+                const int64_t row = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
                 if (row < P.m && col < P.n) {
                     int32_t v = acc[i][j][r];
                     if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
@@ -467,8 +501,18 @@ fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64
         return check_launch("gemm_i8_few_rows_kernel");
     }
     if (af) return fail(FM_ERR_SHAPE, "gemm: float A needs m <= 64, k %% 256 == 0");
-    dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-    gemm_i8_kernel<<<grid, kGemmThreads, 0, s>>>(P);
+    // the largest tiles that still give the chip's 256 CUs a workgroup each
+    auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    if (tiles(128, 128) >= 256) {
+        dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
+        gemm_i8_kernel<128, 128><<<grid, kGemmThreads, 0, s>>>(P);
+    } else if (tiles(64, 128) >= 256) {
+        dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 63) / 64));
+        gemm_i8_kernel<64, 128><<<grid, kGemmThreads, 0, s>>>(P);
+    } else {
+        dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
+        gemm_i8_kernel<64, 64><<<grid, kGemmThreads, 0, s>>>(P);
+    }
     return check_launch("gemm_i8_kernel");
 }
 

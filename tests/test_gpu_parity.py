@@ -76,6 +76,10 @@ def test_hadamard_quant(B, rows, k, mode):
 # --------------------------------------------------------------------------- a3 / a9
 @pytest.mark.parametrize("m,n,k", [(1, 1, 64), (17, 40, 64), (300, 1160, 256), (2048, 3352, 768),
                                    (2048, 768, 1536), (129, 257, 512),
+                                   # tile shapes 64x64 / 64x128 / 128x128 and k-step counts
+                                   # below, at and past the depth of the load ring
+                                   (200, 300, 128), (130, 1100, 192), (2048, 1536, 256),
+                                   (1000, 4100, 448), (70, 90, 320),
                                    # few-row path (m <= 64, k % 256 == 0): decode shapes, ragged n
                                    (16, 10576, 2560), (16, 2560, 5120), (1, 33, 256),
                                    (3, 1160, 256), (40, 300, 768), (64, 777, 1536)])
