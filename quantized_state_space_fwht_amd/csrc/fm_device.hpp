@@ -194,14 +194,26 @@ __device__ __forceinline__ float absmax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// q = sat8(rint(v * c)) for four elements, packed in memory order (byte i =
+// element i).  The product is clamped to [-127, 127] first (rint and the clamp
+// commute there: a product in (127, 127.5] rounds to 127 either way), then
+// adding 1.5 * 2^23 rounds it to an integer, ties to even as rint does, and
+// leaves that integer in the low byte of the sum's bit pattern (two's
+// complement: the sum is 0x4B400000 + q).  Three byte permutes pack the codes.
+__device__ __forceinline__ uint32_t quant_pack4(float4 v, float c) {
+    constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+    const uint32_t a = __float_as_uint(fminf(fmaxf(v.x * c, -127.0f), 127.0f) + kMagic);
+    const uint32_t b = __float_as_uint(fminf(fmaxf(v.y * c, -127.0f), 127.0f) + kMagic);
+    const uint32_t d = __float_as_uint(fminf(fmaxf(v.z * c, -127.0f), 127.0f) + kMagic);
+    const uint32_t e = __float_as_uint(fminf(fmaxf(v.w * c, -127.0f), 127.0f) + kMagic);
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a.b0, b.b0
+    const uint32_t de = __builtin_amdgcn_perm(e, d, 0x0c0c0400u);  // d.b0, e.b0
+    return __builtin_amdgcn_perm(de, ab, 0x05040100u);
+}
+
 // q = sat8(rint(v * c)) per element
 __device__ __forceinline__ char4 quant4(float4 v, float c) {
-    char4 q;
-    q.x = (signed char)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f);
-    q.y = (signed char)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f);
-    q.z = (signed char)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f);
-    q.w = (signed char)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f);
-    return q;
+    return __builtin_bit_cast(char4, quant_pack4(v, c));
 }
 
 // sum of a per-lane partial over the wave in the fixed xor order k = 32, 16, .., 1

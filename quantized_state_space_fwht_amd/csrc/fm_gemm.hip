@@ -180,15 +180,6 @@ void gemm_i8_kernel(GemmParams P) {
 // loads the residual of its share before the product).
 constexpr int kSkU = 8;
 
-// A operand of the one-token step: 16 rotated floats of a row -> 16 int8 codes
-// sat8(rint(v * c)), packed in memory order (byte i of the vector = element i)
-__device__ __forceinline__ uint32_t quant_pack4(float4 v, float c) {
-    const uint32_t b0 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.x * c), -127.0f), 127.0f) & 0xFFu;
-    const uint32_t b1 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.y * c), -127.0f), 127.0f) & 0xFFu;
-    const uint32_t b2 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.z * c), -127.0f), 127.0f) & 0xFFu;
-    const uint32_t b3 = (uint32_t)(int32_t)fminf(fmaxf(rintf(v.w * c), -127.0f), 127.0f) & 0xFFu;
-    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-}
 // kMode 0: int8 A.  1: float A quantized on load; the columns hold z | xBC | dt
 // of a one-token step: SiLU(z) in Q.16 goes to sz_out, xBC runs the conv step
 // (power-of-two code, the 4-tap window from the conv cache shifted in place,
