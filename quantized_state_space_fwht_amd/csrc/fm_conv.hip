@@ -79,7 +79,8 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
         xmax = fmaxf(xmax, fabsf(xv_i));
         const int32_t xq = quant_xbc(xv_i, qscale);
         if constexpr (kXq) xq_out[(uint32_t)i * (uint32_t)K.ch] = (int8_t)xq;
-        const int32_t acc = w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq;
+        // int8 x int8 products: 24-bit multiplies (full rate; 32-bit ones are not)
+        const int32_t acc = __mul24(w0, xm3) + __mul24(w1, xm2) + __mul24(w2, xm1) + __mul24(w3, xq);
         const int32_t a = round_sat32(__builtin_fma((double)acc, ascale, bias));
         const int32_t sv = nau_silu_f(a, tab);
         const int32_t sa = sv < 0 ? -sv : sv;

@@ -380,8 +380,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
                 xmax = fmaxf(xmax, fabsf(o));
                 const int32_t xq = quant_xbc(o, ldexpf(1.0f, p_c));
                 if (ep.xbc_q) ep.xbc_q[row * ch + cx] = (int8_t)xq;
-                const int32_t a = round_sat32(__builtin_fma(
-                    (double)(w0 * xm3 + w1 * xm2 + w2 * xm1 + w3 * xq), ascale, (double)xb[k]));
+                const int32_t acc4 = __mul24(w0, xm3) + __mul24(w1, xm2) + __mul24(w2, xm1) +
+                                     __mul24(w3, xq);  // int8 products: 24-bit multiplies
+                const int32_t a = round_sat32(__builtin_fma((double)acc4, ascale, (double)xb[k]));
                 const int32_t sv = nau_silu_f(a, tab);
                 const int32_t sa = sv < 0 ? -sv : sv;
                 pmax[part_i] = sa > pmax[part_i] ? sa : pmax[part_i];
