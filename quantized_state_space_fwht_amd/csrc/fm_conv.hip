@@ -112,6 +112,23 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if ((int)blockIdx.x == K.ch / 64) {
+        // the extra column of workgroups: dt and the decay for the (token, head)
+        // pairs of this workgroup's steps, as the scan's prologue forms them
+        const int64_t L = A.len, H = A.nheads;
+        const int64_t t0 = (int64_t)blockIdx.y * (kConvThreads / 64) * kConvTL;
+        const int64_t nt = L - t0 < (kConvThreads / 64) * kConvTL ? L - t0 : (kConvThreads / 64) * kConvTL;
+        const int64_t row0 = (int64_t)blockIdx.z * L + t0;
+        for (int64_t i = threadIdx.x; i < nt * H; i += kConvThreads) {
+            const int64_t row = row0 + i / H;
+            const int h = (int)(i % H);
+            const float raw = A.dt_raw[row * A.dt_stride + h];
+            const int32_t dt = nau_softplus_f(f2i_sat(rintf((raw + A.dt_bias[h]) * 65536.0f)), tab);
+            A.dt_out[row * H + h] = dt;
+            A.da_out[row * H + h] = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)A.a_q16[h], 16)), tab);
+        }
+        return;
+    }
     const int p_c = kDyn ? pot_from_f32(*A.xbc_amax) : A.p_fixed[0];
     if (!kDyn && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 4)
         A.p_out[threadIdx.x] = A.p_fixed[threadIdx.x];
@@ -162,15 +179,21 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
     }
     if (c >= K.ch) return;
     const int part = c < di ? 0 : (c < di + N ? 1 : 2);
-    const int sh = 16 - pot_from_q16(A.amax_q16[part]);
+    // sat8(rshr(s, 16 - p)): s * 2^(p-16) + 1/2 is exact in float64 for every
+    // p in [-24, 24] (|s| < 2^31), so floor gives rshr's value, shifts up included
+    const double sc = __builtin_ldexp(1.0, pot_from_q16(A.amax_q16[part]) - 16);
+    auto q8 = [&](int32_t v) {
+        const double q = __builtin_floor(__builtin_fma((double)v, sc, 0.5));
+        return (signed char)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
+    };
     const int64_t rows = A.batch * A.len;
     for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
         const int4 s = *reinterpret_cast<const int4*>(A.s16 + row * K.ch + c);
         char4 q;
-        q.x = sat8(rshr((int64_t)s.x, sh));
-        q.y = sat8(rshr((int64_t)s.y, sh));
-        q.z = sat8(rshr((int64_t)s.z, sh));
-        q.w = sat8(rshr((int64_t)s.w, sh));
+        q.x = q8(s.x);
+        q.y = q8(s.y);
+        q.z = q8(s.z);
+        q.w = q8(s.w);
         if (part == 0) *reinterpret_cast<char4*>(A.x_out + row * di + c) = q;
         else if (part == 1) *reinterpret_cast<char4*>(A.b_out + row * N + (c - di)) = q;
         else *reinterpret_cast<char4*>(A.c_out + row * N + (c - di - N)) = q;
@@ -204,8 +227,8 @@ fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t s
 fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     ConvKParams K{a, (int)(a.d_inner + 2 * a.dstate), a.p_fixed == nullptr ? 1 : 0};
     const int64_t per_block = (kConvThreads / 64) * kConvTL;
-    dim3 grid((unsigned)(K.ch / 64), (unsigned)((a.len + per_block - 1) / per_block),
-              (unsigned)a.batch);
+    dim3 grid((unsigned)(K.ch / 64 + (a.dt_raw ? 1 : 0)),
+              (unsigned)((a.len + per_block - 1) / per_block), (unsigned)a.batch);
     if (K.dynamic) conv_silu_kernel<true><<<grid, kConvThreads, 0, s>>>(K);
     else conv_silu_kernel<false><<<grid, kConvThreads, 0, s>>>(K);
     fm_status st = check_launch("conv_silu_kernel");

@@ -38,7 +38,15 @@ __global__ __launch_bounds__(kHqThreads) void hq_amax_kernel(const float* __rest
     int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
     int64_t stride = (int64_t)gridDim.x * (kHqThreads / 64);
     float m = 0.0f;
-    for (int64_t b = wv; b < nblk_total; b += stride) {
+    int64_t b = wv;
+    for (; b + 3 * stride < nblk_total; b += 4 * stride) {  // four blocks' loads in flight
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = reinterpret_cast<const float4*>(x + (b + k * stride) * 256)[lane];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = fmaxf(m, absmax4(fwht256_lane(v[k], lane)));
+    }
+    for (; b < nblk_total; b += stride) {
         float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
         m = fmaxf(m, absmax4(fwht256_lane(v, lane)));
     }
@@ -102,7 +110,9 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
     fm_status st;
     if (mode == FM_SCALE_DYNAMIC) {  // amax_ws must hold 0 (zeroed by the caller)
         // few workgroups (grid-stride): one same-address atomic per workgroup
-        hq_amax_kernel<<<hq_grid(nb, 512), kHqThreads, 0, s>>>(x, nb, amax_ws, amax_stats);
+        // four blocks per wave at least (their loads go out together)
+        hq_amax_kernel<<<hq_grid((nb + 3) / 4, 512), kHqThreads, 0, s>>>(x, nb, amax_ws,
+                                                                         amax_stats);
         if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
         hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, (char4*)q,
                                                  scale_out, nullptr, 0);

@@ -150,6 +150,15 @@ struct ConvArgs {
     int8_t* c_out;
     int32_t* p_out;            // [4]
     int32_t* amax_stats;       // nullable [4]
+    // nullable: extra workgroups also form dt and the decay of every (token, head)
+    // (the scan's prologue) from the in_proj dt columns
+    const float* dt_raw;
+    int64_t dt_stride;
+    const float* dt_bias;
+    const int32_t* a_q16;
+    int64_t nheads;
+    int32_t* dt_out;           // [T, H]
+    int32_t* da_out;
 };
 fm_status conv_run(const ConvArgs& a, hipStream_t s);
 fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t stride,
@@ -171,6 +180,7 @@ struct ScanArgs {
     int32_t* y;
     int32_t* dt_out;           // [T, H] written by the dt / decay prologue (required)
     int32_t* da_out;
+    bool dt_ready;             // dt_out / da_out already hold them: no prologue launch
 };
 // workspace of the scan (none: B and C are staged through LDS)
 size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);

@@ -313,6 +313,14 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.p_out = pdev;
         // with fixed exponents the conv kernel records the maxima itself (calibration stats)
         a.amax_stats = fixed_p ? small_i + kAmaxXbc : nullptr;
+        // the scan's dt / decay prologue rides along (a6)
+        a.dt_raw = w.v + di + ch;
+        a.dt_stride = dip;
+        a.dt_bias = W->dt_bias;
+        a.a_q16 = W->a_q16;
+        a.nheads = H;
+        a.dt_out = w.dt;
+        a.da_out = w.da;
         if ((st = conv_run(a, s)) != FM_OK) return st;
     }
     // 6-7. dt / decay and the scan
@@ -337,6 +345,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.y = w.y;
         a.dt_out = w.dt;
         a.da_out = w.da;
+        a.dt_ready = !step;  // formed by the conv launch (a one-step scan forms its own)
         hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
         g_ev_start = g_ev_stop = nullptr;
         if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) return st;

@@ -501,11 +501,13 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
             return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
         return FM_OK;
     }
-    const int64_t pairs = a.batch * a.len * a.nheads;
-    scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
-        a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
-    fm_status st = check_launch("scan_prep_kernel");
-    if (st != FM_OK) return st;
+    fm_status st;
+    if (!a.dt_ready) {
+        const int64_t pairs = a.batch * a.len * a.nheads;
+        scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
+            a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
+        if ((st = check_launch("scan_prep_kernel")) != FM_OK) return st;
+    }
     if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
         return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
     const unsigned grid = (unsigned)(a.headdim / kScanP * a.nheads * a.batch);
