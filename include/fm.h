@@ -332,6 +332,32 @@ fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t le
  * their workspace (slower; for tests).  0 (default): they do not. */
 void fm_layer_keep_intermediates(int32_t on);
 
+/* Quantization statistics of a layer's six activation quantization points,
+ * for the static-vs-dynamic scale study (the referee's open question on the
+ * review page of FastMamba, major comment on Sections III-A / IV-B: static
+ * calibrated scales against Algorithm 1's per-input scales).  For each point
+ * and element: value v, code q = sat8(round(v / step)) and whether the rounded
+ * code left [-127, 127] before the clamp.
+ *   FM_QP_U   in_proj input after the rotation; step = the dequant scale s
+ *   FM_QP_G   out_proj input after the rotation; step = s
+ *   FM_QP_XBC conv input xBC; step = 2^-p_c
+ *   FM_QP_X, FM_QP_B, FM_QP_C  SiLU outputs (value = Q.16 / 2^16); step = 2^-p
+ * Sums are float64 (v and q * step as float64, error v - q * step).  Counts
+ * are exact; the sums are added atomically, so their rounding order varies. */
+enum { FM_QP_U = 0, FM_QP_G = 1, FM_QP_XBC = 2, FM_QP_X = 3, FM_QP_B = 4, FM_QP_C = 5,
+       FM_QP_COUNT = 6 };
+typedef struct fm_quant_stats {
+    unsigned long long count[FM_QP_COUNT];    /* elements quantized */
+    unsigned long long clipped[FM_QP_COUNT];  /* elements whose code was clamped */
+    double sq_err[FM_QP_COUNT];               /* sum of (v - q * step)^2 */
+    double sq_val[FM_QP_COUNT];               /* sum of v^2 */
+} fm_quant_stats;
+/* Device pointer to a caller-zeroed fm_quant_stats (8-byte aligned), or NULL
+ * to stop: later prefill layer calls made by this thread add their statistics
+ * into it.  Decode calls do not collect.  Costs a few float64 operations per
+ * quantized element while on. */
+void fm_layer_collect_quant_stats(fm_quant_stats* dev_stats);
+
 /* Profiling hook: the next layer call made by this thread records `start`
  * right before and `stop` right after its scan kernel (the dominant kernel)
  * on its stream; the hook then clears itself.  Both are hipEvent_t handles

@@ -30,7 +30,8 @@ import numpy as np
 from .conv import conv1d_pot, conv_weight_prep, silu_requant, xbc_pot_quant
 from .fixedpoint import f32_to_i32_sat, pot_f32, pot_q16
 from .gate_norm import gate, rmsnorm_fixed_order
-from .hadamard import hadamard_quant
+from . import quant_stats as QS
+from .hadamard import hadamard_quant, hadamard_scale
 from .linear import quantize_weight, w8a8_gemm
 from .scan import dt_dA, ssm_scan_pot
 
@@ -74,15 +75,19 @@ def prepare_layer(params: dict) -> dict:
     }
 
 
-def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p):
-    """Shared body of prefill (L tokens) and decode (L = 1) on rows u2 [Bsz*L, dm]."""
+def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p, collect=False):
+    """Shared body of prefill (L tokens) and decode (L = 1) on rows u2 [Bsz*L, dm].
+
+    ``collect``: also return the quantization statistics of the six points in
+    r["qstats"] (oracle.quant_stats).
+    """
     s = shape
     di, N, H, P, ch = s.d_inner, s.dstate, s.nheads, s.headdim, s.conv_ch
     r = {}
     st = Stats()
     hq_mode = "static" if mode == "static" else "dynamic"
     sc0 = (qp.scoe[0], qp.sshift[0]) if hq_mode == "static" else (None, None)
-    u_q, s_u, amax_u, _ = hadamard_quant(u2, hq_mode, *sc0)
+    u_q, s_u, amax_u, u_rot = hadamard_quant(u2, hq_mode, *sc0)
     acc_in, v = w8a8_gemm(u_q, prep["w_in_q"], s_u, prep["s_w_in"])
     r.update(u_q=u_q, s_u=s_u, acc_in=acc_in, v=v)
     st.amax_u = float(amax_u)
@@ -111,25 +116,37 @@ def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p):
     sc1 = (qp.scoe[1], qp.sshift[1]) if hq_mode == "static" else (None, None)
     g = gate(y.reshape(Bsz * L, di), z, p_y)
     normed = rmsnorm_fixed_order(g, prep["norm_w"])
-    g_q, s_g, amax_g, _ = hadamard_quant(normed, hq_mode, *sc1)
+    g_q, s_g, amax_g, g_rot = hadamard_quant(normed, hq_mode, *sc1)
     st.amax_g = float(amax_g)
     acc_out, out = w8a8_gemm(g_q, prep["w_out_q"], s_g, prep["s_w_out"])
     r.update(z=z, xbc=xbc, dt_raw=dt_raw, xbc_q=xbc_q, conv_acc=conv_acc, conv_a=a,
              silu=silu_a, x_q=x_q, B_q=B_q, C_q=C_q, p=(p_c, p_x, p_B, p_C), dt=dt, dA=dA,
              y=y, g=g, normed=normed, g_q=g_q, s_g=s_g, acc_out=acc_out)
+    if collect:
+        qs = QS.empty()
+        QS.accumulate(qs, "u", QS.hadamard_point_stats(u_rot, hadamard_scale(amax_u, hq_mode, *sc0)))
+        QS.accumulate(qs, "g", QS.hadamard_point_stats(g_rot, hadamard_scale(amax_g, hq_mode, *sc1)))
+        QS.accumulate(qs, "xbc", QS.pot_float_point_stats(xbc, p_c))
+        s_all = silu_a.reshape(-1, ch)
+        QS.accumulate(qs, "x", QS.pot_q16_point_stats(s_all[:, :di], p_x))
+        QS.accumulate(qs, "B", QS.pot_q16_point_stats(s_all[:, di:di + N], p_B))
+        QS.accumulate(qs, "C", QS.pot_q16_point_stats(s_all[:, di + N:], p_C))
+        r["qstats"] = qs
     cache = {"conv_state": conv_state, "ssm_state": state,
              "p": np.array([p_c, p_x, p_B, p_C], dtype=np.int64)}
     return out, r, cache, st
 
 
-def layer_prefill(prep, shape, u, mode="dynamic", qp=None):
+def layer_prefill(prep, shape, u, mode="dynamic", qp=None, collect=False):
     """One mixer layer over u [Bsz, L, d_model] from a fresh state.
 
-    Returns (out float32 [Bsz, L, d_model], intermediates, cache, stats).
+    Returns (out float32 [Bsz, L, d_model], intermediates, cache, stats);
+    ``collect`` adds the quantization statistics as intermediates["qstats"].
     """
     u = np.asarray(u, dtype=np.float32)
     Bsz, L, dm = u.shape
-    out, r, cache, st = _mixer(prep, shape, u.reshape(Bsz * L, dm), Bsz, L, mode, qp, None, None)
+    out, r, cache, st = _mixer(prep, shape, u.reshape(Bsz * L, dm), Bsz, L, mode, qp, None, None,
+                               collect)
     return out.reshape(Bsz, L, dm), r, cache, st
 
 
@@ -141,10 +158,12 @@ def layer_decode(prep, shape, u_t, cache, mode="dynamic", qp=None):
     return out.reshape(Bsz, dm), r, new_cache, st
 
 
-def stack_prefill(preps, shape, u, mode="dynamic", qps=None):
+def stack_prefill(preps, shape, u, mode="dynamic", qps=None, qstats=None):
     """Pre-norm residual stack over u [Bsz, L, d_model].
 
-    Returns (h float32 [Bsz, L, d_model], caches, stats per layer).
+    Returns (h float32 [Bsz, L, d_model], caches, stats per layer).  ``qstats``
+    (a list, one oracle.quant_stats dict per layer) receives each layer's
+    quantization statistics added in.
     """
     h = np.asarray(u, dtype=np.float32)
     Bsz, L, dm = h.shape
@@ -152,7 +171,11 @@ def stack_prefill(preps, shape, u, mode="dynamic", qps=None):
     caches, stats = [], []
     for li, prep in enumerate(preps):
         xin = rmsnorm_fixed_order(h.reshape(Bsz * L, dm), ones).reshape(Bsz, L, dm)
-        out, _, cache, st = layer_prefill(prep, shape, xin, mode, None if qps is None else qps[li])
+        out, r, cache, st = layer_prefill(prep, shape, xin, mode, None if qps is None else qps[li],
+                                          collect=qstats is not None)
+        if qstats is not None:
+            for pt in QS.POINTS:
+                QS.accumulate(qstats[li], pt, r["qstats"][pt])
         h = h + out
         caches.append(cache)
         stats.append(st)

@@ -105,6 +105,7 @@ _SIGS = {
                                             ctypes.POINTER(LayerTaps)]),
     "fm_layer_keep_intermediates": (None, [_c_i32]),
     "fm_layer_set_timing_events": (None, [_vp, _vp]),
+    "fm_layer_collect_quant_stats": (None, [_vp]),
     "fm_qparams_from_stats": (ctypes.c_int, [ctypes.POINTER(QParams),
                                              ctypes.POINTER(StaticParams)]),
 }
@@ -212,3 +213,28 @@ def qparams_from_device(qp_dev) -> QParams:
 
 def keep_intermediates(on: bool):
     lib.fm_layer_keep_intermediates(1 if on else 0)
+
+
+# quantization points of fm_quant_stats
+QP_U, QP_G, QP_XBC, QP_X, QP_B, QP_C = range(6)
+QP_NAMES = ("u", "g", "xbc", "x", "B", "C")
+
+
+class QuantStats(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_ulonglong * 6), ("clipped", ctypes.c_ulonglong * 6),
+                ("sq_err", ctypes.c_double * 6), ("sq_val", ctypes.c_double * 6)]
+
+
+def quant_stats_buffer(device="cuda"):
+    """A zeroed device fm_quant_stats (as a uint8 tensor)."""
+    return torch.zeros(ctypes.sizeof(QuantStats), dtype=torch.uint8, device=device)
+
+
+def collect_quant_stats(buf):
+    """Later prefill layer calls of this thread add their statistics to buf (None: stop)."""
+    lib.fm_layer_collect_quant_stats(None if buf is None else buf.data_ptr())
+
+
+def quant_stats_from_device(buf) -> QuantStats:
+    """Copy a device fm_quant_stats to the host (synchronizes)."""
+    return QuantStats.from_buffer_copy(buf.cpu().numpy().tobytes())

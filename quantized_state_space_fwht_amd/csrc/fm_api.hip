@@ -447,6 +447,8 @@ void fm_layer_keep_intermediates(int32_t on) { set_keep_intermediates(on != 0); 
 
 void fm_layer_set_timing_events(void* start, void* stop) { set_timing_events(start, stop); }
 
+void fm_layer_collect_quant_stats(fm_quant_stats* dev_stats) { set_quant_stats(dev_stats); }
+
 fm_status fm_qparams_from_stats(const fm_qparams* st, fm_static_params* out) {
     g_err[0] = 0;
     if (!st || !out) return fail(FM_ERR_NULL, "fm_qparams_from_stats: NULL argument");

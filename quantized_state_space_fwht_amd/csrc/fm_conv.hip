@@ -24,10 +24,11 @@ struct ConvKParams {
 
 // One thread: channel c, steps t0 .. t0+n-1 (n = kConvTL unless kTail).
 // Dynamic: writes Q.16 SiLU outputs + per-part maxima.  Static: writes codes.
-template <bool kTail, bool kDyn, bool kXq>
+template <bool kTail, bool kDyn, bool kXq, bool kStats>
 __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLds& tab, int c,
                                                int64_t row0, int64_t t0, int n, int p_c,
-                                               int part, int32_t& amax, float& xmax) {
+                                               int part, int32_t& amax, float& xmax,
+                                               QStat& sx, QStat& sp) {
     const ConvArgs& A = K.a;
     const int di = (int)A.d_inner, N = (int)A.dstate;
     const float qscale = ldexpf(1.0f, p_c);
@@ -78,6 +79,9 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
         const float xv_i = xv[i];
         xmax = fmaxf(xmax, fabsf(xv_i));
         const int32_t xq = quant_xbc(xv_i, qscale);
+        if constexpr (kStats)
+            sx.add((double)xv_i, (double)xq, __builtin_ldexp(1.0, -p_c),
+                   fabsf(rintf(xv_i * qscale)) > 127.0f);
         if constexpr (kXq) xq_out[(uint32_t)i * (uint32_t)K.ch] = (int8_t)xq;
         // int8 x int8 products: 24-bit multiplies (full rate; 32-bit ones are not)
         const int32_t acc = __mul24(w0, xm3) + __mul24(w1, xm2) + __mul24(w2, xm1) + __mul24(w3, xq);
@@ -90,7 +94,11 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
         } else {
             // sat8(rshr(sv, 16 - p_part)): sv * 2^(p_part-16) is exact in float64
             const double q = __builtin_floor(__builtin_fma((double)sv, oscale, 0.5));
-            code[(uint32_t)i * cstride] = (int8_t)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
+            const double qc = __builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
+            code[(uint32_t)i * cstride] = (int8_t)qc;
+            if constexpr (kStats)
+                sp.add((double)sv * 0x1p-16, qc, __builtin_ldexp(1.0, -p_part),
+                       __builtin_fabs(q) > 127.0);
         }
         xm3 = xm2;
         xm2 = xm1;
@@ -104,7 +112,7 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
     }
 }
 
-template <bool kDyn>
+template <bool kDyn, bool kStats>
 __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
     __shared__ NauLds tab;
@@ -115,13 +123,16 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     if ((int)blockIdx.x == K.ch / 64) {
         // the extra column of workgroups: dt and the decay for the (token, head)
         // pairs of this workgroup's steps, as the scan's prologue forms them
-        const int64_t L = A.len, H = A.nheads;
+        // 32-bit indices inside the workgroup (at most 64 steps x nheads pairs)
+        const int64_t L = A.len;
+        const int H = (int)A.nheads;
         const int64_t t0 = (int64_t)blockIdx.y * (kConvThreads / 64) * kConvTL;
-        const int64_t nt = L - t0 < (kConvThreads / 64) * kConvTL ? L - t0 : (kConvThreads / 64) * kConvTL;
+        const int nt = (int)(L - t0 < (kConvThreads / 64) * kConvTL ? L - t0
+                                                                    : (kConvThreads / 64) * kConvTL);
         const int64_t row0 = (int64_t)blockIdx.z * L + t0;
-        for (int64_t i = threadIdx.x; i < nt * H; i += kConvThreads) {
-            const int64_t row = row0 + i / H;
-            const int h = (int)(i % H);
+        for (int i = threadIdx.x; i < nt * H; i += kConvThreads) {
+            const int ti = i / H, h = i - ti * H;
+            const int64_t row = row0 + ti;
             const float raw = A.dt_raw[row * A.dt_stride + h];
             const int32_t dt = nau_softplus_f(f2i_sat(rintf((raw + A.dt_bias[h]) * 65536.0f)), tab);
             A.dt_out[row * H + h] = dt;
@@ -143,12 +154,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     const int n = (int)(t0 + kConvTL < L ? kConvTL : L - t0);
     int32_t amax = 0;
     float xmax = 0.0f;
+    QStat sx, sp;
     if (A.xbc_q) {
-        if (n == kConvTL) conv_run_steps<false, kDyn, true>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
-        else conv_run_steps<true, kDyn, true>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
+        if (n == kConvTL) conv_run_steps<false, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
+        else conv_run_steps<true, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
     } else {
-        if (n == kConvTL) conv_run_steps<false, kDyn, false>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
-        else conv_run_steps<true, kDyn, false>(K, tab, c, row0, t0, n, p_c, part, amax, xmax);
+        if (n == kConvTL) conv_run_steps<false, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
+        else conv_run_steps<true, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
+    }
+    if constexpr (kStats) {  // every lane of the wave is here (one part per wave)
+        qstat_flush(sx, A.qs, FM_QP_XBC);
+        if (!kDyn) qstat_flush(sp, A.qs, FM_QP_X + part);
     }
     // per-wave maxima (all lanes of a wave are in one part)
     amax = wave_max_i32(amax);
@@ -177,8 +193,8 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
             for (int i = 0; i < 3; ++i) atomicMax(&A.amax_stats[1 + i], A.amax_q16[i]);
         }
     }
-    if (c >= K.ch) return;
-    const int part = c < di ? 0 : (c < di + N ? 1 : 2);
+    const bool active = c < K.ch;  // idle lanes stay for the statistics' wave sums
+    const int part = !active ? 0 : (c < di ? 0 : (c < di + N ? 1 : 2));
     // sat8(rshr(s, 16 - p)): s * 2^(p-16) + 1/2 is exact in float64 for every
     // p in [-24, 24] (|s| < 2^31), so floor gives rshr's value, shifts up included
     const double sc = __builtin_ldexp(1.0, pot_from_q16(A.amax_q16[part]) - 16);
@@ -187,17 +203,32 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
         return (signed char)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
     };
     const int64_t rows = A.batch * A.len;
-    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    QStat st;
+    const double step = __builtin_ldexp(1.0, 16 - pot_from_q16(A.amax_q16[part]));
+    for (int64_t row = blockIdx.y; active && row < rows; row += gridDim.y) {
         const int4 s = *reinterpret_cast<const int4*>(A.s16 + row * K.ch + c);
         char4 q;
         q.x = q8(s.x);
         q.y = q8(s.y);
         q.z = q8(s.z);
         q.w = q8(s.w);
+        if (A.qs) {
+            const int32_t sv[4] = {s.x, s.y, s.z, s.w};
+            const signed char qc[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const double qr = __builtin_floor(__builtin_fma((double)sv[k], sc, 0.5));
+                st.add((double)sv[k] * 0x1p-16, (double)qc[k], step * 0x1p-16,
+                       __builtin_fabs(qr) > 127.0);
+            }
+        }
         if (part == 0) *reinterpret_cast<char4*>(A.x_out + row * di + c) = q;
         else if (part == 1) *reinterpret_cast<char4*>(A.b_out + row * N + (c - di)) = q;
         else *reinterpret_cast<char4*>(A.c_out + row * N + (c - di - N)) = q;
     }
+    if (A.qs)  // a wave may span two parts: one wave sum per part
+        for (int pt = 0; pt < 3; ++pt)
+            qstat_flush(part == pt && active ? st : QStat{}, A.qs, FM_QP_X + pt);
 }
 
 __global__ __launch_bounds__(256) void amax_strided_kernel(const float* __restrict__ x, int64_t rows,
@@ -229,8 +260,13 @@ fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     const int64_t per_block = (kConvThreads / 64) * kConvTL;
     dim3 grid((unsigned)(K.ch / 64 + (a.dt_raw ? 1 : 0)),
               (unsigned)((a.len + per_block - 1) / per_block), (unsigned)a.batch);
-    if (K.dynamic) conv_silu_kernel<true><<<grid, kConvThreads, 0, s>>>(K);
-    else conv_silu_kernel<false><<<grid, kConvThreads, 0, s>>>(K);
+    if (a.qs) {  // statistics of the quantization points: a separate instance
+        if (K.dynamic) conv_silu_kernel<true, true><<<grid, kConvThreads, 0, s>>>(K);
+        else conv_silu_kernel<false, true><<<grid, kConvThreads, 0, s>>>(K);
+    } else {
+        if (K.dynamic) conv_silu_kernel<true, false><<<grid, kConvThreads, 0, s>>>(K);
+        else conv_silu_kernel<false, false><<<grid, kConvThreads, 0, s>>>(K);
+    }
     fm_status st = check_launch("conv_silu_kernel");
     if (st != FM_OK || !K.dynamic) return st;
     const int64_t rows = a.batch * a.len;

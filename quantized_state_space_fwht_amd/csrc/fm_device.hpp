@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fm.h"
+
 namespace fm {
 
 constexpr int kPMin = -24;
@@ -223,6 +225,21 @@ __device__ __forceinline__ float wave_sum_fixed(float a) {
     return a;
 }
 
+// ---------------------------------------------------------------- quantization statistics
+// Per-thread accumulator of one quantization point (fm_quant_stats), flushed
+// once per wave: wave sums, then one set of atomics from lane 0.
+struct QStat {
+    uint32_t n = 0, clip = 0;
+    double se = 0.0, sv = 0.0;
+    __device__ __forceinline__ void add(double v, double q, double step, bool clipped) {
+        const double e = v - q * step;
+        n += 1;
+        clip += clipped ? 1u : 0u;
+        se = __builtin_fma(e, e, se);
+        sv = __builtin_fma(v, v, sv);
+    }
+};
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ float wave_max_f32(float v) {
     for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k, 64));
@@ -248,6 +265,34 @@ __device__ __forceinline__ void atomic_max_nonneg_f32(float* addr, float v) {
     unsigned int* a = reinterpret_cast<unsigned int*>(addr);
     const unsigned int u = __float_as_uint(v);
     if (__hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < u) atomicMax(a, u);
+}
+
+// statistics of four Hadamard-point elements quantized with coefficient c
+// (code = sat8(rint(v * c)), dequant scale s_dq = 1 / c)
+__device__ __forceinline__ void quant_stat4(QStat& st, float4 v, float c, float s_dq) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float r = rintf(e[i] * c);
+        st.add((double)e[i], (double)fminf(fmaxf(r, -127.0f), 127.0f), (double)s_dq,
+               fabsf(r) > 127.0f);
+    }
+}
+
+// wave sum of the accumulator, then lane 0 adds it into point `pt` of qs
+__device__ inline void qstat_flush(QStat a, fm_quant_stats* qs, int pt) {
+    for (int k = 32; k >= 1; k >>= 1) {
+        a.n += __shfl_xor(a.n, k, 64);
+        a.clip += __shfl_xor(a.clip, k, 64);
+        a.se += __shfl_xor(a.se, k, 64);
+        a.sv += __shfl_xor(a.sv, k, 64);
+    }
+    if ((threadIdx.x & 63) == 0 && a.n > 0) {
+        atomicAdd(&qs->count[pt], (unsigned long long)a.n);
+        if (a.clip) atomicAdd(&qs->clipped[pt], (unsigned long long)a.clip);
+        atomicAdd(&qs->sq_err[pt], a.se);
+        atomicAdd(&qs->sq_val[pt], a.sv);
+    }
 }
 
 }  // namespace fm

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     float c = 0.0f;
     if (!dyn) c = ldexpf((float)G.scoe, -G.sshift);
     float m = 0.0f;
+    QStat st;
     for (int blk = wave; blk < D / 256; blk += W) {
         const int base = blk * 256 + lane * 4;
         float4 g = *reinterpret_cast<const float4*>(&row_buf[base]);
@@ -98,9 +99,14 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
         if (G.normed_out) *reinterpret_cast<float4*>(&G.normed_out[row * D + base]) = n;
         const float4 v = fwht256_lane(n, lane);
         m = fmaxf(m, absmax4(v));
-        if (dyn || G.rowmax) *reinterpret_cast<float4*>(&G.rot_ws[row * D + base]) = v;
-        else *reinterpret_cast<char4*>(&G.q[row * D + base]) = quant4(v, c);
+        if (dyn || G.rowmax) {
+            *reinterpret_cast<float4*>(&G.rot_ws[row * D + base]) = v;
+        } else {
+            *reinterpret_cast<char4*>(&G.q[row * D + base]) = quant4(v, c);
+            if (G.qs) quant_stat4(st, v, c, 1.0f / c);
+        }
     }
+    if (G.qs && !dyn && !G.rowmax) qstat_flush(st, G.qs, FM_QP_G);
     m = wave_max_f32(m);
     if (lane == 0) wmax[wave] = m;
     __syncthreads();
@@ -133,7 +139,7 @@ fm_status gate_run(const GateArgs& g, hipStream_t s) {
     }
     if (g.mode == FM_SCALE_DYNAMIC)
         return hq_quant_rotated(g.rot_ws, g.rows, g.d_inner, FM_SCALE_DYNAMIC, 0, 0, g.amax_ws, g.q,
-                                g.scale_out, s);
+                                g.scale_out, s, g.qs, FM_QP_G);
     if (g.rows == 0) return hq_quant_rotated(g.rot_ws, 0, g.d_inner, g.mode, g.scoe, g.sshift,
                                              nullptr, g.q, g.scale_out, s);
     return FM_OK;

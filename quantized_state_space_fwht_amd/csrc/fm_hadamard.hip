@@ -66,19 +66,23 @@ __device__ __forceinline__ float scale_coef(fm_scale_mode mode, int32_t scoe, in
 __global__ __launch_bounds__(kHqThreads) void hq_quant_kernel(
     const float* __restrict__ x, int64_t nblk_total, fm_scale_mode mode, int32_t scoe,
     int32_t sshift, const float* amax_ws, char4* __restrict__ q, float* scale_out,
-    float* amax_stats, int rotated_input) {
+    float* amax_stats, int rotated_input, fm_quant_stats* qs, int qpt) {
     int lane = threadIdx.x & 63;
     float c = scale_coef(mode, scoe, sshift, amax_ws);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = 1.0f / c;
+    const float s_dq = 1.0f / c;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s_dq;
     int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
     int64_t stride = (int64_t)gridDim.x * (kHqThreads / 64);
     float m = 0.0f;
+    QStat st;
     for (int64_t b = wv; b < nblk_total; b += stride) {
         float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
         if (!rotated_input) v = fwht256_lane(v, lane);
         m = fmaxf(m, absmax4(v));
         q[b * 64 + lane] = quant4(v, c);
+        if (qs) quant_stat4(st, v, c, s_dq);
     }
+    if (qs) qstat_flush(st, qs, qpt);
     if (amax_stats) block_max_to(m, amax_stats, nullptr);
 }
 
@@ -104,7 +108,7 @@ fm_status zero_words(void* p, int64_t n, hipStream_t s) {
 
 fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
                  int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
-                 hipStream_t s) {
+                 hipStream_t s, fm_quant_stats* qs, int qpt) {
     int64_t nb = rows * (k / 256);
     int g = hq_grid(nb);
     fm_status st;
@@ -115,20 +119,20 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
                                                                          amax_stats);
         if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
         hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, (char4*)q,
-                                                 scale_out, nullptr, 0);
+                                                 scale_out, nullptr, 0, qs, qpt);
     } else {
         hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, nullptr, (char4*)q,
-                                                 scale_out, amax_stats, 0);
+                                                 scale_out, amax_stats, 0, qs, qpt);
     }
     return check_launch("hq_quant_kernel");
 }
 
 fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
                            int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
-                           float* scale_out, hipStream_t s) {
+                           float* scale_out, hipStream_t s, fm_quant_stats* qs, int qpt) {
     int64_t nb = rows * (k / 256);
     hq_quant_kernel<<<hq_grid(nb), kHqThreads, 0, s>>>(r, nb, mode, scoe, sshift, amax_ws,
-                                                       (char4*)q, scale_out, nullptr, 1);
+                                                       (char4*)q, scale_out, nullptr, 1, qs, qpt);
     return check_launch("hq_quant_kernel(rotated)");
 }
 

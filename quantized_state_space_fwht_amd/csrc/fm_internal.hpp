@@ -73,13 +73,15 @@ fm_status zero_words(void* p, int64_t n, hipStream_t s);
 // Hadamard rotation + per-tensor int8.  In dynamic mode `amax_ws` (one float,
 // holding 0 on entry: the caller zeroes it) receives the grid maximum between
 // the two passes.
+// qs (nullable): quantization statistics of point qpt (fm_quant_stats)
 fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
                  int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
-                 hipStream_t s);
+                 hipStream_t s, fm_quant_stats* qs = nullptr, int qpt = 0);
 // second pass only: quantize already-rotated rows r (dynamic: amax_ws holds the max)
 fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
                            int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
-                           float* scale_out, hipStream_t s);
+                           float* scale_out, hipStream_t s, fm_quant_stats* qs = nullptr,
+                           int qpt = 0);
 
 struct GemmEpilogue {
     int32_t* acc = nullptr;
@@ -159,6 +161,7 @@ struct ConvArgs {
     int64_t nheads;
     int32_t* dt_out;           // [T, H]
     int32_t* da_out;
+    fm_quant_stats* qs;        // nullable: statistics of the xBC, x, B, C points
 };
 fm_status conv_run(const ConvArgs& a, hipStream_t s);
 fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t stride,
@@ -204,6 +207,7 @@ struct GateArgs {
     float* rot_ws;     // dynamic: [rows, d_inner] rotated values between passes
     float* amax_ws;    // dynamic: 1 float
     const float* sz;   // nullable: SiLU(z) already formed ([rows, d_inner], Q.16 as float)
+    fm_quant_stats* qs;  // nullable: statistics of the out_proj input point
     float* rowmax;     // nullable: one-token form, rotated rows to rot_ws and their maxima
                        // here (the out_proj product quantizes them); q, scale_out unused
 };
@@ -216,6 +220,7 @@ size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);
 void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t);
 void set_keep_intermediates(bool on);
 void set_timing_events(void* start, void* stop);
+void set_quant_stats(fm_quant_stats* qs);
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
                     fm_qparams* qp, void* workspace, bool decode, hipStream_t s);

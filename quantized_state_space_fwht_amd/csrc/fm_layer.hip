@@ -83,6 +83,8 @@ static bool g_keep = false;
 void set_keep_intermediates(bool on) { g_keep = on; }
 
 static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+static thread_local fm_quant_stats* g_qstats = nullptr;
+void set_quant_stats(fm_quant_stats* qs) { g_qstats = qs; }
 void set_timing_events(void* start, void* stop) {
     g_ev_start = (hipEvent_t)start;
     g_ev_stop = (hipEvent_t)stop;
@@ -205,6 +207,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
     const fm_scale_mode mode = (fm_scale_mode)d->mode;
     const bool stat = mode == FM_SCALE_STATIC;
     LayerWs w = layer_ws(d, batch, len, workspace);
+    fm_quant_stats* const qs = decode ? nullptr : g_qstats;  // prefill calls collect
     fm_status st;
     float* small_f = (float*)w.small;
     int32_t* small_i = (int32_t*)w.small;
@@ -246,7 +249,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         // 2. rotate + quantize the in_proj input
         if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0,
                          w.u_q, small_f + kScaleU, stat ? small_f + kAmaxU : nullptr,
-                         small_f + kAmaxU, s)) != FM_OK)
+                         small_f + kAmaxU, s, qs, FM_QP_U)) != FM_OK)
             return st;
     }
     // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
@@ -321,6 +324,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.nheads = H;
         a.dt_out = w.dt;
         a.da_out = w.da;
+        a.qs = qs;
         if ((st = conv_run(a, s)) != FM_OK) return st;
     }
     // 6-7. dt / decay and the scan
@@ -371,6 +375,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         g.amax_ws = small_f + kAmaxG;
         g.rowmax = step ? w.rowmax + 64 : nullptr;
         g.sz = step ? w.sz : nullptr;
+        g.qs = qs;
         if ((st = gate_run(g, s)) != FM_OK) return st;
     }
     // 9. out_proj W8A8 (+ residual for stacks)

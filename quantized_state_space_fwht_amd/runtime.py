@@ -178,13 +178,22 @@ class Mamba2Stack:
                        for p in params_list]
         self.shape = shape
 
-    def prefill(self, u, with_cache=True, stream=None):
+    def prefill(self, u, with_cache=True, stream=None, quant_stats=None):
+        """``quant_stats``: optional list of device fm_quant_stats buffers, one per
+        layer (binding.quant_stats_buffer), into which each layer adds the
+        statistics of its quantization points."""
         h = u.contiguous()
         bufs = [torch.empty_like(h), torch.empty_like(h)]
-        for i, layer in enumerate(self.layers):
-            nxt = bufs[i % 2]
-            layer.prefill(h, out=nxt, with_cache=with_cache, stream=stream)
-            h = nxt
+        try:
+            for i, layer in enumerate(self.layers):
+                nxt = bufs[i % 2]
+                if quant_stats is not None:
+                    B.collect_quant_stats(quant_stats[i])
+                layer.prefill(h, out=nxt, with_cache=with_cache, stream=stream)
+                h = nxt
+        finally:
+            if quant_stats is not None:
+                B.collect_quant_stats(None)
         return h
 
     def decode(self, u_t, stream=None):

@@ -513,3 +513,50 @@ def test_stack_is_prenorm_residual():
     n0 = (x0 / np.sqrt(np.mean(x0 * x0, axis=1, keepdims=True) + 1e-5)).astype(np.float32)
     out0, *_ = O.layer_prefill(preps[0], w.shape, n0.reshape(u.shape))
     assert np.max(np.abs(h - (u + out0))) <= 0.02 * np.max(np.abs(out0))
+
+
+# --------------------------------------------------------------------------- f1 statistics
+def test_quant_stats_hand_computed_cases():
+    """Clip counts and squared errors of the three kinds of point, worked by hand.
+
+    Hadamard point, c = 1: r = (0.5, 1, 200, -300) rounds to (0 [tie to even],
+    1, 200, -300); two codes leave [-127, 127]; q = (0, 1, 127, -127), errors
+    (0.5, 0, 73, -173).  Power-of-two float point, p = 1: v = (1.25, -130, 0.75)
+    times 2 = (2.5 -> 2, -260, 1.5 -> 2), one clipped, q = (2, -127, 2), step
+    1/2, errors (0.25, -66.5, -0.25).  Q.16 point, p = 0: s = (3.5, 200, -0.25)
+    * 2^16, rshr(s, 16) = floor(s/2^16 + 1/2) = (4, 200, 0), one clipped, errors
+    (-0.5, 73, -0.25)."""
+    QS = O.quant_stats
+    st = QS.hadamard_point_stats(np.array([0.5, 1.0, 200.0, -300.0], np.float32), 1.0)
+    assert st == {"count": 4, "clipped": 2, "sq_err": 0.25 + 73.0 ** 2 + 173.0 ** 2,
+                  "sq_val": 0.25 + 1.0 + 200.0 ** 2 + 300.0 ** 2}
+    st = QS.pot_float_point_stats(np.array([1.25, -130.0, 0.75], np.float32), 1)
+    assert st == {"count": 3, "clipped": 1, "sq_err": 0.0625 + 66.5 ** 2 + 0.0625,
+                  "sq_val": 1.25 ** 2 + 130.0 ** 2 + 0.75 ** 2}
+    s = np.array([int(3.5 * 65536), 200 * 65536, -16384], np.int64)
+    st = QS.pot_q16_point_stats(s, 0)
+    assert st == {"count": 3, "clipped": 1, "sq_err": 0.25 + 73.0 ** 2 + 0.0625,
+                  "sq_val": 3.5 ** 2 + 200.0 ** 2 + 0.0625}
+
+
+def test_quant_stats_dynamic_never_clips_and_matches_the_codes():
+    """Dynamic scales come from each tensor's own maximum, so no point clips
+    (c = 127/amax, p = pot(amax)); and the statistics agree with the codes the
+    layer actually produced: sum (v - q*step)^2 recomputed from the layer's own
+    codes and values equals the reported error."""
+    w = configs.with_len(configs.get("tiny_layer"), batch=2, seqlen=40)
+    prep = O.prepare_layer(synth.workload_params(w, 0))
+    out, r, _, _ = O.layer_prefill(prep, w.shape, synth.workload_activations(w), collect=True)
+    qs = r["qstats"]
+    T = 2 * 40
+    s = w.shape
+    assert {k: v["count"] for k, v in qs.items()} == {
+        "u": T * s.d_model, "g": T * s.d_inner, "xbc": T * s.conv_ch, "x": T * s.d_inner,
+        "B": T * s.dstate, "C": T * s.dstate}
+    assert all(v["clipped"] == 0 for v in qs.values())
+    # the xBC point from the layer's own intermediates
+    p_c = r["p"][0]
+    e = r["xbc"].astype(np.float64) - r["xbc_q"].astype(np.float64) * 2.0 ** -p_c
+    assert qs["xbc"]["sq_err"] == pytest.approx(float(np.sum(e * e)), rel=1e-12)
+    # the u point: codes times the stored dequant scale
+    assert qs["u"]["sq_val"] > 0 and 0 < qs["u"]["sq_err"] < qs["u"]["sq_val"]
