@@ -34,6 +34,7 @@ SCAN_OPS_PER_ELEMENT_STEP = 8
 COPY_PROBE_BYTES = 256 << 20
 HBM_PEAK_GBS = 8000.0
 DECODE_WORKLOAD = "m2p7b_decode"
+STUDY_WORKLOAD = "m130m_stack_static"
 
 
 def log(msg):
@@ -125,6 +126,106 @@ def decode_bench(torch, configs, synth, warmup=8, max_steps=None):
                          "bytes_per_token_step": step_bytes}}
 
 
+def study_scales(torch, configs, synth, B):
+    """Static against dynamic scales on held-out inputs (the scale study).
+
+    The 24-layer 130M-shaped static stack is calibrated on its 64 seeded
+    sequences (one per call, as the oracle's calibration runs them), then its
+    8 held-out sequences run once with the static scales and once with dynamic
+    ones.  Per quantization point and layer the library reports the clip count
+    and the dequantization error; this prints the clip rate and the SQNR
+    (10 log10 of sum v^2 over sum (v - q step)^2).  Beside it, the oracle
+    recomputes layer 0 in dynamic mode on the first held-out sequence, checked
+    against the library's record of the same call and timed."""
+    import numpy as np
+    import oracle as O
+    from quantized_state_space_fwht_amd.runtime import Mamba2Stack
+    w = configs.get(STUDY_WORKLOAD)
+    s = w.shape
+    log(f"study: building {w.name} ({w.description})")
+    params = [synth.workload_params(w, l) for l in range(w.nlayers)]
+    stack = Mamba2Stack(s, params)
+    calib = [torch.from_numpy(x).cuda() for x in synth.calibration_sequences(w)]
+    t0 = time.perf_counter()
+    stack.calibrate(calib)
+    torch.cuda.synchronize()
+    calib_s = time.perf_counter() - t0
+    u = torch.from_numpy(synth.eval_batch(w)).cuda()
+    rows = {}
+    outs = {}
+    for mode in ("static", "dynamic"):
+        if mode == "dynamic":
+            for layer in stack.layers:
+                layer.set_dynamic()
+        bufs = [B.quant_stats_buffer() for _ in stack.layers]
+        outs[mode] = stack.prefill(u, with_cache=False, quant_stats=bufs).float().cpu().numpy()
+        rows[mode] = [B.quant_stats_from_device(b) for b in bufs]
+    # time the held-out pass with and without statistics (dynamic mode)
+    def timed(with_stats):
+        bufs = [B.quant_stats_buffer() for _ in stack.layers] if with_stats else None
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        stack.prefill(u, with_cache=False, quant_stats=bufs)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+    timed(False)
+    ms_plain, ms_stats = timed(False), timed(True)
+
+    def summary(recs):
+        out = {}
+        for i, name in enumerate(B.QP_NAMES):
+            cnt = sum(r.count[i] for r in recs)
+            clip = sum(r.clipped[i] for r in recs)
+            se = sum(r.sq_err[i] for r in recs)
+            sv = sum(r.sq_val[i] for r in recs)
+            per_layer_db = [round(10 * np.log10(r.sq_val[i] / r.sq_err[i]), 2) if r.sq_err[i] > 0
+                            else None for r in recs]
+            out[name] = {"clip_rate": clip / cnt if cnt else 0.0, "clipped": int(clip),
+                         "elements": int(cnt),
+                         "sqnr_db": round(10 * np.log10(sv / se), 3) if se > 0 else None,
+                         "sqnr_db_per_layer": per_layer_db,
+                         "clipped_per_layer": [int(r.clipped[i]) for r in recs]}
+        return out
+    diff = outs["static"] - outs["dynamic"]
+    rel_l2 = float(np.linalg.norm(diff) / np.linalg.norm(outs["dynamic"]))
+
+    # the oracle beside: layer 0, dynamic, first held-out sequence
+    log("study: oracle check (layer 0, dynamic, one held-out sequence)")
+    u0 = synth.eval_batch(w)[:1]
+    xin = O.rmsnorm_fixed_order(u0.reshape(-1, s.d_model),
+                                np.ones(s.d_model, np.float32)).reshape(u0.shape)
+    t0 = time.perf_counter()
+    _, r, _, _ = O.layer_prefill(O.prepare_layer(params[0]), s, xin, "dynamic", collect=True)
+    oracle_s = time.perf_counter() - t0
+    buf = B.quant_stats_buffer()
+    stack.layers[0].set_dynamic()
+    B.collect_quant_stats(buf)
+    try:
+        # the stack's layers apply the pre-norm themselves: they take u itself
+        stack.layers[0].prefill(torch.from_numpy(np.ascontiguousarray(u0)).cuda(),
+                                with_cache=False)
+        torch.cuda.synchronize()
+    finally:
+        B.collect_quant_stats(None)
+    g = B.quant_stats_from_device(buf)
+    agree = all(g.count[i] == r["qstats"][n]["count"] and g.clipped[i] == r["qstats"][n]["clipped"]
+                and abs(g.sq_err[i] - r["qstats"][n]["sq_err"]) <= 1e-9 * r["qstats"][n]["sq_err"]
+                for i, n in enumerate(B.QP_NAMES))
+    return {"study": "static_vs_dynamic_scales", "workload": w.name, "layers": w.nlayers,
+            "calibration": f"{len(w.calib_seeds)} sequences x {w.seqlen} tokens (seeds "
+                           f"{w.calib_seeds[0]}-{w.calib_seeds[-1]})",
+            "held_out": f"{len(w.eval_seeds)} sequences x {w.seqlen} tokens (seeds "
+                        f"{w.eval_seeds[0]}-{w.eval_seeds[-1]})",
+            "static": summary(rows["static"]), "dynamic": summary(rows["dynamic"]),
+            "output_rel_l2_static_vs_dynamic": rel_l2,
+            "gpu": {"calibration_s": round(calib_s, 3), "held_out_pass_ms": round(ms_plain, 3),
+                    "held_out_pass_with_stats_ms": round(ms_stats, 3)},
+            "oracle_beside": {"sample": "layer 0, dynamic, held-out sequence 0 (2048 tokens)",
+                              "seconds": round(oracle_s, 2), "agrees": bool(agree)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +237,9 @@ def main():
                     help="skip the decode measurement (64-layer 2.7B-shaped stack)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="time only this many decode steps (default: the workload's)")
+    ap.add_argument("--study-scales", action="store_true",
+                    help="run the static-vs-dynamic scale study instead of the benchmark "
+                         "(one JSON line of clip rates and SQNR per quantization point)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device three times "
                          "(a reference kernel of known traffic for counter runs)")
@@ -149,6 +253,11 @@ def main():
     from quantized_state_space_fwht_amd import binding as B
     from quantized_state_space_fwht_amd import configs, synth
     from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+
+    if args.study_scales:
+        torch.cuda.set_device(0)
+        print(json.dumps(study_scales(torch, configs, synth, B)), flush=True)
+        return
 
     w = configs.get(args.workload)
     if w.nlayers != 1 or w.decode_steps:
