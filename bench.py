@@ -226,6 +226,106 @@ def study_scales(torch, configs, synth, B):
                               "seconds": round(oracle_s, 2), "agrees": bool(agree)}}
 
 
+def study_outliers(torch, configs, synth, B, rows=2048):
+    """The outlier study: Hadamard against plain per-tensor and smoothed W8A8.
+
+    For the in_proj and out_proj of one 130M-shaped and one 2.7B-shaped layer
+    (their inputs: the synthetic activations with four outlier channels at 50x,
+    and the normed gate output of a dynamic layer pass over them; the first
+    `rows` tokens), each scheme runs on the GPU (quantization, int8 GEMM,
+    dequantization) and is compared with the float64 product on the host:
+    output error ||out - x w^T|| / ||x w^T|| and the activation SQNR in the
+    scheme's own domain.  The oracle recomputes the 130M in_proj beside."""
+    import numpy as np
+    import oracle as O
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+
+    def gpu_scheme(xd, wd, name):
+        n, k = wd.shape
+        m = xd.shape[0]
+        qa = torch.empty((m, k), dtype=torch.int8, device="cuda")
+        qb = torch.empty((n, k), dtype=torch.int8, device="cuda")
+        sa = torch.empty(1, dtype=torch.float32, device="cuda")
+        sb = torch.empty(1, dtype=torch.float32, device="cuda")
+        xs = xd
+        if name == "hadamard":
+            B.fm_hadamard_quant(xd, B.DYNAMIC, 0, 0, qa, sa)
+            B.fm_hadamard_quant(wd, B.DYNAMIC, 0, 0, qb, sb)
+        elif name == "naive":
+            B.fm_quant_per_tensor(xd, qa, sa)
+            B.fm_quant_per_tensor(wd, qb, sb)
+        else:
+            s = torch.empty(k, dtype=torch.float32, device="cuda")
+            B.fm_smooth_scales(xd, wd, s)
+            xs = torch.empty_like(xd)
+            ws = torch.empty_like(wd)
+            B.fm_scale_columns(xd, s, True, xs)
+            B.fm_scale_columns(wd, s, False, ws)
+            B.fm_quant_per_tensor(xs, qa, sa)
+            B.fm_quant_per_tensor(ws, qb, sb)
+        out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        B.fm_w8a8_gemm(qa, qb, sa, sb, out=out)
+        return qa, sa, xs, out
+
+    import scipy.linalg
+    h256 = scipy.linalg.hadamard(256).astype(np.float64) / 16.0  # symmetric, orthonormal
+    report = {"study": "outlier_schemes", "rows": rows, "layers": {}}
+    for wl in ("m130m_layer", "m2p7b_stack"):
+        w = configs.get(wl)
+        s = w.shape
+        params = synth.workload_params(w, 0)
+        u = synth.workload_activations(configs.with_len(w, batch=1, seqlen=rows))
+        layer = Mamba2Layer(s, params)
+        B.keep_intermediates(True)
+        try:
+            layer.prefill(torch.from_numpy(u).cuda())
+            normed = layer.tap("normed", torch.float32, (rows, s.d_inner)).clone()
+        finally:
+            B.keep_intermediates(False)
+        cases = {"in_proj": (u.reshape(rows, s.d_model), params["w_in"]),
+                 "out_proj": (normed.cpu().numpy(), params["w_out"])}
+        for lname, (x, wt) in cases.items():
+            x = np.ascontiguousarray(x, np.float32)
+            wt = np.ascontiguousarray(wt, np.float32)
+            ref = x.astype(np.float64) @ wt.astype(np.float64).T
+            nref = np.linalg.norm(ref)
+            xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(wt).cuda()
+            entry = {"m": x.shape[0], "k": x.shape[1], "n": wt.shape[0], "schemes": {}}
+            for sch in ("hadamard", "naive", "smooth"):
+                gpu_scheme(xd, wd, sch)  # warm
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                qa, sa, xs, out = gpu_scheme(xd, wd, sch)
+                torch.cuda.synchronize()
+                ms = (time.perf_counter() - t0) * 1e3
+                o = out.cpu().numpy().astype(np.float64)
+                if sch == "hadamard":  # the rotated activations (exact, float64), for the SQNR
+                    xs_h = (x.astype(np.float64).reshape(-1, 256) @ h256).reshape(x.shape)
+                else:
+                    xs_h = xs.cpu().numpy().astype(np.float64)
+                e = xs_h - qa.cpu().numpy().astype(np.float64) * float(sa.item())
+                entry["schemes"][sch] = {
+                    "output_rel_err": float(np.linalg.norm(o - ref) / nref),
+                    "activation_sqnr_db": float(10 * np.log10(np.sum(xs_h ** 2) / np.sum(e * e))),
+                    "gpu_ms": round(ms, 3)}
+            report["layers"][f"{wl}.{lname}"] = entry
+        del layer
+        torch.cuda.empty_cache()
+    # the oracle beside: the 130M in_proj, all three schemes
+    w = configs.get("m130m_layer")
+    params = synth.workload_params(w, 0)
+    x = synth.workload_activations(configs.with_len(w, batch=1, seqlen=rows)).reshape(rows, -1)
+    t0 = time.perf_counter()
+    errs = {sch: O.outliers.output_error(O.outliers.scheme(x, params["w_in"], sch)["out"], x,
+                                         params["w_in"]) for sch in ("hadamard", "naive", "smooth")}
+    osec = time.perf_counter() - t0
+    got = report["layers"]["m130m_layer.in_proj"]["schemes"]
+    report["oracle_beside"] = {"sample": f"m130m_layer in_proj, {rows} tokens, three schemes",
+                               "seconds": round(osec, 2),
+                               "agrees": all(errs[k] == got[k]["output_rel_err"] for k in errs)}
+    return report
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +340,9 @@ def main():
     ap.add_argument("--study-scales", action="store_true",
                     help="run the static-vs-dynamic scale study instead of the benchmark "
                          "(one JSON line of clip rates and SQNR per quantization point)")
+    ap.add_argument("--study-outliers", action="store_true",
+                    help="run the outlier study (Hadamard against plain per-tensor and smoothed "
+                         "W8A8 on the projections' inputs) instead of the benchmark")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device three times "
                          "(a reference kernel of known traffic for counter runs)")
@@ -257,6 +360,10 @@ def main():
     if args.study_scales:
         torch.cuda.set_device(0)
         print(json.dumps(study_scales(torch, configs, synth, B)), flush=True)
+        return
+    if args.study_outliers:
+        torch.cuda.set_device(0)
+        print(json.dumps(study_outliers(torch, configs, synth, B)), flush=True)
         return
 
     w = configs.get(args.workload)

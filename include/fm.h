@@ -332,6 +332,36 @@ fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t le
  * their workspace (slower; for tests).  0 (default): they do not. */
 void fm_layer_keep_intermediates(int32_t on);
 
+/* ------------------------------------------------------------------------
+ * Outlier-study baselines.  The review page of FastMamba credits the Hadamard
+ * rotation with taming activation outliers (abstract; Fig. 3 caption; Table II
+ * compares it with other 8-bit schemes); the Mamba-PTQ abstract locates them in
+ * a few channels.  These calls build the two reference schemes the study
+ * compares the rotation with, on the same int8 GEMM (fm_w8a8_gemm):
+ *
+ * fm_quant_per_tensor: plain per-tensor int8, fm_hadamard_quant's dynamic
+ *   arithmetic without the rotation: c = 127 / max|x| over the tensor (c = 1
+ *   if the max is 0), q = clamp(rint(x * c), -127, 127), *scale_out = 1 / c.
+ *   x [n] float32 16-byte aligned, q [n] int8 4-byte aligned, n a multiple of
+ *   4 with 0 <= n < 2^31.  Workspace: fm_quant_per_tensor_workspace_size().
+ * fm_smooth_scales: SmoothQuant-style smoothing factors with alpha = 1/2,
+ *   s_j = sqrt(max_i |x_ij|) / sqrt(max_r |w_rj|) (1 if either max is 0), from
+ *   activations x [rows, k] and weights w [n, k] (rows = output features);
+ *   s [k] float32.  Workspace: fm_smooth_scales_workspace_size(k).
+ * fm_scale_columns: out_ij = x_ij / s_j (divide != 0) or x_ij * s_j, for
+ *   x, out [rows, k] float32 (out may equal x), s [k]; rows * k < 2^31.
+ * The smoothed pair x / s, w * s has the same product as x, w in exact
+ * arithmetic; quantize both with fm_quant_per_tensor.
+ * ---------------------------------------------------------------------- */
+size_t fm_quant_per_tensor_workspace_size(void);
+fm_status fm_quant_per_tensor(const float* x, int64_t n, int8_t* q, float* scale_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t fm_smooth_scales_workspace_size(int64_t k);
+fm_status fm_smooth_scales(const float* x, int64_t rows, const float* w, int64_t n, int64_t k,
+                           float* s, void* workspace, size_t workspace_bytes, hipStream_t stream);
+fm_status fm_scale_columns(const float* x, int64_t rows, int64_t k, const float* s,
+                           int32_t divide, float* out, hipStream_t stream);
+
 /* Quantization statistics of a layer's six activation quantization points,
  * for the static-vs-dynamic scale study (the referee's open question on the
  * review page of FastMamba, major comment on Sections III-A / IV-B: static

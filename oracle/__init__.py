@@ -43,4 +43,4 @@ from .scan import dt_dA, ssm_scan_pot
 from .gate_norm import gate, gate_norm_quant, rmsnorm_fixed_order
 from .layer import (QParams, Stats, calibrate_stack, layer_decode, layer_prefill, prepare_layer,
                     qparams_from_stats, stack_decode, stack_prefill)
-from . import quant_stats
+from . import outliers, quant_stats

@@ -106,6 +106,11 @@ _SIGS = {
     "fm_layer_keep_intermediates": (None, [_c_i32]),
     "fm_layer_set_timing_events": (None, [_vp, _vp]),
     "fm_layer_collect_quant_stats": (None, [_vp]),
+    "fm_quant_per_tensor_workspace_size": (_c_sz, []),
+    "fm_quant_per_tensor": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
+    "fm_smooth_scales_workspace_size": (_c_sz, [_c_i64]),
+    "fm_smooth_scales": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _c_sz, _vp]),
+    "fm_scale_columns": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _c_i32, _vp, _vp]),
     "fm_qparams_from_stats": (ctypes.c_int, [ctypes.POINTER(QParams),
                                              ctypes.POINTER(StaticParams)]),
 }
@@ -148,6 +153,28 @@ def fm_hadamard_quant(x, mode, scoe, sshift, q, scale_out, amax_stats=None, ws=N
     _check(lib.fm_hadamard_quant(_ptr(x), rows, k, mode, scoe, sshift, _ptr(q), _ptr(scale_out),
                                  _ptr(amax_stats), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)))
+
+
+def fm_quant_per_tensor(x, q, scale_out, ws=None, stream=None):
+    if ws is None:
+        ws = workspace(lib.fm_quant_per_tensor_workspace_size(), x.device)
+    _check(lib.fm_quant_per_tensor(_ptr(x), x.numel(), _ptr(q), _ptr(scale_out), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+
+
+def fm_smooth_scales(x, w, s, ws=None, stream=None):
+    rows, k = x.shape
+    n = w.shape[0]
+    if ws is None:
+        ws = workspace(lib.fm_smooth_scales_workspace_size(k), x.device)
+    _check(lib.fm_smooth_scales(_ptr(x), rows, _ptr(w), n, k, _ptr(s), _ptr(ws), ws.numel(),
+                                _stream(stream)))
+
+
+def fm_scale_columns(x, s, divide, out, stream=None):
+    rows, k = x.shape
+    _check(lib.fm_scale_columns(_ptr(x), rows, k, _ptr(s), 1 if divide else 0, _ptr(out),
+                                _stream(stream)))
 
 
 def fm_w8a8_gemm(a, b, scale_a, scale_b, acc=None, out=None, stream=None):

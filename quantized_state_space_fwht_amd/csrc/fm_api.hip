@@ -449,6 +449,57 @@ void fm_layer_set_timing_events(void* start, void* stop) { set_timing_events(sta
 
 void fm_layer_collect_quant_stats(fm_quant_stats* dev_stats) { set_quant_stats(dev_stats); }
 
+// ---------------------------------------------------------------- outlier-study baselines
+size_t fm_quant_per_tensor_workspace_size(void) { return 256; }
+
+fm_status fm_quant_per_tensor(const float* x, int64_t n, int8_t* q, float* scale_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "fm_quant_per_tensor";
+    g_err[0] = 0;
+    if (!scale_out) return fail(FM_ERR_NULL, "%s: scale_out is NULL", who);
+    if (n < 0 || n % 4 || n >= ((int64_t)1 << 31))
+        return fail(FM_ERR_SHAPE, "%s: need 0 <= n < 2^31, n a multiple of 4 (n=%lld)", who,
+                    (long long)n);
+    if (n > 0 && (!x || !q)) return fail(FM_ERR_NULL, "%s: x or q is NULL", who);
+    if (n > 0 && (!aligned(x, 16) || !aligned(q, 4)))
+        return fail(FM_ERR_SHAPE, "%s: x must be 16-byte and q 4-byte aligned", who);
+    fm_status st;
+    if ((st = check_ws(workspace, workspace_bytes, fm_quant_per_tensor_workspace_size(), who)) !=
+        FM_OK)
+        return st;
+    return quant_per_tensor_run(x, n, q, scale_out, (float*)workspace, stream);
+}
+
+size_t fm_smooth_scales_workspace_size(int64_t k) {
+    if (k < 0) return 0;
+    return align256((size_t)(2 * k) * sizeof(float));
+}
+
+fm_status fm_smooth_scales(const float* x, int64_t rows, const float* w, int64_t n, int64_t k,
+                           float* s, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "fm_smooth_scales";
+    g_err[0] = 0;
+    if (rows < 0 || n < 0 || k <= 0 || rows * k >= ((int64_t)1 << 31) ||
+        n * k >= ((int64_t)1 << 31))
+        return fail(FM_ERR_SHAPE, "%s: need k > 0, rows, n >= 0, rows*k and n*k < 2^31", who);
+    if (!s || (rows > 0 && !x) || (n > 0 && !w)) return fail(FM_ERR_NULL, "%s: NULL argument", who);
+    fm_status st;
+    if ((st = check_ws(workspace, workspace_bytes, fm_smooth_scales_workspace_size(k), who)) !=
+        FM_OK)
+        return st;
+    return smooth_scales_run(x, rows, w, n, k, s, (float*)workspace, stream);
+}
+
+fm_status fm_scale_columns(const float* x, int64_t rows, int64_t k, const float* s,
+                           int32_t divide, float* out, hipStream_t stream) {
+    const char* who = "fm_scale_columns";
+    g_err[0] = 0;
+    if (rows < 0 || k <= 0 || rows * k >= ((int64_t)1 << 31))
+        return fail(FM_ERR_SHAPE, "%s: need k > 0, rows >= 0, rows*k < 2^31", who);
+    if (rows > 0 && (!x || !s || !out)) return fail(FM_ERR_NULL, "%s: NULL argument", who);
+    return scale_columns_run(x, rows, k, s, divide, out, stream);
+}
+
 fm_status fm_qparams_from_stats(const fm_qparams* st, fm_static_params* out) {
     g_err[0] = 0;
     if (!st || !out) return fail(FM_ERR_NULL, "fm_qparams_from_stats: NULL argument");

@@ -215,6 +215,14 @@ fm_status gate_run(const GateArgs& a, hipStream_t s);
 
 fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s);
 
+// outlier-study baselines (fm_outlier.hip); n a multiple of 4, ws as documented in fm.h
+fm_status quant_per_tensor_run(const float* x, int64_t n, int8_t* q, float* scale_out,
+                               float* amax_ws, hipStream_t s);
+fm_status smooth_scales_run(const float* x, int64_t rows, const float* w, int64_t n, int64_t k,
+                            float* s_out, float* ws, hipStream_t s);
+fm_status scale_columns_run(const float* x, int64_t rows, int64_t k, const float* sc, int divide,
+                            float* out, hipStream_t s);
+
 // layer pipeline (fm_layer.hip)
 size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);
 void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t);

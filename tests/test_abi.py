@@ -133,3 +133,30 @@ def test_qparams_from_stats_on_host(lib):
     want = O.qparams_from_stats(st)
     assert tuple(sp.scoe) == want.scoe and tuple(sp.sshift) == want.sshift
     assert tuple(sp.p) == want.p
+
+
+def test_outlier_baselines_validation(lib):
+    """Per-tensor quantization, smoothing factors and column scaling reject bad
+    sizes, NULLs, misalignment and short workspaces on the host."""
+    vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int32
+    fake = 1 << 20
+    f = lib.fm_quant_per_tensor
+    f.argtypes = [vp, i64, vp, vp, vp, sz, vp]
+    assert f(fake, 6, fake, fake, fake, 256, None) == FM_ERR_SHAPE        # n % 4
+    assert f(fake, -4, fake, fake, fake, 256, None) == FM_ERR_SHAPE
+    assert f(fake + 4, 8, fake, fake, fake, 256, None) == FM_ERR_SHAPE    # x alignment
+    assert f(fake, 8, fake, None, fake, 256, None) == FM_ERR_NULL         # scale_out
+    assert f(fake, 8, fake, fake, fake, 16, None) == FM_ERR_WORKSPACE
+    g = lib.fm_smooth_scales
+    g.argtypes = [vp, i64, vp, i64, i64, vp, vp, sz, vp]
+    lib.fm_smooth_scales_workspace_size.restype = sz
+    lib.fm_smooth_scales_workspace_size.argtypes = [i64]
+    need = lib.fm_smooth_scales_workspace_size(100)
+    assert need >= 800
+    assert g(fake, 4, fake, 4, 0, fake, fake, need, None) == FM_ERR_SHAPE
+    assert g(fake, 4, fake, 4, 100, None, fake, need, None) == FM_ERR_NULL
+    assert g(fake, 4, fake, 4, 100, fake, fake, need - 256, None) == FM_ERR_WORKSPACE
+    h = lib.fm_scale_columns
+    h.argtypes = [vp, i64, i64, vp, i32, vp, vp]
+    assert h(fake, 4, 0, fake, 1, fake, None) == FM_ERR_SHAPE
+    assert h(fake, 4, 8, None, 1, fake, None) == FM_ERR_NULL

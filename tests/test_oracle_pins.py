@@ -560,3 +560,44 @@ def test_quant_stats_dynamic_never_clips_and_matches_the_codes():
     assert qs["xbc"]["sq_err"] == pytest.approx(float(np.sum(e * e)), rel=1e-12)
     # the u point: codes times the stored dequant scale
     assert qs["u"]["sq_val"] > 0 and 0 < qs["u"]["sq_err"] < qs["u"]["sq_val"]
+
+
+# --------------------------------------------------------------------------- f2 baselines
+def test_outlier_baselines_hand_worked_and_invariants():
+    """Smoothing factors worked by hand: x = [[4, -1], [2, 9]], w = [[1, .25],
+    [-4, 1]] give column maxima (4, 9) and (4, 1), so s = (2/2, 3/1) = (1, 3).
+    Smoothing leaves the product unchanged (x / s)(w * s)^T = x w^T up to
+    float32 rounding of the two scalings.  Per-tensor quantization of a
+    nonzero tensor reaches code 127 exactly at its maximum and never errs by
+    more than half a step; a zero tensor has codes 0 and scale 1."""
+    OL = O.outliers
+    x = np.array([[4, -1], [2, 9]], np.float32)
+    w = np.array([[1, 0.25], [-4, 1]], np.float32)
+    assert np.array_equal(OL.smooth_scales(x, w), np.array([1, 3], np.float32))
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 96)).astype(np.float32)
+    x[:, 7] *= 50
+    w = (rng.standard_normal((40, 96)) * 0.02).astype(np.float32)
+    s = OL.smooth_scales(x, w)
+    lhs = (x / s).astype(np.float64) @ (w * s).astype(np.float64).T
+    rhs = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.allclose(lhs, rhs, rtol=1e-5, atol=1e-6)
+    q, sc = OL.per_tensor_quant(x)
+    assert np.max(np.abs(q)) == 127
+    assert np.max(np.abs(x - q.astype(np.float64) * sc)) <= 0.5 * sc * (1 + 1e-6)
+    q0, sc0 = OL.per_tensor_quant(np.zeros((4, 8), np.float32))
+    assert not q0.any() and sc0 == 1.0
+
+
+def test_outlier_channel_hurts_naive_int8_most():
+    """One activation channel at 50x (the synthetic inputs' outlier pattern):
+    plain per-tensor int8 loses most, the rotation and the smoothing both
+    recover most of it.  (Expected behaviour of the schemes, checked with a
+    wide margin; it is what the study measures.)"""
+    OL = O.outliers
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((256, 512)).astype(np.float32)
+    x[:, [3, 200]] *= 50
+    w = (rng.standard_normal((384, 512)) * 0.02).astype(np.float32)
+    err = {k: OL.output_error(OL.scheme(x, w, k)["out"], x, w) for k in ("naive", "hadamard", "smooth")}
+    assert err["hadamard"] < 0.5 * err["naive"] and err["smooth"] < 0.5 * err["naive"], err
