@@ -326,6 +326,74 @@ def study_outliers(torch, configs, synth, B, rows=2048):
     return report
 
 
+def study_nau(torch, configs, synth, B):
+    """Alternative coefficient tables for the 8-segment 2^v unit.
+
+    The pages fix the unit's form (first-order segments on the eighths of an
+    octave) but not its coefficients.  For the chord table, a least-squares and
+    a minimax (relative error) fit of the same form, the library evaluates exp
+    on every Q.16 input in [-16, 0] and SoftPlus, SiLU on every input in
+    [-16, 16]; the host compares with the exact functions (float64): largest
+    and RMS error in units of 2^-16.  The oracle recomputes a sample beside."""
+    import numpy as np
+    import oracle as O
+    tables = synth.nau_knot_tables()
+    span = 16 << 16
+    xs = {"exp": np.arange(-span, 1, dtype=np.int64),
+          "softplus": np.arange(-span, span + 1, dtype=np.int64),
+          "silu": np.arange(-span, span + 1, dtype=np.int64)}
+    exact = {"exp": lambda x: np.exp(x / 65536.0) * 65536.0,
+             "softplus": lambda x: np.logaddexp(0.0, x / 65536.0) * 65536.0,
+             "silu": lambda x: (x / 65536.0) / (1.0 + np.exp(-x / 65536.0)) * 65536.0}
+    # the unit's own form with an exact exponential: SoftPlus is e^-|x| + max(x, 0)
+    # (Eq. (5) and the symmetry), whose gap to ln(1 + e^x) no table can close
+    form = {"exp": exact["exp"],
+            "softplus": lambda x: (np.exp(-np.abs(x) / 65536.0) + np.maximum(x, 0) / 65536.0)
+            * 65536.0,
+            "silu": exact["silu"]}
+    codes = {"exp": B.NAU_EXP, "softplus": B.NAU_SOFTPLUS, "silu": B.NAU_SILU}
+    report = {"study": "nau_knot_tables", "domain": "all Q.16 inputs, exp on [-16, 0], "
+              "SoftPlus and SiLU on [-16, 16]", "tables": {}}
+    for name, knots in tables.items():
+        entry = {"knots_q30": [int(v) for v in knots]}
+        for fn, x in xs.items():
+            xd = torch.from_numpy(x.astype(np.int32)).cuda()
+            yd = torch.empty_like(xd)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            B.fm_nau_eval_knots(codes[fn], knots, xd, yd)
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6
+            got = yd.cpu().numpy().astype(np.float64)
+            err = got - exact[fn](x.astype(np.float64))
+            ferr = got - form[fn](x.astype(np.float64))
+            entry[fn] = {"max_abs_lsb": float(np.max(np.abs(err))),
+                         "rms_lsb": float(np.sqrt(np.mean(err * err))),
+                         "mean_lsb": float(np.mean(err)),
+                         "vs_form_max_abs_lsb": float(np.max(np.abs(ferr))),
+                         "vs_form_rms_lsb": float(np.sqrt(np.mean(ferr * ferr))),
+                         "gpu_us": round(us, 1)}
+        # largest relative error of 2^f itself (the form's accuracy), over all fractions
+        k = np.arange(1 << 16)
+        y = knots.astype(np.float64) / 2 ** 30
+        seg, r = k >> 13, (k & 8191) / 8192.0
+        rel = (y[seg] * (1 - r) + y[seg + 1] * r) / 2.0 ** (k / 65536.0) - 1
+        entry["exp2_max_rel"] = float(np.max(np.abs(rel)))
+        report["tables"][name] = entry
+    # the oracle beside: exp with the minimax table on a strided sample
+    x = np.arange(-span, 1, 31, dtype=np.int64)
+    t0 = time.perf_counter()
+    want = O.exp_q16(x, tables["minimax"])
+    osec = time.perf_counter() - t0
+    xd = torch.from_numpy(x.astype(np.int32)).cuda()
+    yd = torch.empty_like(xd)
+    B.fm_nau_eval_knots(B.NAU_EXP, tables["minimax"], xd, yd)
+    report["oracle_beside"] = {"sample": f"exp, minimax table, {x.size} inputs",
+                               "seconds": round(osec, 3),
+                               "agrees": bool(np.array_equal(yd.cpu().numpy(), want))}
+    return report
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +411,9 @@ def main():
     ap.add_argument("--study-outliers", action="store_true",
                     help="run the outlier study (Hadamard against plain per-tensor and smoothed "
                          "W8A8 on the projections' inputs) instead of the benchmark")
+    ap.add_argument("--study-nau", action="store_true",
+                    help="run the 2^v unit's coefficient study (chord, least-squares and "
+                         "minimax tables) instead of the benchmark")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy 256 MiB device-to-device three times "
                          "(a reference kernel of known traffic for counter runs)")
@@ -360,6 +431,10 @@ def main():
     if args.study_scales:
         torch.cuda.set_device(0)
         print(json.dumps(study_scales(torch, configs, synth, B)), flush=True)
+        return
+    if args.study_nau:
+        torch.cuda.set_device(0)
+        print(json.dumps(study_nau(torch, configs, synth, B)), flush=True)
         return
     if args.study_outliers:
         torch.cuda.set_device(0)

@@ -208,6 +208,13 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
  * ---------------------------------------------------------------------- */
 typedef enum fm_nau_fn { FM_NAU_EXP = 0, FM_NAU_SOFTPLUS = 1, FM_NAU_SILU = 2 } fm_nau_fn;
 fm_status fm_nau_eval(fm_nau_fn fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t stream);
+/* The same unit with another table of the same form: knots_q30 is a HOST
+ * array of nine Q.30 values in (2^29, 2^32), the first below 2^31, replacing
+ * Y[0..8] (the pages leave the coefficients author-chosen: referee minor
+ * comment on Section III-B.2).  Other knots return FM_ERR_SHAPE (the unit's
+ * exact float64 evaluation is argued for that range). */
+fm_status fm_nau_eval_knots(fm_nau_fn fn, const int64_t* knots_q30, const int32_t* x, int32_t* y,
+                            int64_t n, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fm_gate_norm_quant — output gate, gated RMSNorm and the out_proj input

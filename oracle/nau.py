@@ -42,8 +42,12 @@ EXP2_TABLE_Q30 = _exp2_table()
 LOG2E_Q30 = int(np.rint(np.log2(np.e) * 2.0 ** 30))
 
 
-def exp2_q16(v):
-    """2^(v / 2^16) in Q.16 for Q.16 integers v <= 0 (result in [0, 2^16])."""
+def exp2_q16(v, table=None):
+    """2^(v / 2^16) in Q.16 for Q.16 integers v <= 0 (result in [0, 2^16]).
+
+    ``table``: nine Q.30 knots in place of EXP2_TABLE_Q30 (alternative fits of
+    the same piecewise-linear form)."""
+    tab = EXP2_TABLE_Q30 if table is None else np.asarray(table, dtype=np.int64)
     v = np.asarray(v, dtype=np.int64)
     assert np.all(v <= 0), "the exponential unit is used for arguments <= 0 only"
     # below -32 the result is 0 whatever the segment (the shift exceeds 45 bits)
@@ -52,32 +56,32 @@ def exp2_q16(v):
     f = v - (n << 16)                 # fraction in [0, 2^16)
     i = f >> 13                       # segment 0..7
     r = f & 0x1FFF                    # position inside the segment, 13 bits
-    y0 = EXP2_TABLE_Q30[i]
-    y1 = EXP2_TABLE_Q30[i + 1]
+    y0 = tab[i]
+    y1 = tab[i + 1]
     m = y0 + rshr((y1 - y0) * r, 13)  # Q.30 mantissa in [2^30, 2^31]
     return rshr(m, 14 - n)
 
 
-def exp_q16(x):
+def exp_q16(x, table=None):
     """e^(x / 2^16) in Q.16 for Q.16 integers x in [-2^31, 0]."""
     x = np.asarray(x, dtype=np.int64)
     assert np.all((x <= 0) & (x >= I32_MIN))
-    return exp2_q16(rshr(x * LOG2E_Q30, 30))
+    return exp2_q16(rshr(x * LOG2E_Q30, 30), table)
 
 
-def softplus_q16(x):
+def softplus_q16(x, table=None):
     """SoftPlus in Q.16: e^(-|x|) + max(x, 0), saturated to int32."""
     x = np.asarray(x, dtype=np.int64)
     assert np.all((x >= I32_MIN) & (x <= I32_MAX))
-    return sat32(exp_q16(-np.abs(x)) + np.maximum(x, 0))
+    return sat32(exp_q16(-np.abs(x), table) + np.maximum(x, 0))
 
 
-def silu_q16(x):
+def silu_q16(x, table=None):
     """SiLU in Q.16 through the exponential unit and SiLU(x) = x + SiLU(-x)."""
     x = np.asarray(x, dtype=np.int64)
     assert np.all((x >= I32_MIN) & (x <= I32_MAX))
     xn = -np.abs(x)                               # <= 0
-    e = exp_q16(xn)                               # e^xn in [0, 2^16]
+    e = exp_q16(xn, table)                        # e^xn in [0, 2^16] (chord table)
     sig = (e << 16) // ((1 << 16) + e)            # sigma(xn) in Q.16, floor
     sn = rshr(xn * sig, 16)                       # SiLU(xn)
     return np.where(x > 0, x + sn, sn)

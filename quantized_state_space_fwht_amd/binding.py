@@ -106,6 +106,7 @@ _SIGS = {
     "fm_layer_keep_intermediates": (None, [_c_i32]),
     "fm_layer_set_timing_events": (None, [_vp, _vp]),
     "fm_layer_collect_quant_stats": (None, [_vp]),
+    "fm_nau_eval_knots": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i64, _vp]),
     "fm_quant_per_tensor_workspace_size": (_c_sz, []),
     "fm_quant_per_tensor": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
     "fm_smooth_scales_workspace_size": (_c_sz, [_c_i64]),
@@ -153,6 +154,13 @@ def fm_hadamard_quant(x, mode, scoe, sshift, q, scale_out, amax_stats=None, ws=N
     _check(lib.fm_hadamard_quant(_ptr(x), rows, k, mode, scoe, sshift, _ptr(q), _ptr(scale_out),
                                  _ptr(amax_stats), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)))
+
+
+def fm_nau_eval_knots(fn, knots_q30, x, y, stream=None):
+    """knots_q30: nine Q.30 integers (host, any sequence)."""
+    arr = (ctypes.c_int64 * 9)(*[int(v) for v in knots_q30])
+    _check(lib.fm_nau_eval_knots(fn, ctypes.cast(arr, ctypes.c_void_p), _ptr(x), _ptr(y),
+                                 x.numel(), _stream(stream)))
 
 
 def fm_quant_per_tensor(x, q, scale_out, ws=None, stream=None):

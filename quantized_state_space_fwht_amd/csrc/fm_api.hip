@@ -302,6 +302,25 @@ fm_status fm_nau_eval(fm_nau_fn fn, const int32_t* x, int32_t* y, int64_t n, hip
     return nau_run((int)fn, x, y, n, stream);
 }
 
+fm_status fm_nau_eval_knots(fm_nau_fn fn, const int64_t* knots_q30, const int32_t* x, int32_t* y,
+                            int64_t n, hipStream_t stream) {
+    const char* who = "fm_nau_eval_knots";
+    g_err[0] = 0;
+    if (fn != FM_NAU_EXP && fn != FM_NAU_SOFTPLUS && fn != FM_NAU_SILU)
+        return fail(FM_ERR_MODE, "%s: bad function %d", who, (int)fn);
+    if (!knots_q30) return fail(FM_ERR_NULL, "%s: knots is NULL", who);
+    // bounds of the exact float64 evaluation: products below 2^53 for knots
+    // under 2^32, and the exponent clamp at -18 needs Y[0] < 2^31
+    for (int i = 0; i < 9; ++i)
+        if (knots_q30[i] <= ((int64_t)1 << 29) || knots_q30[i] >= ((int64_t)1 << 32) ||
+            (i == 0 && knots_q30[0] >= ((int64_t)1 << 31)))
+            return fail(FM_ERR_SHAPE, "%s: knot %d = %lld outside (2^29, 2^32) (knot 0: < 2^31)",
+                        who, i, (long long)knots_q30[i]);
+    if (n < 0) return fail(FM_ERR_SHAPE, "%s: n < 0", who);
+    if (n > 0 && (!x || !y)) return fail(FM_ERR_NULL, "%s: x or y is NULL", who);
+    return nau_run((int)fn, x, y, n, stream, knots_q30);
+}
+
 // ---------------------------------------------------------------- fm_gate_norm_quant
 size_t fm_gate_norm_quant_workspace_size(int64_t rows, int64_t d_inner) {
     if (rows < 0 || d_inner < 0) return 0;

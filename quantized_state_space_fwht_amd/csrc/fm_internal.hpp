@@ -213,7 +213,9 @@ struct GateArgs {
 };
 fm_status gate_run(const GateArgs& a, hipStream_t s);
 
-fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s);
+// knots: nullable host array of nine Q.30 values replacing the chord table
+fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s,
+                  const int64_t* knots = nullptr);
 
 // outlier-study baselines (fm_outlier.hip); n a multiple of 4, ws as documented in fm.h
 fm_status quant_per_tensor_run(const float* x, int64_t n, int8_t* q, float* scale_out,

@@ -6,10 +6,21 @@
 
 namespace fm {
 
+// nine Q.30 knots of the 2^f unit, by value (use == 0: the chord table)
+struct NauKnots {
+    int64_t y[9];
+    int use;
+};
+
 __global__ __launch_bounds__(256) void nau_eval_kernel(int fn, const int32_t* __restrict__ x,
-                                                       int32_t* __restrict__ y, int64_t n) {
+                                                       int32_t* __restrict__ y, int64_t n,
+                                                       NauKnots kn) {
     __shared__ NauLds tab;
-    nau_lds_init(tab);
+    if (kn.use) {
+        if (threadIdx.x < 9) tab.y[threadIdx.x] = (double)kn.y[threadIdx.x];
+    } else {
+        nau_lds_init(tab);
+    }
     __syncthreads();
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -22,11 +33,17 @@ __global__ __launch_bounds__(256) void nau_eval_kernel(int fn, const int32_t* __
     }
 }
 
-fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s) {
+fm_status nau_run(int fn, const int32_t* x, int32_t* y, int64_t n, hipStream_t s,
+                  const int64_t* knots) {
     if (n == 0) return FM_OK;
     int64_t g = (n + 255) / 256;
     if (g > 8192) g = 8192;
-    nau_eval_kernel<<<(unsigned)g, 256, 0, s>>>(fn, x, y, n);
+    NauKnots kn{};
+    if (knots) {
+        for (int i = 0; i < 9; ++i) kn.y[i] = knots[i];
+        kn.use = 1;
+    }
+    nau_eval_kernel<<<(unsigned)g, 256, 0, s>>>(fn, x, y, n, kn);
     return check_launch("nau_eval_kernel");
 }
 

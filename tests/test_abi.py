@@ -160,3 +160,19 @@ def test_outlier_baselines_validation(lib):
     h.argtypes = [vp, i64, i64, vp, i32, vp, vp]
     assert h(fake, 4, 0, fake, 1, fake, None) == FM_ERR_SHAPE
     assert h(fake, 4, 8, None, 1, fake, None) == FM_ERR_NULL
+
+
+def test_nau_knots_validation(lib):
+    """Knot tables outside the range of the exact evaluation are rejected."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.fm_nau_eval_knots
+    f.argtypes = [i32, vp, vp, vp, i64, vp]
+    fake = 1 << 20
+    good = [int(round(2 ** (i / 8) * 2 ** 30)) for i in range(9)]
+    arr = lambda v: ctypes.cast((ctypes.c_int64 * 9)(*v), vp)
+    assert f(0, None, fake, fake, 4, None) == FM_ERR_NULL
+    assert f(7, arr(good), fake, fake, 4, None) == FM_ERR_MODE
+    assert f(0, arr(good[:8] + [1 << 32]), fake, fake, 4, None) == FM_ERR_SHAPE
+    assert f(0, arr([1 << 31] + good[1:]), fake, fake, 4, None) == FM_ERR_SHAPE   # knot 0
+    assert f(0, arr([1 << 29] + good[1:]), fake, fake, 4, None) == FM_ERR_SHAPE
+    assert f(0, arr(good), fake, fake, -1, None) == FM_ERR_SHAPE

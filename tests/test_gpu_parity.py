@@ -430,3 +430,24 @@ def test_static_stack_calibration_and_prefill(B):
     stack.prefill(dev(u[:, :L0]))
     outs = [host(stack.decode(dev(u[:, t]))) for t in range(L0, 48)]
     assert np.array_equal(np.stack(outs, axis=1), h_o[:, L0:]), "continuation"
+
+
+@pytest.mark.parametrize("fit", ["lsq", "minimax"])
+@pytest.mark.parametrize("fn", ["exp", "softplus", "silu"])
+def test_nau_other_knot_tables(B, fn, fit):
+    """The unit with the fitted knot tables (alternative coefficients of the
+    same form): every Q.16 input in [-2^22, 2^22] plus random int32 values,
+    against the oracle evaluated with the same table."""
+    knots = synth.nau_knot_tables()[fit]
+    rng = np.random.default_rng(19)
+    x = np.concatenate([np.arange(-(1 << 22), (1 << 22) + 1, dtype=np.int64),
+                        rng.integers(-(1 << 31), (1 << 31), size=1 << 18),
+                        np.array([-(1 << 31), (1 << 31) - 1, -1, 0, 1])]).astype(np.int32)
+    code = {"exp": B.NAU_EXP, "softplus": B.NAU_SOFTPLUS, "silu": B.NAU_SILU}[fn]
+    t_y = torch.empty(x.shape, dtype=torch.int32, device="cuda")
+    B.fm_nau_eval_knots(code, knots, dev(x), t_y)
+    xi = x.astype(np.int64)
+    want = {"exp": lambda: O.exp_q16(np.minimum(xi, 0), knots),
+            "softplus": lambda: O.softplus_q16(xi, knots),
+            "silu": lambda: O.silu_q16(xi, knots)}[fn]()
+    assert_exact(host(t_y), want, f"{fn} {fit}")

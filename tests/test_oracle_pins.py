@@ -601,3 +601,31 @@ def test_outlier_channel_hurts_naive_int8_most():
     w = (rng.standard_normal((384, 512)) * 0.02).astype(np.float32)
     err = {k: OL.output_error(OL.scheme(x, w, k)["out"], x, w) for k in ("naive", "hadamard", "smooth")}
     assert err["hadamard"] < 0.5 * err["naive"] and err["smooth"] < 0.5 * err["naive"], err
+
+
+# --------------------------------------------------------------------------- f4 NAU fits
+def test_nau_fitted_tables_against_the_chord():
+    """The unit's form P(f) = Y_i + (Y_(i+1) - Y_i) r over the eighths of an
+    octave: the chord table's largest relative error against 2^f follows the
+    interpolation bound (ln 2 / 8)^2 / 8 for a convex exponential (about
+    9.4e-4); the minimax table roughly halves it (the chord's error has one
+    sign, minimax equioscillates); the least-squares table has the smallest
+    summed squared error.  The chord table passed explicitly gives the default
+    unit."""
+    tabs = synth.nau_knot_tables()
+    f = np.arange(1 << 16) / 65536.0
+    k = np.arange(1 << 16)
+    seg, r = k >> 13, (k & 8191) / 8192.0
+
+    def rel(t):
+        y = t.astype(np.float64) / 2 ** 30
+        return (y[seg] * (1 - r) + y[seg + 1] * r) / 2.0 ** f - 1
+
+    bound = (np.log(2) / 8) ** 2 / 8
+    e_c, e_l, e_m = (rel(tabs[n]) for n in ("chord", "lsq", "minimax"))
+    assert 0.9 * bound < np.max(np.abs(e_c)) <= bound * 1.001
+    assert np.max(np.abs(e_m)) < 0.55 * np.max(np.abs(e_c))
+    assert np.sum(e_l ** 2) < np.sum(e_m ** 2) < np.sum(e_c ** 2)
+    assert np.array_equal(tabs["chord"], O.EXP2_TABLE_Q30)
+    x = np.arange(-(1 << 18), 1, 97, dtype=np.int64)
+    assert np.array_equal(O.exp_q16(x, tabs["chord"]), O.exp_q16(x))
