@@ -33,7 +33,7 @@ from .gate_norm import gate, rmsnorm_fixed_order
 from . import quant_stats as QS
 from .hadamard import hadamard_quant, hadamard_scale
 from .linear import quantize_weight, w8a8_gemm
-from .scan import dt_dA, ssm_scan_pot
+from .scan import dt_dA, narrow_state, ssm_scan_pot, widen_state
 
 
 @dataclass
@@ -150,11 +150,20 @@ def layer_prefill(prep, shape, u, mode="dynamic", qp=None, collect=False):
     return out.reshape(Bsz, L, dm), r, cache, st
 
 
-def layer_decode(prep, shape, u_t, cache, mode="dynamic", qp=None):
-    """One token per sequence, u_t [Bsz, d_model], continuing from ``cache``."""
+def layer_decode(prep, shape, u_t, cache, mode="dynamic", qp=None, state_fmt=None):
+    """One token per sequence, u_t [Bsz, d_model], continuing from ``cache``.
+
+    ``state_fmt`` = (bits, shift): the cache's "ssm_state" holds narrow codes
+    (scan.narrow_state); the step widens them, runs as with an int32 state, and
+    narrows the new state into the returned cache."""
     u_t = np.asarray(u_t, dtype=np.float32)
     Bsz, dm = u_t.shape
+    if state_fmt is not None:
+        bits, shift = state_fmt
+        cache = dict(cache, ssm_state=widen_state(cache["ssm_state"], shift))
     out, r, new_cache, st = _mixer(prep, shape, u_t, Bsz, 1, mode, qp, cache, cache["p"])
+    if state_fmt is not None:
+        new_cache["ssm_state"] = narrow_state(new_cache["ssm_state"], bits, shift)
     return out.reshape(Bsz, dm), r, new_cache, st
 
 
@@ -182,8 +191,10 @@ def stack_prefill(preps, shape, u, mode="dynamic", qps=None, qstats=None):
     return h, caches, stats
 
 
-def stack_decode(preps, shape, u_t, caches, mode="dynamic", qps=None):
-    """One decode step through the stack; returns (h_t [Bsz, d_model], new caches)."""
+def stack_decode(preps, shape, u_t, caches, mode="dynamic", qps=None, state_fmts=None):
+    """One decode step through the stack; returns (h_t [Bsz, d_model], new caches).
+
+    ``state_fmts``: one (bits, shift) per layer for narrow state caches."""
     h = np.asarray(u_t, dtype=np.float32)
     dm = h.shape[-1]
     ones = np.ones((dm,), dtype=np.float32)
@@ -191,7 +202,8 @@ def stack_decode(preps, shape, u_t, caches, mode="dynamic", qps=None):
     for li, prep in enumerate(preps):
         xin = rmsnorm_fixed_order(h, ones)
         out, _, cache, _ = layer_decode(prep, shape, xin, caches[li], mode,
-                                        None if qps is None else qps[li])
+                                        None if qps is None else qps[li],
+                                        None if state_fmts is None else state_fmts[li])
         h = h + out
         new_caches.append(cache)
     return h, new_caches

@@ -70,3 +70,61 @@ def ssm_scan_pot(x_q, B_q, C_q, dt, dA, D_q16, p_B, p_C, state_in=None):
         y_acc = np.sum(Cm[:, t, None, None, :] * h, axis=-1)            # exact int64
         y[:, t] = sat32(rshr(y_acc, ky) + rshr(D[None, :, None] * x[:, t], 8))
     return y, h
+
+
+# --- narrower state cache ----------------------------------------------------
+# The state width sets the decode step's memory traffic (the state is read and
+# written once per token).  Reading for a cache narrower than int32, in the
+# method's own power-of-two idiom: the cache holds codes c of `bits` bits on
+# the coarser grid 2^shift of the state's own (exponent p_h - shift), rounded
+# half up and saturated:
+#     c = clamp(floor((h + 2^(shift-1)) / 2^shift), -2^(bits-1), 2^(bits-1) - 1)
+# (no rounding term when shift = 0); a step widens the cache to h = c * 2^shift,
+# takes the exact step of ssm_scan_pot (its y from the int32 state of the step)
+# and narrows the new state for the cache.  Stored layout: int16, or the low 24
+# bits of the two's-complement code as three little-endian bytes, in the state's
+# [batch, nheads, headdim, dstate] order.
+
+STATE_BITS = (16, 24)
+
+
+def narrow_state(h, bits, shift):
+    """int32 state values -> cache codes of `bits` bits on the grid 2^shift."""
+    assert bits in STATE_BITS and 0 <= shift <= 32 - bits
+    h = np.asarray(h, dtype=np.int64)
+    c = (h + ((1 << shift) >> 1)) >> shift        # floor division: half up
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    return np.clip(c, lo, hi)
+
+
+def widen_state(c, shift):
+    """Cache codes -> state values on the int32 grid (exact: c * 2^shift)."""
+    return np.asarray(c, dtype=np.int64) << shift
+
+
+def pack_state(c, bits):
+    """Codes -> the stored bytes (little endian, 2 or 3 bytes per value)."""
+    c = np.asarray(c, dtype=np.int64).reshape(-1)
+    nb = bits // 8
+    u = c & ((1 << bits) - 1)
+    out = np.zeros((c.size, nb), dtype=np.uint8)
+    for k in range(nb):
+        out[:, k] = (u >> (8 * k)) & 0xFF
+    return out.reshape(-1)
+
+
+def unpack_state(buf, bits):
+    """The stored bytes -> codes (sign-extended from `bits`)."""
+    nb = bits // 8
+    b = np.asarray(buf, dtype=np.uint8).reshape(-1, nb).astype(np.int64)
+    u = np.zeros(b.shape[0], dtype=np.int64)
+    for k in range(nb):
+        u |= b[:, k] << (8 * k)
+    return np.where(u >= (1 << (bits - 1)), u - (1 << bits), u)
+
+
+def state_shift_for(amax, bits, headroom=1):
+    """Smallest shift whose codes hold |h| <= amax * 2^headroom without clipping:
+    max(0, bitlength(amax) + headroom - (bits - 1)), at most 32 - bits."""
+    need = int(amax).bit_length() + int(headroom)
+    return min(max(0, need - (bits - 1)), 32 - bits)

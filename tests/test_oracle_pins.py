@@ -629,3 +629,71 @@ def test_nau_fitted_tables_against_the_chord():
     assert np.array_equal(tabs["chord"], O.EXP2_TABLE_Q30)
     x = np.arange(-(1 << 18), 1, 97, dtype=np.int64)
     assert np.array_equal(O.exp_q16(x, tabs["chord"]), O.exp_q16(x))
+
+
+def test_narrow_state_hand_cases():
+    # half up onto the grid 2^4, saturation at the int16 range (worked by hand)
+    h = [24, 23, -24, -25, 8, -8, 7, -9, 1 << 20, -(1 << 31)]
+    assert O.narrow_state(h, 16, 4).tolist() == [2, 1, -1, -2, 1, 0, 0, -1, 32767, -32768]
+    assert O.narrow_state([5, -5, 1 << 23, -(1 << 23) - 1], 24, 0).tolist() == \
+        [5, -5, (1 << 23) - 1, -(1 << 23)]
+    assert O.pack_state([-2, 0x123456, -(1 << 23)], 24).tolist() == \
+        [0xFE, 0xFF, 0xFF, 0x56, 0x34, 0x12, 0x00, 0x00, 0x80]
+    assert O.pack_state([-1, 0x1234], 16).tolist() == [0xFF, 0xFF, 0x34, 0x12]
+    # the smallest shift keeping amax * 2 unclipped
+    assert [O.state_shift_for(a, b) for a, b in
+            [(2 ** 20 - 1, 16), (2 ** 31 - 1, 16), (100, 24), (2 ** 22, 24)]] == [6, 16, 0, 1]
+
+
+def test_narrow_state_against_float_rounding_and_library_bytes():
+    rng = np.random.default_rng(5)
+    h = np.concatenate([rng.integers(-(1 << 31), 1 << 31, size=20000),
+                        rng.integers(-3000, 3000, size=5000)])
+    for bits in (16, 24):
+        lim = 1 << (bits - 1)
+        for s in (0, 3, 32 - bits):
+            c = O.narrow_state(h, bits, s)
+            # half up in float64 (exact: |h| < 2^31, division by a power of two)
+            want = np.clip(np.floor(h.astype(np.float64) / 2.0 ** s + 0.5), -lim, lim - 1)
+            assert np.array_equal(c, want.astype(np.int64))
+            inside = np.abs(c) < lim - 1
+            err = h[inside] - O.widen_state(c[inside], s)
+            assert np.all(err >= -(1 << s) // 2) and np.all(err < max(1, (1 << s) // 2))
+            buf = O.pack_state(c, bits)
+            if bits == 16:
+                lib = c.astype("<i2").view(np.uint8)
+            else:
+                lib = c.astype("<i4").view(np.uint8).reshape(-1, 4)[:, :3].reshape(-1)
+            assert np.array_equal(buf, lib)
+            assert np.array_equal(O.unpack_state(buf, bits), c)
+
+
+def test_narrow_state_decode_reduces_to_int32_and_is_bounded():
+    w, prep, u, qp = _static_setup()
+    L = u.shape[1]
+    _, _, cache, _ = O.layer_prefill(prep, w.shape, u[:, :L - 1], "static", qp)
+    amax = int(np.max(np.abs(cache["ssm_state"])))
+    assert 1 << 15 <= amax < 1 << 23
+    o32, r32, c32, _ = O.layer_decode(prep, w.shape, u[:, L - 1], cache, "static", qp)
+    # 24 bits on the state's own grid: every value fits, so the step is the int32 step
+    n24 = dict(cache, ssm_state=O.narrow_state(cache["ssm_state"], 24, 0))
+    o24, _, c24, _ = O.layer_decode(prep, w.shape, u[:, L - 1], n24, "static", qp, (24, 0))
+    assert np.array_equal(o24, o32)
+    assert np.array_equal(c24["ssm_state"], c32["ssm_state"])
+    # 16 bits: the cache error |e| <= 2^(s-1) moves the stepped state by at most
+    # 2^(s-1) + 1 (dA <= 2^16, one floor), so y moves by at most
+    # sum_n |C_n| (2^(s-1) + 1) / 2^(p_B + p_C) + 1
+    s = O.state_shift_for(amax, 16)
+    assert s >= 1
+    n16 = dict(cache, ssm_state=O.narrow_state(cache["ssm_state"], 16, s))
+    _, r16, c16, _ = O.layer_decode(prep, w.shape, u[:, L - 1], n16, "static", qp, (16, s))
+    _, _, p_B, p_C = r32["p"]
+    Bsz = u.shape[0]
+    csum = np.abs(np.asarray(r32["C_q"], np.int64)).reshape(Bsz, -1).sum(axis=1)
+    bound = csum * ((1 << (s - 1)) + 1) / 2.0 ** (p_B + p_C) + 1
+    dy = np.abs(np.asarray(r16["y"], np.int64) - np.asarray(r32["y"], np.int64)).reshape(Bsz, -1)
+    assert np.all(dy <= bound[:, None])
+    assert np.any(dy > 0)
+    # the new cache holds the 16-bit codes of a state within 2^(s-1) + 1 of the int32 step's
+    dh = np.abs(O.widen_state(c16["ssm_state"], s) - c32["ssm_state"])
+    assert np.all(dh <= (1 << s) + 1)
