@@ -83,47 +83,167 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=3):
                       f"({w.batch}x{w.seqlen} tokens, seeds as the GPU run), {dt:.1f} s"}
 
 
-def decode_bench(torch, configs, synth, warmup=8, max_steps=None):
+def decode_bench(torch, configs, synth, warmup=8, max_steps=None, narrow_bits=(16, 24)):
     """Decode tokens/s of the 64-layer 2.7B-shaped stack, batch 16.
 
     A 1024-token seeding prefill fills the caches; then the workload's 512 one-token
     steps run as replays of one captured graph (every layer of a step): `warmup`
     untimed, the rest timed with HIP events.  Roofline: HBM, with the algorithmic
-    bytes of a layer step = SSM state read + written (int32) + both int8 weight
-    matrices + the conv window read + written."""
+    bytes of a layer step = SSM state read + written + both int8 weight matrices +
+    the conv window read + written.  The int32 state is the method's; the same
+    stack then runs again from a fresh seeding prefill with each narrow state
+    width in `narrow_bits` (codes on a per-layer power-of-two grid)."""
     import numpy as np
     from quantized_state_space_fwht_amd.runtime import DecodeGraph, Mamba2Stack
     w = configs.get(DECODE_WORKLOAD)
     s = w.shape
     log(f"bench: building decode stack {w.name} ({w.description})")
     stack = Mamba2Stack(s, (synth.workload_params(w, l) for l in range(w.nlayers)))
-    stack.prefill(torch.from_numpy(synth.workload_activations(w)).cuda(), with_cache=True)
-    g = DecodeGraph(stack, w.batch)
+    u0 = torch.from_numpy(synth.workload_activations(w)).cuda()
     nsteps = w.decode_steps if max_steps is None else min(w.decode_steps, warmup + max_steps)
     inputs = torch.from_numpy(np.stack([synth.decode_step_input(w, t)
                                         for t in range(nsteps)])).cuda()
-    for t in range(warmup):
-        g.step(inputs[t])
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for t in range(warmup, nsteps):
-        g.step(inputs[t])
-    e1.record()
-    torch.cuda.synchronize()
-    timed = nsteps - warmup
-    ms = e0.elapsed_time(e1) / timed
-    state_b = 2 * w.batch * s.nheads * s.headdim * s.dstate * 4
     weight_b = s.d_in_proj * s.d_model + s.d_model * s.d_inner
     conv_b = 2 * w.batch * s.conv_ch * 3
-    step_bytes = w.nlayers * (state_b + weight_b + conv_b)
-    gbs = step_bytes / (ms / 1e3) / 1e9
-    return {"workload": w.name, "value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s",
-            "ms_per_token_step": round(ms, 4), "batch": w.batch, "layers": w.nlayers,
-            "steps_timed": timed, "steps_warmup": warmup, "seeding_prefill": w.seqlen,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "bytes_per_token_step": step_bytes}}
+
+    def run(bits):
+        stack.prefill(u0, with_cache=True)
+        shifts = stack.narrow_states(bits) if bits != 32 else None
+        g = DecodeGraph(stack, w.batch)
+        for t in range(warmup):
+            g.step(inputs[t])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warmup, nsteps):
+            g.step(inputs[t])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (nsteps - warmup)
+        state_b = 2 * w.batch * s.nheads * s.headdim * s.dstate * bits // 8
+        step_bytes = w.nlayers * (state_b + weight_b + conv_b)
+        gbs = step_bytes / (ms / 1e3) / 1e9
+        res = {"value": round(w.batch / (ms / 1e3), 1), "unit": "tokens/s",
+               "ms_per_token_step": round(ms, 4),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "bytes_per_token_step": step_bytes}}
+        if shifts is not None:
+            res["state_shift_range"] = [min(shifts), max(shifts)]
+        del g
+        return res
+
+    out = {"workload": w.name, **run(32), "batch": w.batch, "layers": w.nlayers,
+           "steps_timed": nsteps - warmup, "steps_warmup": warmup, "seeding_prefill": w.seqlen,
+           "state": "int32"}
+    out["narrow_state"] = {f"int{b}": run(b) for b in narrow_bits}
+    return out
+
+
+def study_state(torch, configs, synth, B, steps=128):
+    """Narrow decode-state caches: accuracy against the int32 state over decode steps.
+
+    The 64-layer 2.7B-shaped stack (batch 16) is seeded by the same 1024-token
+    prefill, then decodes the same `steps` tokens with the int32 state, 24-bit
+    and 16-bit codes (each layer's shift chosen from its prefill state with one
+    bit of headroom), and, as a control, with the int32 state and every decode
+    input scaled by (1 + 2^-20).  Reported per step: the relative L2 error of the stack's
+    contribution h_t - u_t against the int32 run; after the last step, for layers
+    0, 31 and 63, the relative L2 error of the widened state and the share of
+    codes at the saturation limits; the relative L2 error of layer 0's mixer output,
+    whose input is the same in every run, isolates the format's own error from
+    its propagation through the stack.  The oracle beside recomputes a 2.7B-shaped
+    layer from an 8-token prefill through three 16-bit decode steps."""
+    import numpy as np
+    import oracle as O
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer, Mamba2Stack
+    w = configs.get(DECODE_WORKLOAD)
+    s = w.shape
+    log(f"study: building {w.name} ({w.description})")
+    stack = Mamba2Stack(s, (synth.workload_params(w, l) for l in range(w.nlayers)))
+    u0 = torch.from_numpy(synth.workload_activations(w)).cuda()
+    inputs = torch.from_numpy(np.stack([synth.decode_step_input(w, t)
+                                        for t in range(steps)])).cuda()
+    probe_layers = (0, w.nlayers // 2 - 1, w.nlayers - 1)
+    runs = {}
+    # "ctl": the int32 state with every decode input scaled by (1 + 2^-20), the
+    # stack's own sensitivity to a perturbation far below any state rounding
+    for bits in (32, 24, 16, "ctl"):
+        stack.prefill(u0, with_cache=True)
+        shifts = stack.narrow_states(bits) if bits in (16, 24) else [0] * w.nlayers
+        xs = inputs * (1.0 + 2.0 ** -20) if bits == "ctl" else inputs
+        contrib, mix0 = [], []
+        t0 = time.perf_counter()
+        for t in range(steps):
+            h = xs[t].contiguous()
+            for l, layer in enumerate(stack.layers):
+                nxt = layer.decode(h)
+                if l == 0:
+                    mix0.append((nxt - h).double())  # layer 0: the same input in every run
+                h = nxt
+            contrib.append((h - xs[t]).double())
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t0
+        states, sat = {}, {}
+        for l in probe_layers:
+            layer = stack.layers[l]
+            st = layer.wide_state() if bits in (16, 24) else layer.cache_t["ssm_state"]
+            states[l] = st.double()
+            if bits in (16, 24):
+                lim = (1 << (bits - 1))
+                c = torch.div(st.long(), 1 << shifts[l], rounding_mode="floor")
+                sat[l] = float(((c == lim - 1) | (c == -lim)).double().mean().item())
+        runs[bits] = {"contrib": torch.stack(contrib), "mix0": torch.stack(mix0),
+                      "states": states, "sat": sat,
+                      "shifts": shifts, "sec": sec}
+        log(f"study: {bits} done ({sec:.1f} s eager)")
+    ref = runs[32]
+    report = {"study": "narrow_state", "workload": w.name, "steps": steps,
+              "seeding_prefill": w.seqlen, "batch": w.batch, "layers": w.nlayers, "widths": {}}
+    marks = [t for t in (0, 1, 7, 31, 63, steps - 1) if t < steps]
+    for bits in (24, 16, "ctl"):
+        r = runs[bits]
+        d = r["contrib"] - ref["contrib"]
+        rel = (d.flatten(1).norm(dim=1) / ref["contrib"].flatten(1).norm(dim=1)).cpu().numpy()
+        d0 = r["mix0"] - ref["mix0"]
+        rel0 = (d0.flatten(1).norm(dim=1) / ref["mix0"].flatten(1).norm(dim=1)).cpu().numpy()
+        report["widths"]["int32_input_x(1+2^-20)" if bits == "ctl" else f"int{bits}"] = {
+            "shift_min": min(r["shifts"]), "shift_max": max(r["shifts"]),
+            "shift_mean": round(float(np.mean(r["shifts"])), 2),
+            "contrib_rel_l2_at_step": {str(t + 1): float(rel[t]) for t in marks},
+            "contrib_rel_l2_max": float(rel.max()),
+            "layer0_out_rel_l2_at_step": {str(t + 1): float(rel0[t]) for t in marks},
+            "layer0_out_rel_l2_max": float(rel0.max()),
+            "state_rel_l2_after": {str(l): float(((r["states"][l] - ref["states"][l]).norm()
+                                                  / ref["states"][l].norm()).item())
+                                   for l in probe_layers},
+            "saturated_code_share_after": {str(l): r["sat"].get(l, 0.0) for l in probe_layers}}
+    # the oracle beside: one 2.7B-shaped layer, 8-token prefill, three 16-bit steps
+    wl = configs.with_len(w, w.batch, 11)
+    params = synth.workload_params(wl, 0)
+    u = synth.workload_activations(wl)
+    t0 = time.perf_counter()
+    prep = O.prepare_layer(params)
+    _, _, cache, _ = O.layer_prefill(prep, s, u[:, :8])
+    sh = O.state_shift_for(int(np.max(np.abs(cache["ssm_state"]))), 16)
+    cache["ssm_state"] = O.narrow_state(cache["ssm_state"], 16, sh)
+    want = []
+    for t in range(8, 11):
+        o, _, cache, _ = O.layer_decode(prep, s, u[:, t], cache, state_fmt=(16, sh))
+        want.append(o)
+    osec = time.perf_counter() - t0
+    layer = Mamba2Layer(s, params)
+    layer.prefill(torch.from_numpy(u[:, :8]).cuda())
+    agree = layer.narrow_state(16) == sh
+    for t, o in zip(range(8, 11), want):
+        got = layer.decode(torch.from_numpy(np.ascontiguousarray(u[:, t])).cuda())
+        agree = agree and bool(np.array_equal(got.cpu().numpy(), o))
+    agree = agree and bool(np.array_equal(layer.cache_t["ssm_codes"].cpu().numpy(),
+                                          O.pack_state(cache["ssm_state"], 16)))
+    report["oracle_beside"] = {"sample": "one 2.7B-shaped layer, batch 16, 8-token prefill, "
+                                         "three decode steps with 16-bit codes",
+                               "seconds": round(osec, 2), "agrees": agree}
+    return report
 
 
 def study_scales(torch, configs, synth, B):
@@ -411,6 +531,9 @@ def main():
     ap.add_argument("--study-outliers", action="store_true",
                     help="run the outlier study (Hadamard against plain per-tensor and smoothed "
                          "W8A8 on the projections' inputs) instead of the benchmark")
+    ap.add_argument("--study-state", action="store_true",
+                    help="run the narrow decode-state accuracy study (int32 against 24- and "
+                         "16-bit codes on the 2.7B-shaped stack) instead of the benchmark")
     ap.add_argument("--study-nau", action="store_true",
                     help="run the 2^v unit's coefficient study (chord, least-squares and "
                          "minimax tables) instead of the benchmark")
@@ -431,6 +554,10 @@ def main():
     if args.study_scales:
         torch.cuda.set_device(0)
         print(json.dumps(study_scales(torch, configs, synth, B)), flush=True)
+        return
+    if args.study_state:
+        torch.cuda.set_device(0)
+        print(json.dumps(study_state(torch, configs, synth, B)), flush=True)
         return
     if args.study_nau:
         torch.cuda.set_device(0)

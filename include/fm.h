@@ -324,6 +324,53 @@ fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights*
                                  const fm_cache* cache, float* out_t, fm_qparams* qp,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Narrow state caches.  The decode step reads and writes the whole SSM state
+ * once per token, so the state's width sets that step's memory traffic; in
+ * the method's power-of-two idiom (review page "What carries the argument":
+ * every rescaling in the SSM block is a shift) a cache narrower than int32
+ * holds the state on a grid 2^shift coarser than its own:
+ *   code c = clamp(floor((h + 2^(shift-1)) / 2^shift), -2^(bits-1), 2^(bits-1)-1)
+ * (no rounding term at shift 0), bits 16 or 24, 0 <= shift <= 32 - bits.
+ * Stored in the state's [batch, nheads, headdim, dstate] order: int16, or the
+ * low 24 bits of the two's complement as three little-endian bytes.
+ * A narrow decode step widens each code to h = c * 2^shift, takes the step of
+ * fm_ssm_scan_pot exactly as with an int32 state (y from the stepped int32
+ * state), and stores the new state's codes.  bits 24 with shift 0 gives the
+ * int32 results whenever every state value fits in 24 bits.
+ * Bad bits / shift: FM_ERR_SHAPE.
+ * ---------------------------------------------------------------------- */
+typedef struct fm_cache_narrow {
+    int8_t* conv_state;   /* as fm_cache */
+    void* ssm_state;      /* codes, fm_state_narrow_bytes(count, state_bits) bytes, 16-byte aligned */
+    int32_t* p;           /* as fm_cache */
+    int32_t state_bits;   /* 16 or 24 */
+    int32_t state_shift;  /* 0 .. 32 - state_bits */
+} fm_cache_narrow;
+
+/* Bytes of `count` codes of `bits` bits (0 for count <= 0 or other bits). */
+size_t fm_state_narrow_bytes(int64_t count, int32_t bits);
+
+/* int32 state [count] (device) -> codes (device, fm_state_narrow_bytes bytes):
+ * converts a prefill's cache->ssm_state for a narrow decode. */
+fm_status fm_state_narrow(const int32_t* state, int64_t count, int32_t bits, int32_t shift,
+                          void* codes, hipStream_t stream);
+
+/* codes -> int32 state values c * 2^shift (device). */
+fm_status fm_state_widen(const void* codes, int64_t count, int32_t bits, int32_t shift,
+                         int32_t* state, hipStream_t stream);
+
+/* *amax (device uint32, max-accumulated: zero it first) = max(*amax, max |state|),
+ * |INT32_MIN| counting as 2^31: the input for choosing `shift`. */
+fm_status fm_state_absmax(const int32_t* state, int64_t count, uint32_t* amax, hipStream_t stream);
+
+/* fm_mamba2_layer_decode with a narrow state cache (updated in place). */
+fm_status fm_mamba2_layer_decode_narrow(const fm_layer_desc* d, const fm_layer_weights* w,
+                                        const fm_static_params* sp, const float* u_t,
+                                        int64_t batch, const fm_cache_narrow* cache, float* out_t,
+                                        fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
 /* Byte offsets, inside the layer workspace, of the intermediates the last
  * prefill / decode call on that workspace left there (for parity tests):
  * u_q [T, d_model] i8, v [T, dip] f32 (in_proj out: z|xBC|dt), xbc_q [T, ch] i8,

@@ -61,6 +61,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("conv_state", _vp), ("ssm_state", _vp), ("p", _vp)]
 
 
+class CacheNarrow(ctypes.Structure):
+    _fields_ = [("conv_state", _vp), ("ssm_state", _vp), ("p", _vp), ("state_bits", _c_i32),
+                ("state_shift", _c_i32)]
+
+
 class LayerTaps(ctypes.Structure):
     _fields_ = [(n, _c_sz) for n in ("u_q", "v", "xbc_q", "x_q", "b_q", "c_q", "y", "g_q",
                                      "normed", "dt", "da")]
@@ -114,6 +119,15 @@ _SIGS = {
     "fm_scale_columns": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _c_i32, _vp, _vp]),
     "fm_qparams_from_stats": (ctypes.c_int, [ctypes.POINTER(QParams),
                                              ctypes.POINTER(StaticParams)]),
+    "fm_state_narrow_bytes": (_c_sz, [_c_i64, _c_i32]),
+    "fm_state_narrow": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
+    "fm_state_widen": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
+    "fm_state_absmax": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
+    "fm_mamba2_layer_decode_narrow": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
+                                                     ctypes.POINTER(LayerWeights),
+                                                     ctypes.POINTER(StaticParams), _vp, _c_i64,
+                                                     ctypes.POINTER(CacheNarrow), _vp, _vp, _vp,
+                                                     _c_sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -161,6 +175,32 @@ def fm_nau_eval_knots(fn, knots_q30, x, y, stream=None):
     arr = (ctypes.c_int64 * 9)(*[int(v) for v in knots_q30])
     _check(lib.fm_nau_eval_knots(fn, ctypes.cast(arr, ctypes.c_void_p), _ptr(x), _ptr(y),
                                  x.numel(), _stream(stream)))
+
+
+def fm_state_narrow(state, bits, shift, codes, stream=None):
+    """int32 state tensor -> codes (a uint8 device tensor of fm_state_narrow_bytes bytes)."""
+    n = state.numel()
+    if codes.numel() * codes.element_size() < lib.fm_state_narrow_bytes(n, bits):
+        raise ValueError("codes buffer too small")
+    _check(lib.fm_state_narrow(_ptr(state), n, bits, shift, _ptr(codes), _stream(stream)))
+
+
+def fm_state_widen(codes, bits, shift, state, stream=None):
+    n = state.numel()
+    if codes.numel() * codes.element_size() < lib.fm_state_narrow_bytes(n, bits):
+        raise ValueError("codes buffer too small")
+    _check(lib.fm_state_widen(_ptr(codes), n, bits, shift, _ptr(state), _stream(stream)))
+
+
+def fm_state_absmax(state, amax, stream=None):
+    """amax: one-element int32/uint32 device tensor, max-accumulated."""
+    _check(lib.fm_state_absmax(_ptr(state), state.numel(), _ptr(amax), _stream(stream)))
+
+
+def state_shift_for(amax, bits, headroom=1):
+    """The smallest shift whose codes hold amax * 2^headroom unclipped."""
+    need = int(amax).bit_length() + int(headroom)
+    return min(max(0, need - (bits - 1)), 32 - bits)
 
 
 def fm_quant_per_tensor(x, q, scale_out, ws=None, stream=None):

@@ -452,6 +452,67 @@ fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights*
     return layer_run(d, w, sp, u_t, batch, 1, out_t, cache, qp, workspace, true, stream);
 }
 
+static fm_status check_state_fmt(int32_t bits, int32_t shift, const char* who) {
+    if (bits != 16 && bits != 24) return fail(FM_ERR_SHAPE, "%s: state_bits %d not 16 or 24", who, bits);
+    if (shift < 0 || shift > 32 - bits)
+        return fail(FM_ERR_SHAPE, "%s: state_shift %d not in [0, %d]", who, shift, 32 - bits);
+    return FM_OK;
+}
+
+fm_status fm_mamba2_layer_decode_narrow(const fm_layer_desc* d, const fm_layer_weights* w,
+                                        const fm_static_params* sp, const float* u_t,
+                                        int64_t batch, const fm_cache_narrow* cache, float* out_t,
+                                        fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    const char* who = "fm_mamba2_layer_decode_narrow";
+    g_err[0] = 0;
+    fm_status st = check_layer_call(d, w, sp, u_t, batch, 1, out_t, qp, workspace,
+                                    workspace_bytes, who);
+    if (st != FM_OK) return st;
+    if (!cache || !cache->conv_state || !cache->ssm_state || !cache->p)
+        return fail(FM_ERR_NULL, "%s: decode needs a complete cache", who);
+    if ((st = check_state_fmt(cache->state_bits, cache->state_shift, who)) != FM_OK) return st;
+    if (!aligned(cache->ssm_state, 16))
+        return fail(FM_ERR_SHAPE, "%s: ssm_state must be 16-byte aligned", who);
+    const fm_cache c32{cache->conv_state, (int32_t*)cache->ssm_state, cache->p};
+    return layer_run(d, w, sp, u_t, batch, 1, out_t, &c32, qp, workspace, true, stream,
+                     cache->state_bits, cache->state_shift);
+}
+
+size_t fm_state_narrow_bytes(int64_t count, int32_t bits) {
+    return count > 0 && (bits == 16 || bits == 24) ? (size_t)count * (size_t)(bits / 8) : 0;
+}
+
+fm_status fm_state_narrow(const int32_t* state, int64_t count, int32_t bits, int32_t shift,
+                          void* codes, hipStream_t stream) {
+    const char* who = "fm_state_narrow";
+    g_err[0] = 0;
+    fm_status st = check_state_fmt(bits, shift, who);
+    if (st != FM_OK) return st;
+    if (count < 0) return fail(FM_ERR_SHAPE, "%s: count %lld < 0", who, (long long)count);
+    if (count > 0 && (!state || !codes)) return fail(FM_ERR_NULL, "%s: NULL pointer", who);
+    return state_narrow_run(state, count, bits, shift, codes, stream);
+}
+
+fm_status fm_state_widen(const void* codes, int64_t count, int32_t bits, int32_t shift,
+                         int32_t* state, hipStream_t stream) {
+    const char* who = "fm_state_widen";
+    g_err[0] = 0;
+    fm_status st = check_state_fmt(bits, shift, who);
+    if (st != FM_OK) return st;
+    if (count < 0) return fail(FM_ERR_SHAPE, "%s: count %lld < 0", who, (long long)count);
+    if (count > 0 && (!state || !codes)) return fail(FM_ERR_NULL, "%s: NULL pointer", who);
+    return state_widen_run(codes, count, bits, shift, state, stream);
+}
+
+fm_status fm_state_absmax(const int32_t* state, int64_t count, uint32_t* amax, hipStream_t stream) {
+    const char* who = "fm_state_absmax";
+    g_err[0] = 0;
+    if (count < 0) return fail(FM_ERR_SHAPE, "%s: count %lld < 0", who, (long long)count);
+    if (!amax || (count > 0 && !state)) return fail(FM_ERR_NULL, "%s: NULL pointer", who);
+    return state_absmax_run(state, count, amax, stream);
+}
+
 fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len,
                                fm_layer_taps* taps) {
     g_err[0] = 0;

@@ -408,6 +408,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
             }
             continue;
         }
+        if (kConv && col0 >= ep.amax_c1) {  // dt: the raw value, dt and the decay
+            if (ok) {
+                const float o = (float)v * sab;
+                ep.out[row * ep.ld_out + col] = o;
+                const int64_t h = col - ep.amax_c1, nh = P.n - ep.amax_c1;
+                const int32_t dt_in = f2i_sat(rintf((o + ep.dt_bias[h]) * 65536.0f));
+                const int32_t dt = nau_softplus_f(dt_in, tab);
+                ep.dt_out[row * nh + h] = dt;
+                ep.da_out[row * nh + h] =
+                    nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)ep.a_q16[h], 16)), tab);
+            }
+            continue;
+        }
         if (ok) {
             if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
             if (ep.out) {

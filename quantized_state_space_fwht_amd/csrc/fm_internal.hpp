@@ -109,6 +109,12 @@ struct GemmEpilogue {
     int32_t* conv_amax_q16 = nullptr;   // int[3]: max |SiLU| of x, B, C (Q.16)
     int64_t d_inner = 0, dstate = 0;
     float* sz_out = nullptr;            // [rows, d_inner]: SiLU(z) of the z columns [0, amax_c0)
+    // dt columns [amax_c1, n): also dt = SoftPlus(dt_in) and dA = e^(dt * A) in Q.16
+    // (row-major [rows, n - amax_c1]), for the one-step scan
+    const float* dt_bias = nullptr;
+    const int32_t* a_q16 = nullptr;
+    int32_t* dt_out = nullptr;
+    int32_t* da_out = nullptr;
     bool write_xbc = false;             // also write the float z and xBC columns to out
     // one-token step (few-rows kernel only): A comes as rotated float rows with
     // their row maxima; every workgroup forms the tensor scale c from them
@@ -184,6 +190,11 @@ struct ScanArgs {
     int32_t* dt_out;           // [T, H] written by the dt / decay prologue (required)
     int32_t* da_out;
     bool dt_ready;             // dt_out / da_out already hold them: no prologue launch
+    // One-step scans only: state_in / state_out hold codes of state_bits bits
+    // (16: int16; 24: three little-endian bytes) on the grid 2^state_shift of
+    // the state's own, behind the int32 pointer type.  0 or 32: int32 values.
+    int state_bits;
+    int state_shift;
 };
 // workspace of the scan (none: B and C are staged through LDS)
 size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);
@@ -231,9 +242,18 @@ void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_tap
 void set_keep_intermediates(bool on);
 void set_timing_events(void* start, void* stop);
 void set_quant_stats(fm_quant_stats* qs);
+// state_bits / state_shift: the decode cache's state format (ScanArgs)
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
-                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s);
+                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s,
+                    int state_bits = 32, int state_shift = 0);
+
+// narrow state codes (fm_state.hip)
+fm_status state_narrow_run(const int32_t* h, int64_t n, int bits, int shift, void* out,
+                           hipStream_t s);
+fm_status state_widen_run(const void* c, int64_t n, int bits, int shift, int32_t* out,
+                          hipStream_t s);
+fm_status state_absmax_run(const int32_t* h, int64_t n, uint32_t* amax, hipStream_t s);
 fm_status prepare_run(const fm_layer_desc* d, const float* w_in, const float* w_out,
                       const float* conv_w, const float* conv_b, const float* a, const float* dv,
                       int8_t* w_in_q, float* s_w_in, int8_t* w_out_q, float* s_w_out,

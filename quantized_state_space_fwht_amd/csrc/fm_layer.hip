@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs
 // Shared body of prefill (len tokens, fresh state) and decode (len = 1, cache).
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
-                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s) {
+                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s, int state_bits,
+                    int state_shift) {
     const int64_t T = batch * len;
     const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads, P = d->headdim;
     const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
@@ -287,6 +288,10 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.dstate = N;
             ep.sz_out = w.sz;
             ep.write_xbc = g_keep;
+            ep.dt_bias = W->dt_bias;  // 6 fused: dt and the decay for the scan step
+            ep.a_q16 = W->a_q16;
+            ep.dt_out = w.dt;
+            ep.da_out = w.da;
         }
         if ((st = gemm_run(w.u_q, W->w_in_q, T, dip, dm, ep, s)) != FM_OK) return st;
     }
@@ -349,7 +354,9 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.y = w.y;
         a.dt_out = w.dt;
         a.da_out = w.da;
-        a.dt_ready = !step;  // formed by the conv launch (a one-step scan forms its own)
+        a.dt_ready = true;  // formed by the conv launch, or by in_proj's epilogue (step)
+        a.state_bits = decode ? state_bits : 32;
+        a.state_shift = decode ? state_shift : 0;
         hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
         g_ev_start = g_ev_stop = nullptr;
         if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) return st;

@@ -365,55 +365,172 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
 // ---------------------------------------------------------------- one step (decode)
 // len == 1: the work is reading and writing the state once, so the kernel is
 // laid out for coalesced state traffic with many bytes in flight.  A wave owns
-// (b, head) and kStepPairs pairs of rows p: in each pair lanes 0..31 hold the
+// (b, head) and G pairs of rows p: in each pair lanes 0..31 hold the
 // row p0, lanes 32..63 the row p0 + 1, lane l the NN2 = N/32 consecutive
 // n = NN2*(l % 32) .. (16 or 8 contiguous bytes of state).  Every load of the
 // wave (state rows, x, B, C, dt) is issued before any arithmetic.  dt and the
 // decay of (b, head) are computed by every lane (wave-uniform); the wave with
 // p0 = 0 stores them.  The update takes the clamped form always.
-constexpr int kStepPairs = 2;
+//
+// SB < 32: the cache holds SB-bit codes on the grid 2^shift (int16, or
+// three little-endian bytes per value): a lane's NN2 values are 2*NN2 or
+// 3*NN2 contiguous bytes, loaded and stored as whole words (16-bit words for
+// NN2 = 2 at 24 bits, whose 6-byte runs are only 2-byte aligned), widened to
+// c * 2^shift before the step and narrowed half up with saturation after it.
+//
+// The load phase of a wave is one batch of state loads, so the kernel runs at
+// (bytes in flight per wave) x (waves resident) / latency: narrower codes get
+// more row pairs per wave (G) to keep the bytes in flight of the int32 case.
+template <int SB>
+constexpr int step_pairs() { return SB == 32 ? 2 : 4; }
 
-template <int NN2>
+template <int NN2, int SB>
+struct StateIo {
+    // wave-uniform byte address of element e (the per-lane offsets below stay 32-bit)
+    __device__ static const uint8_t* at(const void* base, int64_t e) {
+        return static_cast<const uint8_t*>(base) + e * (SB / 8);
+    }
+    __device__ static uint8_t* at(void* base, int64_t e) {
+        return static_cast<uint8_t*>(base) + e * (SB / 8);
+    }
+    // load NN2 values at element offset `off` (a multiple of NN2) from `row` as int32 states
+    __device__ static void load(const uint8_t* row, int off, int shift, int32_t* h) {
+        const uint8_t* p0 = row + off * (SB / 8);
+        if constexpr (SB == 32) {
+            const int32_t* p = reinterpret_cast<const int32_t*>(p0);
+#pragma unroll
+            for (int j = 0; j < NN2; ++j) h[j] = __builtin_nontemporal_load(p + j);
+        } else if constexpr (SB == 16) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(p0);
+#pragma unroll
+            for (int k = 0; k < NN2 / 2; ++k) {
+                const uint32_t w = __builtin_nontemporal_load(p + k);
+                h[2 * k] = (int32_t)((uint32_t)(int32_t)(int16_t)(w & 0xFFFFu) << shift);
+                h[2 * k + 1] = (int32_t)((uint32_t)((int32_t)w >> 16) << shift);
+            }
+        } else {  // 24 bits
+            uint32_t v[NN2];
+            if constexpr (NN2 == 4) {  // 12 bytes at a multiple of 12: three words
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(p0);
+                const uint32_t w0 = __builtin_nontemporal_load(p);
+                const uint32_t w1 = __builtin_nontemporal_load(p + 1);
+                const uint32_t w2 = __builtin_nontemporal_load(p + 2);
+                v[0] = w0;
+                v[1] = (w0 >> 24) | (w1 << 8);
+                v[2] = (w1 >> 16) | (w2 << 16);
+                v[3] = w2 >> 8;
+            } else {  // 6 bytes at a multiple of 6: three 16-bit words
+                const uint16_t* p = reinterpret_cast<const uint16_t*>(p0);
+                const uint32_t u0 = __builtin_nontemporal_load(p);
+                const uint32_t u1 = __builtin_nontemporal_load(p + 1);
+                const uint32_t u2 = __builtin_nontemporal_load(p + 2);
+                v[0] = u0 | (u1 << 16);
+                v[1] = (u1 >> 8) | (u2 << 8);
+            }
+#pragma unroll
+            for (int j = 0; j < NN2; ++j)
+                h[j] = (int32_t)((uint32_t)__builtin_amdgcn_sbfe((int32_t)v[j], 0, 24) << shift);
+        }
+    }
+    // narrow (SB < 32) and store NN2 int32 state values at element offset `off` of `row`
+    __device__ static void store(uint8_t* row, int off, int shift, const int32_t* h) {
+        uint8_t* p0 = row + off * (SB / 8);
+        if constexpr (SB == 32) {
+            int32_t* p = reinterpret_cast<int32_t*>(p0);
+#pragma unroll
+            for (int j = 0; j < NN2; ++j) __builtin_nontemporal_store(h[j], p + j);
+        } else {
+            constexpr int32_t lo = -(1 << (SB - 1)), hi = (1 << (SB - 1)) - 1;
+            // floor((h + 2^(s-1)) / 2^s) = (h >> s) + bit s-1 of h, in int32 (s >= 1)
+            const int sm1 = shift > 0 ? shift - 1 : 0;
+            const int32_t rbit = shift > 0 ? 1 : 0;
+            uint32_t c[NN2];
+#pragma unroll
+            for (int j = 0; j < NN2; ++j) {
+                const int32_t q = (h[j] >> shift) + ((h[j] >> sm1) & rbit);
+                c[j] = (uint32_t)(q < lo ? lo : (q > hi ? hi : q));
+            }
+            if constexpr (SB == 16) {
+                uint32_t* p = reinterpret_cast<uint32_t*>(p0);
+#pragma unroll
+                for (int k = 0; k < NN2 / 2; ++k)
+                    __builtin_nontemporal_store((c[2 * k] & 0xFFFFu) | (c[2 * k + 1] << 16), p + k);
+            } else if constexpr (NN2 == 4) {
+                uint32_t* p = reinterpret_cast<uint32_t*>(p0);
+                __builtin_nontemporal_store((c[0] & 0xFFFFFFu) | (c[1] << 24), p);
+                __builtin_nontemporal_store(((c[1] >> 8) & 0xFFFFu) | (c[2] << 16), p + 1);
+                __builtin_nontemporal_store(((c[2] >> 16) & 0xFFu) | (c[3] << 8), p + 2);
+            } else {
+                uint16_t* p = reinterpret_cast<uint16_t*>(p0);
+                __builtin_nontemporal_store((uint16_t)(c[0] & 0xFFFFu), p);
+                __builtin_nontemporal_store((uint16_t)(((c[0] >> 16) & 0xFFu) | ((c[1] & 0xFFu) << 8)),
+                                            p + 1);
+                __builtin_nontemporal_store((uint16_t)((c[1] >> 8) & 0xFFFFu), p + 2);
+            }
+        }
+    }
+};
+
+// kDtReady: dt and the decay of each (b, head) are already in dt_out / da_out
+// (formed with the in_proj or conv launch) and load as two wave-uniform words;
+// otherwise every lane forms them through the 2^v unit and the wave with
+// p0 = 0 stores them.  Wave indices are wave-uniform 32-bit values (the
+// launcher checks batch * nheads * headdim / (2G) < 2^31) and every address
+// is a wave-uniform base plus a small per-lane offset, so the vector unit
+// spends its instructions on the update itself.
+template <int NN2, int SB, bool kDtReady>
 __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
     __shared__ NauLds tab;
-    nau_lds_init(tab);
+    if constexpr (!kDtReady) nau_lds_init(tab);
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int H = (int)A.nheads, P = (int)A.headdim;
     constexpr int N = 32 * NN2;
-    constexpr int G = kStepPairs;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, head, pair group)
+    constexpr int G = step_pairs<SB>();
     const int ngrp = P / (2 * G);
-    const bool live = wid < A.batch * H * ngrp;  // the tail of the last workgroup idles
-    const int64_t wq = live ? wid : 0;
-    const int grp = (int)(wq % ngrp);
-    const int head = (int)((wq / ngrp) % H);
-    const int64_t b = wq / ((int64_t)ngrp * H);
+    const int wid = (int)blockIdx.x * 4 + wave;
+    const bool live = wid < (int)A.batch * H * ngrp;  // the tail of the last workgroup idles
+    const int wq = live ? wid : 0;
+    const int grp = wq % ngrp;
+    const int bh = wq / ngrp;  // b * H + head: the (token, head) row, len 1
+    const int head = bh % H;
+    const int b = bh / H;
     const int r = lane >> 5, l32 = lane & 31;
     const int n0 = NN2 * l32;
-    const int64_t q = b * H + head;  // token row b (len 1)
+    const int64_t prow = (int64_t)bh * P + 2 * grp * G;  // first row p of this wave
     // every load first
-    const float raw = A.dt_raw[b * A.dt_stride + head];
-    const float bias = A.dt_bias[head];
-    const int32_t aq = A.a_q16[head];
-    int32_t bw, cw;  // NN2 int8 codes each
-    if constexpr (NN2 == 4) {
-        bw = *reinterpret_cast<const int32_t*>(A.bm + b * N + n0);
-        cw = *reinterpret_cast<const int32_t*>(A.cm + b * N + n0);
+    int32_t dt, da;
+    float raw = 0.0f, bias = 0.0f;
+    int32_t aq = 0;
+    if constexpr (kDtReady) {
+        dt = A.dt_out[bh];
+        da = A.da_out[bh];
     } else {
-        bw = *reinterpret_cast<const int16_t*>(A.bm + b * N + n0);
-        cw = *reinterpret_cast<const int16_t*>(A.cm + b * N + n0);
+        raw = A.dt_raw[(int64_t)b * A.dt_stride + head];
+        bias = A.dt_bias[head];
+        aq = A.a_q16[head];
     }
+    int32_t bw, cw;  // NN2 int8 codes each
+    const int8_t* bmr = A.bm + (int64_t)b * N;
+    const int8_t* cmr = A.cm + (int64_t)b * N;
+    if constexpr (NN2 == 4) {
+        bw = *reinterpret_cast<const int32_t*>(bmr + n0);
+        cw = *reinterpret_cast<const int32_t*>(cmr + n0);
+    } else {
+        bw = *reinterpret_cast<const int16_t*>(bmr + n0);
+        cw = *reinterpret_cast<const int16_t*>(cmr + n0);
+    }
+    const int8_t* xr = A.x + prow;
+    const uint8_t* sin = A.state_in ? StateIo<NN2, SB>::at((const void*)A.state_in, prow * N)
+                                    : nullptr;
     int32_t xi[G];
     int32_t hs[G][NN2];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int p = 2 * (grp * G + g) + r;
-        xi[g] = A.x[q * P + p];
-        const int64_t sidx = (q * P + p) * N + n0;
-        if (A.state_in) {
+        xi[g] = xr[2 * g + r];
+        if (sin) {
             // the state streams through once: non-temporal loads and stores
-#pragma unroll
-            for (int j = 0; j < NN2; ++j) hs[g][j] = __builtin_nontemporal_load(A.state_in + sidx + j);
+            StateIo<NN2, SB>::load(sin, (2 * g + r) * N + n0, A.state_shift, hs[g]);
         } else {
 #pragma unroll
             for (int j = 0; j < NN2; ++j) hs[g][j] = 0;
@@ -421,11 +538,12 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
     }
     const int ky = A.p[2] + A.p[3];
     const int32_t dq = A.d_q16[head];
-    __syncthreads();  // the chord table
-    // dt and the decay of (b, head)
-    const int32_t dt_in = f2i_sat(rintf((raw + bias) * 65536.0f));
-    const int32_t dt = nau_softplus_f(dt_in, tab);
-    const int32_t da = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)aq, 16)), tab);
+    if constexpr (!kDtReady) {
+        __syncthreads();  // the chord table
+        const int32_t dt_in = f2i_sat(rintf((raw + bias) * 65536.0f));
+        dt = nau_softplus_f(dt_in, tab);
+        da = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)aq, 16)), tab);
+    }
     const double dd = (double)da * 0x1p-16;
     double bj[NN2], cj[NN2];
 #pragma unroll
@@ -448,18 +566,15 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
         }
     }
     if (!live) return;
-    if (grp == 0 && lane == 0) {
-        A.dt_out[q] = dt;
-        A.da_out[q] = da;
+    if (!kDtReady && grp == 0 && lane == 0) {
+        A.dt_out[bh] = dt;
+        A.da_out[bh] = da;
     }
+    uint8_t* sout = A.state_out ? StateIo<NN2, SB>::at((void*)A.state_out, prow * N) : nullptr;
+    int32_t* yr = A.y + prow;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int p = 2 * (grp * G + g) + r;
-        const int64_t sidx = (q * P + p) * N + n0;
-        if (A.state_out) {
-#pragma unroll
-            for (int j = 0; j < NN2; ++j) __builtin_nontemporal_store(hs[g][j], A.state_out + sidx + j);
-        }
+        if (sout) StateIo<NN2, SB>::store(sout, (2 * g + r) * N + n0, A.state_shift, hs[g]);
         // sum over the 32 lanes of this half-wave: DPP rotations inside each
         // 16-lane row, then one swap of the row pair (the terms are integers
         // below 2^46, so any order gives the exact sum)
@@ -473,7 +588,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
             const double ya = __builtin_floor(__builtin_fma(yy, __builtin_ldexp(1.0, -ky), 0.5));
             const double yd =
                 __builtin_floor(__builtin_fma((double)dq * (double)xi[g], 0x1p-8, 0.5));
-            A.y[q * P + p] =
+            yr[2 * g + r] =
                 (int32_t)__builtin_fmin(__builtin_fmax(ya + yd, -2147483648.0), 2147483647.0);
         }
     }
@@ -486,15 +601,32 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
     if (a.dstate != 64 && a.dstate != 128)
         return fail(FM_ERR_SHAPE, "scan: dstate %lld not in {64, 128}", (long long)a.dstate);
     if (a.len == 1) {  // one step: state traffic only
-        if (a.headdim % (2 * kStepPairs))
+        const int sb = a.state_bits == 16 || a.state_bits == 24 ? a.state_bits : 32;
+        if (sb != 32 && !a.dt_ready)
+            return fail(FM_ERR_SHAPE, "scan: a narrow state needs dt and the decay formed first");
+        const int gp = sb == 16 ? step_pairs<16>() : (sb == 24 ? step_pairs<24>() : step_pairs<32>());
+        if (a.headdim % (2 * gp))
             return fail(FM_ERR_SHAPE, "scan: headdim %lld not a multiple of %d", (long long)a.headdim,
-                        2 * kStepPairs);
-        const int64_t waves = a.batch * a.nheads * (a.headdim / (2 * kStepPairs));
+                        2 * gp);
+        const int64_t waves = a.batch * a.nheads * (a.headdim / (2 * gp));
         const unsigned g1 = (unsigned)((waves + 3) / 4);
         if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
             return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
-        if (a.dstate == 128) scan_step_kernel<4><<<g1, 256, 0, s>>>(a);
-        else scan_step_kernel<2><<<g1, 256, 0, s>>>(a);
+        if (waves >= ((int64_t)1 << 31))
+            return fail(FM_ERR_SHAPE, "scan: %lld waves for one step", (long long)waves);
+        if (!a.dt_ready) {  // the standalone call forms dt and the decay itself
+            if (a.dstate == 128) scan_step_kernel<4, 32, false><<<g1, 256, 0, s>>>(a);
+            else scan_step_kernel<2, 32, false><<<g1, 256, 0, s>>>(a);
+        } else if (sb == 16) {
+            if (a.dstate == 128) scan_step_kernel<4, 16, true><<<g1, 256, 0, s>>>(a);
+            else scan_step_kernel<2, 16, true><<<g1, 256, 0, s>>>(a);
+        } else if (sb == 24) {
+            if (a.dstate == 128) scan_step_kernel<4, 24, true><<<g1, 256, 0, s>>>(a);
+            else scan_step_kernel<2, 24, true><<<g1, 256, 0, s>>>(a);
+        } else {
+            if (a.dstate == 128) scan_step_kernel<4, 32, true><<<g1, 256, 0, s>>>(a);
+            else scan_step_kernel<2, 32, true><<<g1, 256, 0, s>>>(a);
+        }
         fm_status st1 = check_launch("scan_step_kernel");
         if (st1 != FM_OK) return st1;
         if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess)

@@ -82,6 +82,7 @@ class Mamba2Layer:
         self._ws = None
         self._ws_key = None
         self.cache = None
+        self.ncache = None  # narrow state cache (narrow_state), used by decode when set
 
     # ------------------------------------------------------------ memory
     def workspace_for(self, batch, length):
@@ -105,6 +106,32 @@ class Mamba2Layer:
                              self.cache_t["ssm_state"].data_ptr(), self.cache_t["p"].data_ptr())
         return self.cache
 
+    def narrow_state(self, bits, shift=None, headroom=1):
+        """Convert the cache's int32 SSM state (as the last prefill left it) to
+        `bits`-bit codes on the grid 2^shift; later decode calls use them.
+        shift None: the smallest that holds 2^headroom times the current
+        largest |state| unclipped.  Returns the shift."""
+        st = self.cache_t["ssm_state"]
+        if shift is None:
+            amax = torch.zeros(1, dtype=torch.int32, device=self.device)
+            B.fm_state_absmax(st, amax)
+            shift = B.state_shift_for(int(amax.item()) & 0xFFFFFFFF, bits, headroom)
+        codes = torch.empty(B.lib.fm_state_narrow_bytes(st.numel(), bits), dtype=torch.uint8,
+                            device=self.device)
+        B.fm_state_narrow(st, bits, shift, codes)
+        self.cache_t["ssm_codes"] = codes
+        self.ncache = B.CacheNarrow(self.cache_t["conv_state"].data_ptr(), codes.data_ptr(),
+                                    self.cache_t["p"].data_ptr(), bits, shift)
+        return shift
+
+    def wide_state(self):
+        """The narrow cache's state as int32 values c * 2^shift (a new tensor)."""
+        st = self.cache_t["ssm_state"]
+        out = torch.empty_like(st)
+        B.fm_state_widen(self.cache_t["ssm_codes"], self.ncache.state_bits,
+                         self.ncache.state_shift, out)
+        return out
+
     def set_static(self, sp: "B.StaticParams"):
         self.static = sp
         self.desc.mode = B.STATIC
@@ -127,6 +154,7 @@ class Mamba2Layer:
         ws = self.workspace_for(batch, length)
         cache = None
         if with_cache:
+            self.ncache = None  # the prefill writes the int32 state
             if self.cache is None or self.cache_t["ssm_state"].shape[0] != batch:
                 self.alloc_cache(batch)
             cache = ctypes.byref(self.cache)
@@ -144,6 +172,12 @@ class Mamba2Layer:
             out = torch.empty_like(u_t)
         ws = self.workspace_for(batch, 1)
         sp = ctypes.byref(self.static) if self.static is not None else None
+        if self.ncache is not None:
+            B._check(B.lib.fm_mamba2_layer_decode_narrow(
+                ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u_t.data_ptr(), batch,
+                ctypes.byref(self.ncache), out.data_ptr(), self.qp.data_ptr(), ws.data_ptr(),
+                ws.numel(), B._stream(stream)))
+            return out
         B._check(B.lib.fm_mamba2_layer_decode(
             ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u_t.data_ptr(), batch,
             ctypes.byref(self.cache), out.data_ptr(), self.qp.data_ptr(), ws.data_ptr(),
@@ -204,6 +238,10 @@ class Mamba2Stack:
             layer.decode(h, out=nxt, stream=stream)
             h = nxt
         return h
+
+    def narrow_states(self, bits, headroom=1):
+        """Every layer's cache to `bits`-bit codes (Mamba2Layer.narrow_state); the shifts."""
+        return [layer.narrow_state(bits, None, headroom) for layer in self.layers]
 
     def calibrate(self, inputs):
         """Dynamic passes over `inputs` (list of [B, L, dm] device tensors), then static."""

@@ -176,3 +176,48 @@ def test_nau_knots_validation(lib):
     assert f(0, arr([1 << 31] + good[1:]), fake, fake, 4, None) == FM_ERR_SHAPE   # knot 0
     assert f(0, arr([1 << 29] + good[1:]), fake, fake, 4, None) == FM_ERR_SHAPE
     assert f(0, arr(good), fake, fake, -1, None) == FM_ERR_SHAPE
+
+
+def test_narrow_state_validation(lib):
+    """Bad code widths, shifts, counts and pointers are rejected before any launch."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.fm_state_narrow_bytes.restype = ctypes.c_size_t
+    lib.fm_state_narrow_bytes.argtypes = [i64, i32]
+    assert lib.fm_state_narrow_bytes(10, 24) == 30 and lib.fm_state_narrow_bytes(10, 16) == 20
+    assert lib.fm_state_narrow_bytes(10, 8) == 0 and lib.fm_state_narrow_bytes(-1, 16) == 0
+    fake = 1 << 20
+    for name in ("fm_state_narrow", "fm_state_widen"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, i64, i32, i32, vp, vp]
+        assert f(fake, 4, 8, 0, fake, None) == FM_ERR_SHAPE, _last_error(lib)
+        assert f(fake, 4, 32, 0, fake, None) == FM_ERR_SHAPE
+        assert f(fake, 4, 16, 17, fake, None) == FM_ERR_SHAPE
+        assert f(fake, 4, 24, 9, fake, None) == FM_ERR_SHAPE
+        assert f(fake, 4, 24, -1, fake, None) == FM_ERR_SHAPE
+        assert f(fake, -1, 16, 0, fake, None) == FM_ERR_SHAPE
+        assert f(None, 4, 16, 0, fake, None) == FM_ERR_NULL
+        assert f(None, 0, 16, 0, None, None) == FM_OK  # nothing to convert
+    f = lib.fm_state_absmax
+    f.argtypes = [vp, i64, vp, vp]
+    assert f(fake, 4, None, None) == FM_ERR_NULL
+    assert f(fake, -1, fake, None) == FM_ERR_SHAPE
+
+    class CacheNarrow(ctypes.Structure):
+        _fields_ = [("conv_state", vp), ("ssm_state", vp), ("p", vp), ("state_bits", i32),
+                    ("state_shift", i32)]
+
+    lib.fm_mamba2_layer_workspace_size.restype = ctypes.c_size_t
+    lib.fm_mamba2_layer_workspace_size.argtypes = [ctypes.POINTER(Desc), i64, i64]
+    d = Desc(768, 1536, 24, 64, 128, 4, 0, 0)
+    ws = lib.fm_mamba2_layer_workspace_size(ctypes.byref(d), 4, 1)
+    weights = (vp * 11)(*([fake] * 11))
+    f = lib.fm_mamba2_layer_decode_narrow
+    f.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, ctypes.POINTER(CacheNarrow), vp, vp, vp,
+                  ctypes.c_size_t, vp]
+    call = lambda c: f(ctypes.byref(d), ctypes.cast(weights, vp), None, fake, 4,
+                       None if c is None else ctypes.byref(c), 2 * fake, fake, fake, ws, None)
+    assert call(None) == FM_ERR_NULL
+    assert call(CacheNarrow(fake, None, fake, 16, 0)) == FM_ERR_NULL
+    assert call(CacheNarrow(fake, fake, fake, 8, 0)) == FM_ERR_SHAPE, _last_error(lib)
+    assert call(CacheNarrow(fake, fake, fake, 16, 17)) == FM_ERR_SHAPE
+    assert call(CacheNarrow(fake, fake + 8, fake, 16, 2)) == FM_ERR_SHAPE  # 16-byte alignment

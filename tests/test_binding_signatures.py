@@ -23,7 +23,8 @@ def binding_sigs():
     end = txt.index("\n}\n", start)
     env = {"ctypes": ctypes, "_c_i64": ctypes.c_int64, "_c_i32": ctypes.c_int32,
            "_c_sz": ctypes.c_size_t, "_vp": ctypes.c_void_p}
-    for cls in ("LayerDesc", "StaticParams", "QParams", "LayerTaps", "LayerWeights", "Cache"):
+    for cls in ("LayerDesc", "StaticParams", "QParams", "LayerTaps", "LayerWeights", "Cache",
+                "CacheNarrow"):
         env[cls] = type(cls, (ctypes.Structure,), {"_fields_": []})
     exec(txt[start:end + 2], env)
     return env["_SIGS"]

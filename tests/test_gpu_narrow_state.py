@@ -1,0 +1,153 @@
+"""GPU parity of the narrow decode-state caches against the oracle.
+
+The conversions (int32 state <-> 16- or 24-bit codes on the grid 2^shift)
+must give the oracle's codes and bytes exactly; a decode that continues a
+prefill from a narrow cache must give the oracle's outputs, codes and conv
+window bit for bit at every step.  Every oracle input is seeded and synthetic
+(or the oracle's own prefill); nothing the GPU computed is fed to the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from quantized_state_space_fwht_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from quantized_state_space_fwht_amd import binding
+    return binding
+
+
+def dev(a):
+    return torch.as_tensor(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_exact(got, want, what):
+    got = np.asarray(got).astype(np.int64)
+    want = np.asarray(want).astype(np.int64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[0]}: " \
+                          f"gpu {got[tuple(bad[0])]} oracle {want[tuple(bad[0])]}"
+
+
+@pytest.mark.parametrize("count", [0, 1, 7, 1_000_003])
+def test_state_codes_against_the_oracle(B, count):
+    rng = np.random.default_rng(count + 1)
+    h = rng.integers(-(1 << 31), 1 << 31, size=count).astype(np.int64)
+    special = np.array([-(1 << 31), (1 << 31) - 1, 0, 16, -16, 15, -17, 1 << 20, -(1 << 22)])
+    h[:min(count, special.size)] = special[:count]
+    small = rng.integers(-3000, 3000, size=count // 2)  # ties and small codes at every shift
+    h[count - small.size:] = small
+    hd = dev(h.astype(np.int32))
+    for bits in (16, 24):
+        for shift in (0, 5, 32 - bits):
+            nbytes = B.lib.fm_state_narrow_bytes(count, bits)
+            assert nbytes == count * bits // 8
+            codes = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            B.fm_state_narrow(hd, bits, shift, codes)
+            c_o = O.narrow_state(h, bits, shift)
+            assert_exact(host(codes), O.pack_state(c_o, bits), f"codes {bits}/{shift}")
+            back = torch.empty(count, dtype=torch.int32, device="cuda")
+            B.fm_state_widen(codes, bits, shift, back)
+            assert_exact(host(back), O.widen_state(c_o, shift), f"widened {bits}/{shift}")
+    amax = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.fm_state_absmax(hd, amax)
+    want = int(np.max(np.abs(h))) if count else 0
+    assert int(host(amax)[0]) & 0xFFFFFFFF == want
+
+
+def _decode_case(B, wname, batch, L0, steps, bits, shift, mode="dynamic"):
+    """Prefill L0 tokens on both sides, narrow the cache, then `steps` decode steps."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+    w = configs.with_len(configs.get(wname), batch, L0 + steps)
+    s = w.shape
+    params = synth.workload_params(w, 0)
+    u = synth.workload_activations(w)
+    prep = O.prepare_layer(params)
+    qp = None
+    if mode == "static":
+        qps, _ = O.calibrate_stack([prep], s, [synth.workload_activations(w, seed=sd)
+                                                for sd in (41, 42)])
+        qp = qps[0]
+    _, _, cache, _ = O.layer_prefill(prep, s, u[:, :L0], mode, qp)
+    layer = Mamba2Layer(s, params)
+    if mode == "static":
+        layer.set_static(B.StaticParams(tuple(qp.scoe), tuple(qp.sshift), tuple(qp.p)))
+    layer.prefill(dev(u[:, :L0]))
+    amax = int(np.max(np.abs(cache["ssm_state"])))
+    got_shift = layer.narrow_state(bits, shift)
+    want_shift = O.state_shift_for(amax, bits) if shift is None else shift
+    assert got_shift == want_shift
+    cache = dict(cache, ssm_state=O.narrow_state(cache["ssm_state"], bits, want_shift))
+    assert_exact(host(layer.cache_t["ssm_codes"]), O.pack_state(cache["ssm_state"], bits),
+                 "codes after the prefill")
+    fmt = (bits, want_shift)
+    for t in range(L0, L0 + steps):
+        o_out, _, cache, _ = O.layer_decode(prep, s, u[:, t], cache, mode, qp, fmt)
+        g_out = layer.decode(dev(u[:, t]))
+        assert np.array_equal(host(g_out), o_out), f"decode step {t}"
+        assert_exact(host(layer.cache_t["ssm_codes"]), O.pack_state(cache["ssm_state"], bits),
+                     f"codes step {t}")
+        assert_exact(host(layer.cache_t["conv_state"]), cache["conv_state"], f"conv step {t}")
+    assert_exact(host(layer.wide_state()), O.widen_state(cache["ssm_state"], want_shift),
+                 "widened final state")
+    return want_shift
+
+
+# dstate 64 (tiny) and 128 (130M): both lane layouts of the step kernel; shift None
+# is the automatic choice, 0 at 16 bits saturates, 3 at 24 bits rounds
+@pytest.mark.parametrize("wname,batch", [("tiny_layer", 3), ("m130m_layer", 2)])
+@pytest.mark.parametrize("bits,shift", [(16, None), (24, None), (16, 0), (24, 3)])
+def test_layer_decode_narrow(B, wname, batch, bits, shift):
+    _decode_case(B, wname, batch, 16, 6, bits, shift)
+
+
+def test_layer_decode_narrow_static(B):
+    _decode_case(B, "m130m_layer", 3, 20, 4, 16, None, mode="static")
+
+
+@pytest.mark.parametrize("bits", [16, 24])
+def test_layer_decode_narrow_at_the_decode_shape(B, bits):
+    """2.7B layer shapes, batch 16 (the decode workload's per-layer launch): an
+    8-token prefill on both sides, then steps through the narrow cache."""
+    w = configs.get("m2p7b_decode")
+    _decode_case(B, "m2p7b_decode", w.batch, 8, 3, bits, None)
+
+
+def test_decode_graph_with_narrow_states(B):
+    """A captured decode step of a 2-layer stack replays the oracle's narrow-state steps."""
+    from quantized_state_space_fwht_amd.runtime import DecodeGraph, Mamba2Stack
+    w = configs.with_len(configs.get("tiny_layer"), 2, 24)
+    s = w.shape
+    params = [synth.workload_params(w, l) for l in range(2)]
+    u = synth.workload_activations(w)
+    preps = [O.prepare_layer(p) for p in params]
+    L0 = 18
+    _, caches, _ = O.stack_prefill(preps, s, u[:, :L0])
+    stack = Mamba2Stack(s, params)
+    stack.prefill(dev(u[:, :L0]))
+    shifts = stack.narrow_states(16)
+    fmts = []
+    for c, sh in zip(caches, shifts):
+        assert sh == O.state_shift_for(int(np.max(np.abs(c["ssm_state"]))), 16)
+        c["ssm_state"] = O.narrow_state(c["ssm_state"], 16, sh)
+        fmts.append((16, sh))
+    g = DecodeGraph(stack, 2)
+    for t in range(L0, 24):
+        h_o, caches = O.stack_decode(preps, s, u[:, t], caches, state_fmts=fmts)
+        h_g = g.step(dev(u[:, t]))
+        assert np.array_equal(host(h_g), h_o), f"graph step {t}"
+        for layer, c in zip(stack.layers, caches):
+            assert_exact(host(layer.cache_t["ssm_codes"]), O.pack_state(c["ssm_state"], 16),
+                         f"codes step {t}")
