@@ -40,8 +40,10 @@ def rshr(v, s):
     """
     v = np.asarray(v, dtype=np.int64)
     s = np.asarray(s, dtype=np.int64)
-    v, s = np.broadcast_arrays(v, s)
     assert np.all(np.abs(v) < _LIM), "rshr operand out of range"
+    if s.ndim == 0 and 1 <= int(s) <= 62:  # one shift for every element: no masks
+        return (v + np.int64(1 << (int(s) - 1))) >> np.int64(s)
+    v, s = np.broadcast_arrays(v, s)
     out = np.zeros(v.shape, dtype=np.int64)
     # s in [1, 62]: add half, arithmetic shift (numpy >> on int64 is floor division)
     m = (s >= 1) & (s <= 62)

@@ -75,7 +75,7 @@ def prepare_layer(params: dict) -> dict:
     }
 
 
-def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p, collect=False):
+def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p, collect=False, scan=None):
     """Shared body of prefill (L tokens) and decode (L = 1) on rows u2 [Bsz*L, dm].
 
     ``collect``: also return the quantization statistics of the six points in
@@ -110,8 +110,8 @@ def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p, collect=False)
     st.amax_q16 = list(amaxes)
     dt, dA = dt_dA(dt_raw.reshape(Bsz, L, H), prep["dt_bias"], prep["A_q16"])
     state_in = None if cache_in is None else cache_in["ssm_state"]
-    y, state = ssm_scan_pot(x_q.reshape(Bsz, L, H, P), B_q, C_q, dt, dA, prep["D_q16"],
-                            p_B, p_C, state_in)
+    y, state = (scan or ssm_scan_pot)(x_q.reshape(Bsz, L, H, P), B_q, C_q, dt, dA,
+                                      prep["D_q16"], p_B, p_C, state_in)
     p_y = p_x + 8
     sc1 = (qp.scoe[1], qp.sshift[1]) if hq_mode == "static" else (None, None)
     g = gate(y.reshape(Bsz * L, di), z, p_y)
@@ -137,16 +137,18 @@ def _mixer(prep, shape, u2, Bsz, L, mode, qp, cache_in, frozen_p, collect=False)
     return out, r, cache, st
 
 
-def layer_prefill(prep, shape, u, mode="dynamic", qp=None, collect=False):
+def layer_prefill(prep, shape, u, mode="dynamic", qp=None, collect=False, scan=None):
     """One mixer layer over u [Bsz, L, d_model] from a fresh state.
 
     Returns (out float32 [Bsz, L, d_model], intermediates, cache, stats);
-    ``collect`` adds the quantization statistics as intermediates["qstats"].
+    ``collect`` adds the quantization statistics as intermediates["qstats"];
+    ``scan``: another implementation of scan.ssm_scan_pot (scan_c's, for full
+    sizes).
     """
     u = np.asarray(u, dtype=np.float32)
     Bsz, L, dm = u.shape
     out, r, cache, st = _mixer(prep, shape, u.reshape(Bsz * L, dm), Bsz, L, mode, qp, None, None,
-                               collect)
+                               collect, scan)
     return out.reshape(Bsz, L, dm), r, cache, st
 
 

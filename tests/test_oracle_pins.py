@@ -36,6 +36,12 @@ def test_rshr_matches_exact_rational_rounding():
     assert int(O.rshr(-3, 1)) == -1 and int(O.rshr(3, 1)) == 2 and int(O.rshr(-1, 1)) == 0
     # shifts past the operand width
     assert int(O.rshr(-(1 << 40), 70)) == 0 and int(O.rshr((1 << 40), 70)) == 0
+    # vectors under one shift (the unmasked path) and under a shift per element
+    va = np.array(vs[:120], dtype=np.int64)
+    for s in (1, 5, 16, 62):
+        assert O.rshr(va, s).tolist() == [_rshr_exact(int(v), s) for v in va]
+    sa = RNG.integers(-9, 64, size=va.size)
+    assert O.rshr(va, sa).tolist() == [_rshr_exact(int(v), int(k)) for v, k in zip(va, sa)]
 
 
 def test_pot_exponent_property():
@@ -291,11 +297,21 @@ def _tiny_scan_inputs(L=32, H=2, P=2, N=4, seed=3):
     return x, Bm, Cm, dt, dA
 
 
-def test_P11_scan_matches_real_recurrence_within_rounding():
+def _scan_impls():
+    from oracle.scan_c import ssm_scan_pot_c
+    return [O.ssm_scan_pot, ssm_scan_pot_c]
+
+
+SCAN_IDS = ["numpy", "c"]
+
+
+@pytest.mark.parametrize("impl", [0, 1], ids=SCAN_IDS)
+def test_P11_scan_matches_real_recurrence_within_rounding(impl):
+    scan = _scan_impls()[impl]
     p_x, p_B, p_C = 7, 6, 7
     x, Bm, Cm, dt, dA = _tiny_scan_inputs()
     D_q16 = np.array([65536, 32768], np.int64)
-    y, h = O.ssm_scan_pot(x, Bm, Cm, dt, dA, D_q16, p_B, p_C)
+    y, h = scan(x, Bm, Cm, dt, dA, D_q16, p_B, p_C)
     p_h, p_y = p_x + p_B + 8, p_x + 8
     L, H, P, N = x.shape[1], x.shape[2], x.shape[3], Bm.shape[2]
     xr = x[0].astype(np.float64) * 2.0 ** -p_x
@@ -317,7 +333,9 @@ def test_P11_scan_matches_real_recurrence_within_rounding():
     assert np.all(np.abs(h[0] * lsb - hs) <= ebound[:, None, None] + 1e-12)
 
 
-def test_P12_unit_decay_is_an_integer_cumsum():
+@pytest.mark.parametrize("impl", [0, 1], ids=SCAN_IDS)
+def test_P12_unit_decay_is_an_integer_cumsum(impl):
+    scan = _scan_impls()[impl]
     L, N = 50, 3
     rng = np.random.default_rng(9)
     x = rng.integers(-127, 128, size=(1, L, 1, 1)).astype(np.int8)
@@ -327,13 +345,15 @@ def test_P12_unit_decay_is_an_integer_cumsum():
     for n0 in range(N):
         Cm = np.zeros((1, L, N), np.int8)
         Cm[..., n0] = 1
-        y, _ = O.ssm_scan_pot(x, Bm, Cm, dt, dA, np.zeros(1, np.int64), 0, 0)
+        y, _ = scan(x, Bm, Cm, dt, dA, np.zeros(1, np.int64), 0, 0)
         inc = dt[0, :, 0] * x[0, :, 0, 0].astype(np.int64) * Bm[0, :, n0].astype(np.int64) * 256
         steps = np.array([_rshr_exact(int(v), 16) for v in inc])
         assert np.array_equal(y[0, :, 0, 0], np.cumsum(steps))
 
 
-def test_P12_constant_decay_is_a_first_order_filter():
+@pytest.mark.parametrize("impl", [0, 1], ids=SCAN_IDS)
+def test_P12_constant_decay_is_a_first_order_filter(impl):
+    scan = _scan_impls()[impl]
     L = 64
     rng = np.random.default_rng(5)
     x = rng.integers(-127, 128, size=(1, L, 1, 1)).astype(np.int8)
@@ -342,7 +362,7 @@ def test_P12_constant_decay_is_a_first_order_filter():
     dt = np.full((1, L, 1), 3 * 65536 // 4, np.int64)
     dA = np.full((1, L, 1), 52000, np.int64)
     p_x, p_B = 7, 7
-    y, _ = O.ssm_scan_pot(x, Bm, Cm, dt, dA, np.zeros(1, np.int64), p_B, 0)
+    y, _ = scan(x, Bm, Cm, dt, dA, np.zeros(1, np.int64), p_B, 0)
     a = 52000 / 65536.0
     drive = 0.75 * x[0, :, 0, 0] * 2.0 ** -p_x * Bm[0, :, 0] * 2.0 ** -p_B
     h = scipy.signal.lfilter([1.0], [1.0, -a], drive)
@@ -350,6 +370,30 @@ def test_P12_constant_decay_is_a_first_order_filter():
     # y = rshr(h, p_B) with exponent p_x + 8: compare h in real units
     bound = 0.5 * 2.0 ** -p_h / (1 - a) + 2.0 ** -(p_x + 8)
     assert np.all(np.abs(y[0, :, 0, 0] * 2.0 ** -(p_x + 8) - h) <= bound)
+
+
+@pytest.mark.parametrize("p_B,p_C", [(6, 7), (-20, -24), (24, 24), (40, 30), (0, 0)])
+def test_c_scan_equals_the_numpy_scan(p_B, p_C):
+    """The C scan (full-size checks) against the numpy one, saturating and not."""
+    from oracle.scan_c import ssm_scan_pot_c
+    rng = np.random.default_rng(abs(p_B) * 100 + abs(p_C))
+    Bsz, L, H, P, N = 2, 37, 3, 5, 7
+    x = rng.integers(-127, 128, size=(Bsz, L, H, P)).astype(np.int8)
+    Bm = rng.integers(-127, 128, size=(Bsz, L, N)).astype(np.int8)
+    Cm = rng.integers(-127, 128, size=(Bsz, L, N)).astype(np.int8)
+    dt = rng.integers(0, 1 << 22, size=(Bsz, L, H)).astype(np.int64)
+    dA = rng.integers(0, 65537, size=(Bsz, L, H)).astype(np.int64)
+    dt[0, :5] = (1 << 31) - 1                                 # saturating states, early
+    dt[0, -3:] = (1 << 31) - 1                                # and at the end
+    dA[0, -3:] = 65536
+    D = rng.integers(-(1 << 18), 1 << 18, size=H).astype(np.int64)
+    st0 = rng.integers(-(1 << 31), 1 << 31, size=(Bsz, H, P, N)).astype(np.int64)
+    for state_in in (None, st0):
+        y_o, h_o = O.ssm_scan_pot(x, Bm, Cm, dt, dA, D, p_B, p_C, state_in)
+        for threads in (1, 4):
+            y_c, h_c = ssm_scan_pot_c(x, Bm, Cm, dt, dA, D, p_B, p_C, state_in, threads=threads)
+            assert np.array_equal(y_c, y_o) and np.array_equal(h_c, h_o)
+    assert np.any(np.abs(h_o) == (1 << 31) - 1) or np.any(h_o == -(1 << 31))
 
 
 def test_dt_and_decay_from_nau():
