@@ -39,7 +39,7 @@ from .hadamard import fwht256_f32, hadamard_quant, hadamard_scale, quantize_code
 from .linear import quantize_weight, w8a8_gemm
 from .nau import (EXP2_TABLE_Q30, LOG2E_Q30, exp2_q16, exp_q16, silu_q16, softplus_q16)
 from .conv import conv1d_pot, conv_weight_prep, silu_requant, xbc_pot_quant
-from .scan import (dt_dA, narrow_state, pack_state, ssm_scan_pot, state_shift_for,
+from .scan import (dt_dA, narrow_state, pack_state, ssm_scan_pot, ssm_scan_real, state_shift_for,
                    unpack_state, widen_state)
 from .gate_norm import gate, gate_norm_quant, rmsnorm_fixed_order
 from .layer import (QParams, Stats, calibrate_stack, layer_decode, layer_prefill, prepare_layer,

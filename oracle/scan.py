@@ -128,3 +128,43 @@ def state_shift_for(amax, bits, headroom=1):
     max(0, bitlength(amax) + headroom - (bits - 1)), at most 32 - bits."""
     need = int(amax).bit_length() + int(headroom)
     return min(max(0, need - (bits - 1)), 32 - bits)
+
+
+# --- the chunked (SSD-form) variant: the real recurrence -----------------------
+# A chunked scan sums the recurrence in matrix form over chunks of tokens, so it
+# cannot reproduce the per-step rounding above; what it computes exactly (up to
+# the order of its float64 roundings) is the recurrence with that rounding left
+# out.  Reading: in the state's own grid units, with a_t = dA_t / 2^16,
+#     h_t = a_t * h_{t-1} + dt_t * x_t[p] * B_t[n] / 2^8      (no rounding)
+#     y_t = sat32(floor(sum_n C_t[n] h_t / 2^(p_B + p_C) + 1/2) + rshr(D x_t, 8))
+# and the final state is h rounded half up onto the grid and saturated.  No
+# saturation happens inside the sequence (inputs whose exact state saturates lie
+# outside the variant's contract).
+
+
+def ssm_scan_real(x_q, B_q, C_q, dt, dA, D_q16, p_B, p_C, state_in=None):
+    """The recurrence without per-step rounding, in float64, t ascending.
+
+    Same arguments as ssm_scan_pot.  Returns (y int64, state_out int64, y_acc
+    float64 [Bsz, L, H, P] = sum_n C h before the output rounding)."""
+    x = np.asarray(x_q, dtype=np.float64)
+    Bm = np.asarray(B_q, dtype=np.float64)
+    Cm = np.asarray(C_q, dtype=np.float64)
+    a = np.asarray(dA, dtype=np.float64) / 65536.0
+    dtf = np.asarray(dt, dtype=np.float64)
+    Bsz, L, H, P = x.shape
+    N = Bm.shape[-1]
+    h = (np.zeros((Bsz, H, P, N)) if state_in is None
+         else np.asarray(state_in, dtype=np.float64).copy())
+    y_acc = np.zeros((Bsz, L, H, P))
+    for t in range(L):
+        u = dtf[:, t, :, None] * x[:, t] / 256.0                          # [Bsz, H, P]
+        h = a[:, t, :, None, None] * h + u[..., None] * Bm[:, t, None, None, :]
+        y_acc[:, t] = np.einsum("bn,bhpn->bhp", Cm[:, t], h)
+    ky = int(p_B) + int(p_C)
+    xi = np.asarray(x_q, dtype=np.int64)
+    yd = rshr(np.asarray(D_q16, dtype=np.int64)[None, None, :, None] * xi, 8)
+    big = 2.0 ** 62  # beyond the int32 range either way: clip before converting
+    y = sat32(np.clip(np.floor(y_acc * 2.0 ** -ky + 0.5), -big, big).astype(np.int64) + yd)
+    st = sat32(np.clip(np.floor(h + 0.5), -big, big).astype(np.int64))
+    return y, st, y_acc

@@ -741,3 +741,107 @@ def test_narrow_state_decode_reduces_to_int32_and_is_bounded():
     # the new cache holds the 16-bit codes of a state within 2^(s-1) + 1 of the int32 step's
     dh = np.abs(O.widen_state(c16["ssm_state"], s) - c32["ssm_state"])
     assert np.all(dh <= (1 << s) + 1)
+
+
+# --------------------------------------------------------------------------- chunked scan
+def test_real_scan_equals_the_integer_scan_when_nothing_rounds():
+    """Unit decay and increments that are whole grid steps: no rounding happens,
+    so the real recurrence is the integer one, bit for bit."""
+    rng = np.random.default_rng(21)
+    Bsz, L, H, P, N = 2, 40, 2, 3, 5
+    x = rng.integers(-127, 128, size=(Bsz, L, H, P)).astype(np.int8)
+    Bm = rng.integers(-127, 128, size=(Bsz, L, N)).astype(np.int8)
+    Cm = rng.integers(-127, 128, size=(Bsz, L, N)).astype(np.int8)
+    dt = (rng.integers(1, 1 << 8, size=(Bsz, L, H)) * 256).astype(np.int64)
+    dA = np.full((Bsz, L, H), 65536, np.int64)
+    D = np.array([65536, -3000], np.int64)
+    st0 = rng.integers(-(1 << 20), 1 << 20, size=(Bsz, H, P, N))
+    for p_B, p_C in ((6, 7), (0, 0), (-3, 2)):
+        y_i, h_i = O.ssm_scan_pot(x, Bm, Cm, dt, dA, D, p_B, p_C, st0)
+        y_r, h_r, _ = O.ssm_scan_real(x, Bm, Cm, dt, dA, D, p_B, p_C, st0)
+        assert np.array_equal(y_r, y_i) and np.array_equal(h_r, h_i)
+
+
+def test_real_scan_against_exact_rationals():
+    x, Bm, Cm, dt, dA = _tiny_scan_inputs(L=12, H=2, P=2, N=3)
+    D = np.array([40000, -7000], np.int64)
+    p_B, p_C = 5, 6
+    y, st, y_acc = O.ssm_scan_real(x, Bm, Cm, dt, dA, D, p_B, p_C)
+    L, H, P, N = x.shape[1], x.shape[2], x.shape[3], Bm.shape[2]
+    hs = [[[Fraction(0)] * N for _ in range(P)] for _ in range(H)]
+    for t in range(L):
+        for h in range(H):
+            a = Fraction(int(dA[0, t, h]), 65536)
+            for p in range(P):
+                u = Fraction(int(dt[0, t, h]) * int(x[0, t, h, p]), 256)
+                acc = Fraction(0)
+                for n in range(N):
+                    hs[h][p][n] = a * hs[h][p][n] + u * int(Bm[0, t, n])
+                    acc += int(Cm[0, t, n]) * hs[h][p][n]
+                assert abs(float(acc) - y_acc[0, t, h, p]) <= 1e-9 * max(1.0, abs(float(acc)))
+                v = acc / 2 ** (p_B + p_C) + Fraction(1, 2)
+                if abs(v - math.floor(v)) > Fraction(1, 10 ** 6):  # not at a rounding tie
+                    want = math.floor(v) + _rshr_exact(int(D[h]) * int(x[0, t, h, p]), 8)
+                    assert y[0, t, h, p] == want, (t, h, p)
+    for h in range(H):
+        for p in range(P):
+            for n in range(N):
+                assert st[0, h, p, n] == math.floor(hs[h][p][n] + Fraction(1, 2))
+
+
+def test_real_scan_within_the_propagated_bound_of_the_integer_scan():
+    """The variant's contract: the sequential integer scan stays within the
+    half-step-per-step bound of the real recurrence (the P11 bound in y steps)."""
+    x, Bm, Cm, dt, dA = _tiny_scan_inputs(L=64, H=2, P=4, N=8, seed=11)
+    D = np.array([65536, 32768], np.int64)
+    p_B, p_C = 6, 7
+    y_i, h_i = O.ssm_scan_pot(x, Bm, Cm, dt, dA, D, p_B, p_C)
+    y_r, h_r, _ = O.ssm_scan_real(x, Bm, Cm, dt, dA, D, p_B, p_C)
+    a = dA[0] / 65536.0
+    eb = np.zeros(x.shape[2])
+    for t in range(x.shape[1]):
+        eb = a[t] * eb + 0.5                             # state error, grid steps
+        bound = np.sum(np.abs(Cm[0, t].astype(np.float64))) * eb / 2.0 ** (p_B + p_C) + 1.0
+        assert np.all(np.abs(y_i[0, t] - y_r[0, t]) <= bound[:, None])
+    assert np.all(np.abs(h_i[0] - h_r[0]) <= eb[:, None, None] + 0.5)
+
+
+def _chunked_real_scan(x_q, B_q, C_q, dt, dA, p_B, Q):
+    """The recurrence summed in chunks of Q tokens in matrix form (the algebra of
+    a chunked scan): per chunk, y = ((C B^T) o L o dt) x / 2^8 + decay * C H_in^T and
+    H_out = A H_in + x^T (w o B) / 2^8, with L[t, s] = prod_{s<r<=t} a_r."""
+    x = np.asarray(x_q, np.float64)[0]
+    Bm = np.asarray(B_q, np.float64)[0]
+    Cm = np.asarray(C_q, np.float64)[0]
+    a = np.asarray(dA, np.float64)[0] / 65536.0
+    dtf = np.asarray(dt, np.float64)[0]
+    L, H, P = x.shape
+    N = Bm.shape[1]
+    y_acc = np.zeros((L, H, P))
+    Hs = np.zeros((H, P, N))
+    for c0 in range(0, L, Q):
+        c1 = min(L, c0 + Q)
+        q = c1 - c0
+        G = Cm[c0:c1] @ Bm[c0:c1].T                                    # [q, q]
+        for h in range(H):
+            ah = a[c0:c1, h]
+            Lm = np.zeros((q, q))
+            for s_ in range(q):
+                Lm[s_, s_] = 1.0
+                for t in range(s_ + 1, q):
+                    Lm[t, s_] = Lm[t - 1, s_] * ah[t]
+            pre = np.cumprod(ah)                                       # decay from c0 to t
+            M = G * Lm * dtf[c0:c1, h][None, :] / 256.0
+            y_acc[c0:c1, h] = M @ x[c0:c1, h] + pre[:, None] * (Cm[c0:c1] @ Hs[h].T)
+            w = dtf[c0:c1, h] * np.array([np.prod(ah[s_ + 1:]) for s_ in range(q)]) / 256.0
+            Hs[h] = np.prod(ah) * Hs[h] + (x[c0:c1, h] * w[:, None]).T @ Bm[c0:c1]
+    return y_acc, Hs
+
+
+@pytest.mark.parametrize("Q", [1, 5, 16, 64])
+def test_chunked_form_equals_the_real_recurrence(Q):
+    x, Bm, Cm, dt, dA = _tiny_scan_inputs(L=50, H=2, P=3, N=4, seed=13)
+    _, _, y_acc = O.ssm_scan_real(x, Bm, Cm, dt, dA, np.zeros(2, np.int64), 0, 0)
+    yc, Hc = _chunked_real_scan(x, Bm, Cm, dt, dA, 0, Q)
+    scale = np.max(np.abs(y_acc))
+    assert np.max(np.abs(yc - y_acc[0])) <= 1e-12 * scale
