@@ -83,6 +83,48 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=3):
                       f"({w.batch}x{w.seqlen} tokens, seeds as the GPU run), {dt:.1f} s"}
 
 
+FP64_PEAK_TFLOPS = 78.6   # MI355X float64 vector / matrix rate
+
+
+def ssd_prefill_bench(torch, B, layer, u, out, stream, w, steps, warmup, ms_sequential):
+    """The same layer prefill with the chunked (SSD-form) scan variant.  Its
+    contract differs from the method's (no per-step rounding of the state), so
+    it is reported beside the headline, never as it.  Roofline: the three chunk
+    kernels are float64 multiply-add bound; per (batch, head, chunk of Q = 64):
+    2 Q P N (chunk state) + 2 Q Q P (within the chunk) + 2 Q N P (from the
+    entering state) + 2 P N (across chunks) flops."""
+    s = w.shape
+    for _ in range(warmup):
+        layer.prefill(u, out, stream=stream, scan="ssd")
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        B.lib.fm_layer_set_timing_events(evs[i][0].cuda_event, evs[i][1].cuda_event)
+        layer.prefill(u, out, stream=stream, scan="ssd")
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    Q, P, N = 64, s.headdim, s.dstate
+    nc = (w.seqlen + Q - 1) // Q
+    flops = w.batch * s.nheads * nc * (2 * Q * P * N + 2 * Q * Q * P + 2 * Q * N * P + 2 * P * N)
+    achieved = flops / (scan_ms / 1e3) / 1e12
+    return {"value": round(w.tokens / (ms / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 4), "scan_ms": round(scan_ms, 4),
+            "speedup_vs_sequential": round(ms_sequential / ms, 3),
+            "contract": "scan without per-step state rounding (float64): y within 1 of the "
+                        "correctly rounded real recurrence",
+            "roofline": {"bound": "fp64", "kernel": "ssd_chunk_*_kernel",
+                         "achieved": round(achieved, 3), "peak": FP64_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / FP64_PEAK_TFLOPS, 4),
+                         "work": f"{flops} flops per call"}}
+
+
 def decode_bench(torch, configs, synth, warmup=8, max_steps=None, narrow_bits=(16, 24)):
     """Decode tokens/s of the 64-layer 2.7B-shaped stack, batch 16.
 
@@ -619,6 +661,8 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
     }
+    line["prefill_ssd"] = ssd_prefill_bench(torch, B, layer, u, out, stream, w, K, args.warmup,
+                                            ms_per_step)
     if not args.no_decode:
         del layer
         torch.cuda.empty_cache()

@@ -192,6 +192,34 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fm_ssm_scan_ssd — the chunked (SSD-form) variant of fm_ssm_scan_pot: the
+ * same recurrence summed over chunks of 64 tokens in matrix form (Mamba2's
+ * state space duality; a sequence-chunked schedule for prefill), which cannot
+ * keep the per-step rounding and so computes, in float64 and in the state's
+ * grid units,
+ *     h_t = (dA_t / 2^16) h_{t-1} + dt_t x_t B_t / 2^8         (no rounding)
+ *     y   = sat32(floor(sum_n C_t h_t / 2^(p_B + p_C) + 1/2) + rshr(d_q16 x, 8))
+ * with dt and dA formed as in fm_ssm_scan_pot, and the final state rounded
+ * half up onto the grid and saturated; no saturation inside the sequence.
+ * Contract: y within 1 of the correctly rounded real recurrence (only the
+ * float64 summation order differs), hence within the sequential scan's
+ * propagated half-step bound plus 1 of fm_ssm_scan_pot's y.
+ * Arguments, layouts and limits as fm_ssm_scan_pot, and headdim == 64, x
+ * 16-byte aligned.
+ * Workspace: fm_ssm_scan_ssd_workspace_size(batch, len, nheads, headdim,
+ * dstate) bytes, 256-byte aligned (the chunk states, float64).
+ * ---------------------------------------------------------------------- */
+size_t fm_ssm_scan_ssd_workspace_size(int64_t batch, int64_t len, int64_t nheads,
+                                      int64_t headdim, int64_t dstate);
+fm_status fm_ssm_scan_ssd(const int8_t* x, const int8_t* bm, const int8_t* cm,
+                          const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
+                          const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
+                          int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
+                          int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
+                          int32_t* dt_out, int32_t* da_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fm_nau_eval — the nonlinear approximation unit elementwise, Q.16 in and
  * out (review page "What carries the argument": an 8-segment first-order
  * approximation of 2^v, e^x = 2^(x log2 e), SoftPlus(x) = x + SoftPlus(-x);
@@ -314,6 +342,17 @@ fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights
                                   const fm_static_params* sp, const float* u, int64_t batch,
                                   int64_t len, float* out, const fm_cache* cache, fm_qparams* qp,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fm_mamba2_layer_prefill_ssd — fm_mamba2_layer_prefill with the chunked
+ * scan (fm_ssm_scan_ssd) in place of the sequential one; everything else is
+ * the same launch sequence.  headdim must be 64.  Workspace:
+ * fm_mamba2_layer_workspace_size_ssd (the layer's plus the chunk states). */
+size_t fm_mamba2_layer_workspace_size_ssd(const fm_layer_desc* d, int64_t batch, int64_t len);
+fm_status fm_mamba2_layer_prefill_ssd(const fm_layer_desc* d, const fm_layer_weights* w,
+                                      const fm_static_params* sp, const float* u, int64_t batch,
+                                      int64_t len, float* out, const fm_cache* cache,
+                                      fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* fm_mamba2_layer_decode — one token per sequence, u_t [batch, d_model],
  * continuing from `cache` (updated in place): the conv window shifts, the

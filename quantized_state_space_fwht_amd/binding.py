@@ -119,6 +119,16 @@ _SIGS = {
     "fm_scale_columns": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _c_i32, _vp, _vp]),
     "fm_qparams_from_stats": (ctypes.c_int, [ctypes.POINTER(QParams),
                                              ctypes.POINTER(StaticParams)]),
+    "fm_ssm_scan_ssd_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64]),
+    "fm_ssm_scan_ssd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _vp, _c_i64,
+                                       _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _c_sz, _vp]),
+    "fm_mamba2_layer_workspace_size_ssd": (_c_sz, [ctypes.POINTER(LayerDesc), _c_i64, _c_i64]),
+    "fm_mamba2_layer_prefill_ssd": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
+                                                   ctypes.POINTER(LayerWeights),
+                                                   ctypes.POINTER(StaticParams), _vp, _c_i64,
+                                                   _c_i64, _vp, ctypes.POINTER(Cache), _vp, _vp,
+                                                   _c_sz, _vp]),
     "fm_state_narrow_bytes": (_c_sz, [_c_i64, _c_i32]),
     "fm_state_narrow": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
     "fm_state_widen": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
@@ -251,6 +261,20 @@ def fm_ssm_scan_pot(x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p, 
     if ws is None:
         ws = workspace(lib.fm_ssm_scan_pot_workspace_size(batch, length, dstate), y.device)
     _check(lib.fm_ssm_scan_pot(_ptr(x), _ptr(bm), _ptr(cm), dt_raw.data_ptr(), dt_row_stride,
+                               _ptr(dt_bias), _ptr(a_q16), _ptr(d_q16), _ptr(p), batch, length,
+                               nheads, headdim, dstate, _ptr(state_in), _ptr(state_out), _ptr(y),
+                               _ptr(dt_out), _ptr(da_out), _ptr(ws), ws.numel(),
+                               _stream(stream)))
+
+
+def fm_ssm_scan_ssd(x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p, batch, length,
+                    nheads, headdim, dstate, state_in, state_out, y, dt_out=None, da_out=None,
+                    ws=None, stream=None):
+    """The chunked variant of fm_ssm_scan_pot (same arguments)."""
+    if ws is None:
+        ws = workspace(lib.fm_ssm_scan_ssd_workspace_size(batch, length, nheads, headdim,
+                                                          dstate), y.device)
+    _check(lib.fm_ssm_scan_ssd(_ptr(x), _ptr(bm), _ptr(cm), dt_raw.data_ptr(), dt_row_stride,
                                _ptr(dt_bias), _ptr(a_q16), _ptr(d_q16), _ptr(p), batch, length,
                                nheads, headdim, dstate, _ptr(state_in), _ptr(state_out), _ptr(y),
                                _ptr(dt_out), _ptr(da_out), _ptr(ws), ws.numel(),

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfm.so")
 SOURCES = ["fm_api.hip", "fm_hadamard.hip", "fm_gemm.hip", "fm_conv.hip", "fm_scan.hip",
-           "fm_gate.hip", "fm_layer.hip", "fm_nau.hip", "fm_outlier.hip", "fm_state.hip"]
+           "fm_gate.hip", "fm_layer.hip", "fm_nau.hip", "fm_outlier.hip", "fm_state.hip",
+           "fm_ssd.hip"]
 ARCH = os.environ.get("FM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -243,15 +243,12 @@ size_t fm_ssm_scan_pot_workspace_size(int64_t batch, int64_t len, int64_t dstate
     return scan_ws_bytes(batch, len, dstate);
 }
 
-fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
-                          const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
-                          const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
-                          int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
-                          int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
-                          int32_t* dt_out, int32_t* da_out, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
-    const char* who = "fm_ssm_scan_pot";
-    g_err[0] = 0;
+static fm_status scan_args(const char* who, const int8_t* x, const int8_t* bm, const int8_t* cm,
+                           const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
+                           const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
+                           int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
+                           int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
+                           int32_t* dt_out, int32_t* da_out, ScanArgs* out) {
     if (!x || !bm || !cm || !dt_raw || !dt_bias || !a_q16 || !d_q16 || !p || !y || !dt_out ||
         !da_out)
         return fail(FM_ERR_NULL, "%s: a required pointer is NULL", who);
@@ -285,10 +282,56 @@ fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
     a.y = y;
     a.dt_out = dt_out;
     a.da_out = da_out;
-    fm_status st = check_ws(workspace, workspace_bytes,
-                            scan_ws_bytes(batch, len, dstate), who);
+    *out = a;
+    return FM_OK;
+}
+
+fm_status fm_ssm_scan_pot(const int8_t* x, const int8_t* bm, const int8_t* cm,
+                          const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
+                          const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
+                          int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
+                          int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
+                          int32_t* dt_out, int32_t* da_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "fm_ssm_scan_pot";
+    g_err[0] = 0;
+    ScanArgs a;
+    fm_status st = scan_args(who, x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p,
+                             batch, len, nheads, headdim, dstate, state_in, state_out, y, dt_out,
+                             da_out, &a);
     if (st != FM_OK) return st;
+    if ((st = check_ws(workspace, workspace_bytes, scan_ws_bytes(batch, len, dstate), who)) !=
+        FM_OK)
+        return st;
     return scan_run(a, workspace, stream);
+}
+
+size_t fm_ssm_scan_ssd_workspace_size(int64_t batch, int64_t len, int64_t nheads,
+                                      int64_t headdim, int64_t dstate) {
+    if (batch < 1 || len < 1 || nheads < 1 || headdim < 1 || dstate < 1) return 0;
+    return ssd_ws_bytes(batch, len, nheads, headdim, dstate);
+}
+
+fm_status fm_ssm_scan_ssd(const int8_t* x, const int8_t* bm, const int8_t* cm,
+                          const float* dt_raw, int64_t dt_row_stride, const float* dt_bias,
+                          const int32_t* a_q16, const int32_t* d_q16, const int32_t* p,
+                          int64_t batch, int64_t len, int64_t nheads, int64_t headdim,
+                          int64_t dstate, const int32_t* state_in, int32_t* state_out, int32_t* y,
+                          int32_t* dt_out, int32_t* da_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    const char* who = "fm_ssm_scan_ssd";
+    g_err[0] = 0;
+    ScanArgs a;
+    fm_status st = scan_args(who, x, bm, cm, dt_raw, dt_row_stride, dt_bias, a_q16, d_q16, p,
+                             batch, len, nheads, headdim, dstate, state_in, state_out, y, dt_out,
+                             da_out, &a);
+    if (st != FM_OK) return st;
+    if (headdim != 64) return fail(FM_ERR_SHAPE, "%s: headdim must be 64", who);
+    if (!aligned(x, 16)) return fail(FM_ERR_SHAPE, "%s: x must be 16-byte aligned", who);
+    if ((st = check_ws(workspace, workspace_bytes,
+                       ssd_ws_bytes(batch, len, nheads, headdim, dstate), who)) != FM_OK)
+        return st;
+    return ssd_run(a, workspace, stream);
 }
 
 // ---------------------------------------------------------------- fm_nau_eval
@@ -406,7 +449,7 @@ size_t fm_mamba2_layer_workspace_size(const fm_layer_desc* d, int64_t batch, int
 static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights* w,
                                   const fm_static_params* sp, const float* u, int64_t batch,
                                   int64_t len, const float* out, fm_qparams* qp, void* ws,
-                                  size_t ws_bytes, const char* who) {
+                                  size_t ws_bytes, const char* who, bool ssd = false) {
     fm_status st;
     if ((st = check_layer_desc(d, who)) != FM_OK) return st;
     if ((st = check_weights(w, who)) != FM_OK) return st;
@@ -421,7 +464,11 @@ static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights
         T * dip >= ((int64_t)1 << 31))
         return fail(FM_ERR_SHAPE, "%s: batch=%lld len=%lld out of range", who, (long long)batch,
                     (long long)len);
-    return check_ws(ws, ws_bytes, fm_mamba2_layer_workspace_size(d, batch, len), who);
+    if (ssd && d->headdim != 64) return fail(FM_ERR_SHAPE, "%s: headdim must be 64", who);
+    return check_ws(ws, ws_bytes,
+                    ssd ? fm_mamba2_layer_workspace_size_ssd(d, batch, len)
+                        : fm_mamba2_layer_workspace_size(d, batch, len),
+                    who);
 }
 
 fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights* w,
@@ -436,6 +483,29 @@ fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights
     if (cache && (!cache->conv_state || !cache->ssm_state || !cache->p))
         return fail(FM_ERR_NULL, "%s: cache has a NULL member", who);
     return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream);
+}
+
+size_t fm_mamba2_layer_workspace_size_ssd(const fm_layer_desc* d, int64_t batch, int64_t len) {
+    const size_t base = fm_mamba2_layer_workspace_size(d, batch, len);
+    if (!base) return 0;
+    return align256(base) + ssd_ws_bytes(batch, len, d->nheads, d->headdim, d->dstate);
+}
+
+fm_status fm_mamba2_layer_prefill_ssd(const fm_layer_desc* d, const fm_layer_weights* w,
+                                      const fm_static_params* sp, const float* u, int64_t batch,
+                                      int64_t len, float* out, const fm_cache* cache,
+                                      fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    const char* who = "fm_mamba2_layer_prefill_ssd";
+    g_err[0] = 0;
+    fm_status st = check_layer_call(d, w, sp, u, batch, len, out, qp, workspace, workspace_bytes,
+                                    who, true);
+    if (st != FM_OK) return st;
+    if (cache && (!cache->conv_state || !cache->ssm_state || !cache->p))
+        return fail(FM_ERR_NULL, "%s: cache has a NULL member", who);
+    void* ssd_ws = (char*)workspace + align256(fm_mamba2_layer_workspace_size(d, batch, len));
+    return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream, 32, 0,
+                     ssd_ws);
 }
 
 fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights* w,

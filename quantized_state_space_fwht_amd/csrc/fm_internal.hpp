@@ -196,6 +196,14 @@ struct ScanArgs {
     int state_bits;
     int state_shift;
 };
+// dt and the decay of every (token, head) into dt_out / da_out
+fm_status scan_prep_run(const ScanArgs& a, hipStream_t s);
+// chunked (SSD-form) variant: the recurrence without per-step rounding, in
+// float64 over chunks of kSsdChunk tokens (fm_ssd.hip); headdim 64 only
+constexpr int kSsdChunk = 64;
+size_t ssd_ws_bytes(int64_t batch, int64_t len, int64_t nheads, int64_t headdim, int64_t dstate);
+fm_status ssd_run(const ScanArgs& a, void* ws, hipStream_t s, hipEvent_t ev_start = nullptr,
+                  hipEvent_t ev_stop = nullptr);
 // workspace of the scan (none: B and C are staged through LDS)
 size_t scan_ws_bytes(int64_t batch, int64_t len, int64_t dstate);
 // ev_start / ev_stop (nullable): recorded on s right around the scan kernel
@@ -242,11 +250,12 @@ void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_tap
 void set_keep_intermediates(bool on);
 void set_timing_events(void* start, void* stop);
 void set_quant_stats(fm_quant_stats* qs);
-// state_bits / state_shift: the decode cache's state format (ScanArgs)
+// state_bits / state_shift: the decode cache's state format (ScanArgs);
+// ssd_ws (prefill only): run the chunked scan variant with this workspace
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
                     fm_qparams* qp, void* workspace, bool decode, hipStream_t s,
-                    int state_bits = 32, int state_shift = 0);
+                    int state_bits = 32, int state_shift = 0, void* ssd_ws = nullptr);
 
 // narrow state codes (fm_state.hip)
 fm_status state_narrow_run(const int32_t* h, int64_t n, int bits, int shift, void* out,

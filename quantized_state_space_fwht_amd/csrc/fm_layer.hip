@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
                     fm_qparams* qp, void* workspace, bool decode, hipStream_t s, int state_bits,
-                    int state_shift) {
+                    int state_shift, void* ssd_ws) {
     const int64_t T = batch * len;
     const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads, P = d->headdim;
     const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
@@ -359,7 +359,11 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.state_shift = decode ? state_shift : 0;
         hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
         g_ev_start = g_ev_stop = nullptr;
-        if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) return st;
+        if (ssd_ws && !decode) {
+            if ((st = ssd_run(a, ssd_ws, s, ev0, ev1)) != FM_OK) return st;
+        } else if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) {
+            return st;
+        }
     }
     // 8. gate + RMSNorm + rotate + quantize the out_proj input
     {

@@ -596,6 +596,14 @@ __global__ __launch_bounds__(256) void scan_step_kernel(ScanArgs A) {
 
 size_t scan_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 
+fm_status scan_prep_run(const ScanArgs& a, hipStream_t s) {
+    const int64_t pairs = a.batch * a.len * a.nheads;
+    if (pairs == 0) return FM_OK;
+    scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
+        a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
+    return check_launch("scan_prep_kernel");
+}
+
 fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
                    hipEvent_t ev_stop) {
     if (a.dstate != 64 && a.dstate != 128)
@@ -634,12 +642,7 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
         return FM_OK;
     }
     fm_status st;
-    if (!a.dt_ready) {
-        const int64_t pairs = a.batch * a.len * a.nheads;
-        scan_prep_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, s>>>(
-            a.dt_raw, a.dt_stride, a.dt_bias, a.a_q16, pairs, (int)a.nheads, a.dt_out, a.da_out);
-        if ((st = check_launch("scan_prep_kernel")) != FM_OK) return st;
-    }
+    if (!a.dt_ready && (st = scan_prep_run(a, s)) != FM_OK) return st;
     if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
         return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
     const unsigned grid = (unsigned)(a.headdim / kScanP * a.nheads * a.batch);

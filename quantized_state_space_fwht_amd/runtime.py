@@ -85,8 +85,10 @@ class Mamba2Layer:
         self.ncache = None  # narrow state cache (narrow_state), used by decode when set
 
     # ------------------------------------------------------------ memory
-    def workspace_for(self, batch, length):
-        need = B.lib.fm_mamba2_layer_workspace_size(ctypes.byref(self.desc), batch, length)
+    def workspace_for(self, batch, length, ssd=False):
+        size = B.lib.fm_mamba2_layer_workspace_size_ssd if ssd else \
+            B.lib.fm_mamba2_layer_workspace_size
+        need = size(ctypes.byref(self.desc), batch, length)
         if self._pool is not None:
             self._ws = self._pool.get(need)
         elif self._ws is None or self._ws.numel() < need:
@@ -146,12 +148,16 @@ class Mamba2Layer:
         return B.qparams_from_device(self.qp)
 
     # ------------------------------------------------------------ calls
-    def prefill(self, u, out=None, with_cache=True, stream=None):
-        """u [batch, len, d_model] float32 device tensor -> out (same shape)."""
+    def prefill(self, u, out=None, with_cache=True, stream=None, scan="sequential"):
+        """u [batch, len, d_model] float32 device tensor -> out (same shape).
+        scan "ssd": the chunked scan variant (fm_mamba2_layer_prefill_ssd)."""
         batch, length, dm = u.shape
         if out is None:
             out = torch.empty_like(u)
-        ws = self.workspace_for(batch, length)
+        ssd = scan == "ssd"
+        if not ssd and scan != "sequential":
+            raise ValueError(f"scan {scan!r}: 'sequential' or 'ssd'")
+        ws = self.workspace_for(batch, length, ssd)
         cache = None
         if with_cache:
             self.ncache = None  # the prefill writes the int32 state
@@ -159,7 +165,8 @@ class Mamba2Layer:
                 self.alloc_cache(batch)
             cache = ctypes.byref(self.cache)
         sp = ctypes.byref(self.static) if self.static is not None else None
-        B._check(B.lib.fm_mamba2_layer_prefill(
+        fn = B.lib.fm_mamba2_layer_prefill_ssd if ssd else B.lib.fm_mamba2_layer_prefill
+        B._check(fn(
             ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u.data_ptr(), batch, length,
             out.data_ptr(), cache, self.qp.data_ptr(), ws.data_ptr(), ws.numel(),
             B._stream(stream)))

@@ -1,0 +1,187 @@
+"""GPU parity of the chunked (SSD-form) scan variant against the oracle.
+
+The variant computes the recurrence without per-step rounding
+(oracle.ssm_scan_real); its contract, checked here element by element:
+dt and the decay bit for bit; y and the final state within 1 of the oracle's
+correctly rounded real recurrence (only the float64 summation order differs,
+so almost every element is equal); and y within the sequential scan's
+propagated half-step bound plus 2 of the sequential oracle's y.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle.scan_c import ssm_scan_pot_c
+from quantized_state_space_fwht_amd import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from quantized_state_space_fwht_amd import binding
+    return binding
+
+
+def dev(a, dtype=None):
+    t = torch.as_tensor(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda().contiguous()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_exact(got, want, what):
+    got = np.asarray(got).astype(np.int64)
+    want = np.asarray(want).astype(np.int64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[0]}"
+
+
+def assert_within_one(got, want, what, min_equal=0.999):
+    d = np.abs(np.asarray(got, np.int64) - np.asarray(want, np.int64))
+    assert d.max(initial=0) <= 1, f"{what}: off by {d.max()} at {np.unravel_index(d.argmax(), d.shape)}"
+    if d.size:
+        assert np.mean(d == 0) >= min_equal, f"{what}: only {np.mean(d == 0):.5f} equal"
+
+
+def sequential_bound(cm, dA, ky):
+    """Largest |y_sequential - y_real| per (b, t, h): the state's propagated
+    half-step error through C, plus the output roundings."""
+    a = np.asarray(dA, np.float64) / 65536.0               # [b, L, H]
+    csum = np.sum(np.abs(np.asarray(cm, np.float64)), axis=-1)   # [b, L]
+    eb = np.zeros((a.shape[0], a.shape[2]))                # [b, H]
+    out = np.zeros(a.shape)
+    for t in range(a.shape[1]):
+        eb = a[:, t] * eb + 0.5
+        out[:, t] = csum[:, t, None] * eb / 2.0 ** ky
+    return out + 2.0
+
+
+def scan_case(wname, batch, length, heads, with_state, seed=0):
+    s = configs.get(wname).shape
+    H = heads or s.nheads
+    P, N = s.headdim, s.dstate
+    rng = np.random.default_rng(1000 * seed + length + H)
+    x = rng.integers(-127, 128, size=(batch, length, H, P)).astype(np.int8)
+    bm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    cm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    stride = H + 3
+    dt_wide = (rng.standard_normal((batch * length, stride)) * 2).astype(np.float32)
+    dt_bias = rng.uniform(-4, -2, H).astype(np.float32)
+    A = (-np.exp(rng.uniform(0, 2, H))).astype(np.float32)
+    a_q16 = O.f32_to_i32_sat(np.rint(A * np.float32(65536)))
+    d_q16 = rng.integers(-(1 << 17), 1 << 17, size=H).astype(np.int64)
+    p = np.array([0, 7, 6, 7], np.int32)
+    state = rng.integers(-(1 << 20), 1 << 20, size=(batch, H, P, N)).astype(np.int32) \
+        if with_state else None
+    return dict(x=x, bm=bm, cm=cm, stride=stride, dt_wide=dt_wide, dt_bias=dt_bias,
+                a_q16=a_q16, d_q16=d_q16, p=p, state=state, batch=batch, length=length, H=H,
+                P=P, N=N)
+
+
+def run_ssd(B, c):
+    batch, length, H, P, N = c["batch"], c["length"], c["H"], c["P"], c["N"]
+    t_y = torch.empty((batch, length, H, P), dtype=torch.int32, device="cuda")
+    t_st = torch.empty((batch, H, P, N), dtype=torch.int32, device="cuda")
+    t_dt = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+    t_da = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+    B.fm_ssm_scan_ssd(dev(c["x"]), dev(c["bm"]), dev(c["cm"]), dev(c["dt_wide"]), c["stride"],
+                      dev(c["dt_bias"]), dev(c["a_q16"], torch.int32), dev(c["d_q16"], torch.int32),
+                      dev(c["p"]), batch, length, H, P, N,
+                      None if c["state"] is None else dev(c["state"]), t_st, t_y, t_dt, t_da)
+    return host(t_y), host(t_st), host(t_dt), host(t_da)
+
+
+# ragged chunk counts and tails: L = 1, < 64, = 64, 65, several chunks plus a tail
+@pytest.mark.parametrize("wname,batch,length,heads", [("tiny_layer", 2, 1, 3),
+                                                      ("tiny_layer", 2, 37, 3),
+                                                      ("tiny_layer", 1, 64, None),
+                                                      ("tiny_layer", 3, 65, 2),
+                                                      ("tiny_layer", 2, 300, 4),
+                                                      ("m130m_layer", 1, 2048, None),
+                                                      ("m130m_layer", 2, 130, 3),
+                                                      ("m2p7b_stack", 1, 200, 4)])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_ssm_scan_ssd_against_the_real_recurrence(B, wname, batch, length, heads, with_state):
+    c = scan_case(wname, batch, length, heads, with_state)
+    dt, dA = O.dt_dA(c["dt_wide"][:, :c["H"]].reshape(batch, length, c["H"]), c["dt_bias"],
+                     c["a_q16"])
+    y_r, st_r, _ = O.ssm_scan_real(c["x"], c["bm"], c["cm"], dt, dA, c["d_q16"], c["p"][2],
+                                   c["p"][3], c["state"])
+    y, st, t_dt, t_da = run_ssd(B, c)
+    assert_exact(t_dt, dt, "dt")
+    assert_exact(t_da, dA, "dA")
+    assert_within_one(y, y_r, "y")
+    assert_within_one(st, st_r, "final state")
+    # against the sequential (per-step rounding) oracle: the propagated bound
+    y_s, _ = ssm_scan_pot_c(c["x"], c["bm"], c["cm"], dt, dA, c["d_q16"], c["p"][2], c["p"][3],
+                            c["state"])
+    bound = sequential_bound(c["cm"], dA, int(c["p"][2] + c["p"][3]))
+    assert np.all(np.abs(y.astype(np.int64) - y_s) <= bound[..., None])
+
+
+def test_ssm_scan_ssd_validation(B):
+    """headdim other than 64 and a short workspace are refused before any launch."""
+    c = scan_case("tiny_layer", 1, 10, 2, False)
+    need = B.lib.fm_ssm_scan_ssd_workspace_size(1, 10, 2, 64, c["N"])
+    assert need > 0
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(B.FmError, match="workspace"):
+        B.fm_ssm_scan_ssd(dev(c["x"]), dev(c["bm"]), dev(c["cm"]), dev(c["dt_wide"]), c["stride"],
+                          dev(c["dt_bias"]), dev(c["a_q16"], torch.int32),
+                          dev(c["d_q16"], torch.int32), dev(c["p"]), 1, 10, 2, 64, c["N"], None,
+                          torch.empty((1, 2, 64, c["N"]), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2, 64), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2), dtype=torch.int32, device="cuda"), ws=ws)
+    x56 = np.zeros((1, 10, 2, 56), np.int8)
+    with pytest.raises(B.FmError, match="headdim"):
+        B.fm_ssm_scan_ssd(dev(x56), dev(c["bm"]), dev(c["cm"]), dev(c["dt_wide"]), c["stride"],
+                          dev(c["dt_bias"]), dev(c["a_q16"], torch.int32),
+                          dev(c["d_q16"], torch.int32), dev(c["p"]), 1, 10, 2, 56, c["N"], None,
+                          torch.empty((1, 2, 56, c["N"]), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2, 56), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2), dtype=torch.int32, device="cuda"),
+                          torch.empty((1, 10, 2), dtype=torch.int32, device="cuda"),
+                          ws=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("wname,batch,seqlen", [("tiny_layer", 2, 150), ("m130m_layer", None, None)])
+def test_layer_prefill_ssd(B, wname, batch, seqlen):
+    """The layer with the chunked scan: every stage before the scan bit for bit,
+    y within 1 of the oracle layer run with the real recurrence, the output
+    within float rounding of it where y agrees (and close everywhere)."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+    w = configs.with_len(configs.get(wname), batch, seqlen)
+    s = w.shape
+    params = synth.workload_params(w, 0)
+    u = synth.workload_activations(w)
+    prep = O.prepare_layer(params)
+    out_o, r, cache_o, _ = O.layer_prefill(prep, s, u, scan=lambda *a: O.ssm_scan_real(*a)[:2])
+    T = w.batch * w.seqlen
+    B.keep_intermediates(True)
+    try:
+        layer = Mamba2Layer(s, params)
+        out = host(layer.prefill(dev(u), scan="ssd"))
+        g = lambda name, dt, shp: layer.tap(name, dt, shp).cpu().numpy()
+        assert_exact(g("x_q", torch.int8, (T, s.d_inner)), r["x_q"].reshape(T, -1), "x_q")
+        assert_exact(g("b_q", torch.int8, (T, s.dstate)), r["B_q"].reshape(T, -1), "B_q")
+        assert_exact(g("c_q", torch.int8, (T, s.dstate)), r["C_q"].reshape(T, -1), "C_q")
+        assert_exact(g("da", torch.int32, (T, s.nheads)), r["dA"].reshape(T, -1), "dA")
+        y = g("y", torch.int32, (T, s.d_inner))
+        assert_within_one(y, r["y"].reshape(T, -1), "y")
+        assert_within_one(host(layer.cache_t["ssm_state"]), cache_o["ssm_state"], "state")
+        rel = np.linalg.norm(out - out_o) / np.linalg.norm(out_o)
+        assert rel <= 1e-3, rel
+        rows = np.all(y == r["y"].reshape(T, -1), axis=1)
+        assert np.mean(rows) > 0.5
+    finally:
+        B.keep_intermediates(False)
