@@ -42,9 +42,16 @@ def log(msg):
 
 
 def scan_source_hash():
-    p = os.path.join(ROOT, "quantized_state_space_fwht_amd", "csrc", "fm_scan.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the scan kernel is compiled from (its file and the
+    device headers it inlines): counters taken on another build are stale."""
+    h = hashlib.sha256()
+    for rel in (("quantized_state_space_fwht_amd", "csrc", "fm_scan.hip"),
+                ("quantized_state_space_fwht_amd", "csrc", "fm_device.hpp"),
+                ("quantized_state_space_fwht_amd", "csrc", "fm_internal.hpp"),
+                ("include", "fm.h")):
+        with open(os.path.join(ROOT, *rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload, per_launch_units):
