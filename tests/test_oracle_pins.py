@@ -563,17 +563,19 @@ def test_stack_is_prenorm_residual():
 def test_quant_stats_hand_computed_cases():
     """Clip counts and squared errors of the three kinds of point, worked by hand.
 
-    Hadamard point, c = 1: r = (0.5, 1, 200, -300) rounds to (0 [tie to even],
-    1, 200, -300); two codes leave [-127, 127]; q = (0, 1, 127, -127), errors
-    (0.5, 0, 73, -173).  Power-of-two float point, p = 1: v = (1.25, -130, 0.75)
+    Hadamard point, c = 1: r = (0.5, 1, 200, -300, 128, 127) rounds to (0 [tie
+    to even], 1, 200, -300, 128, 127); three codes leave [-127, 127] (128 is one
+    of them, 127 is not); q = (0, 1, 127, -127, 127, 127), errors (0.5, 0, 73,
+    -173, 1, 0).  Power-of-two float point, p = 1: v = (1.25, -130, 0.75)
     times 2 = (2.5 -> 2, -260, 1.5 -> 2), one clipped, q = (2, -127, 2), step
     1/2, errors (0.25, -66.5, -0.25).  Q.16 point, p = 0: s = (3.5, 200, -0.25)
     * 2^16, rshr(s, 16) = floor(s/2^16 + 1/2) = (4, 200, 0), one clipped, errors
     (-0.5, 73, -0.25)."""
     QS = O.quant_stats
-    st = QS.hadamard_point_stats(np.array([0.5, 1.0, 200.0, -300.0], np.float32), 1.0)
-    assert st == {"count": 4, "clipped": 2, "sq_err": 0.25 + 73.0 ** 2 + 173.0 ** 2,
-                  "sq_val": 0.25 + 1.0 + 200.0 ** 2 + 300.0 ** 2}
+    st = QS.hadamard_point_stats(np.array([0.5, 1.0, 200.0, -300.0, 128.0, 127.0], np.float32),
+                                 1.0)
+    assert st == {"count": 6, "clipped": 3, "sq_err": 0.25 + 73.0 ** 2 + 173.0 ** 2 + 1.0,
+                  "sq_val": 0.25 + 1.0 + 200.0 ** 2 + 300.0 ** 2 + 128.0 ** 2 + 127.0 ** 2}
     st = QS.pot_float_point_stats(np.array([1.25, -130.0, 0.75], np.float32), 1)
     assert st == {"count": 3, "clipped": 1, "sq_err": 0.0625 + 66.5 ** 2 + 0.0625,
                   "sq_val": 1.25 ** 2 + 130.0 ** 2 + 0.75 ** 2}
@@ -673,6 +675,17 @@ def test_nau_fitted_tables_against_the_chord():
     assert np.array_equal(tabs["chord"], O.EXP2_TABLE_Q30)
     x = np.arange(-(1 << 18), 1, 97, dtype=np.int64)
     assert np.array_equal(O.exp_q16(x, tabs["chord"]), O.exp_q16(x))
+    # the unit follows the knots it is given: 2^v with the minimax knots within one
+    # output step of their float64 interpolant (two half-step roundings), and not
+    # the chord's codes
+    v = np.arange(-3 * 65536, 1, dtype=np.int64)
+    n, fr = v >> 16, v & 0xFFFF
+    ym = tabs["minimax"].astype(np.float64) / 2 ** 30
+    sg, rr = fr >> 13, (fr & 8191) / 8192.0
+    want = (ym[sg] * (1 - rr) + ym[sg + 1] * rr) * 2.0 ** n * 65536.0
+    got = O.exp2_q16(v, tabs["minimax"])
+    assert np.max(np.abs(got - want)) <= 1.0
+    assert not np.array_equal(got, O.exp2_q16(v))
 
 
 def test_narrow_state_hand_cases():
