@@ -216,7 +216,6 @@ __global__ __launch_bounds__(kOutThreads) void ssd_chunk_out_kernel(ScanArgs A,
     __shared__ double pre_s[Q], lg_s[Q], z_s[Q];
     __shared__ double M[Q][Q + 1];
     __shared__ __attribute__((aligned(16))) int8_t cs[Q][NR];
-    __shared__ __attribute__((aligned(16))) int8_t bsm[Q][NR];
     __shared__ __attribute__((aligned(16))) int8_t xs[Q][kSsdP + 16];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int H = (int)A.nheads;
@@ -239,15 +238,25 @@ __global__ __launch_bounds__(kOutThreads) void ssd_chunk_out_kernel(ScanArgs A,
         av = (double)A.da_out[i] * 0x1p-16;
         dv = (double)A.dt_out[i] * 0x1p-8;
     }
+    // B operands of G = C B^T straight from memory (the chunk's 8 KB sit in L2):
+    // lane holds B codes [s = 16 j + lr][k0 + 8 lk .. + 7]; rows past the end are 0
+    int64_t gb[4][N / 32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int sr = 16 * j + lr;
+        const int8_t* brow = A.bm + ((int64_t)b * L + t0 + sr) * N + 8 * lk;
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k)
+            gb[j][k] = sr < q ? *reinterpret_cast<const int64_t*>(brow + 32 * k) : (int64_t)0;
+    }
     {  // staging: every global load of a thread issued before any LDS store
-        constexpr int CL = Q * N / 16 / kOutThreads;  // 16-byte pieces of C (and of B)
-        int4 cv[CL], bv[CL];
+        constexpr int CL = Q * N / 16 / kOutThreads;  // 16-byte pieces of C
+        int4 cv[CL];
 #pragma unroll
         for (int k = 0; k < CL; ++k) {
             const int e = tid + kOutThreads * k, r = e / (N / 16), col = 16 * (e % (N / 16));
             const int64_t off = ((int64_t)b * L + t0 + r) * N + col;
             cv[k] = r < q ? *reinterpret_cast<const int4*>(A.cm + off) : int4{0, 0, 0, 0};
-            bv[k] = r < q ? *reinterpret_cast<const int4*>(A.bm + off) : int4{0, 0, 0, 0};
         }
         const int xr = tid >> 2, xc = 16 * (tid & 3);  // x: 64 rows of 64 bytes
         int4 xv = {0, 0, 0, 0};
@@ -257,16 +266,8 @@ __global__ __launch_bounds__(kOutThreads) void ssd_chunk_out_kernel(ScanArgs A,
         for (int k = 0; k < CL; ++k) {
             const int e = tid + kOutThreads * k, r = e / (N / 16), col = 16 * (e % (N / 16));
             *reinterpret_cast<int4*>(&cs[r][col]) = cv[k];
-            *reinterpret_cast<int4*>(&bsm[r][col]) = bv[k];
         }
         *reinterpret_cast<int4*>(&xs[xr][xc]) = xv;
-    }
-    if (wave == 0) {
-        pre_s[lane] = wave_prefix_prod(av, lane);  // decay from the chunk start to t
-        // prod_{s<r<=t} a_r = 2^(lg_t - lg_s) when no a_r in (s, t] is 0, i.e. z_t == z_s,
-        // with lg, z the prefix sums of log2 a (a > 0) and of [a == 0]
-        lg_s[lane] = wave_prefix_sum(av > 0.0 ? log2(av) : 0.0, lane);
-        z_s[lane] = wave_prefix_sum(av > 0.0 ? 0.0 : 1.0, lane);
     }
     __syncthreads();
     {  // G = C B^T, exact: wave w takes the t tile w, every s
@@ -274,17 +275,22 @@ __global__ __launch_bounds__(kOutThreads) void ssd_chunk_out_kernel(ScanArgs A,
 #pragma unroll
         for (int j = 0; j < 4; ++j) g[j] = i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int k0 = 0; k0 < N; k0 += 32) {
-            const int64_t ac = *reinterpret_cast<const int64_t*>(&cs[16 * wave + lr][k0 + 8 * lk]);
+        for (int k = 0; k < N / 32; ++k) {
+            const int64_t ac = *reinterpret_cast<const int64_t*>(&cs[16 * wave + lr][32 * k + 8 * lk]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                g[j] = mfma_i8(ac, *reinterpret_cast<const int64_t*>(&bsm[16 * j + lr][k0 + 8 * lk]),
-                               g[j]);
+            for (int j = 0; j < 4; ++j) g[j] = mfma_i8(ac, gb[j][k], g[j]);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) M[16 * wave + 4 * lk + v][16 * j + lr] = (double)g[j][v];
+    }
+    if (wave == 0) {  // beside the other waves' products
+        pre_s[lane] = wave_prefix_prod(av, lane);  // decay from the chunk start to t
+        // prod_{s<r<=t} a_r = 2^(lg_t - lg_s) when no a_r in (s, t] is 0, i.e. z_t == z_s,
+        // with lg, z the prefix sums of log2 a (a > 0) and of [a == 0]
+        lg_s[lane] = wave_prefix_sum(av > 0.0 ? log2(av) : 0.0, lane);
+        z_s[lane] = wave_prefix_sum(av > 0.0 ? 0.0 : 1.0, lane);
     }
     __syncthreads();
     // M[t][s] = G[t][s] prod_{s<r<=t} a_r dt_s for s <= t, 0 above: wave w takes the
