@@ -28,7 +28,7 @@ follows, using these short names for the pages:
        abstract (outlier channels in Mamba activations).
 
 Where the pages leave a step open the docstring says "reading:" and states the
-choice; the same readings are listed in the design doc.
+choice.
 
 Pinning: tests/test_oracle_pins.py checks every function here against
 mathematics the pages fix or a library routine (see each test's docstring).

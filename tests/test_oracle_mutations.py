@@ -66,8 +66,10 @@ MUTATIONS = [
 
 
 def _copy(dst):
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
-        ".git", "_work", "gpurun_out", "__pycache__", ".pytest_cache", "*.so", "profiles"))
+    """The pins need the oracle, the tests and the package's configs / synth."""
+    skip = shutil.ignore_patterns("__pycache__", ".pytest_cache", "*.so", "csrc")
+    for sub in ("oracle", "tests", "quantized_state_space_fwht_amd"):
+        shutil.copytree(os.path.join(ROOT, sub), os.path.join(dst, sub), ignore=skip)
 
 
 def _run_pins(root):
