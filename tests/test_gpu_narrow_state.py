@@ -113,6 +113,12 @@ def test_layer_decode_narrow(B, wname, batch, bits, shift):
     _decode_case(B, wname, batch, 16, 6, bits, shift)
 
 
+@pytest.mark.parametrize("batch", [64, 65])
+def test_layer_decode_narrow_many_rows(B, batch):
+    """64 rows (the fused step's largest) and 65 (the general launch sequence)."""
+    _decode_case(B, "tiny_layer", batch, 12, 3, 16, None)
+
+
 def test_layer_decode_narrow_static(B):
     _decode_case(B, "m130m_layer", 3, 20, 4, 16, None, mode="static")
 

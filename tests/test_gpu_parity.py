@@ -387,9 +387,12 @@ def test_layer_prefill_dynamic(B, wname, batch, seqlen):
         B.keep_intermediates(False)
 
 
-def test_layer_decode_continues_prefill(B):
+# 64 rows: the largest one-token step of the fused five-kernel form; 65: the
+# general launch sequence with the windows and states carried in
+@pytest.mark.parametrize("batch", [2, 64, 65])
+def test_layer_decode_continues_prefill(B, batch):
     from quantized_state_space_fwht_amd.runtime import Mamba2Layer
-    w, params, u = _layer_case("tiny_layer", 2, 40)
+    w, params, u = _layer_case("tiny_layer", batch, 40)
     s = w.shape
     prep = O.prepare_layer(params)
     L0 = 30
