@@ -110,6 +110,12 @@ def test_layer_validation_and_workspace_query(lib):
         == FM_ERR_SHAPE
     assert f(ctypes.byref(d), None, None, None, 1, 16, None, None, None, None, 0, None) \
         == FM_ERR_NULL
+    # empty calls are refused, not launched: a batch or a length of 0
+    fake = 1 << 20
+    weights = (ctypes.c_void_p * 11)(*([fake] * 11))
+    for batch, length in ((0, 16), (1, 0), (-1, 4)):
+        assert f(ctypes.byref(d), ctypes.cast(weights, ctypes.c_void_p), None, fake, batch, length,
+                 2 * fake, None, fake, fake, 1 << 40, None) == FM_ERR_SHAPE
 
 
 def test_qparams_from_stats_on_host(lib):

@@ -355,6 +355,7 @@ def _check_layer_intermediates(layer, r, T, s):
 
 
 @pytest.mark.parametrize("wname,batch,seqlen", [("tiny_layer", None, None), ("tiny_layer", 3, 50),
+                                                ("tiny_layer", 1, 1), ("tiny_layer", 4, 1),
                                                 ("m130m_layer", None, None)])
 def test_layer_prefill_dynamic(B, wname, batch, seqlen):
     from quantized_state_space_fwht_amd.runtime import Mamba2Layer
