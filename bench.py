@@ -97,6 +97,24 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=30):
 FP64_PEAK_TFLOPS = 78.6   # MI355X float64 vector / matrix rate
 
 
+def measured_copy_gbs(torch, nbytes=512 << 20, reps=10):
+    """Achievable HBM bandwidth: read + write bytes of a device-to-device copy."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def ssd_prefill_bench(torch, B, layer, u, out, stream, w, steps, warmup, ms_sequential):
     """The same layer prefill with the chunked (SSD-form) scan variant.  Its
     contract differs from the method's (no per-step rounding of the state), so
@@ -678,6 +696,14 @@ def main():
         del layer
         torch.cuda.empty_cache()
         line["decode"] = decode_bench(torch, configs, synth, max_steps=args.decode_steps)
+    # the achievable HBM rate on this machine: a device-to-device copy of 512 MiB
+    hbm_meas = measured_copy_gbs(torch)
+    line["measured_peaks"] = {"hbm_copy_GBs": round(hbm_meas, 1),
+                              "how": "512 MiB device-to-device copy, 10 timed, 2 x bytes"}
+    if "decode" in line:
+        for r in [line["decode"]["roofline"]] + [v["roofline"] for v in
+                                                 line["decode"].get("narrow_state", {}).values()]:
+            r["frac_of_measured"] = round(r["achieved"] / hbm_meas, 4)
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
