@@ -130,13 +130,29 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
         const int nt = (int)(L - t0 < (kConvThreads / 64) * kConvTL ? L - t0
                                                                     : (kConvThreads / 64) * kConvTL);
         const int64_t row0 = (int64_t)blockIdx.z * L + t0;
-        for (int i = threadIdx.x; i < nt * H; i += kConvThreads) {
-            const int ti = i / H, h = i - ti * H;
-            const int64_t row = row0 + ti;
-            const float raw = A.dt_raw[row * A.dt_stride + h];
-            const int32_t dt = nau_softplus_f(f2i_sat(rintf((raw + A.dt_bias[h]) * 65536.0f)), tab);
-            A.dt_out[row * H + h] = dt;
-            A.da_out[row * H + h] = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)A.a_q16[h], 16)), tab);
+        constexpr int kB = 8;  // pairs per thread whose loads go out together
+        for (int i0 = threadIdx.x; i0 < nt * H; i0 += kB * kConvThreads) {
+            float raw[kB], bias[kB];
+            int32_t aq[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int i = i0 + k * kConvThreads;
+                const int ti = i / H, h = i - ti * H;
+                const bool ok = i < nt * H;
+                raw[k] = ok ? A.dt_raw[(row0 + ti) * A.dt_stride + h] : 0.0f;
+                bias[k] = ok ? A.dt_bias[h] : 0.0f;
+                aq[k] = ok ? A.a_q16[h] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int i = i0 + k * kConvThreads;
+                if (i >= nt * H) break;
+                const int ti = i / H, h = i - ti * H;
+                const int64_t row = row0 + ti;
+                const int32_t dt = nau_softplus_f(f2i_sat(rintf((raw[k] + bias[k]) * 65536.0f)), tab);
+                A.dt_out[row * H + h] = dt;
+                A.da_out[row * H + h] = nau_exp_f(sat32(rshr((int64_t)dt * (int64_t)aq[k], 16)), tab);
+            }
         }
         return;
     }
