@@ -173,7 +173,8 @@ fm_status fm_w8a8_gemm(const int8_t* a, const int8_t* b, int64_t m, int64_t n, i
 // ---------------------------------------------------------------- fm_conv1d_pot
 size_t fm_conv1d_pot_workspace_size(int64_t batch, int64_t len, int64_t d_inner, int64_t dstate) {
     if (batch < 0 || len < 0 || d_inner < 0 || dstate < 0) return 0;
-    return 256 + align256((size_t)(batch * len * (d_inner + 2 * dstate)) * sizeof(int32_t));
+    return 256 + 3 * kSlotRegionWords * sizeof(int32_t) +
+           align256((size_t)(batch * len * (d_inner + 2 * dstate)) * sizeof(int32_t));
 }
 
 fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch, int64_t len,
@@ -227,11 +228,12 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
     const size_t need = fm_conv1d_pot_workspace_size(batch, len, d_inner, dstate);
     if ((st = check_ws(workspace, workspace_bytes, need, who)) != FM_OK) return st;
     float* amax_x = (float*)workspace;           // word 0: max|xBC|
-    int32_t* amax_q = (int32_t*)workspace + 1;   // words 1..3
+    int32_t* amax_q = (int32_t*)workspace + 1;   // words 1..3: the part maxima
     a.xbc_amax = amax_x;
     a.amax_q16 = amax_q;
-    a.s16 = (int32_t*)((char*)workspace + 256);
-    if ((st = zero_words(workspace, 4, stream)) != FM_OK) return st;
+    a.amax_slots = (int32_t*)((char*)workspace + 256);  // three slot regions
+    a.s16 = (int32_t*)((char*)workspace + 256 + 3 * kSlotRegionWords * sizeof(int32_t));
+    if ((st = zero_words(workspace, 64 + 3 * kSlotRegionWords, stream)) != FM_OK) return st;
     if ((st = amax_strided_run(xbc, batch * len, ch, xbc_row_stride, amax_x, stream)) != FM_OK)
         return st;
     return conv_run(a, stream);
@@ -367,7 +369,8 @@ fm_status fm_nau_eval_knots(fm_nau_fn fn, const int64_t* knots_q30, const int32_
 // ---------------------------------------------------------------- fm_gate_norm_quant
 size_t fm_gate_norm_quant_workspace_size(int64_t rows, int64_t d_inner) {
     if (rows < 0 || d_inner < 0) return 0;
-    return 256 + align256((size_t)(rows * d_inner) * sizeof(float));
+    return 256 + kSlotRegionWords * sizeof(int32_t) +
+           align256((size_t)(rows * d_inner) * sizeof(float));
 }
 
 fm_status fm_gate_norm_quant(const int32_t* y, const float* z, int64_t z_row_stride,
@@ -410,8 +413,9 @@ fm_status fm_gate_norm_quant(const int32_t* y, const float* z, int64_t z_row_str
     const size_t need = fm_gate_norm_quant_workspace_size(rows, d_inner);
     if ((st = check_ws(workspace, workspace_bytes, need, who)) != FM_OK) return st;
     g.amax_ws = (float*)workspace;
-    g.rot_ws = (float*)((char*)workspace + 256);
-    if ((st = zero_words(workspace, 1, stream)) != FM_OK) return st;
+    g.amax_slots = (int32_t*)((char*)workspace + 256);  // one slot region
+    g.rot_ws = (float*)((char*)workspace + 256 + kSlotRegionWords * sizeof(int32_t));
+    if ((st = zero_words(workspace, 64 + kSlotRegionWords, stream)) != FM_OK) return st;
     return gate_run(g, stream);
 }
 

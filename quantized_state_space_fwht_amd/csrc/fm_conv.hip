@@ -182,12 +182,15 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
         qstat_flush(sx, A.qs, FM_QP_XBC);
         if (!kDyn) qstat_flush(sp, A.qs, FM_QP_X + part);
     }
-    // per-wave maxima (all lanes of a wave are in one part)
+    // per-wave maxima (all lanes of a wave are in one part); dynamic: into a slot
+    // of the part's region, by the wave's time block
     amax = wave_max_i32(amax);
     xmax = wave_max_f32(xmax);
     if (lane == 0) {
         if (kDyn) {
-            if (amax > 0) atomic_max_i32(&A.amax_q16[part], amax);
+            const int64_t tb = (int64_t)blockIdx.z * gridDim.y * (kConvThreads / 64) +
+                               (int64_t)blockIdx.y * (kConvThreads / 64) + wave;
+            slot_max(A.amax_slots + part * kSlotRegionWords, tb, amax);
         } else if (A.amax_stats) {
             if (amax > 0) atomic_max_i32(&A.amax_stats[1 + part], amax);
             if (xmax > 0.0f) atomic_max_nonneg_f32((float*)&A.amax_stats[0], xmax);
@@ -197,50 +200,84 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
 
 // Dynamic second pass: exponents from the maxima, Q.16 -> int8 codes.
 // grid.y = token row, threads over groups of 4 channels.
+constexpr int kRqRows = 4;  // rows per thread in the requantization pass
+
 __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
     const int di = (int)A.d_inner, N = (int)A.dstate;
     const int c = (blockIdx.x * kConvThreads + threadIdx.x) * 4;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        A.p_out[0] = pot_from_f32(*A.xbc_amax);
-        for (int i = 0; i < 3; ++i) A.p_out[1 + i] = pot_from_q16(A.amax_q16[i]);
-        if (A.amax_stats) {
-            atomicMax((unsigned int*)&A.amax_stats[0], __float_as_uint(*A.xbc_amax));
-            for (int i = 0; i < 3; ++i) atomicMax(&A.amax_stats[1 + i], A.amax_q16[i]);
+    const bool active = c < K.ch;  // idle lanes stay for the statistics' wave sums
+    const int64_t rows = A.batch * A.len;
+    // kRqRows rows per thread and round, their loads issued before any use (the
+    // first round's before the maxima are known)
+    int4 sr[kRqRows];
+    auto load_round = [&](int64_t r0) {
+#pragma unroll
+        for (int k = 0; k < kRqRows; ++k)
+            sr[k] = r0 + k < rows ? *reinterpret_cast<const int4*>(A.s16 + (r0 + k) * K.ch + c)
+                                  : make_int4(0, 0, 0, 0);
+    };
+    const int64_t rfirst = (int64_t)blockIdx.y * kRqRows;
+    if (active) load_round(rfirst);
+    // the part maxima from the conv pass's slot regions: wave 0 reduces, LDS shares
+    __shared__ int32_t pm_s[3];
+    if (threadIdx.x < 64) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int32_t v = slots_wave_max(A.amax_slots + i * kSlotRegionWords);
+            if (threadIdx.x == 0) pm_s[i] = v;
         }
     }
-    const bool active = c < K.ch;  // idle lanes stay for the statistics' wave sums
+    __syncthreads();
+    const int32_t pm[3] = {pm_s[0], pm_s[1], pm_s[2]};
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        A.p_out[0] = pot_from_f32(*A.xbc_amax);
+        for (int i = 0; i < 3; ++i) {
+            A.amax_q16[i] = pm[i];
+            A.p_out[1 + i] = pot_from_q16(pm[i]);
+        }
+        if (A.amax_stats) {
+            atomicMax((unsigned int*)&A.amax_stats[0], __float_as_uint(*A.xbc_amax));
+            for (int i = 0; i < 3; ++i) atomicMax(&A.amax_stats[1 + i], pm[i]);
+        }
+    }
     const int part = !active ? 0 : (c < di ? 0 : (c < di + N ? 1 : 2));
+    const int32_t amax_part = part == 0 ? pm[0] : (part == 1 ? pm[1] : pm[2]);
     // sat8(rshr(s, 16 - p)): s * 2^(p-16) + 1/2 is exact in float64 for every
     // p in [-24, 24] (|s| < 2^31), so floor gives rshr's value, shifts up included
-    const double sc = __builtin_ldexp(1.0, pot_from_q16(A.amax_q16[part]) - 16);
+    const double sc = __builtin_ldexp(1.0, pot_from_q16(amax_part) - 16);
     auto q8 = [&](int32_t v) {
         const double q = __builtin_floor(__builtin_fma((double)v, sc, 0.5));
         return (signed char)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
     };
-    const int64_t rows = A.batch * A.len;
     QStat st;
-    const double step = __builtin_ldexp(1.0, 16 - pot_from_q16(A.amax_q16[part]));
-    for (int64_t row = blockIdx.y; active && row < rows; row += gridDim.y) {
-        const int4 s = *reinterpret_cast<const int4*>(A.s16 + row * K.ch + c);
-        char4 q;
-        q.x = q8(s.x);
-        q.y = q8(s.y);
-        q.z = q8(s.z);
-        q.w = q8(s.w);
-        if (A.qs) {
-            const int32_t sv[4] = {s.x, s.y, s.z, s.w};
-            const signed char qc[4] = {q.x, q.y, q.z, q.w};
+    const double step = __builtin_ldexp(1.0, 16 - pot_from_q16(amax_part));
+    for (int64_t r0 = rfirst; active && r0 < rows; r0 += (int64_t)gridDim.y * kRqRows) {
+        if (r0 != rfirst) load_round(r0);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const double qr = __builtin_floor(__builtin_fma((double)sv[k], sc, 0.5));
-                st.add((double)sv[k] * 0x1p-16, (double)qc[k], step * 0x1p-16,
-                       __builtin_fabs(qr) > 127.0);
+        for (int k = 0; k < kRqRows; ++k) {
+            const int64_t row = r0 + k;
+            if (row >= rows) break;
+            const int4 s = sr[k];
+            char4 q;
+            q.x = q8(s.x);
+            q.y = q8(s.y);
+            q.z = q8(s.z);
+            q.w = q8(s.w);
+            if (A.qs) {
+                const int32_t sv[4] = {s.x, s.y, s.z, s.w};
+                const signed char qc[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double qr = __builtin_floor(__builtin_fma((double)sv[e], sc, 0.5));
+                    st.add((double)sv[e] * 0x1p-16, (double)qc[e], step * 0x1p-16,
+                           __builtin_fabs(qr) > 127.0);
+                }
             }
+            if (part == 0) *reinterpret_cast<char4*>(A.x_out + row * di + c) = q;
+            else if (part == 1) *reinterpret_cast<char4*>(A.b_out + row * N + (c - di)) = q;
+            else *reinterpret_cast<char4*>(A.c_out + row * N + (c - di - N)) = q;
         }
-        if (part == 0) *reinterpret_cast<char4*>(A.x_out + row * di + c) = q;
-        else if (part == 1) *reinterpret_cast<char4*>(A.b_out + row * N + (c - di)) = q;
-        else *reinterpret_cast<char4*>(A.c_out + row * N + (c - di - N)) = q;
     }
     if (A.qs)  // a wave may span two parts: one wave sum per part
         for (int pt = 0; pt < 3; ++pt)
@@ -285,9 +322,9 @@ fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     }
     fm_status st = check_launch("conv_silu_kernel");
     if (st != FM_OK || !K.dynamic) return st;
-    const int64_t rows = a.batch * a.len;
+    const int64_t rows = a.batch * a.len, rblocks = (rows + kRqRows - 1) / kRqRows;
     dim3 rgrid((unsigned)((K.ch / 4 + kConvThreads - 1) / kConvThreads),
-               (unsigned)(rows < 65535 ? rows : 65535));
+               (unsigned)(rblocks < 65535 ? rblocks : 65535));
     requant_kernel<<<rgrid, kConvThreads, 0, s>>>(K);
     return check_launch("requant_kernel");
 }

@@ -253,6 +253,26 @@ __device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
     return v;
 }
 
+// Slotted grid maxima.  A region is kSlots words kSlotStride words (256 bytes)
+// apart, zeroed before the producing launch.  Producers add their value to one
+// slot, chosen by a key (a block or wave index), with an atomic max that
+// returns nothing; consumers reduce the slots with one load per lane.  Atomics
+// and coherent reads of one cache line from thousands of waves serialize at
+// the memory side; spread over 32 lines they do not.  Values are non-negative
+// (magnitudes, or the bit patterns of non-negative floats, which order alike).
+constexpr int kSlots = 32;
+constexpr int kSlotStride = 64;
+constexpr int kSlotRegionWords = kSlots * kSlotStride;
+
+__device__ __forceinline__ void slot_max(int32_t* region, int64_t key, int32_t v) {
+    if (v > 0) atomicMax(region + (int)(key % kSlots) * kSlotStride, v);
+}
+// every lane of the wave must call it
+__device__ __forceinline__ int32_t slots_wave_max(const int32_t* region) {
+    const int lane = threadIdx.x & 63;
+    return wave_max_i32(lane < kSlots ? region[lane * kSlotStride] : 0);
+}
+
 // Maxima shared by a whole grid.  The stored value only grows, so the atomic
 // is skipped when a plain (device-coherent) read already covers v: a stale
 // read can only cost an extra atomic, never lose one.  Thousands of waves

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
             G.rowmax[row] = m;
             return;
         }
-        if (dyn) atomic_max_nonneg_f32(G.amax_ws, m);
+        if (dyn) slot_max(G.amax_slots, row, (int32_t)__float_as_uint(m));
         if (G.amax_stats) atomic_max_nonneg_f32(G.amax_stats, m);
         if (!dyn && row == 0) *G.scale_out = 1.0f / c;
     }
@@ -138,10 +138,10 @@ fm_status gate_run(const GateArgs& g, hipStream_t s) {
         if (st != FM_OK) return st;
     }
     if (g.mode == FM_SCALE_DYNAMIC)
-        return hq_quant_rotated(g.rot_ws, g.rows, g.d_inner, FM_SCALE_DYNAMIC, 0, 0, g.amax_ws, g.q,
-                                g.scale_out, s, g.qs, FM_QP_G);
+        return hq_quant_rotated(g.rot_ws, g.rows, g.d_inner, FM_SCALE_DYNAMIC, 0, 0, g.amax_ws,
+                                g.amax_slots, g.q, g.scale_out, s, g.qs, FM_QP_G);
     if (g.rows == 0) return hq_quant_rotated(g.rot_ws, 0, g.d_inner, g.mode, g.scoe, g.sshift,
-                                             nullptr, g.q, g.scale_out, s);
+                                             nullptr, nullptr, g.q, g.scale_out, s);
     return FM_OK;
 }
 

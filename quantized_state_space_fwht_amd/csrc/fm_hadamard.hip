@@ -15,6 +15,7 @@
 namespace fm {
 
 constexpr int kHqThreads = 256;  // 4 waves, one 256-block each per iteration
+constexpr int kHqBatch = 4;      // quant pass: blocks per wave whose loads go out together
 
 __device__ __forceinline__ void block_max_to(float m, float* a0, float* a1) {
     __shared__ float red[kHqThreads / 64];
@@ -54,33 +55,66 @@ __global__ __launch_bounds__(kHqThreads) void hq_amax_kernel(const float* __rest
 }
 
 __device__ __forceinline__ float scale_coef(fm_scale_mode mode, int32_t scoe, int32_t sshift,
-                                            const float* amax_ws) {
-    if (mode == FM_SCALE_DYNAMIC) {
-        float amax = *amax_ws;
-        return amax == 0.0f ? 1.0f : 127.0f / amax;
-    }
+                                            float amax) {
+    if (mode == FM_SCALE_DYNAMIC) return amax == 0.0f ? 1.0f : 127.0f / amax;
     return ldexpf((float)scoe, -sshift);
 }
 
 // pass 2 (or the only pass in static mode): rotate again and quantize
+// amax_slots (dynamic, nullable): the grid maximum is the slot region's, and
+// block 0 also stores it to amax_ws; otherwise it is read from amax_ws.
 __global__ __launch_bounds__(kHqThreads) void hq_quant_kernel(
     const float* __restrict__ x, int64_t nblk_total, fm_scale_mode mode, int32_t scoe,
-    int32_t sshift, const float* amax_ws, char4* __restrict__ q, float* scale_out,
-    float* amax_stats, int rotated_input, fm_quant_stats* qs, int qpt) {
+    int32_t sshift, float* amax_ws, const int32_t* amax_slots, char4* __restrict__ q,
+    float* scale_out, float* amax_stats, int rotated_input, fm_quant_stats* qs, int qpt) {
     int lane = threadIdx.x & 63;
-    float c = scale_coef(mode, scoe, sshift, amax_ws);
-    const float s_dq = 1.0f / c;
-    if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s_dq;
     int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
     int64_t stride = (int64_t)gridDim.x * (kHqThreads / 64);
+    // the first block's load goes out before the scale is known
+    float4 v0 = wv < nblk_total ? reinterpret_cast<const float4*>(x + wv * 256)[lane]
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float amax = 0.0f;
+    if (mode == FM_SCALE_DYNAMIC) {
+        if (amax_slots) {  // wave 0 reduces the slots, LDS shares
+            __shared__ float amax_s;
+            if (threadIdx.x < 64) {
+                const float v = __int_as_float(slots_wave_max(amax_slots));
+                if (threadIdx.x == 0) amax_s = v;
+            }
+            __syncthreads();
+            amax = amax_s;
+        } else {
+            amax = *amax_ws;
+        }
+    }
+    float c = scale_coef(mode, scoe, sshift, amax);
+    const float s_dq = 1.0f / c;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *scale_out = s_dq;
+        if (amax_slots) *amax_ws = amax;
+    }
     float m = 0.0f;
     QStat st;
-    for (int64_t b = wv; b < nblk_total; b += stride) {
-        float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
-        if (!rotated_input) v = fwht256_lane(v, lane);
-        m = fmaxf(m, absmax4(v));
-        q[b * 64 + lane] = quant4(v, c);
-        if (qs) quant_stat4(st, v, c, s_dq);
+    // kHqBatch blocks per wave and round, their loads issued together
+    for (int64_t b0 = wv; b0 < nblk_total; b0 += kHqBatch * stride) {
+        float4 vb[kHqBatch];
+#pragma unroll
+        for (int k = 0; k < kHqBatch; ++k) {
+            const int64_t b = b0 + k * stride;
+            vb[k] = (b0 == wv && k == 0) ? v0
+                    : (b < nblk_total ? reinterpret_cast<const float4*>(x + b * 256)[lane]
+                                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+        }
+#pragma unroll
+        for (int k = 0; k < kHqBatch; ++k) {
+            const int64_t b = b0 + k * stride;
+            if (b >= nblk_total) break;
+            float4 v = vb[k];
+            if (!rotated_input) v = fwht256_lane(v, lane);
+            m = fmaxf(m, absmax4(v));
+            q[b * 64 + lane] = quant4(v, c);
+            if (qs) quant_stat4(st, v, c, s_dq);
+        }
     }
     if (qs) qstat_flush(st, qs, qpt);
     if (amax_stats) block_max_to(m, amax_stats, nullptr);
@@ -118,21 +152,24 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
         hq_amax_kernel<<<hq_grid((nb + 3) / 4, 512), kHqThreads, 0, s>>>(x, nb, amax_ws,
                                                                          amax_stats);
         if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
-        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, (char4*)q,
-                                                 scale_out, nullptr, 0, qs, qpt);
+        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, nullptr,
+                                                 (char4*)q, scale_out, nullptr, 0, qs, qpt);
     } else {
-        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, nullptr, (char4*)q,
-                                                 scale_out, amax_stats, 0, qs, qpt);
+        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, nullptr, nullptr,
+                                                 (char4*)q, scale_out, amax_stats, 0, qs, qpt);
     }
     return check_launch("hq_quant_kernel");
 }
 
 fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
-                           int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
-                           float* scale_out, hipStream_t s, fm_quant_stats* qs, int qpt) {
+                           int32_t scoe, int32_t sshift, float* amax_ws,
+                           const int32_t* amax_slots, int8_t* q, float* scale_out,
+                           hipStream_t s, fm_quant_stats* qs, int qpt) {
     int64_t nb = rows * (k / 256);
-    hq_quant_kernel<<<hq_grid(nb), kHqThreads, 0, s>>>(r, nb, mode, scoe, sshift, amax_ws,
-                                                       (char4*)q, scale_out, nullptr, 1, qs, qpt);
+    hq_quant_kernel<<<hq_grid((nb + kHqBatch - 1) / kHqBatch), kHqThreads, 0, s>>>(
+                                                       r, nb, mode, scoe, sshift, amax_ws,
+                                                       amax_slots, (char4*)q, scale_out, nullptr,
+                                                       1, qs, qpt);
     return check_launch("hq_quant_kernel(rotated)");
 }
 

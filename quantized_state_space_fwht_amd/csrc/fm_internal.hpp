@@ -44,6 +44,12 @@ enum SmallSlot {
     kP = 8,         // int[4]: p_c, p_x, p_B, p_C
     kSmallWords = 16
 };
+// Slot regions of a layer workspace (slotted grid maxima, fm_device.hpp)
+enum SlotRegion {
+    kRegionConvX = 0,  // conv pass: max |SiLU| of x, B, C in Q.16 (three regions)
+    kRegionG = 3,      // gate pass: max |n H| as float bits
+    kRegions = 4
+};
 
 // Publish what a layer call used into qp (scales, exponents, statistics) and,
 // when given, the exponents into the cache.  One thread, after every kernel
@@ -78,10 +84,12 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
                  int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
                  hipStream_t s, fm_quant_stats* qs = nullptr, int qpt = 0);
 // second pass only: quantize already-rotated rows r (dynamic: amax_ws holds the max)
+// amax_slots (dynamic): the slot region holding the grid maximum; it is also
+// written to amax_ws
 fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
-                           int32_t scoe, int32_t sshift, const float* amax_ws, int8_t* q,
-                           float* scale_out, hipStream_t s, fm_quant_stats* qs = nullptr,
-                           int qpt = 0);
+                           int32_t scoe, int32_t sshift, float* amax_ws,
+                           const int32_t* amax_slots, int8_t* q, float* scale_out,
+                           hipStream_t s, fm_quant_stats* qs = nullptr, int qpt = 0);
 
 struct GemmEpilogue {
     int32_t* acc = nullptr;
@@ -152,7 +160,8 @@ struct ConvArgs {
     int8_t* state_out;
     int8_t* xbc_q;
     int32_t* s16;              // dynamic: [T, ch] Q.16 SiLU outputs
-    int32_t* amax_q16;         // dynamic: [3] zeroed before
+    int32_t* amax_q16;         // dynamic: [3] the part maxima (written by the requant pass)
+    int32_t* amax_slots;       // dynamic: three slot regions (x, B, C) zeroed before
     int8_t* x_out;
     int8_t* b_out;
     int8_t* c_out;
@@ -224,7 +233,8 @@ struct GateArgs {
     float* amax_stats;
     float* normed_out;
     float* rot_ws;     // dynamic: [rows, d_inner] rotated values between passes
-    float* amax_ws;    // dynamic: 1 float
+    float* amax_ws;    // dynamic: 1 float, the grid maximum (written by the quant pass)
+    int32_t* amax_slots;  // dynamic: a slot region zeroed before (the gate pass's maxima)
     const float* sz;   // nullable: SiLU(z) already formed ([rows, d_inner], Q.16 as float)
     fm_quant_stats* qs;  // nullable: statistics of the out_proj input point
     float* rowmax;     // nullable: one-token form, rotated rows to rot_ws and their maxima

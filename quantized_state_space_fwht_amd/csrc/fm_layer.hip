@@ -11,6 +11,7 @@ namespace fm {
 
 struct LayerWs {
     uint32_t* small;
+    int32_t* slots;  // kRegions slot regions (grid maxima of the prefill passes)
     float* un;       // pre-norm output [T, dm]
     int8_t* u_q;     // [T, dm]
     float* v;        // [T, dip]
@@ -38,6 +39,7 @@ static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void
     Arena ar(base);
     LayerWs w;
     w.small = ar.take<uint32_t>(kSmallWords);
+    w.slots = ar.take<int32_t>((size_t)kRegions * kSlotRegionWords);
     w.un = ar.take<float>((size_t)T * dm);
     w.u_q = ar.take<int8_t>((size_t)T * dm);
     w.v = ar.take<float>((size_t)T * dip);
@@ -90,11 +92,14 @@ void set_timing_events(void* start, void* stop) {
     g_ev_stop = (hipEvent_t)stop;
 }
 
-// zero the small block; optionally load the exponents (static values or a device copy)
-__global__ void layer_setup_kernel(uint32_t* small, const int32_t* p_src, int p0, int p1, int p2,
-                                   int p3, int how) {
+// zero the small block and the slots of the slot regions; optionally load the
+// exponents (static values or a device copy)
+__global__ void layer_setup_kernel(uint32_t* small, int32_t* slots, const int32_t* p_src, int p0,
+                                   int p1, int p2, int p3, int how) {
     const int i = threadIdx.x;
-    if (i < kSmallWords) small[i] = 0u;
+    for (int k = i; k < kSmallWords; k += blockDim.x) small[k] = 0u;
+    for (int k = i; k < kRegions * kSlots; k += blockDim.x)
+        slots[(k / kSlots) * kSlotRegionWords + (k % kSlots) * kSlotStride] = 0;
     __syncthreads();
     if (i == 0 && how != 0) {
         int32_t* p = (int32_t*)(small + kP);
@@ -117,6 +122,7 @@ __global__ void layer_setup_kernel(uint32_t* small, const int32_t* p_src, int p0
 // scale.  Workgroup 0 also zeroes the call's small block and loads the frozen
 // exponents (nothing in this kernel reads the block).
 constexpr int kStepRowThreads = 256;
+static_assert(kSmallWords <= kStepRowThreads, "workgroup 0 zeroes the small block in one pass");
 
 struct StepRowsArgs {
     const float* u;
@@ -233,12 +239,12 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
     } else {
         // 0. setup: zero the per-call block, load exponents (static values or the cache's)
         if (decode)
-            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, cache->p, 0, 0, 0, 0, 2);
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, w.slots, cache->p, 0, 0, 0, 0, 2);
         else if (stat)
-            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, sp->p[0], sp->p[1], sp->p[2],
-                                                sp->p[3], 1);
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, w.slots, nullptr, sp->p[0], sp->p[1],
+                                                sp->p[2], sp->p[3], 1);
         else
-            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, nullptr, 0, 0, 0, 0, 0);
+            layer_setup_kernel<<<1, 64, 0, s>>>(w.small, w.slots, nullptr, 0, 0, 0, 0, 0);
         if ((st = check_launch("layer_setup_kernel")) != FM_OK) return st;
 
         // 1. (stacks) pre-norm of the residual stream
@@ -315,6 +321,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.xbc_q = g_keep ? w.xbc_q : nullptr;
         a.s16 = w.s16;
         a.amax_q16 = small_i + kAmaxQ;
+        a.amax_slots = w.slots + kRegionConvX * kSlotRegionWords;
         a.x_out = w.x_q;
         a.b_out = w.b_q;
         a.c_out = w.c_q;
@@ -384,6 +391,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         g.normed_out = g_keep ? w.normed : nullptr;
         g.rot_ws = w.rot;
         g.amax_ws = small_f + kAmaxG;
+        g.amax_slots = w.slots + kRegionG * kSlotRegionWords;
         g.rowmax = step ? w.rowmax + 64 : nullptr;
         g.sz = step ? w.sz : nullptr;
         g.qs = qs;
