@@ -173,7 +173,7 @@ fm_status fm_w8a8_gemm(const int8_t* a, const int8_t* b, int64_t m, int64_t n, i
 // ---------------------------------------------------------------- fm_conv1d_pot
 size_t fm_conv1d_pot_workspace_size(int64_t batch, int64_t len, int64_t d_inner, int64_t dstate) {
     if (batch < 0 || len < 0 || d_inner < 0 || dstate < 0) return 0;
-    return 256 + 3 * kSlotRegionWords * sizeof(int32_t) +
+    return 256 + 4 * kSlotRegionWords * sizeof(int32_t) +
            align256((size_t)(batch * len * (d_inner + 2 * dstate)) * sizeof(int32_t));
 }
 
@@ -231,10 +231,13 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
     int32_t* amax_q = (int32_t*)workspace + 1;   // words 1..3: the part maxima
     a.xbc_amax = amax_x;
     a.amax_q16 = amax_q;
-    a.amax_slots = (int32_t*)((char*)workspace + 256);  // three slot regions
-    a.s16 = (int32_t*)((char*)workspace + 256 + 3 * kSlotRegionWords * sizeof(int32_t));
-    if ((st = zero_words(workspace, 64 + 3 * kSlotRegionWords, stream)) != FM_OK) return st;
-    if ((st = amax_strided_run(xbc, batch * len, ch, xbc_row_stride, amax_x, stream)) != FM_OK)
+    // slot regions: x, B, C maxima, then max |xBC|
+    a.amax_slots = (int32_t*)((char*)workspace + 256);
+    int32_t* xbc_slots = a.amax_slots + 3 * kSlotRegionWords;
+    a.xbc_amax_slots = xbc_slots;
+    a.s16 = (int32_t*)((char*)workspace + 256 + 4 * kSlotRegionWords * sizeof(int32_t));
+    if ((st = zero_words(workspace, 64 + 4 * kSlotRegionWords, stream)) != FM_OK) return st;
+    if ((st = amax_strided_run(xbc, batch * len, ch, xbc_row_stride, xbc_slots, stream)) != FM_OK)
         return st;
     return conv_run(a, stream);
 }

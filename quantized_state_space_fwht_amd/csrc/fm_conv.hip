@@ -116,7 +116,15 @@ template <bool kDyn, bool kStats>
 __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
     __shared__ NauLds tab;
+    __shared__ float xa_s;  // dynamic: max |xBC|, reduced from its slots by wave 0
     nau_lds_init(tab);
+    if (kDyn && (int)blockIdx.x != K.ch / 64 && threadIdx.x < 64) {
+        const float v = __int_as_float(slots_wave_max(A.xbc_amax_slots));
+        if (threadIdx.x == 0) {
+            xa_s = v;
+            if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) *A.xbc_amax = v;
+        }
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
         }
         return;
     }
-    const int p_c = kDyn ? pot_from_f32(*A.xbc_amax) : A.p_fixed[0];
+    const int p_c = kDyn ? pot_from_f32(xa_s) : A.p_fixed[0];
     if (!kDyn && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 4)
         A.p_out[threadIdx.x] = A.p_fixed[threadIdx.x];
     const int c0 = blockIdx.x * 64;  // a wave covers 64 channels of one part
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
 
 __global__ __launch_bounds__(256) void amax_strided_kernel(const float* __restrict__ x, int64_t rows,
                                                            int64_t cols, int64_t stride,
-                                                           float* amax) {
+                                                           int32_t* amax_slots) {
     float m = 0.0f;
     const int64_t total = rows * cols;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -295,16 +303,17 @@ __global__ __launch_bounds__(256) void amax_strided_kernel(const float* __restri
         m = fmaxf(m, fabsf(x[r * stride + c]));
     }
     m = wave_max_f32(m);
-    if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_nonneg_f32(amax, m);
+    if ((threadIdx.x & 63) == 0)
+        slot_max(amax_slots, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), (int32_t)__float_as_uint(m));
 }
 
 fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t stride,
-                           float* amax, hipStream_t s) {
+                           int32_t* amax_slots, hipStream_t s) {
     int64_t total = rows * cols;
     int g = (int)((total + 255) / 256);
     if (g > 2048) g = 2048;
     if (g < 1) g = 1;
-    amax_strided_kernel<<<g, 256, 0, s>>>(x, rows, cols, stride, amax);
+    amax_strided_kernel<<<g, 256, 0, s>>>(x, rows, cols, stride, amax_slots);
     return check_launch("amax_strided_kernel");
 }
 

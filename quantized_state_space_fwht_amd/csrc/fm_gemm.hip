@@ -165,7 +165,12 @@ void gemm_i8_kernel(GemmParams P) {
             }
         }
     }
-    if (ep.amax) {
+    if (ep.amax_slots) {
+        amax = wave_max_f32(amax);
+        if (lane == 0)
+            slot_max(ep.amax_slots, ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave,
+                     (int32_t)__float_as_uint(amax));
+    } else if (ep.amax) {
         amax = wave_max_f32(amax);
         if (lane == 0 && amax > 0.0f) atomic_max_nonneg_f32(ep.amax, amax);
     }
@@ -432,7 +437,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
         }
     }
     // the workgroup's maxima, then one atomic per quantity
-    if (!kConv && !ep.amax) return;
+    if (!kConv && !ep.amax && !ep.amax_slots) return;
     amax = wave_max_f32(amax);
     xmax = wave_max_f32(xmax);
 #pragma unroll
@@ -454,6 +459,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
             if (xmax > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(ep.amax), __float_as_uint(xmax));
             for (int i = 0; i < 3; ++i)
                 if (pmax[i] > 0) atomicMax(&ep.conv_amax_q16[i], pmax[i]);
+        } else if (ep.amax_slots) {
+            slot_max(ep.amax_slots, blockIdx.x, (int32_t)__float_as_uint(amax));
         } else if (amax > 0.0f) {
             atomicMax(reinterpret_cast<unsigned int*>(ep.amax), __float_as_uint(amax));
         }

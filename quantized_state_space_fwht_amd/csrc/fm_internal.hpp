@@ -48,7 +48,8 @@ enum SmallSlot {
 enum SlotRegion {
     kRegionConvX = 0,  // conv pass: max |SiLU| of x, B, C in Q.16 (three regions)
     kRegionG = 3,      // gate pass: max |n H| as float bits
-    kRegions = 4
+    kRegionXbc = 4,    // in_proj epilogue: max |xBC| as float bits
+    kRegions = 5
 };
 
 // Publish what a layer call used into qp (scales, exponents, statistics) and,
@@ -101,6 +102,8 @@ struct GemmEpilogue {
     const float* resid = nullptr;  // out = resid + acc * s (pre-norm residual stacks)
     int64_t ld_resid = 0;
     float* amax = nullptr;         // max |out| over columns [amax_c0, amax_c1)
+    int32_t* amax_slots = nullptr; // instead of amax (tiled and plain few-rows kernels): a
+                                   // slot region receiving that maximum as float bits
     int64_t amax_c0 = 0, amax_c1 = 0;
     // one-token step (few-rows kernel only): the columns [amax_c0, amax_c1) are
     // xBC and go through its power-of-two quantization, the conv window held in
@@ -154,7 +157,8 @@ struct ConvArgs {
     const int8_t* w_q;
     const int32_t* p_w;
     const int32_t* b_q16;
-    const float* xbc_amax;     // dynamic: device max |xBC| (from the GEMM epilogue or a pass)
+    float* xbc_amax;           // dynamic: max |xBC| (written by workgroup 0 from the slots)
+    const int32_t* xbc_amax_slots;  // dynamic: slot region of max |xBC| (GEMM epilogue or a pass)
     const int32_t* p_fixed;    // static: device int32[4]
     const int8_t* state_in;
     int8_t* state_out;
@@ -179,8 +183,9 @@ struct ConvArgs {
     fm_quant_stats* qs;        // nullable: statistics of the xBC, x, B, C points
 };
 fm_status conv_run(const ConvArgs& a, hipStream_t s);
+// max |x| of a strided matrix into a slot region (zeroed before)
 fm_status amax_strided_run(const float* x, int64_t rows, int64_t cols, int64_t stride,
-                           float* amax, hipStream_t s);
+                           int32_t* amax_slots, hipStream_t s);
 
 struct ScanArgs {
     const int8_t* x;

@@ -266,7 +266,10 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         ep.ld_out = dip;
         ep.s_a = small_f + kScaleU;
         ep.s_b = W->s_w_in;
-        ep.amax = small_f + kAmaxXbc;
+        // the conv pass reduces max |xBC| from a slot region when its exponents are
+        // dynamic; the fused step and fixed exponents keep the one word
+        if (step || stat || decode) ep.amax = small_f + kAmaxXbc;
+        else ep.amax_slots = w.slots + kRegionXbc * kSlotRegionWords;
         ep.amax_c0 = di;
         ep.amax_c1 = di + ch;
         if (step) {  // 2 fused: codes of the rotated rows with the tensor scale
@@ -314,6 +317,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.p_w = W->conv_p_w;
         a.b_q16 = W->conv_b_q16;
         a.xbc_amax = small_f + kAmaxXbc;
+        a.xbc_amax_slots = w.slots + kRegionXbc * kSlotRegionWords;
         const bool fixed_p = stat || decode;
         a.p_fixed = fixed_p ? pdev : nullptr;
         a.state_in = decode ? cache->conv_state : nullptr;
