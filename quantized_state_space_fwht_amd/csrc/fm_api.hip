@@ -115,7 +115,7 @@ const char* fm_last_error(void) { return g_err; }
 size_t fm_hadamard_quant_workspace_size(int64_t rows, int64_t k) {
     (void)rows;
     (void)k;
-    return 256;
+    return 256 + kSlotRegionWords * sizeof(int32_t);  // the maximum, then its slot region
 }
 
 fm_status fm_hadamard_quant(const float* x, int64_t rows, int64_t k, fm_scale_mode mode,
@@ -133,13 +133,16 @@ fm_status fm_hadamard_quant(const float* x, int64_t rows, int64_t k, fm_scale_mo
         return fail(FM_ERR_SHAPE, "%s: x must be 16-byte and q 4-byte aligned", who);
     fm_status st;
     if (mode == FM_SCALE_DYNAMIC) {
-        if ((st = check_ws(workspace, workspace_bytes, 256, who)) != FM_OK) return st;
-        if ((st = zero_words(workspace, 1, stream)) != FM_OK) return st;
-        return hq_run(x, rows, k, mode, 0, 0, q, scale_out, amax_stats, (float*)workspace, stream);
+        const size_t need = fm_hadamard_quant_workspace_size(rows, k);
+        if ((st = check_ws(workspace, workspace_bytes, need, who)) != FM_OK) return st;
+        if ((st = zero_words(workspace, 64 + kSlotRegionWords, stream)) != FM_OK) return st;
+        return hq_run(x, rows, k, mode, 0, 0, q, scale_out, amax_stats, (float*)workspace,
+                      (int32_t*)((char*)workspace + 256), stream);
     }
     if (mode != FM_SCALE_STATIC) return fail(FM_ERR_MODE, "%s: bad mode %d", who, (int)mode);
     if ((st = check_static_hq(scoe, sshift, who)) != FM_OK) return st;
-    return hq_run(x, rows, k, mode, scoe, sshift, q, scale_out, amax_stats, nullptr, stream);
+    return hq_run(x, rows, k, mode, scoe, sshift, q, scale_out, amax_stats, nullptr, nullptr,
+                  stream);
 }
 
 // ---------------------------------------------------------------- fm_w8a8_gemm
@@ -425,7 +428,7 @@ fm_status fm_gate_norm_quant(const int32_t* y, const float* z, int64_t z_row_str
 // ---------------------------------------------------------------- layer
 size_t fm_prepare_layer_workspace_size(const fm_layer_desc* d) {
     (void)d;
-    return 256;
+    return 256 + 2 * kSlotRegionWords * sizeof(int32_t);  // two maxima, two slot regions
 }
 
 fm_status fm_prepare_layer(const fm_layer_desc* d, const float* w_in, const float* w_out,
@@ -443,7 +446,9 @@ fm_status fm_prepare_layer(const fm_layer_desc* d, const float* w_in, const floa
         return fail(FM_ERR_NULL, "%s: a required pointer is NULL", who);
     if (!aligned(w_in, 16) || !aligned(w_out, 16) || !aligned(w_in_q, 4) || !aligned(w_out_q, 4))
         return fail(FM_ERR_SHAPE, "%s: weights 16-byte, codes 4-byte aligned", who);
-    if ((st = check_ws(workspace, workspace_bytes, 256, who)) != FM_OK) return st;
+    if ((st = check_ws(workspace, workspace_bytes, fm_prepare_layer_workspace_size(d), who)) !=
+        FM_OK)
+        return st;
     return prepare_run(d, w_in, w_out, conv_w, conv_b, a, dvec, w_in_q, s_w_in, w_out_q, s_w_out,
                        conv_w_q, conv_p_w, conv_b_q16, a_q16, d_q16, workspace, stream);
 }

@@ -31,9 +31,10 @@ __device__ __forceinline__ void block_max_to(float m, float* a0, float* a1) {
     }
 }
 
-// pass 1 (dynamic): grid maximum of |x H| into amax_ws (and amax_stats)
+// pass 1 (dynamic): grid maximum of |x H| into the slot region (and amax_stats)
 __global__ __launch_bounds__(kHqThreads) void hq_amax_kernel(const float* __restrict__ x,
-                                                             int64_t nblk_total, float* amax_ws,
+                                                             int64_t nblk_total,
+                                                             int32_t* amax_slots,
                                                              float* amax_stats) {
     int lane = threadIdx.x & 63;
     int64_t wv = (int64_t)blockIdx.x * (kHqThreads / 64) + (threadIdx.x >> 6);
@@ -51,7 +52,16 @@ __global__ __launch_bounds__(kHqThreads) void hq_amax_kernel(const float* __rest
         float4 v = reinterpret_cast<const float4*>(x + b * 256)[lane];
         m = fmaxf(m, absmax4(fwht256_lane(v, lane)));
     }
-    block_max_to(m, amax_ws, amax_stats);
+    __shared__ float red[kHqThreads / 64];
+    m = wave_max_f32(m);
+    if (lane == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+        for (int i = 1; i < kHqThreads / 64; ++i) r = fmaxf(r, red[i]);
+        slot_max(amax_slots, blockIdx.x, (int32_t)__float_as_uint(r));
+        if (amax_stats) atomic_max_nonneg_f32(amax_stats, r);
+    }
 }
 
 __device__ __forceinline__ float scale_coef(fm_scale_mode mode, int32_t scoe, int32_t sshift,
@@ -142,17 +152,17 @@ fm_status zero_words(void* p, int64_t n, hipStream_t s) {
 
 fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
                  int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
-                 hipStream_t s, fm_quant_stats* qs, int qpt) {
+                 int32_t* amax_slots, hipStream_t s, fm_quant_stats* qs, int qpt) {
     int64_t nb = rows * (k / 256);
-    int g = hq_grid(nb);
+    int g = hq_grid((nb + kHqBatch - 1) / kHqBatch);
     fm_status st;
-    if (mode == FM_SCALE_DYNAMIC) {  // amax_ws must hold 0 (zeroed by the caller)
-        // few workgroups (grid-stride): one same-address atomic per workgroup
-        // four blocks per wave at least (their loads go out together)
-        hq_amax_kernel<<<hq_grid((nb + 3) / 4, 512), kHqThreads, 0, s>>>(x, nb, amax_ws,
+    if (mode == FM_SCALE_DYNAMIC) {  // amax_slots must hold 0 (zeroed by the caller)
+        // few workgroups (grid-stride): four blocks per wave at least (their loads
+        // go out together), one slot atomic per workgroup
+        hq_amax_kernel<<<hq_grid((nb + 3) / 4, 512), kHqThreads, 0, s>>>(x, nb, amax_slots,
                                                                          amax_stats);
         if ((st = check_launch("hq_amax_kernel")) != FM_OK) return st;
-        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, nullptr,
+        hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, amax_ws, amax_slots,
                                                  (char4*)q, scale_out, nullptr, 0, qs, qpt);
     } else {
         hq_quant_kernel<<<g, kHqThreads, 0, s>>>(x, nb, mode, scoe, sshift, nullptr, nullptr,

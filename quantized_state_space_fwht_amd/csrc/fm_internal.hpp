@@ -49,7 +49,8 @@ enum SlotRegion {
     kRegionConvX = 0,  // conv pass: max |SiLU| of x, B, C in Q.16 (three regions)
     kRegionG = 3,      // gate pass: max |n H| as float bits
     kRegionXbc = 4,    // in_proj epilogue: max |xBC| as float bits
-    kRegions = 5
+    kRegionU = 5,      // in_proj input rotation: max |u H| as float bits
+    kRegions = 6
 };
 
 // Publish what a layer call used into qp (scales, exponents, statistics) and,
@@ -77,13 +78,13 @@ __device__ inline void layer_publish(const uint32_t* small, fm_qparams* qp, int3
 // Zero `n` 32-bit words (a kernel, so it can sit inside captured graphs).
 fm_status zero_words(void* p, int64_t n, hipStream_t s);
 
-// Hadamard rotation + per-tensor int8.  In dynamic mode `amax_ws` (one float,
-// holding 0 on entry: the caller zeroes it) receives the grid maximum between
-// the two passes.
+// Hadamard rotation + per-tensor int8.  In dynamic mode the first pass leaves
+// the grid maximum in the slot region `amax_slots` (zeroed by the caller) and
+// the second writes it to `amax_ws` (one float).
 // qs (nullable): quantization statistics of point qpt (fm_quant_stats)
 fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, int32_t scoe,
                  int32_t sshift, int8_t* q, float* scale_out, float* amax_stats, float* amax_ws,
-                 hipStream_t s, fm_quant_stats* qs = nullptr, int qpt = 0);
+                 int32_t* amax_slots, hipStream_t s, fm_quant_stats* qs = nullptr, int qpt = 0);
 // second pass only: quantize already-rotated rows r (dynamic: amax_ws holds the max)
 // amax_slots (dynamic): the slot region holding the grid maximum; it is also
 // written to amax_ws

@@ -256,7 +256,8 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         // 2. rotate + quantize the in_proj input
         if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0,
                          w.u_q, small_f + kScaleU, stat ? small_f + kAmaxU : nullptr,
-                         small_f + kAmaxU, s, qs, FM_QP_U)) != FM_OK)
+                         small_f + kAmaxU, w.slots + kRegionU * kSlotRegionWords, s, qs,
+                         FM_QP_U)) != FM_OK)
             return st;
     }
     // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
@@ -460,14 +461,16 @@ fm_status prepare_run(const fm_layer_desc* d, const float* w_in, const float* w_
                       int32_t* d_q16, void* ws, hipStream_t s) {
     const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads;
     const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
+    // two maxima, then one slot region for each
     float* amax = (float*)ws;
+    int32_t* slots = (int32_t*)((char*)ws + 256);
     fm_status st;
-    if ((st = zero_words(amax, 2, s)) != FM_OK) return st;
-    if ((st = hq_run(w_in, dip, dm, FM_SCALE_DYNAMIC, 0, 0, w_in_q, s_w_in, nullptr, amax, s)) !=
-        FM_OK)
+    if ((st = zero_words(ws, 64 + 2 * kSlotRegionWords, s)) != FM_OK) return st;
+    if ((st = hq_run(w_in, dip, dm, FM_SCALE_DYNAMIC, 0, 0, w_in_q, s_w_in, nullptr, amax, slots,
+                     s)) != FM_OK)
         return st;
     if ((st = hq_run(w_out, dm, di, FM_SCALE_DYNAMIC, 0, 0, w_out_q, s_w_out, nullptr, amax + 1,
-                     s)) != FM_OK)
+                     slots + kSlotRegionWords, s)) != FM_OK)
         return st;
     prep_conv_kernel<<<(unsigned)((ch + 255) / 256), 256, 0, s>>>(conv_w, conv_b, ch, conv_w_q,
                                                                  conv_p_w, conv_b_q16);

@@ -183,7 +183,7 @@ def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
         ("wi", (s.d_in_proj, s.d_model), torch.int8), ("si", 1, torch.float32),
         ("wo", (s.d_model, s.d_inner), torch.int8), ("so", 1, torch.float32),
         ("aq", s.nheads, torch.int32), ("dq", s.nheads, torch.int32))}
-    ws = B.workspace(256)
+    ws = B.workspace(B.lib.fm_prepare_layer_workspace_size(ctypes.byref(desc)))
     B._check(B.lib.fm_prepare_layer(
         ctypes.byref(desc), src["w_in"].data_ptr(), src["w_out"].data_ptr(),
         src["conv_w"].data_ptr(), src["conv_b"].data_ptr(), src["A"].data_ptr(),
