@@ -18,7 +18,6 @@ namespace fm {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kBK = 64;
-constexpr int kLdsRow = kBK + 16;  // bytes per staged row (padding against bank conflicts)
 constexpr int kGemmThreads = 256;
 constexpr int kDepth = 3;          // k-steps whose global loads are in flight ahead of use
 
@@ -42,8 +41,8 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)
 void gemm_i8_kernel(GemmParams P) {
     constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave
     constexpr int RA = BM / 64, RB = BN / 64;  // 64-row load passes per operand
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kLdsRow];
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kBK];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kBK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -79,13 +78,17 @@ void gemm_i8_kernel(GemmParams P) {
 #pragma unroll
         for (int i = 0; i < RB; ++i) g[RA + i] = *reinterpret_cast<const v4i*>(pb[i] + k0);
     };
+    // 64-byte rows, the four 16-byte granules of row r XOR-swizzled by (r >> 2) & 3:
+    // a store pass (4 rows x 4 granules) and a fragment read (16 rows, one
+    // granule) both touch 64 distinct banks
+    auto swz = [](int row, int col) { return row * kBK + (col ^ (((row >> 2) & 3) << 4)); };
     auto lstore = [&](const v4i* g, int buf) {
 #pragma unroll
         for (int i = 0; i < RA; ++i)
-            *reinterpret_cast<v4i*>(&As[buf][(ld_row + 64 * i) * kLdsRow + ld_col]) = g[i];
+            *reinterpret_cast<v4i*>(&As[buf][swz(ld_row + 64 * i, ld_col)]) = g[i];
 #pragma unroll
         for (int i = 0; i < RB; ++i)
-            *reinterpret_cast<v4i*>(&Bs[buf][(ld_row + 64 * i) * kLdsRow + ld_col]) = g[RA + i];
+            *reinterpret_cast<v4i*>(&Bs[buf][swz(ld_row + 64 * i, ld_col)]) = g[RA + i];
     };
 
     v4i acc[TM][TN];
@@ -95,6 +98,11 @@ void gemm_i8_kernel(GemmParams P) {
         for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
     const int64_t KT = K / kBK;
+    // Every load and LDS store of the pipeline is issued unconditionally (steps
+    // past the end reload the last one), so the compiler counts the loads in
+    // flight exactly and each step waits only for its own slot; only the
+    // products are skipped past the end.
+    auto kofs = [&](int64_t s) { return (s < KT ? s : KT - 1) * kBK; };
     const bool live = P.m > 0 && P.n > 0;
     if (live) {
         gload(ring[0], 0);
@@ -102,7 +110,7 @@ void gemm_i8_kernel(GemmParams P) {
         // steps 1 .. kDepth into slots 1 .. kDepth (mod kDepth)
         for_slots(std::make_integer_sequence<int, kDepth>{}, [&](auto S) {
             constexpr int s = decltype(S)::value + 1;
-            if (s < KT) gload(ring[s % kDepth], (int64_t)s * kBK);
+            gload(ring[s % kDepth], kofs(s));
         });
     }
     __syncthreads();
@@ -113,30 +121,30 @@ void gemm_i8_kernel(GemmParams P) {
     auto step = [&](int64_t kt, auto S) {
         constexpr int slot = (decltype(S)::value + 1) % kDepth;
         const int buf = (int)(kt & 1);
-        v4i af[TM], bf[TN];
+        if (kt < KT) {
+            v4i af[TM], bf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            af[i] = *reinterpret_cast<const v4i*>(
-                &As[buf][(wm * (BM / 2) + i * 16 + frag_row) * kLdsRow + frag_k]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            bf[j] = *reinterpret_cast<const v4i*>(
-                &Bs[buf][(wn * (BN / 2) + j * 16 + frag_row) * kLdsRow + frag_k]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const v4i*>(
+                    &As[buf][swz(wm * (BM / 2) + i * 16 + frag_row, frag_k)]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        if (kt + 1 < KT) {
-            lstore(ring[slot], buf ^ 1);
-            if (kt + 1 + kDepth < KT) gload(ring[slot], (kt + 1 + kDepth) * kBK);
+                bf[j] = *reinterpret_cast<const v4i*>(
+                    &Bs[buf][swz(wn * (BN / 2) + j * 16 + frag_row, frag_k)]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] =
+                        __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
+        lstore(ring[slot], buf ^ 1);
+        gload(ring[slot], kofs(kt + 1 + kDepth));
         __syncthreads();
     };
     for (int64_t kt = 0; kt < KT; kt += kDepth) {
-        for_slots(std::make_integer_sequence<int, kDepth>{}, [&](auto S) {
-            if (kt + decltype(S)::value < KT) step(kt + decltype(S)::value, S);
-        });
+        for_slots(std::make_integer_sequence<int, kDepth>{},
+                  [&](auto S) { step(kt + decltype(S)::value, S); });
     }
 
     // epilogue
