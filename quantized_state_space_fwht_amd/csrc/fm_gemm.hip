@@ -499,6 +499,40 @@ static void launch_few_rows_kw(const GemmParams& P, int64_t n, int mt, int kw, b
     }
 }
 
+// Codes of m <= 64 rotated rows with the tensor scale formed from their row
+// maxima (the same float operations as the few-rows kernel's quantize-on-load:
+// one pass here instead of one per workgroup of the product).  Thread = four
+// consecutive elements.
+__global__ __launch_bounds__(256) void quant_rows_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ rowmax,
+                                                         int64_t m, int64_t k, fm_scale_mode mode,
+                                                         int32_t scoe, int32_t sshift,
+                                                         uint32_t* __restrict__ q,
+                                                         float* scale_out, float* amax_out) {
+    const int lane = threadIdx.x & 63;
+    const float amax = wave_max_f32(lane < m ? rowmax[lane] : 0.0f);
+    float c;
+    if (mode == FM_SCALE_DYNAMIC) c = amax == 0.0f ? 1.0f : 127.0f / amax;
+    else c = ldexpf((float)scoe, -sshift);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *amax_out = amax;
+        *scale_out = 1.0f / c;
+    }
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < m * k / 4) q[i] = quant_pack4(reinterpret_cast<const float4*>(x)[i], c);
+}
+
+fm_status quant_rows_run(const float* x, const float* rowmax, int64_t m, int64_t k,
+                         fm_scale_mode mode, int32_t scoe, int32_t sshift, int8_t* q,
+                         float* scale_out, float* amax_out, hipStream_t s) {
+    if (m < 1 || m > 64 || k % 4) return fail(FM_ERR_SHAPE, "quant_rows: m %lld k %lld",
+                                              (long long)m, (long long)k);
+    const int64_t n4 = m * k / 4;
+    quant_rows_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(
+        x, rowmax, m, k, mode, scoe, sshift, reinterpret_cast<uint32_t*>(q), scale_out, amax_out);
+    return check_launch("quant_rows_kernel");
+}
+
 fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
                    const GemmEpilogue& ep, hipStream_t s) {
     if (m == 0 || n == 0) return FM_OK;

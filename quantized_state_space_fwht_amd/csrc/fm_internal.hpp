@@ -146,6 +146,11 @@ struct GemmEpilogue {
     fm_qparams* pub_qp = nullptr;
     int32_t* pub_cache_p = nullptr;
 };
+// int8 codes of m <= 64 rotated rows (x [m, k] float, 16-byte aligned) with the
+// tensor scale from their row maxima; writes the dequant scale and the maximum
+fm_status quant_rows_run(const float* x, const float* rowmax, int64_t m, int64_t k,
+                         fm_scale_mode mode, int32_t scoe, int32_t sshift, int8_t* q,
+                         float* scale_out, float* amax_out, hipStream_t s);
 fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
                    const GemmEpilogue& ep, hipStream_t s);
 

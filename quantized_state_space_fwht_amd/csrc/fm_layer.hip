@@ -220,10 +220,10 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
     int32_t* small_i = (int32_t*)w.small;
     int32_t* pdev = small_i + kP;
 
-    // A decode step with few rows takes the fused form, five kernels: rotated
+    // A decode step with few rows takes the fused form, six kernels: rotated
     // input rows; in_proj quantizing them on load, with the conv step in its
-    // epilogue; the scan step; rotated gate rows; out_proj quantizing them on
-    // load, adding the residual and publishing the call's scalars.
+    // epilogue; the scan step; rotated gate rows; their codes (one pass);
+    // out_proj, adding the residual and publishing the call's scalars.
     const bool step = decode && T <= 64;
     if (step) {
         StepRowsArgs a{};
@@ -413,16 +413,12 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.resid = u;
             ep.ld_resid = dm;
         }
-        if (step) {  // 8 fused: codes of the rotated gate rows with the tensor scale
-            ep.a_f = w.rot;
-            ep.a_rowmax = w.rowmax + 64;
-            ep.a_mode = mode;
-            ep.a_scoe = stat ? sp->scoe[1] : 0;
-            ep.a_sshift = stat ? sp->sshift[1] : 0;
-            ep.a_amax_out = small_f + kAmaxG;
-            ep.a_scale_out = small_f + kScaleG;
-            ep.a_q_tap = g_keep ? w.g_q : nullptr;
-        }
+        // one-token step: the codes of the rotated gate rows with the tensor scale,
+        // formed once (the product then reads int8 A)
+        if (step && (st = quant_rows_run(w.rot, w.rowmax + 64, T, di, mode,
+                                         stat ? sp->scoe[1] : 0, stat ? sp->sshift[1] : 0, w.g_q,
+                                         small_f + kScaleG, small_f + kAmaxG, s)) != FM_OK)
+            return st;
         // the call's scales, exponents and statistics go out with this last kernel
         ep.pub_small = w.small;
         ep.pub_qp = qp;
