@@ -33,16 +33,19 @@ __device__ __forceinline__ void for_slots(std::integer_sequence<int, Ss...>, F&&
     (f(std::integral_constant<int, Ss>{}), ...);
 }
 
-// BM x BN x 64 tiles, 4 waves as 2 x 2, each (BM/2) x (BN/2) = TM x TN tiles of
-// 16 x 16.  The global loads of k-steps kt+1 .. kt+kDepth are in flight (in a
-// register ring) while step kt is multiplied from LDS.
-template <int BM, int BN>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// BM x BN x BK tiles (BK 64 or 128), 4 waves as 2 x 2, each (BM/2) x (BN/2) =
+// TM x TN tiles of 16 x 16.  The global loads of k-steps kt+1 .. kt+kD are in
+// flight (in a register ring) while step kt is multiplied from LDS; a 128-wide
+// step runs two 64-wide rounds of products per barrier.
+template <int BM, int BN, int BK>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(BK == 128 ? 2 : 3)))
 void gemm_i8_kernel(GemmParams P) {
     constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave
-    constexpr int RA = BM / 64, RB = BN / 64;  // 64-row load passes per operand
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * kBK];
+    constexpr int kRowsPerPass = kGemmThreads * 16 / BK;  // rows one load pass covers
+    constexpr int RA = BM / kRowsPerPass, RB = BN / kRowsPerPass;
+    constexpr int kD = BK == 128 ? 2 : kDepth;  // ring slots (the same bytes in flight)
+    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[2][BN * BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -55,40 +58,45 @@ void gemm_i8_kernel(GemmParams P) {
     const int64_t K = P.k;
 
     // global -> register staging: each thread moves RA + RB pieces of 16 bytes
-    const int ld_row = tid >> 2;          // 0..63 (+64 per further pass)
-    const int ld_col = (tid & 3) * 16;    // byte offset inside the 64-wide k slice
+    const int ld_row = tid / (BK / 16);        // row inside a pass
+    const int ld_col = (tid % (BK / 16)) * 16;  // byte offset inside the k slice
     const int8_t* pa[RA];
     const int8_t* pb[RB];
 #pragma unroll
     for (int i = 0; i < RA; ++i) {
-        int64_t r = m0 + ld_row + 64 * i;
+        int64_t r = m0 + ld_row + kRowsPerPass * i;
         r = r < P.m ? r : P.m - 1;  // rows past the edge: computed, never stored
         pa[i] = P.a + r * K + ld_col;
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-        int64_t r = n0 + ld_row + 64 * i;
+        int64_t r = n0 + ld_row + kRowsPerPass * i;
         r = r < P.n ? r : P.n - 1;
         pb[i] = P.b + r * K + ld_col;
     }
-    v4i ring[kDepth][RA + RB];
+    v4i ring[kD][RA + RB];
     auto gload = [&](v4i* g, int64_t k0) {
 #pragma unroll
         for (int i = 0; i < RA; ++i) g[i] = *reinterpret_cast<const v4i*>(pa[i] + k0);
 #pragma unroll
         for (int i = 0; i < RB; ++i) g[RA + i] = *reinterpret_cast<const v4i*>(pb[i] + k0);
     };
-    // 64-byte rows, the four 16-byte granules of row r XOR-swizzled by (r >> 2) & 3:
-    // a store pass (4 rows x 4 granules) and a fragment read (16 rows, one
-    // granule) both touch 64 distinct banks
-    auto swz = [](int row, int col) { return row * kBK + (col ^ (((row >> 2) & 3) << 4)); };
+    // BK-byte rows with their 16-byte granules XOR-swizzled by row (64-byte rows
+    // by (r >> 2) & 3, 128-byte rows by (r >> 1) & 7): a store pass (16 lanes
+    // over 4 or 2 rows) and a fragment read (16 rows, one granule) both touch 64
+    // distinct banks
+    auto swz = [](int row, int col) {
+        const int g = BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+        return row * BK + (col ^ (g << 4));
+    };
     auto lstore = [&](const v4i* g, int buf) {
 #pragma unroll
         for (int i = 0; i < RA; ++i)
-            *reinterpret_cast<v4i*>(&As[buf][swz(ld_row + 64 * i, ld_col)]) = g[i];
+            *reinterpret_cast<v4i*>(&As[buf][swz(ld_row + kRowsPerPass * i, ld_col)]) = g[i];
 #pragma unroll
         for (int i = 0; i < RB; ++i)
-            *reinterpret_cast<v4i*>(&Bs[buf][swz(ld_row + 64 * i, ld_col)]) = g[RA + i];
+            *reinterpret_cast<v4i*>(&Bs[buf][swz(ld_row + kRowsPerPass * i, ld_col)]) =
+                g[RA + i];
     };
 
     v4i acc[TM][TN];
@@ -97,53 +105,56 @@ void gemm_i8_kernel(GemmParams P) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    const int64_t KT = K / kBK;
+    const int64_t KT = K / BK;
     // Every load and LDS store of the pipeline is issued unconditionally (steps
     // past the end reload the last one), so the compiler counts the loads in
     // flight exactly and each step waits only for its own slot; only the
     // products are skipped past the end.
-    auto kofs = [&](int64_t s) { return (s < KT ? s : KT - 1) * kBK; };
+    auto kofs = [&](int64_t s) { return (s < KT ? s : KT - 1) * BK; };
     const bool live = P.m > 0 && P.n > 0;
     if (live) {
         gload(ring[0], 0);
         lstore(ring[0], 0);
-        // steps 1 .. kDepth into slots 1 .. kDepth (mod kDepth)
-        for_slots(std::make_integer_sequence<int, kDepth>{}, [&](auto S) {
+        // steps 1 .. kD into slots 1 .. kD (mod kD)
+        for_slots(std::make_integer_sequence<int, kD>{}, [&](auto S) {
             constexpr int s = decltype(S)::value + 1;
-            gload(ring[s % kDepth], kofs(s));
+            gload(ring[s % kD], kofs(s));
         });
     }
     __syncthreads();
     const int frag_row = lane & 15;
     const int frag_k = (lane >> 4) * 16;
-    // step kt: multiply buffer kt & 1; store step kt + 1 (slot (kt+1) % kDepth)
-    // into the other buffer; refill that slot with step kt + 1 + kDepth
+    // step kt: multiply buffer kt & 1; store step kt + 1 (slot (kt+1) % kD)
+    // into the other buffer; refill that slot with step kt + 1 + kD
     auto step = [&](int64_t kt, auto S) {
-        constexpr int slot = (decltype(S)::value + 1) % kDepth;
+        constexpr int slot = (decltype(S)::value + 1) % kD;
         const int buf = (int)(kt & 1);
         if (kt < KT) {
-            v4i af[TM], bf[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const v4i*>(
-                    &As[buf][swz(wm * (BM / 2) + i * 16 + frag_row, frag_k)]);
+            for (int kk = 0; kk < BK; kk += 64) {
+                v4i af[TM], bf[TN];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bf[j] = *reinterpret_cast<const v4i*>(
-                    &Bs[buf][swz(wn * (BN / 2) + j * 16 + frag_row, frag_k)]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
+                    af[i] = *reinterpret_cast<const v4i*>(
+                        &As[buf][swz(wm * (BM / 2) + i * 16 + frag_row, kk + frag_k)]);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] =
-                        __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    bf[j] = *reinterpret_cast<const v4i*>(
+                        &Bs[buf][swz(wn * (BN / 2) + j * 16 + frag_row, kk + frag_k)]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j],
+                                                                          acc[i][j], 0, 0, 0);
+            }
         }
         lstore(ring[slot], buf ^ 1);
-        gload(ring[slot], kofs(kt + 1 + kDepth));
+        gload(ring[slot], kofs(kt + 1 + kD));
         __syncthreads();
     };
-    for (int64_t kt = 0; kt < KT; kt += kDepth) {
-        for_slots(std::make_integer_sequence<int, kDepth>{},
+    for (int64_t kt = 0; kt < KT; kt += kD) {
+        for_slots(std::make_integer_sequence<int, kD>{},
                   [&](auto S) { step(kt + decltype(S)::value, S); });
     }
 
@@ -557,15 +568,20 @@ fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64
     if (af) return fail(FM_ERR_SHAPE, "gemm: float A needs m <= 64, k %% 256 == 0");
     // the largest tiles that still give the chip's 256 CUs a workgroup each
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    // 128-wide k-steps when k allows (half the barriers and waits per product)
+    const bool k128 = k % 128 == 0;
     if (tiles(128, 128) >= 256) {
         dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
-        gemm_i8_kernel<128, 128><<<grid, kGemmThreads, 0, s>>>(P);
+        if (k128) gemm_i8_kernel<128, 128, 128><<<grid, kGemmThreads, 0, s>>>(P);
+        else gemm_i8_kernel<128, 128, 64><<<grid, kGemmThreads, 0, s>>>(P);
     } else if (tiles(64, 128) >= 256) {
         dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 63) / 64));
-        gemm_i8_kernel<64, 128><<<grid, kGemmThreads, 0, s>>>(P);
+        if (k128) gemm_i8_kernel<64, 128, 128><<<grid, kGemmThreads, 0, s>>>(P);
+        else gemm_i8_kernel<64, 128, 64><<<grid, kGemmThreads, 0, s>>>(P);
     } else {
         dim3 grid((unsigned)((n + 63) / 64), (unsigned)((m + 63) / 64));
-        gemm_i8_kernel<64, 64><<<grid, kGemmThreads, 0, s>>>(P);
+        if (k128) gemm_i8_kernel<64, 64, 128><<<grid, kGemmThreads, 0, s>>>(P);
+        else gemm_i8_kernel<64, 64, 64><<<grid, kGemmThreads, 0, s>>>(P);
     }
     return check_launch("gemm_i8_kernel");
 }
