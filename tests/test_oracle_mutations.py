@@ -62,6 +62,15 @@ MUTATIONS = [
      "return _summary(r, q, step, np.abs(rc) > 128)"),
     ("oracle/outliers.py", "s[ok] = (np.sqrt(ax[ok]) / np.sqrt(aw[ok])).astype(np.float32)",
      "s[ok] = (np.sqrt(aw[ok]) / np.sqrt(ax[ok])).astype(np.float32)"),
+    # calibration: the running maximum replaced by the last sequence's, or one sequence only
+    ("oracle/layer.py", "self.amax_u = max(self.amax_u, other.amax_u)", "self.amax_u = other.amax_u"),
+    ("oracle/layer.py", "self.amax_q16 = [max(a, b) for a, b in zip(self.amax_q16, other.amax_q16)]",
+     "self.amax_q16 = list(other.amax_q16)"),
+    ("oracle/layer.py", "    for u in calib_inputs:", "    for u in calib_inputs[:1]:"),
+    # stack decode: the pre-norm dropped, or the residual dropped
+    ("oracle/layer.py", "        xin = rmsnorm_fixed_order(h, ones)", "        xin = h"),
+    ("oracle/layer.py", "        h = h + out\n        new_caches.append(cache)",
+     "        h = out\n        new_caches.append(cache)"),
 ]
 
 

@@ -858,3 +858,118 @@ def test_chunked_form_equals_the_real_recurrence(Q):
     yc, Hc = _chunked_real_scan(x, Bm, Cm, dt, dA, 0, Q)
     scale = np.max(np.abs(y_acc))
     assert np.max(np.abs(yc - y_acc[0])) <= 1e-12 * scale
+
+
+# --------------------------------------------------------------------------- calibration, stack decode
+def test_stats_update_is_an_elementwise_running_maximum_hand_worked():
+    """Calibration keeps, per quantization point, the largest value seen over the
+    calibration set ([FM] major comment on Sections III-A / IV-B; [FMV] skeptic
+    critique: one static scale per point from a set of inputs).  Three
+    hand-written observations whose maxima sit in different ones."""
+    obs = [O.Stats(amax_u=4.0, amax_g=0.5, amax_xbc=1.0, amax_q16=[10, 700, 3]),
+           O.Stats(amax_u=1.0, amax_g=2.5, amax_xbc=0.25, amax_q16=[90, 20, 1]),
+           O.Stats(amax_u=3.0, amax_g=1.5, amax_xbc=7.0, amax_q16=[5, 30, 40])]
+    acc = O.Stats()
+    for s in obs:
+        acc.update(s)
+    assert (acc.amax_u, acc.amax_g, acc.amax_xbc) == (4.0, 2.5, 7.0)
+    assert acc.amax_q16 == [90, 700, 40]
+    # the fold does not depend on the order of the observations
+    acc2 = O.Stats()
+    for s in obs[::-1]:
+        acc2.update(s)
+    assert acc2 == acc
+
+
+def test_calibrate_stack_takes_the_maximum_over_sequences_per_point():
+    """calibrate_stack: per layer and point, the maximum over the calibration
+    sequences of the dynamic path's maximum on each sequence alone; the
+    coefficients then follow the static format (c = 127/amax, 2^14 <= scoe < 2^15)
+    and the exponent rule a*2^p <= 127 < a*2^(p+1).  Layer 0's in_proj maximum is
+    also recomputed in float64 from the definitions (RMSNorm, then the block
+    Sylvester rotation / 16)."""
+    w = configs.with_len(configs.get("tiny_layer"), batch=1, seqlen=16)
+    preps = [O.prepare_layer(synth.workload_params(w, l)) for l in range(2)]
+    seqs = [synth.workload_activations(w, seed=s) for s in (21, 22, 23)]
+    qps, acc = O.calibrate_stack(preps, w.shape, seqs)
+    per = [O.stack_prefill(preps, w.shape, u, "dynamic")[2] for u in seqs]
+    names = ("amax_u", "amax_g", "amax_xbc")
+    winners = set()
+    for l in range(2):
+        for nm in names:
+            vals = [getattr(p[l], nm) for p in per]
+            assert getattr(acc[l], nm) == max(vals), (l, nm)
+            winners.add(int(np.argmax(vals)))
+        for j in range(3):
+            vals = [p[l].amax_q16[j] for p in per]
+            assert acc[l].amax_q16[j] == max(vals), (l, j)
+            winners.add(int(np.argmax(vals)))
+        for k, nm in enumerate(("amax_u", "amax_g")):
+            amax = max(getattr(p[l], nm) for p in per)
+            scoe, sh = qps[l].scoe[k], qps[l].sshift[k]
+            assert (1 << 14) <= scoe < (1 << 15)
+            assert abs(scoe * 2.0 ** -sh - 127.0 / amax) <= 2.0 ** -15 * 127.0 / amax
+        a_xbc = max(p[l].amax_xbc for p in per)
+        p_c = qps[l].p[0]
+        assert a_xbc * 2.0 ** p_c <= 127.0 < a_xbc * 2.0 ** (p_c + 1)
+        for j in range(3):
+            a = max(p[l].amax_q16[j] for p in per) / 65536.0
+            pj = qps[l].p[1 + j]
+            assert a * 2.0 ** pj <= 127.0 < a * 2.0 ** (pj + 1)
+    # every sequence supplies some point's maximum: a fold that keeps only the
+    # first or the last sequence cannot pass the equalities above
+    assert winners == {0, 1, 2}
+    H = scipy.linalg.hadamard(256) / 16.0
+    m64 = 0.0
+    for u in seqs:
+        x = u.reshape(16, -1).astype(np.float64)
+        n = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-5)
+        m64 = max(m64, float(np.max(np.abs(n @ H))))
+    assert abs(acc[0].amax_u - m64) <= 1e-5 * m64
+
+
+def test_stack_decode_is_prenorm_residual():
+    """A decode step through the stack ([FM] Fig. 2 block, stacked pre-norm
+    residual): with zero out_proj weights every mixer returns 0 and the step
+    passes u_t through exactly; layer 0's input is RMSNorm(u_t) (a float64
+    RMSNorm feeding the layer gives the same output up to float32 rounding)."""
+    w = configs.with_len(configs.get("tiny_layer"), batch=2, seqlen=12)
+    params = [synth.workload_params(w, l) for l in range(2)]
+    u = synth.workload_activations(w, seed=5)
+    zp = [O.prepare_layer(dict(p, w_out=np.zeros_like(p["w_out"]))) for p in params]
+    _, caches, _ = O.stack_prefill(zp, w.shape, u[:, :8])
+    h, caches2 = O.stack_decode(zp, w.shape, u[:, 8], caches)
+    assert np.array_equal(h, u[:, 8])
+    assert not np.array_equal(caches2[1]["ssm_state"], caches[1]["ssm_state"])
+    preps = [O.prepare_layer(p) for p in params]
+    _, caches, _ = O.stack_prefill(preps[:1], w.shape, u[:, :8])
+    h, _ = O.stack_decode(preps[:1], w.shape, u[:, 8], caches)
+    x0 = u[:, 8].astype(np.float64)
+    n0 = (x0 / np.sqrt(np.mean(x0 * x0, axis=1, keepdims=True) + 1e-5)).astype(np.float32)
+    out0, *_ = O.layer_decode(preps[0], w.shape, n0, caches[0])
+    assert np.max(np.abs(h - (u[:, 8] + out0))) <= 0.02 * np.max(np.abs(out0))
+    raw, *_ = O.layer_decode(preps[0], w.shape, u[:, 8], caches[0])
+    assert np.max(np.abs(h - (u[:, 8] + raw))) > 0.05 * np.max(np.abs(out0))
+
+
+def test_stack_prefill_equals_stack_prefill_then_decode_static():
+    """Static mode (fixed scales and exponents): a stack prefill over L tokens
+    equals a prefill over L-k tokens followed by k decode steps, outputs and
+    caches bit for bit (sequences are causal and the step keeps the scan's
+    per-step rounding)."""
+    w = configs.with_len(configs.get("tiny_layer"), batch=2, seqlen=14)
+    preps = [O.prepare_layer(synth.workload_params(w, l)) for l in range(2)]
+    qps, _ = O.calibrate_stack(preps, w.shape, [synth.workload_activations(w, seed=s)
+                                                for s in (31, 32)])
+    u = synth.workload_activations(w, seed=33)
+    L, k = u.shape[1], 4
+    h_full, c_full, _ = O.stack_prefill(preps, w.shape, u, "static", qps)
+    h_pre, caches, _ = O.stack_prefill(preps, w.shape, u[:, :L - k], "static", qps)
+    hs = [h_pre]
+    for t in range(L - k, L):
+        h_t, caches = O.stack_decode(preps, w.shape, u[:, t], caches, "static", qps)
+        hs.append(h_t[:, None, :])
+    assert np.array_equal(np.concatenate(hs, axis=1), h_full)
+    for a, b in zip(caches, c_full):
+        assert np.array_equal(a["ssm_state"], b["ssm_state"])
+        assert np.array_equal(a["conv_state"], b["conv_state"])
