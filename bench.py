@@ -1,16 +1,22 @@
 #!/usr/bin/env python3
-"""Benchmark: quantized Mamba2 mixer layer prefill tokens/s on one MI355X.
+"""Benchmark: quantized Mamba2 mixer prefill tokens/s on one MI355X.
 
-One step = one full prefill pass of the mixer layer (Hadamard-quant, in_proj
-W8A8 GEMM, PoT conv1d + SiLU, NAU dt/decay + fixed-point scan, gate +
-RMSNorm + Hadamard-quant, out_proj W8A8 GEMM) over one batch of seeded
-synthetic input already resident in HBM.  Default workload: one
-Mamba2-130M-shaped layer, batch 1, L 2048, dynamic scales.
+One step = one full prefill pass of the workload over one batch of seeded
+synthetic input already resident in HBM: per layer the pre-norm (stacks),
+Hadamard-quant, in_proj W8A8 GEMM, PoT conv1d + SiLU, NAU dt / decay +
+fixed-point scan, gate + RMSNorm + Hadamard-quant, out_proj W8A8 GEMM and the
+residual add.  Default workload: the 64-layer Mamba2-2.7B-shaped stack, batch
+4, L 4096, dynamic scales (the largest prefill configuration that fits one
+GPU).
 
 Prints ONE JSON line.  `roofline` describes the dominant kernel (the scan),
-timed live with HIP events recorded by the library around that kernel on the
-layer's stream inside the timed region.  `cpu_baseline` times the CPU oracle
-(test infrastructure, never tuned) on the same workload on the host cores.
+timed live with HIP events the library records around that kernel on the
+layer's stream inside the timed region; `stages` times every stage of a layer
+the same way in one extra pass and gives each its own roofline fraction.  The
+other workloads (one 130M layer, the 24-layer static 130M stack, the 2.7B
+decode) are extra keys.  `cpu_baseline` times the CPU oracle (test
+infrastructure, never tuned) on a bounded sample of the headline workload on
+the host cores.
 """
 import argparse
 import hashlib
@@ -33,6 +39,8 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 SCAN_OPS_PER_ELEMENT_STEP = 8
 COPY_PROBE_BYTES = 256 << 20
 HBM_PEAK_GBS = 8000.0
+I8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix rate, 5.0 POP/s
+HEADLINE_WORKLOAD = "m2p7b_stack"
 DECODE_WORKLOAD = "m2p7b_decode"
 STUDY_WORKLOAD = "m130m_stack_static"
 
@@ -66,32 +74,77 @@ def load_traffic(workload, per_launch_units):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, min_seconds=10.0, max_reps=30):
-    """The oracle as it stands (numpy) on the benchmark's workload: whole prefill
-    passes until at least `min_seconds` of CPU work (a bounded sample)."""
-    import numpy as np
-    import oracle as O
-    from quantized_state_space_fwht_amd import synth
+def host_cpu():
+    """What the host offers: logical CPUs, the ones this process may run on, the
+    model string, and the BLAS thread count numpy's products use."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:
+        usable = os.cpu_count()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
-    prep = O.prepare_layer(synth.workload_params(w, 0))
-    u = synth.workload_activations(w)
-    reps, t0 = 0, time.perf_counter()
-    while reps < max_reps:
-        O.layer_prefill(prep, w.shape, u)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(w.tokens * reps / dt, 1), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{reps} full oracle prefill pass(es) of the same workload "
-                      f"({w.batch}x{w.seqlen} tokens, seeds as the GPU run), {dt:.1f} s; "
-                      f"numpy: the matrix products on {int(cores)} BLAS threads, "
-                      f"elementwise work on one"}
+        blas = None
+    return {"nproc": os.cpu_count(), "usable": usable, "model": model, "blas_threads": blas}
+
+
+def cpu_baseline(w, sample_layers=2, sample_batch=1, sample_len=1024):
+    """The oracle as it stands (numpy) on a bounded sample of the workload.
+
+    Stacks: the first `sample_layers` layers over `sample_batch` x `sample_len`
+    tokens of the same seeded input (about 10-20 s of CPU work); every layer of a
+    stack costs the same and the oracle's cost is linear in tokens, so the
+    whole stack's rate is the sample's tokens / (its time x layers / sample
+    layers), reported beside the measured sample.  A single layer runs whole
+    prefill passes until at least 10 s of work."""
+    import oracle as O
+    from quantized_state_space_fwht_amd import configs, synth
+    cpu = host_cpu()
+    if w.nlayers == 1:
+        prep = O.prepare_layer(synth.workload_params(w, 0))
+        u = synth.workload_activations(w)
+        reps, t0 = 0, time.perf_counter()
+        while reps < 30:
+            O.layer_prefill(prep, w.shape, u)
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0:
+                break
+        dt = time.perf_counter() - t0
+        value = w.tokens * reps / dt
+        sample = (f"{reps} full oracle prefill pass(es) of the workload ({w.batch}x{w.seqlen} "
+                  f"tokens, seeds as the GPU run), {dt:.1f} s")
+        measured = {"seconds": round(dt, 2), "tokens": w.tokens * reps, "layers": 1}
+    else:
+        nl = min(sample_layers, w.nlayers)
+        preps = [O.prepare_layer(synth.workload_params(w, l)) for l in range(nl)]
+        u = synth.workload_activations(configs.with_len(w, batch=sample_batch, seqlen=sample_len))
+        qps = None
+        if w.mode == "static":
+            qps, _ = O.calibrate_stack(preps, w.shape, [u])
+        t0 = time.perf_counter()
+        O.stack_prefill(preps, w.shape, u, w.mode, qps)
+        dt = time.perf_counter() - t0
+        tokens = sample_batch * sample_len
+        value = tokens / (dt * w.nlayers / nl)
+        sample = (f"the first {nl} of {w.nlayers} layers over {sample_batch}x{sample_len} "
+                  f"tokens of the same seeded input, {dt:.1f} s; extrapolated linearly to all "
+                  f"{w.nlayers} layers (identical cost per layer, linear in tokens)")
+        measured = {"seconds": round(dt, 2), "tokens": tokens, "layers": nl,
+                    "tokens_per_s_of_the_sample_layers": round(tokens / dt, 1)}
+    return {"value": round(value, 1), "unit": "tokens/s", "cores": cpu["usable"],
+            "kind": "oracle", "sample": sample + "; numpy: the matrix products on "
+            f"{cpu['blas_threads']} BLAS threads, elementwise work on one",
+            "measured": measured, "host": cpu}
 
 
 FP64_PEAK_TFLOPS = 78.6   # MI355X float64 vector / matrix rate
@@ -132,10 +185,10 @@ def ssd_prefill_bench(torch, B, layer, u, out, stream, w, steps, warmup, ms_sequ
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
+    opts = [B.layer_opts(events=[None, None, None, a, b, None, None]) for a, b in evs]
     t0 = time.perf_counter()
     for i in range(steps):
-        B.lib.fm_layer_set_timing_events(evs[i][0].cuda_event, evs[i][1].cuda_event)
-        layer.prefill(u, out, stream=stream, scan="ssd")
+        layer.prefill(u, out, stream=stream, scan="ssd", opts=opts[i])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     scan_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
@@ -154,7 +207,8 @@ def ssd_prefill_bench(torch, B, layer, u, out, stream, w, steps, warmup, ms_sequ
                          "work": f"{flops} flops per call"}}
 
 
-def decode_bench(torch, configs, synth, warmup=8, max_steps=None, narrow_bits=(16, 24)):
+def decode_bench(torch, configs, synth, stack=None, warmup=8, max_steps=None,
+                 narrow_bits=(16, 24)):
     """Decode tokens/s of the 64-layer 2.7B-shaped stack, batch 16.
 
     A 1024-token seeding prefill fills the caches; then the workload's 512 one-token
@@ -168,8 +222,11 @@ def decode_bench(torch, configs, synth, warmup=8, max_steps=None, narrow_bits=(1
     from quantized_state_space_fwht_amd.runtime import DecodeGraph, Mamba2Stack
     w = configs.get(DECODE_WORKLOAD)
     s = w.shape
-    log(f"bench: building decode stack {w.name} ({w.description})")
-    stack = Mamba2Stack(s, (synth.workload_params(w, l) for l in range(w.nlayers)))
+    if stack is None:
+        log(f"bench: building decode stack {w.name} ({w.description})")
+        stack = Mamba2Stack(s, (synth.workload_params(w, l) for l in range(w.nlayers)))
+    else:
+        log(f"bench: decode {w.name} on the same weights ({w.description})")
     u0 = torch.from_numpy(synth.workload_activations(w)).cuda()
     nsteps = w.decode_steps if max_steps is None else min(w.decode_steps, warmup + max_steps)
     inputs = torch.from_numpy(np.stack([synth.decode_step_input(w, t)
@@ -201,6 +258,7 @@ def decode_bench(torch, configs, synth, warmup=8, max_steps=None, narrow_bits=(1
                             "bytes_per_token_step": step_bytes}}
         if shifts is not None:
             res["state_shift_range"] = [min(shifts), max(shifts)]
+        g.close()
         del g
         return res
 
@@ -392,14 +450,10 @@ def study_scales(torch, configs, synth, B):
     oracle_s = time.perf_counter() - t0
     buf = B.quant_stats_buffer()
     stack.layers[0].set_dynamic()
-    B.collect_quant_stats(buf)
-    try:
-        # the stack's layers apply the pre-norm themselves: they take u itself
-        stack.layers[0].prefill(torch.from_numpy(np.ascontiguousarray(u0)).cuda(),
-                                with_cache=False)
-        torch.cuda.synchronize()
-    finally:
-        B.collect_quant_stats(None)
+    # the stack's layers apply the pre-norm themselves: they take u itself
+    stack.layers[0].prefill(torch.from_numpy(np.ascontiguousarray(u0)).cuda(),
+                            with_cache=False, opts=B.layer_opts(quant_stats=buf))
+    torch.cuda.synchronize()
     g = B.quant_stats_from_device(buf)
     agree = all(g.count[i] == r["qstats"][n]["count"] and g.clipped[i] == r["qstats"][n]["clipped"]
                 and abs(g.sq_err[i] - r["qstats"][n]["sq_err"]) <= 1e-9 * r["qstats"][n]["sq_err"]
@@ -467,12 +521,8 @@ def study_outliers(torch, configs, synth, B, rows=2048):
         params = synth.workload_params(w, 0)
         u = synth.workload_activations(configs.with_len(w, batch=1, seqlen=rows))
         layer = Mamba2Layer(s, params)
-        B.keep_intermediates(True)
-        try:
-            layer.prefill(torch.from_numpy(u).cuda())
-            normed = layer.tap("normed", torch.float32, (rows, s.d_inner)).clone()
-        finally:
-            B.keep_intermediates(False)
+        layer.prefill(torch.from_numpy(u).cuda(), opts=B.layer_opts(keep=True))
+        normed = layer.tap("normed", torch.float32, (rows, s.d_inner)).clone()
         cases = {"in_proj": (u.reshape(rows, s.d_model), params["w_in"]),
                  "out_proj": (normed.cpu().numpy(), params["w_out"])}
         for lname, (x, wt) in cases.items():
@@ -585,13 +635,144 @@ def study_nau(torch, configs, synth, B):
     return report
 
 
+def stage_work(s, T):
+    """Algorithmic work of each stage of one layer call over T tokens, with the
+    roofline that bounds it: (bound, amount, unit of the amount, what counts).
+    The stage boundaries are the library's stage events (fm_layer_opts)."""
+    dm, di, N, H, P = s.d_model, s.d_inner, s.dstate, s.nheads, s.headdim
+    ch, dip = di + 2 * N, 2 * di + 2 * N + H
+    return {
+        "in_quant": ("hbm", 5 * T * dm, "B", "4 B read + 1 B code written per in_proj input "
+                                              "element (rotation, maximum, codes)"),
+        "in_proj": ("mfma", 2 * T * dip * dm, "op", "2 M N K int8 operations"),
+        "conv": ("hbm", T * (5 * ch + 12 * H), "B",
+                 "4 B float read + 1 B code written per xBC element; 4 B read + 8 B written "
+                 "per (token, head) for dt and the decay"),
+        "scan": ("alu", SCAN_OPS_PER_ELEMENT_STEP * T * H * P * N, "op",
+                 "8 integer operations per state element and step"),
+        "gate_quant": ("hbm", 9 * T * di, "B", "4 B y + 4 B z read + 1 B code written per "
+                                               "out_proj input element"),
+        "out_proj": ("mfma", 2 * T * dm * di, "op", "2 M N K int8 operations"),
+    }
+
+
+def stage_report(s, T, ms):
+    """Per stage: average milliseconds per layer call and its roofline fraction."""
+    peaks = {"hbm": (HBM_PEAK_GBS, "GB/s", 1e9), "mfma": (I8_MFMA_PEAK_TOPS, "TOP/s", 1e12),
+             "alu": (VALU_PEAK_TOPS, "TOP/s", 1e12)}
+    out = {}
+    for name, (bound, amount, _, what) in stage_work(s, T).items():
+        peak, unit, scale = peaks[bound]
+        t = ms[name]
+        ach = amount / (t / 1e3) / scale if t > 0 else 0.0
+        out[name] = {"ms": round(t, 4), "bound": bound, "achieved": round(ach, 1), "peak": peak,
+                     "unit": unit, "frac": round(ach / peak, 4), "work_per_call": amount,
+                     "work": what}
+    return out
+
+
+class Model:
+    """The workload's layers on the GPU: one bare layer, or a pre-norm residual
+    stack (static stacks calibrated on their seeded calibration sequences)."""
+
+    def __init__(self, torch, configs, synth, w):
+        from quantized_state_space_fwht_amd.runtime import Mamba2Layer, Mamba2Stack
+        self.w = w
+        if w.nlayers == 1:
+            self.layers = [Mamba2Layer(w.shape, synth.workload_params(w, 0))]
+            self.stack = None
+        else:
+            self.stack = Mamba2Stack(w.shape, (synth.workload_params(w, l)
+                                               for l in range(w.nlayers)), mode="dynamic")
+            self.layers = self.stack.layers
+            if w.mode == "static":
+                log(f"bench: calibrating {w.name} on {len(w.calib_seeds)} sequences")
+                self.stack.calibrate([torch.from_numpy(x).cuda()
+                                      for x in synth.calibration_sequences(w)])
+        u = synth.eval_batch(w) if w.mode == "static" else synth.workload_activations(w)
+        self.u = torch.from_numpy(u).cuda()
+        self.bufs = [torch.empty_like(self.u), torch.empty_like(self.u)]
+
+    def step(self, stream, opts=None):
+        """One prefill pass; opts: None or one LayerOpts per layer."""
+        if self.stack is None:
+            self.layers[0].prefill(self.u, self.bufs[0], stream=stream,
+                                   opts=None if opts is None else opts[0])
+            return self.bufs[0]
+        return self.stack.prefill(self.u, with_cache=True, stream=stream, layer_opts=opts,
+                                  bufs=self.bufs)
+
+
+def prefill_bench(torch, B, model, steps, warmup):
+    """Time `steps` prefill passes after `warmup`; the scan kernel of every layer
+    is bracketed by HIP events on its stream; then one more pass with every
+    stage boundary recorded gives the per-stage times."""
+    w, s = model.w, model.w.shape
+    stream = torch.cuda.current_stream()
+    nl = len(model.layers)
+    for _ in range(warmup):
+        model.step(stream)
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    scan_evs = [[(ev(), ev()) for _ in range(nl)] for _ in range(steps)]
+    for row in scan_evs:  # create the underlying HIP events outside the timed region
+        for a, b in row:
+            a.record(stream)
+            b.record(stream)
+    opts = [[B.layer_opts(events=[None, None, None, a, b, None, None]) for a, b in row]
+            for row in scan_evs]
+    torch.cuda.synchronize()
+    log(f"bench: timing {steps} steps of {w.name}")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        model.step(stream, opts[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    scan_ms = sum(a.elapsed_time(b) for row in scan_evs for a, b in row) / (steps * nl)
+    # the stage breakdown: one more pass, every boundary of every layer recorded
+    stage_evs = [[ev() for _ in range(B.LAYER_EVENTS)] for _ in range(nl)]
+    for row in stage_evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    model.step(stream, [B.layer_opts(events=row) for row in stage_evs])
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(row[k].elapsed_time(row[k + 1]) for row in stage_evs) / nl
+                for k, name in enumerate(B.STAGES)}
+    T = w.batch * w.seqlen
+    elem_steps = T * s.nheads * s.headdim * s.dstate
+    achieved = SCAN_OPS_PER_ELEMENT_STEP * elem_steps / (scan_ms / 1e3) / 1e12
+    roofline = {"bound": "alu", "kernel": "scan_kernel", "achieved": round(achieved, 3),
+                "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(achieved / VALU_PEAK_TOPS, 4),
+                "traffic": load_traffic(w.name, elem_steps),
+                "launch_ms": round(scan_ms, 4), "launches_timed": steps * nl,
+                "work": f"{SCAN_OPS_PER_ELEMENT_STEP} ops x {elem_steps} element-steps per launch"}
+    return {"value": round(w.tokens / (ms_per_step / 1e3), 1), "ms_per_step": ms_per_step,
+            "roofline": roofline, "stages": stage_report(s, T, stage_ms),
+            "stage_ms_sum_per_layer": round(sum(stage_ms.values()), 4)}
+
+
+def workload_config(w):
+    s = w.shape
+    return {"workload": w.name, "layers": w.nlayers, "batch": w.batch, "seq_len": w.seqlen,
+            "d_model": s.d_model, "d_inner": s.d_inner, "nheads": s.nheads,
+            "headdim": s.headdim, "d_state": s.dstate, "mode": w.mode,
+            "parallelism": "single-gpu"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="m130m_layer")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=HEADLINE_WORKLOAD,
+                    help="prefill workload timed for the headline (default: the 64-layer "
+                         "2.7B-shaped stack, batch 4, L 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload (no 130M layer / static stack / "
+                         "decode / chunked-scan lines)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode measurement (64-layer 2.7B-shaped stack)")
     ap.add_argument("--decode-steps", type=int, default=None,
@@ -620,7 +801,6 @@ def main():
     import torch
     from quantized_state_space_fwht_amd import binding as B
     from quantized_state_space_fwht_amd import configs, synth
-    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
 
     if args.study_scales:
         torch.cuda.set_device(0)
@@ -640,70 +820,58 @@ def main():
         return
 
     w = configs.get(args.workload)
-    if w.nlayers != 1 or w.decode_steps:
-        print("bench.py times single-layer prefill workloads", file=sys.stderr)
+    if w.decode_steps:
+        print("bench.py times prefill workloads (decode is an extra key)", file=sys.stderr)
         sys.exit(2)
-    s = w.shape
     torch.cuda.set_device(0)
-    log(f"bench: building layer {w.name} ({w.description})")
-    layer = Mamba2Layer(s, synth.workload_params(w, 0))
-    u = torch.from_numpy(synth.workload_activations(w)).cuda()
-    out = torch.empty_like(u)
-    stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        layer.prefill(u, out, stream=stream)
-    torch.cuda.synchronize()
-    K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    for a, b in evs:  # create the underlying HIP events
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    log(f"bench: timing {K} steps")
-    t0 = time.perf_counter()
-    for i in range(K):
-        B.lib.fm_layer_set_timing_events(evs[i][0].cuda_event, evs[i][1].cuda_event)
-        layer.prefill(u, out, stream=stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    scan_ms = sum(a.elapsed_time(b) for a, b in evs) / K
-    tokens_per_s = w.tokens / (ms_per_step / 1e3)
-
-    elem_steps = w.batch * w.seqlen * s.nheads * s.headdim * s.dstate
-    achieved = SCAN_OPS_PER_ELEMENT_STEP * elem_steps / (scan_ms / 1e3) / 1e12
-    roofline = {"bound": "alu", "kernel": "scan_kernel", "achieved": round(achieved, 3),
-                "peak": round(VALU_PEAK_TOPS, 2), "unit": "TOP/s",
-                "frac": round(achieved / VALU_PEAK_TOPS, 4),
-                "traffic": load_traffic(w.name, elem_steps),
-                "launch_ms": round(scan_ms, 4),
-                "work": f"{SCAN_OPS_PER_ELEMENT_STEP} ops x {elem_steps} element-steps"}
+    log(f"bench: building {w.name} ({w.description})")
+    model = Model(torch, configs, synth, w)
+    r = prefill_bench(torch, B, model, args.steps, args.warmup)
     line = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8+int32", "data": "synthetic (seeded; random-init weights)",
-        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen,
-                   "d_model": s.d_model, "d_inner": s.d_inner, "nheads": s.nheads,
-                   "headdim": s.headdim, "d_state": s.dstate, "mode": w.mode,
-                   "parallelism": "single-gpu"},
-        "roofline": roofline,
+        "config": workload_config(w), "roofline": r["roofline"], "stages": r["stages"],
+        "stage_ms_sum_per_layer": r["stage_ms_sum_per_layer"],
     }
-    line["prefill_ssd"] = ssd_prefill_bench(torch, B, layer, u, out, stream, w, K, args.warmup,
-                                            ms_per_step)
-    if not args.no_decode:
-        del layer
+    extras = not args.no_extras
+    if extras and not args.no_decode and w.name == HEADLINE_WORKLOAD:
+        # the decode workload has the same layer shapes and weights
+        model.u = model.bufs = None
         torch.cuda.empty_cache()
-        line["decode"] = decode_bench(torch, configs, synth, max_steps=args.decode_steps)
+        line["decode"] = decode_bench(torch, configs, synth, stack=model.stack,
+                                      max_steps=args.decode_steps)
+    del model
+    torch.cuda.empty_cache()
+    if extras:
+        for name in ("m130m_layer", "m130m_stack_static"):
+            if name == w.name:
+                continue
+            wx = configs.get(name)
+            log(f"bench: building {wx.name} ({wx.description})")
+            mx = Model(torch, configs, synth, wx)
+            steps = 20 if wx.nlayers == 1 else 5
+            rx = prefill_bench(torch, B, mx, steps, 3)
+            line[name] = {"value": rx["value"], "unit": "tokens/s",
+                          "ms_per_step": round(rx["ms_per_step"], 4), "steps": steps,
+                          "config": workload_config(wx), "roofline": rx["roofline"],
+                          "stages": rx["stages"]}
+            if wx.nlayers == 1:
+                stream = torch.cuda.current_stream()
+                line[name]["prefill_ssd"] = ssd_prefill_bench(
+                    torch, B, mx.layers[0], mx.u, mx.bufs[0], stream, wx, steps, 3,
+                    rx["ms_per_step"])
+            del mx
+            torch.cuda.empty_cache()
     # the achievable HBM rate on this machine: a device-to-device copy of 512 MiB
     hbm_meas = measured_copy_gbs(torch)
     line["measured_peaks"] = {"hbm_copy_GBs": round(hbm_meas, 1),
                               "how": "512 MiB device-to-device copy, 10 timed, 2 x bytes"}
     if "decode" in line:
-        for r in [line["decode"]["roofline"]] + [v["roofline"] for v in
-                                                 line["decode"].get("narrow_state", {}).values()]:
-            r["frac_of_measured"] = round(r["achieved"] / hbm_meas, 4)
+        for rr in [line["decode"]["roofline"]] + [v["roofline"] for v in
+                                                  line["decode"].get("narrow_state", {}).values()]:
+            rr["frac_of_measured"] = round(rr["achieved"] / hbm_meas, 4)
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FM_ABI_VERSION 1
+#define FM_ABI_VERSION 2
 #define FM_HADAMARD_BLOCK 256
 #define FM_PMIN (-24)
 #define FM_PMAX 24
@@ -170,7 +170,9 @@ fm_status fm_conv1d_pot(const float* xbc, int64_t xbc_row_stride, int64_t batch,
  * x [batch, len, nheads, headdim] int8; bm, cm [batch, len, dstate] int8;
  * dt_raw: float32 rows (one per token, [batch, len] order) of >= nheads
  *   values, row r at dt_raw + r*dt_row_stride; dt_bias [nheads] float32;
- * a_q16 [nheads] int32 (<= 0), d_q16 [nheads] int32;
+ * a_q16 [nheads] int32, d_q16 [nheads] int32; the method's A = -exp(.) is
+ *   <= 0, and an argument dt * a_q16 > 0 (a_q16 > 0) is taken as 0 by the
+ *   exponential (decay 2^16, as with a_q16 = 0);
  * p: device int32[4] = (p_c, p_x, p_B, p_C) (only p_B + p_C is used);
  * state_in / state_out [batch, nheads, headdim, dstate] int32 (NULL: zeros
  *   / not written); y [batch, len, nheads, headdim] int32;
@@ -329,6 +331,34 @@ fm_status fm_prepare_layer(const fm_layer_desc* d, const float* w_in, const floa
                            int32_t* conv_b_q16, int32_t* a_q16, int32_t* d_q16, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Per-call options of the layer calls (NULL: all off).  Nothing here is
+ * remembered between calls: each call reads only the options it is given.
+ *   keep_intermediates: 1 also writes xbc_q, normed, dt and dA into the
+ *       workspace for fm_mamba2_layer_taps (slower; for tests); 0 does not.
+ *   reserved: must be 0.
+ *   quant_stats: device pointer to a caller-zeroed fm_quant_stats (8-byte
+ *       aligned) into which a prefill call adds the statistics of its six
+ *       quantization points, or NULL.  Decode calls do not collect: a
+ *       non-NULL pointer there is FM_ERR_MODE.
+ *   stage_events: NULL, or a host array of FM_LAYER_EVENTS hipEvent_t
+ *       handles (caller-owned; any entry may be NULL) recorded on the call's
+ *       stream at the stage boundaries:
+ *         [0] call start                 [1] in_proj input quantized
+ *         [2] in_proj done               [3] right before the scan kernel
+ *         [4] right after the scan kernel
+ *         [5] out_proj input quantized   [6] call end (out_proj done)
+ *       so [k] -> [k+1] times one stage (the one-token decode form runs the
+ *       conv step inside in_proj: [2] -> [3] is then empty).
+ * fm_quant_stats is declared below with the scale-study calls. */
+#define FM_LAYER_EVENTS 7
+struct fm_quant_stats;
+typedef struct fm_layer_opts {
+    int32_t keep_intermediates;
+    int32_t reserved;
+    struct fm_quant_stats* quant_stats;
+    void* const* stage_events;
+} fm_layer_opts;
+
 /* fm_mamba2_layer_prefill — the whole mixer over u [batch, len, d_model]
  * from a zero state (Fig. 2 flow: in_proj, conv1d + SiLU, SSM, gated
  * RMSNorm, out_proj), each step as the calls above.  out [batch, len,
@@ -336,12 +366,14 @@ fm_status fm_prepare_layer(const fm_layer_desc* d, const float* w_in, const floa
  * window, the final int32 state and the exponents used.  qp (device,
  * required): receives the scales / exponents used; its stat_* fields are
  * max-accumulated (zero them before a calibration run).  sp: required in
- * static mode, ignored otherwise.  Workspace: fm_mamba2_layer_workspace_size. */
+ * static mode, ignored otherwise.  opts: per-call options or NULL.
+ * Workspace: fm_mamba2_layer_workspace_size. */
 size_t fm_mamba2_layer_workspace_size(const fm_layer_desc* d, int64_t batch, int64_t len);
 fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights* w,
                                   const fm_static_params* sp, const float* u, int64_t batch,
                                   int64_t len, float* out, const fm_cache* cache, fm_qparams* qp,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const fm_layer_opts* opts, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* fm_mamba2_layer_prefill_ssd — fm_mamba2_layer_prefill with the chunked
  * scan (fm_ssm_scan_ssd) in place of the sequential one; everything else is
@@ -351,17 +383,19 @@ size_t fm_mamba2_layer_workspace_size_ssd(const fm_layer_desc* d, int64_t batch,
 fm_status fm_mamba2_layer_prefill_ssd(const fm_layer_desc* d, const fm_layer_weights* w,
                                       const fm_static_params* sp, const float* u, int64_t batch,
                                       int64_t len, float* out, const fm_cache* cache,
-                                      fm_qparams* qp, void* workspace, size_t workspace_bytes,
-                                      hipStream_t stream);
+                                      fm_qparams* qp, const fm_layer_opts* opts, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 /* fm_mamba2_layer_decode — one token per sequence, u_t [batch, d_model],
  * continuing from `cache` (updated in place): the conv window shifts, the
  * state advances one step, the exponents stay frozen at cache->p, the
- * Hadamard scales follow the layer mode.  out_t [batch, d_model]. */
+ * Hadamard scales follow the layer mode.  out_t [batch, d_model].  opts:
+ * per-call options or NULL (quant_stats must be NULL). */
 fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights* w,
                                  const fm_static_params* sp, const float* u_t, int64_t batch,
                                  const fm_cache* cache, float* out_t, fm_qparams* qp,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                 const fm_layer_opts* opts, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Narrow state caches.  The decode step reads and writes the whole SSM state
@@ -395,6 +429,12 @@ size_t fm_state_narrow_bytes(int64_t count, int32_t bits);
 fm_status fm_state_narrow(const int32_t* state, int64_t count, int32_t bits, int32_t shift,
                           void* codes, hipStream_t stream);
 
+/* Host helper: the smallest shift whose codes hold every |h| <= amax * 2^headroom
+ * unclipped, max(0, bitlength(amax) + headroom - (bits - 1)), at most
+ * 32 - bits (amax as fm_state_absmax leaves it, |INT32_MIN| = 2^31).
+ * Bad bits or headroom outside [0, 32]: FM_ERR_SHAPE. */
+fm_status fm_state_shift_for(uint32_t amax, int32_t bits, int32_t headroom, int32_t* shift);
+
 /* codes -> int32 state values c * 2^shift (device). */
 fm_status fm_state_widen(const void* codes, int64_t count, int32_t bits, int32_t shift,
                          int32_t* state, hipStream_t stream);
@@ -407,23 +447,22 @@ fm_status fm_state_absmax(const int32_t* state, int64_t count, uint32_t* amax, h
 fm_status fm_mamba2_layer_decode_narrow(const fm_layer_desc* d, const fm_layer_weights* w,
                                         const fm_static_params* sp, const float* u_t,
                                         int64_t batch, const fm_cache_narrow* cache, float* out_t,
-                                        fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                        fm_qparams* qp, const fm_layer_opts* opts,
+                                        void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
 /* Byte offsets, inside the layer workspace, of the intermediates the last
  * prefill / decode call on that workspace left there (for parity tests):
  * u_q [T, d_model] i8, v [T, dip] f32 (in_proj out: z|xBC|dt), xbc_q [T, ch] i8,
  * x_q [T, d_inner] i8, b_q / c_q [T, dstate] i8, y [T, d_inner] i32,
- * g_q [T, d_inner] i8, normed [T, d_inner] f32 (written only if requested
- * by fm_layer_keep_intermediates), with T = batch * len. */
+ * g_q [T, d_inner] i8, normed [T, d_inner] f32, dt / da [T, nheads] i32
+ * (xbc_q, normed, dt and da written only when the call's opts ask to keep
+ * intermediates), with T = batch * len. */
 typedef struct fm_layer_taps {
     size_t u_q, v, xbc_q, x_q, b_q, c_q, y, g_q, normed, dt, da;
 } fm_layer_taps;
 fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len,
                                fm_layer_taps* taps);
-/* 1: later layer calls in this process also write xbc_q, normed, dt, dA into
- * their workspace (slower; for tests).  0 (default): they do not. */
-void fm_layer_keep_intermediates(int32_t on);
 
 /* ------------------------------------------------------------------------
  * Outlier-study baselines.  The review page of FastMamba credits the Hadamard
@@ -469,23 +508,15 @@ fm_status fm_scale_columns(const float* x, int64_t rows, int64_t k, const float*
  * are exact; the sums are added atomically, so their rounding order varies. */
 enum { FM_QP_U = 0, FM_QP_G = 1, FM_QP_XBC = 2, FM_QP_X = 3, FM_QP_B = 4, FM_QP_C = 5,
        FM_QP_COUNT = 6 };
-typedef struct fm_quant_stats {
+struct fm_quant_stats {
     unsigned long long count[FM_QP_COUNT];    /* elements quantized */
     unsigned long long clipped[FM_QP_COUNT];  /* elements whose code was clamped */
     double sq_err[FM_QP_COUNT];               /* sum of (v - q * step)^2 */
     double sq_val[FM_QP_COUNT];               /* sum of v^2 */
-} fm_quant_stats;
-/* Device pointer to a caller-zeroed fm_quant_stats (8-byte aligned), or NULL
- * to stop: later prefill layer calls made by this thread add their statistics
- * into it.  Decode calls do not collect.  Costs a few float64 operations per
- * quantized element while on. */
-void fm_layer_collect_quant_stats(fm_quant_stats* dev_stats);
-
-/* Profiling hook: the next layer call made by this thread records `start`
- * right before and `stop` right after its scan kernel (the dominant kernel)
- * on its stream; the hook then clears itself.  Both are hipEvent_t handles
- * owned by the caller; NULL clears the hook. */
-void fm_layer_set_timing_events(void* start, void* stop);
+};
+typedef struct fm_quant_stats fm_quant_stats;
+/* A prefill call collects into one when fm_layer_opts.quant_stats points to
+ * it (a few float64 operations per quantized element while on). */
 
 /* Host helper: static parameters from the max statistics of a calibration
  * run (fm_qparams copied to the host).  Hadamard points: c = 127 / amax in

@@ -66,6 +66,38 @@ class CacheNarrow(ctypes.Structure):
                 ("state_shift", _c_i32)]
 
 
+LAYER_EVENTS = 7  # FM_LAYER_EVENTS: stage boundaries of a layer call
+STAGES = ("in_quant", "in_proj", "conv", "scan", "gate_quant", "out_proj")
+
+
+class LayerOpts(ctypes.Structure):
+    _fields_ = [("keep_intermediates", _c_i32), ("reserved", _c_i32), ("quant_stats", _vp),
+                ("stage_events", ctypes.POINTER(_vp))]
+
+
+def layer_opts(keep=False, quant_stats=None, events=None):
+    """A per-call fm_layer_opts, or None when every option is off.
+
+    quant_stats: a device fm_quant_stats buffer (quant_stats_buffer);
+    events: LAYER_EVENTS torch.cuda.Event or None entries (stage boundaries)."""
+    if not keep and quant_stats is None and events is None:
+        return None
+    o = LayerOpts()
+    o.keep_intermediates = 1 if keep else 0
+    o.quant_stats = None if quant_stats is None else quant_stats.data_ptr()
+    if events is not None:
+        if len(events) != LAYER_EVENTS:
+            raise ValueError(f"events: {LAYER_EVENTS} entries")
+        arr = (_vp * LAYER_EVENTS)(*[None if e is None else e.cuda_event for e in events])
+        o._events = arr  # keep the array alive with the struct
+        o.stage_events = ctypes.cast(arr, ctypes.POINTER(_vp))
+    return o
+
+
+def opts_ref(o):
+    return None if o is None else ctypes.byref(o)
+
+
 class LayerTaps(ctypes.Structure):
     _fields_ = [(n, _c_sz) for n in ("u_q", "v", "xbc_q", "x_q", "b_q", "c_q", "y", "g_q",
                                      "normed", "dt", "da")]
@@ -101,16 +133,15 @@ _SIGS = {
     "fm_mamba2_layer_prefill": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
                                                ctypes.POINTER(LayerWeights),
                                                ctypes.POINTER(StaticParams), _vp, _c_i64, _c_i64,
-                                               _vp, ctypes.POINTER(Cache), _vp, _vp, _c_sz, _vp]),
+                                               _vp, ctypes.POINTER(Cache), _vp,
+                                               ctypes.POINTER(LayerOpts), _vp, _c_sz, _vp]),
     "fm_mamba2_layer_decode": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
                                               ctypes.POINTER(LayerWeights),
                                               ctypes.POINTER(StaticParams), _vp, _c_i64,
-                                              ctypes.POINTER(Cache), _vp, _vp, _vp, _c_sz, _vp]),
+                                              ctypes.POINTER(Cache), _vp, _vp,
+                                              ctypes.POINTER(LayerOpts), _vp, _c_sz, _vp]),
     "fm_mamba2_layer_taps": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _c_i64, _c_i64,
                                             ctypes.POINTER(LayerTaps)]),
-    "fm_layer_keep_intermediates": (None, [_c_i32]),
-    "fm_layer_set_timing_events": (None, [_vp, _vp]),
-    "fm_layer_collect_quant_stats": (None, [_vp]),
     "fm_nau_eval_knots": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i64, _vp]),
     "fm_quant_per_tensor_workspace_size": (_c_sz, []),
     "fm_quant_per_tensor": (ctypes.c_int, [_vp, _c_i64, _vp, _vp, _vp, _c_sz, _vp]),
@@ -127,17 +158,19 @@ _SIGS = {
     "fm_mamba2_layer_prefill_ssd": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
                                                    ctypes.POINTER(LayerWeights),
                                                    ctypes.POINTER(StaticParams), _vp, _c_i64,
-                                                   _c_i64, _vp, ctypes.POINTER(Cache), _vp, _vp,
-                                                   _c_sz, _vp]),
+                                                   _c_i64, _vp, ctypes.POINTER(Cache), _vp,
+                                                   ctypes.POINTER(LayerOpts), _vp, _c_sz, _vp]),
     "fm_state_narrow_bytes": (_c_sz, [_c_i64, _c_i32]),
     "fm_state_narrow": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
     "fm_state_widen": (ctypes.c_int, [_vp, _c_i64, _c_i32, _c_i32, _vp, _vp]),
     "fm_state_absmax": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
+    "fm_state_shift_for": (ctypes.c_int, [ctypes.c_uint32, _c_i32, _c_i32,
+                                          ctypes.POINTER(_c_i32)]),
     "fm_mamba2_layer_decode_narrow": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
                                                      ctypes.POINTER(LayerWeights),
                                                      ctypes.POINTER(StaticParams), _vp, _c_i64,
-                                                     ctypes.POINTER(CacheNarrow), _vp, _vp, _vp,
-                                                     _c_sz, _vp]),
+                                                     ctypes.POINTER(CacheNarrow), _vp, _vp,
+                                                     ctypes.POINTER(LayerOpts), _vp, _c_sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -207,10 +240,11 @@ def fm_state_absmax(state, amax, stream=None):
     _check(lib.fm_state_absmax(_ptr(state), state.numel(), _ptr(amax), _stream(stream)))
 
 
-def state_shift_for(amax, bits, headroom=1):
-    """The smallest shift whose codes hold amax * 2^headroom unclipped."""
-    need = int(amax).bit_length() + int(headroom)
-    return min(max(0, need - (bits - 1)), 32 - bits)
+def fm_state_shift_for(amax, bits, headroom=1):
+    """The narrow-state shift for a largest |state| of amax (host call)."""
+    out = _c_i32()
+    _check(lib.fm_state_shift_for(int(amax) & 0xFFFFFFFF, bits, headroom, ctypes.byref(out)))
+    return out.value
 
 
 def fm_quant_per_tensor(x, q, scale_out, ws=None, stream=None):
@@ -310,10 +344,6 @@ def qparams_from_device(qp_dev) -> QParams:
     return QParams.from_buffer_copy(raw)
 
 
-def keep_intermediates(on: bool):
-    lib.fm_layer_keep_intermediates(1 if on else 0)
-
-
 # quantization points of fm_quant_stats
 QP_U, QP_G, QP_XBC, QP_X, QP_B, QP_C = range(6)
 QP_NAMES = ("u", "g", "xbc", "x", "B", "C")
@@ -327,11 +357,6 @@ class QuantStats(ctypes.Structure):
 def quant_stats_buffer(device="cuda"):
     """A zeroed device fm_quant_stats (as a uint8 tensor)."""
     return torch.zeros(ctypes.sizeof(QuantStats), dtype=torch.uint8, device=device)
-
-
-def collect_quant_stats(buf):
-    """Later prefill layer calls of this thread add their statistics to buf (None: stop)."""
-    lib.fm_layer_collect_quant_stats(None if buf is None else buf.data_ptr())
 
 
 def quant_stats_from_device(buf) -> QuantStats:

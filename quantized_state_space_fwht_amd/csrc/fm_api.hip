@@ -483,10 +483,31 @@ static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights
                     who);
 }
 
+// Per-call options: everything off when NULL; validated before any launch.
+static fm_status check_opts(const fm_layer_opts* o, bool decode, LayerOpts* out, const char* who) {
+    *out = LayerOpts{};
+    if (!o) return FM_OK;
+    if (o->keep_intermediates != 0 && o->keep_intermediates != 1)
+        return fail(FM_ERR_MODE, "%s: opts.keep_intermediates %d not 0 or 1", who,
+                    o->keep_intermediates);
+    if (o->reserved != 0) return fail(FM_ERR_MODE, "%s: opts.reserved must be 0", who);
+    if (o->quant_stats) {
+        if (decode) return fail(FM_ERR_MODE, "%s: decode calls do not collect quant_stats", who);
+        if (!aligned(o->quant_stats, 8))
+            return fail(FM_ERR_SHAPE, "%s: opts.quant_stats must be 8-byte aligned", who);
+    }
+    out->keep = o->keep_intermediates != 0;
+    out->qs = o->quant_stats;
+    if (o->stage_events)
+        for (int i = 0; i < FM_LAYER_EVENTS; ++i) out->ev[i] = (hipEvent_t)o->stage_events[i];
+    return FM_OK;
+}
+
 fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights* w,
                                   const fm_static_params* sp, const float* u, int64_t batch,
                                   int64_t len, float* out, const fm_cache* cache, fm_qparams* qp,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                  const fm_layer_opts* opts, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
     const char* who = "fm_mamba2_layer_prefill";
     g_err[0] = 0;
     fm_status st = check_layer_call(d, w, sp, u, batch, len, out, qp, workspace, workspace_bytes,
@@ -494,7 +515,9 @@ fm_status fm_mamba2_layer_prefill(const fm_layer_desc* d, const fm_layer_weights
     if (st != FM_OK) return st;
     if (cache && (!cache->conv_state || !cache->ssm_state || !cache->p))
         return fail(FM_ERR_NULL, "%s: cache has a NULL member", who);
-    return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream);
+    LayerOpts lo;
+    if ((st = check_opts(opts, false, &lo, who)) != FM_OK) return st;
+    return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream, lo);
 }
 
 size_t fm_mamba2_layer_workspace_size_ssd(const fm_layer_desc* d, int64_t batch, int64_t len) {
@@ -506,8 +529,8 @@ size_t fm_mamba2_layer_workspace_size_ssd(const fm_layer_desc* d, int64_t batch,
 fm_status fm_mamba2_layer_prefill_ssd(const fm_layer_desc* d, const fm_layer_weights* w,
                                       const fm_static_params* sp, const float* u, int64_t batch,
                                       int64_t len, float* out, const fm_cache* cache,
-                                      fm_qparams* qp, void* workspace, size_t workspace_bytes,
-                                      hipStream_t stream) {
+                                      fm_qparams* qp, const fm_layer_opts* opts, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
     const char* who = "fm_mamba2_layer_prefill_ssd";
     g_err[0] = 0;
     fm_status st = check_layer_call(d, w, sp, u, batch, len, out, qp, workspace, workspace_bytes,
@@ -515,15 +538,18 @@ fm_status fm_mamba2_layer_prefill_ssd(const fm_layer_desc* d, const fm_layer_wei
     if (st != FM_OK) return st;
     if (cache && (!cache->conv_state || !cache->ssm_state || !cache->p))
         return fail(FM_ERR_NULL, "%s: cache has a NULL member", who);
+    LayerOpts lo;
+    if ((st = check_opts(opts, false, &lo, who)) != FM_OK) return st;
     void* ssd_ws = (char*)workspace + align256(fm_mamba2_layer_workspace_size(d, batch, len));
-    return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream, 32, 0,
+    return layer_run(d, w, sp, u, batch, len, out, cache, qp, workspace, false, stream, lo, 32, 0,
                      ssd_ws);
 }
 
 fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights* w,
                                  const fm_static_params* sp, const float* u_t, int64_t batch,
                                  const fm_cache* cache, float* out_t, fm_qparams* qp,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                 const fm_layer_opts* opts, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
     const char* who = "fm_mamba2_layer_decode";
     g_err[0] = 0;
     fm_status st = check_layer_call(d, w, sp, u_t, batch, 1, out_t, qp, workspace,
@@ -531,7 +557,9 @@ fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights*
     if (st != FM_OK) return st;
     if (!cache || !cache->conv_state || !cache->ssm_state || !cache->p)
         return fail(FM_ERR_NULL, "%s: decode needs a complete cache", who);
-    return layer_run(d, w, sp, u_t, batch, 1, out_t, cache, qp, workspace, true, stream);
+    LayerOpts lo;
+    if ((st = check_opts(opts, true, &lo, who)) != FM_OK) return st;
+    return layer_run(d, w, sp, u_t, batch, 1, out_t, cache, qp, workspace, true, stream, lo);
 }
 
 static fm_status check_state_fmt(int32_t bits, int32_t shift, const char* who) {
@@ -544,7 +572,8 @@ static fm_status check_state_fmt(int32_t bits, int32_t shift, const char* who) {
 fm_status fm_mamba2_layer_decode_narrow(const fm_layer_desc* d, const fm_layer_weights* w,
                                         const fm_static_params* sp, const float* u_t,
                                         int64_t batch, const fm_cache_narrow* cache, float* out_t,
-                                        fm_qparams* qp, void* workspace, size_t workspace_bytes,
+                                        fm_qparams* qp, const fm_layer_opts* opts,
+                                        void* workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
     const char* who = "fm_mamba2_layer_decode_narrow";
     g_err[0] = 0;
@@ -556,8 +585,10 @@ fm_status fm_mamba2_layer_decode_narrow(const fm_layer_desc* d, const fm_layer_w
     if ((st = check_state_fmt(cache->state_bits, cache->state_shift, who)) != FM_OK) return st;
     if (!aligned(cache->ssm_state, 16))
         return fail(FM_ERR_SHAPE, "%s: ssm_state must be 16-byte aligned", who);
+    LayerOpts lo;
+    if ((st = check_opts(opts, true, &lo, who)) != FM_OK) return st;
     const fm_cache c32{cache->conv_state, (int32_t*)cache->ssm_state, cache->p};
-    return layer_run(d, w, sp, u_t, batch, 1, out_t, &c32, qp, workspace, true, stream,
+    return layer_run(d, w, sp, u_t, batch, 1, out_t, &c32, qp, workspace, true, stream, lo,
                      cache->state_bits, cache->state_shift);
 }
 
@@ -574,6 +605,22 @@ fm_status fm_state_narrow(const int32_t* state, int64_t count, int32_t bits, int
     if (count < 0) return fail(FM_ERR_SHAPE, "%s: count %lld < 0", who, (long long)count);
     if (count > 0 && (!state || !codes)) return fail(FM_ERR_NULL, "%s: NULL pointer", who);
     return state_narrow_run(state, count, bits, shift, codes, stream);
+}
+
+fm_status fm_state_shift_for(uint32_t amax, int32_t bits, int32_t headroom, int32_t* shift) {
+    const char* who = "fm_state_shift_for";
+    g_err[0] = 0;
+    if (!shift) return fail(FM_ERR_NULL, "%s: shift is NULL", who);
+    if (bits != 16 && bits != 24) return fail(FM_ERR_SHAPE, "%s: bits %d not 16 or 24", who, bits);
+    if (headroom < 0 || headroom > 32)
+        return fail(FM_ERR_SHAPE, "%s: headroom %d not in [0, 32]", who, headroom);
+    int need = headroom;  // bit length of amax, plus the headroom
+    for (uint32_t a = amax; a; a >>= 1) ++need;
+    int sh = need - (bits - 1);
+    if (sh < 0) sh = 0;
+    if (sh > 32 - bits) sh = 32 - bits;
+    *shift = sh;
+    return FM_OK;
 }
 
 fm_status fm_state_widen(const void* codes, int64_t count, int32_t bits, int32_t shift,
@@ -605,11 +652,6 @@ fm_status fm_mamba2_layer_taps(const fm_layer_desc* d, int64_t batch, int64_t le
     return FM_OK;
 }
 
-void fm_layer_keep_intermediates(int32_t on) { set_keep_intermediates(on != 0); }
-
-void fm_layer_set_timing_events(void* start, void* stop) { set_timing_events(start, stop); }
-
-void fm_layer_collect_quant_stats(fm_quant_stats* dev_stats) { set_quant_stats(dev_stats); }
 
 // ---------------------------------------------------------------- outlier-study baselines
 size_t fm_quant_per_tensor_workspace_size(void) { return 256; }

@@ -124,7 +124,8 @@ __device__ __forceinline__ void nau_lds_init(NauLds& t) {
 // there (the product is exact wherever v >= -17*2^16, |x * log2e| < 2^51).
 __device__ __forceinline__ int32_t nau_exp_f(int32_t x, const NauLds& t) {
     double vf = __builtin_floor(__builtin_fma((double)x, (double)kLog2eQ30, 0x1p29) * 0x1p-30);
-    vf = __builtin_fmax(vf, -1179648.0);
+    // arguments > 0 (outside the unit's domain) are taken as 0
+    vf = __builtin_fmin(__builtin_fmax(vf, -1179648.0), 0.0);
     const int v = (int)vf;
     const int n = v >> 16;  // -18..0
     const int f = v & 0xFFFF;

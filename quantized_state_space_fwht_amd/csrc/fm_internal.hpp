@@ -268,15 +268,19 @@ fm_status scale_columns_run(const float* x, int64_t rows, int64_t k, const float
 // layer pipeline (fm_layer.hip)
 size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);
 void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t);
-void set_keep_intermediates(bool on);
-void set_timing_events(void* start, void* stop);
-void set_quant_stats(fm_quant_stats* qs);
+// the per-call options of a layer call (fm_layer_opts, validated)
+struct LayerOpts {
+    bool keep = false;               // also write the intermediates the taps name
+    fm_quant_stats* qs = nullptr;    // prefill: add the quantization statistics here
+    hipEvent_t ev[FM_LAYER_EVENTS] = {};  // stage boundaries (fm_layer_opts.stage_events)
+};
 // state_bits / state_shift: the decode cache's state format (ScanArgs);
 // ssd_ws (prefill only): run the chunked scan variant with this workspace
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
                     fm_qparams* qp, void* workspace, bool decode, hipStream_t s,
-                    int state_bits = 32, int state_shift = 0, void* ssd_ws = nullptr);
+                    const LayerOpts& opts, int state_bits = 32, int state_shift = 0,
+                    void* ssd_ws = nullptr);
 
 // narrow state codes (fm_state.hip)
 fm_status state_narrow_run(const int32_t* h, int64_t n, int bits, int shift, void* out,

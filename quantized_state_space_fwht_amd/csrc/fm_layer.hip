@@ -81,17 +81,6 @@ void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_tap
     t->da = off(w.da);
 }
 
-static bool g_keep = false;
-void set_keep_intermediates(bool on) { g_keep = on; }
-
-static thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
-static thread_local fm_quant_stats* g_qstats = nullptr;
-void set_quant_stats(fm_quant_stats* qs) { g_qstats = qs; }
-void set_timing_events(void* start, void* stop) {
-    g_ev_start = (hipEvent_t)start;
-    g_ev_stop = (hipEvent_t)stop;
-}
-
 // zero the small block and the slots of the slot regions; optionally load the
 // exponents (static values or a device copy)
 __global__ void layer_setup_kernel(uint32_t* small, int32_t* slots, const int32_t* p_src, int p0,
@@ -206,19 +195,26 @@ __global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs
 // Shared body of prefill (len tokens, fresh state) and decode (len = 1, cache).
 fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_static_params* sp,
                     const float* u, int64_t batch, int64_t len, float* out, const fm_cache* cache,
-                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s, int state_bits,
-                    int state_shift, void* ssd_ws) {
+                    fm_qparams* qp, void* workspace, bool decode, hipStream_t s,
+                    const LayerOpts& opts, int state_bits, int state_shift, void* ssd_ws) {
     const int64_t T = batch * len;
     const int64_t dm = d->d_model, di = d->d_inner, N = d->dstate, H = d->nheads, P = d->headdim;
     const int64_t ch = di + 2 * N, dip = 2 * di + 2 * N + H;
     const fm_scale_mode mode = (fm_scale_mode)d->mode;
     const bool stat = mode == FM_SCALE_STATIC;
     LayerWs w = layer_ws(d, batch, len, workspace);
-    fm_quant_stats* const qs = decode ? nullptr : g_qstats;  // prefill calls collect
+    fm_quant_stats* const qs = decode ? nullptr : opts.qs;  // prefill calls collect
+    const bool keep = opts.keep;
     fm_status st;
     float* small_f = (float*)w.small;
     int32_t* small_i = (int32_t*)w.small;
     int32_t* pdev = small_i + kP;
+    auto mark = [&](int i) -> fm_status {
+        if (opts.ev[i] && hipEventRecord(opts.ev[i], s) != hipSuccess)
+            return fail(FM_ERR_HIP, "hipEventRecord(stage event %d) failed", i);
+        return FM_OK;
+    };
+    if ((st = mark(0)) != FM_OK) return st;
 
     // A decode step with few rows takes the fused form, six kernels: rotated
     // input rows; in_proj quantizing them on load, with the conv step in its
@@ -260,6 +256,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
                          FM_QP_U)) != FM_OK)
             return st;
     }
+    if ((st = mark(1)) != FM_OK) return st;
     // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
     {
         GemmEpilogue ep;
@@ -281,7 +278,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.a_sshift = stat ? sp->sshift[0] : 0;
             ep.a_amax_out = small_f + kAmaxU;
             ep.a_scale_out = small_f + kScaleU;
-            ep.a_q_tap = g_keep ? w.u_q : nullptr;
+            ep.a_q_tap = keep ? w.u_q : nullptr;
         }
         if (step) {  // 4-5 fused: conv step + SiLU + requant with the frozen exponents
             ep.conv_w_q = W->conv_w_q;
@@ -292,12 +289,12 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.x_out = w.x_q;
             ep.b_out = w.b_q;
             ep.c_out = w.c_q;
-            ep.xbc_q = g_keep ? w.xbc_q : nullptr;
+            ep.xbc_q = keep ? w.xbc_q : nullptr;
             ep.conv_amax_q16 = small_i + kAmaxQ;
             ep.d_inner = di;
             ep.dstate = N;
             ep.sz_out = w.sz;
-            ep.write_xbc = g_keep;
+            ep.write_xbc = keep;
             ep.dt_bias = W->dt_bias;  // 6 fused: dt and the decay for the scan step
             ep.a_q16 = W->a_q16;
             ep.dt_out = w.dt;
@@ -305,6 +302,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         }
         if ((st = gemm_run(w.u_q, W->w_in_q, T, dip, dm, ep, s)) != FM_OK) return st;
     }
+    if ((st = mark(2)) != FM_OK) return st;
     // 4-5. conv1d + SiLU + requant of x / B / C
     if (!step) {
         ConvArgs a{};
@@ -323,7 +321,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.p_fixed = fixed_p ? pdev : nullptr;
         a.state_in = decode ? cache->conv_state : nullptr;
         a.state_out = cache ? cache->conv_state : nullptr;
-        a.xbc_q = g_keep ? w.xbc_q : nullptr;
+        a.xbc_q = keep ? w.xbc_q : nullptr;
         a.s16 = w.s16;
         a.amax_q16 = small_i + kAmaxQ;
         a.amax_slots = w.slots + kRegionConvX * kSlotRegionWords;
@@ -369,8 +367,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.dt_ready = true;  // formed by the conv launch, or by in_proj's epilogue (step)
         a.state_bits = decode ? state_bits : 32;
         a.state_shift = decode ? state_shift : 0;
-        hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-        g_ev_start = g_ev_stop = nullptr;
+        hipEvent_t ev0 = opts.ev[3], ev1 = opts.ev[4];
         if (ssd_ws && !decode) {
             if ((st = ssd_run(a, ssd_ws, s, ev0, ev1)) != FM_OK) return st;
         } else if ((st = scan_run(a, w.scan_ws, s, ev0, ev1)) != FM_OK) {
@@ -393,7 +390,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         g.q = w.g_q;
         g.scale_out = small_f + kScaleG;
         g.amax_stats = stat ? small_f + kAmaxG : nullptr;
-        g.normed_out = g_keep ? w.normed : nullptr;
+        g.normed_out = keep ? w.normed : nullptr;
         g.rot_ws = w.rot;
         g.amax_ws = small_f + kAmaxG;
         g.amax_slots = w.slots + kRegionG * kSlotRegionWords;
@@ -419,11 +416,13 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
                                          stat ? sp->scoe[1] : 0, stat ? sp->sshift[1] : 0, w.g_q,
                                          small_f + kScaleG, small_f + kAmaxG, s)) != FM_OK)
             return st;
+        if ((st = mark(5)) != FM_OK) return st;
         // the call's scales, exponents and statistics go out with this last kernel
         ep.pub_small = w.small;
         ep.pub_qp = qp;
         ep.pub_cache_p = (cache && !decode) ? cache->p : nullptr;
-        return gemm_run(w.g_q, W->w_out_q, T, dm, di, ep, s);
+        if ((st = gemm_run(w.g_q, W->w_out_q, T, dm, di, ep, s)) != FM_OK) return st;
+        return mark(6);
     }
 }
 

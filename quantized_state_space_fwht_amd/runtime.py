@@ -19,15 +19,26 @@ def _dev(a, dtype=None, device="cuda"):
     return t.to(device).contiguous()
 
 
+class GraphHeld(RuntimeError):
+    """A buffer a captured graph points at would be reallocated."""
+
+
 class WorkspacePool:
-    """One device workspace shared by layers that run one call at a time."""
+    """One device workspace shared by layers that run one call at a time.
+
+    While a captured graph holds the pool (``holds`` > 0) it never regrows:
+    the graph's kernels keep the current buffer's address."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.t = None
+        self.holds = 0
 
     def get(self, need):
         if self.t is None or self.t.numel() < need:
+            if self.holds:
+                raise GraphHeld(f"workspace of {0 if self.t is None else self.t.numel()} bytes "
+                                f"would grow to {need} while a captured graph uses it")
             self.t = None  # release before growing
             self.t = B.workspace(need, self.device)
         return self.t
@@ -83,6 +94,11 @@ class Mamba2Layer:
         self._ws_key = None
         self.cache = None
         self.ncache = None  # narrow state cache (narrow_state), used by decode when set
+        self.holds = 0      # captured graphs pointing at this layer's caches / workspace
+
+    def _check_not_held(self, what):
+        if self.holds:
+            raise GraphHeld(f"{what} would replace buffers a captured graph uses")
 
     # ------------------------------------------------------------ memory
     def workspace_for(self, batch, length, ssd=False):
@@ -92,11 +108,13 @@ class Mamba2Layer:
         if self._pool is not None:
             self._ws = self._pool.get(need)
         elif self._ws is None or self._ws.numel() < need:
+            self._check_not_held("growing the workspace")
             self._ws = B.workspace(need, self.device)
         self._ws_key = (batch, length)
         return self._ws
 
     def alloc_cache(self, batch):
+        self._check_not_held("a new cache")
         s = self.shape
         self.cache_t = {
             "conv_state": torch.zeros((batch, s.conv_ch, 3), dtype=torch.int8, device=self.device),
@@ -113,11 +131,12 @@ class Mamba2Layer:
         `bits`-bit codes on the grid 2^shift; later decode calls use them.
         shift None: the smallest that holds 2^headroom times the current
         largest |state| unclipped.  Returns the shift."""
+        self._check_not_held("narrowing the state")
         st = self.cache_t["ssm_state"]
         if shift is None:
             amax = torch.zeros(1, dtype=torch.int32, device=self.device)
             B.fm_state_absmax(st, amax)
-            shift = B.state_shift_for(int(amax.item()) & 0xFFFFFFFF, bits, headroom)
+            shift = B.fm_state_shift_for(int(amax.item()) & 0xFFFFFFFF, bits, headroom)
         codes = torch.empty(B.lib.fm_state_narrow_bytes(st.numel(), bits), dtype=torch.uint8,
                             device=self.device)
         B.fm_state_narrow(st, bits, shift, codes)
@@ -148,9 +167,10 @@ class Mamba2Layer:
         return B.qparams_from_device(self.qp)
 
     # ------------------------------------------------------------ calls
-    def prefill(self, u, out=None, with_cache=True, stream=None, scan="sequential"):
+    def prefill(self, u, out=None, with_cache=True, stream=None, scan="sequential", opts=None):
         """u [batch, len, d_model] float32 device tensor -> out (same shape).
-        scan "ssd": the chunked scan variant (fm_mamba2_layer_prefill_ssd)."""
+        scan "ssd": the chunked scan variant (fm_mamba2_layer_prefill_ssd);
+        opts: a binding.LayerOpts for this call (binding.layer_opts) or None."""
         batch, length, dm = u.shape
         if out is None:
             out = torch.empty_like(u)
@@ -160,19 +180,21 @@ class Mamba2Layer:
         ws = self.workspace_for(batch, length, ssd)
         cache = None
         if with_cache:
-            self.ncache = None  # the prefill writes the int32 state
+            if self.ncache is not None:  # a graph stepping the narrow codes would go stale
+                self._check_not_held("a prefill over a narrow state")
             if self.cache is None or self.cache_t["ssm_state"].shape[0] != batch:
                 self.alloc_cache(batch)
+            self.ncache = None  # the prefill writes the int32 state
             cache = ctypes.byref(self.cache)
         sp = ctypes.byref(self.static) if self.static is not None else None
         fn = B.lib.fm_mamba2_layer_prefill_ssd if ssd else B.lib.fm_mamba2_layer_prefill
         B._check(fn(
             ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u.data_ptr(), batch, length,
-            out.data_ptr(), cache, self.qp.data_ptr(), ws.data_ptr(), ws.numel(),
-            B._stream(stream)))
+            out.data_ptr(), cache, self.qp.data_ptr(), B.opts_ref(opts), ws.data_ptr(),
+            ws.numel(), B._stream(stream)))
         return out
 
-    def decode(self, u_t, out=None, stream=None):
+    def decode(self, u_t, out=None, stream=None, opts=None):
         """u_t [batch, d_model] -> out_t, advancing the cache by one token."""
         batch, dm = u_t.shape
         if out is None:
@@ -182,13 +204,13 @@ class Mamba2Layer:
         if self.ncache is not None:
             B._check(B.lib.fm_mamba2_layer_decode_narrow(
                 ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u_t.data_ptr(), batch,
-                ctypes.byref(self.ncache), out.data_ptr(), self.qp.data_ptr(), ws.data_ptr(),
-                ws.numel(), B._stream(stream)))
+                ctypes.byref(self.ncache), out.data_ptr(), self.qp.data_ptr(),
+                B.opts_ref(opts), ws.data_ptr(), ws.numel(), B._stream(stream)))
             return out
         B._check(B.lib.fm_mamba2_layer_decode(
             ctypes.byref(self.desc), ctypes.byref(self.weights), sp, u_t.data_ptr(), batch,
-            ctypes.byref(self.cache), out.data_ptr(), self.qp.data_ptr(), ws.data_ptr(),
-            ws.numel(), B._stream(stream)))
+            ctypes.byref(self.cache), out.data_ptr(), self.qp.data_ptr(), B.opts_ref(opts),
+            ws.data_ptr(), ws.numel(), B._stream(stream)))
         return out
 
     def taps(self, batch, length):
@@ -219,22 +241,25 @@ class Mamba2Stack:
                        for p in params_list]
         self.shape = shape
 
-    def prefill(self, u, with_cache=True, stream=None, quant_stats=None):
+    def prefill(self, u, with_cache=True, stream=None, quant_stats=None, layer_opts=None,
+                bufs=None):
         """``quant_stats``: optional list of device fm_quant_stats buffers, one per
         layer (binding.quant_stats_buffer), into which each layer adds the
-        statistics of its quantization points."""
+        statistics of its quantization points.  ``layer_opts``: optional list of
+        per-layer binding.LayerOpts (taking precedence over quant_stats).
+        ``bufs``: two tensors shaped like u for the residual stream (allocated
+        if None); the result is one of them."""
         h = u.contiguous()
-        bufs = [torch.empty_like(h), torch.empty_like(h)]
-        try:
-            for i, layer in enumerate(self.layers):
-                nxt = bufs[i % 2]
-                if quant_stats is not None:
-                    B.collect_quant_stats(quant_stats[i])
-                layer.prefill(h, out=nxt, with_cache=with_cache, stream=stream)
-                h = nxt
-        finally:
-            if quant_stats is not None:
-                B.collect_quant_stats(None)
+        if bufs is None:
+            bufs = [torch.empty_like(h), torch.empty_like(h)]
+        for i, layer in enumerate(self.layers):
+            nxt = bufs[i % 2]
+            if layer_opts is not None:
+                opts = layer_opts[i]
+            else:
+                opts = None if quant_stats is None else B.layer_opts(quant_stats=quant_stats[i])
+            layer.prefill(h, out=nxt, with_cache=with_cache, stream=stream, opts=opts)
+            h = nxt
         return h
 
     def decode(self, u_t, stream=None):
@@ -271,7 +296,15 @@ class DecodeGraph:
     returned tensor is the graph's output buffer (the next replay overwrites
     it).  Capture records work without running it, so the caches are not
     advanced by building the graph; the stack's workspace must already be
-    sized (any earlier prefill or decode call on it does that)."""
+    sized (any earlier prefill or decode call on it does that).
+
+    The graph's kernels hold raw addresses of the shared workspace and of every
+    layer's caches.  While the graph is open it keeps references to those
+    tensors and holds the pool and the layers: a call that would replace one
+    (a prefill with another batch or a larger workspace, narrowing the state)
+    raises GraphHeld instead.  ``close()`` (or leaving a ``with`` block) lets
+    them go; ``step`` also checks the recorded addresses and refuses to replay
+    a closed graph."""
 
     def __init__(self, stack: Mamba2Stack, batch: int, device="cuda"):
         self.stack = stack
@@ -281,8 +314,46 @@ class DecodeGraph:
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             self.out = stack.decode(self.x)
+        self._held = self._buffers()
+        self._ptrs = tuple(t.data_ptr() for t in self._held)
+        stack.pool.holds += 1
+        for layer in stack.layers:
+            layer.holds += 1
+        self.open = True
+
+    def _buffers(self):
+        ts = [self.stack.pool.t]
+        for layer in self.stack.layers:
+            ts += [layer.cache_t[k] for k in ("conv_state", "ssm_state", "p")]
+            if layer.ncache is not None:
+                ts.append(layer.cache_t["ssm_codes"])
+        return ts
+
+    def close(self):
+        if self.open:
+            self.open = False
+            self.stack.pool.holds -= 1
+            for layer in self.stack.layers:
+                layer.holds -= 1
+            self._held = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
     def step(self, x):
+        if not self.open:
+            raise GraphHeld("the decode graph is closed")
+        if tuple(t.data_ptr() for t in self._buffers()) != self._ptrs:
+            raise GraphHeld("a buffer the decode graph uses was replaced")
         self.x.copy_(x)
         self.graph.replay()
         return self.out

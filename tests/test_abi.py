@@ -32,7 +32,7 @@ def test_exports_every_declared_entry_point(lib):
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     lib.fm_abi_version.restype = ctypes.c_int
-    assert lib.fm_abi_version() == 1
+    assert lib.fm_abi_version() == 2
 
 
 def _last_error(lib):
@@ -104,18 +104,19 @@ def test_layer_validation_and_workspace_query(lib):
     f = lib.fm_mamba2_layer_prefill
     f.argtypes = [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
     bad = Desc(768, 1536, 24, 64, 128, 3, 0, 0)  # d_conv != 4
-    assert f(ctypes.byref(bad), None, None, None, 1, 16, None, None, None, None, 0, None) \
-        == FM_ERR_SHAPE
-    assert f(ctypes.byref(d), None, None, None, 1, 16, None, None, None, None, 0, None) \
-        == FM_ERR_NULL
+    assert f(ctypes.byref(bad), None, None, None, 1, 16, None, None, None, None, None, 0,
+             None) == FM_ERR_SHAPE
+    assert f(ctypes.byref(d), None, None, None, 1, 16, None, None, None, None, None, 0,
+             None) == FM_ERR_NULL
     # empty calls are refused, not launched: a batch or a length of 0
     fake = 1 << 20
     weights = (ctypes.c_void_p * 11)(*([fake] * 11))
     for batch, length in ((0, 16), (1, 0), (-1, 4)):
         assert f(ctypes.byref(d), ctypes.cast(weights, ctypes.c_void_p), None, fake, batch, length,
-                 2 * fake, None, fake, fake, 1 << 40, None) == FM_ERR_SHAPE
+                 2 * fake, None, fake, None, fake, 1 << 40, None) == FM_ERR_SHAPE
 
 
 def test_qparams_from_stats_on_host(lib):
@@ -219,11 +220,70 @@ def test_narrow_state_validation(lib):
     weights = (vp * 11)(*([fake] * 11))
     f = lib.fm_mamba2_layer_decode_narrow
     f.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, ctypes.POINTER(CacheNarrow), vp, vp, vp,
-                  ctypes.c_size_t, vp]
+                  vp, ctypes.c_size_t, vp]
     call = lambda c: f(ctypes.byref(d), ctypes.cast(weights, vp), None, fake, 4,
-                       None if c is None else ctypes.byref(c), 2 * fake, fake, fake, ws, None)
+                       None if c is None else ctypes.byref(c), 2 * fake, fake, None, fake, ws,
+                       None)
     assert call(None) == FM_ERR_NULL
     assert call(CacheNarrow(fake, None, fake, 16, 0)) == FM_ERR_NULL
     assert call(CacheNarrow(fake, fake, fake, 8, 0)) == FM_ERR_SHAPE, _last_error(lib)
     assert call(CacheNarrow(fake, fake, fake, 16, 17)) == FM_ERR_SHAPE
     assert call(CacheNarrow(fake, fake + 8, fake, 16, 2)) == FM_ERR_SHAPE  # 16-byte alignment
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("keep_intermediates", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("quant_stats", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+def test_layer_opts_validation(lib):
+    """The per-call options are checked before any launch: keep_intermediates
+    0 or 1, reserved 0, quant_stats aligned and refused by decode calls."""
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    fake = 1 << 20
+    d = Desc(768, 1536, 24, 64, 128, 4, 0, 0)
+    weights = ctypes.cast((vp * 11)(*([fake] * 11)), vp)
+
+    class Cache(ctypes.Structure):
+        _fields_ = [("conv_state", vp), ("ssm_state", vp), ("p", vp)]
+    cache = Cache(fake, fake, fake)
+    pre = lib.fm_mamba2_layer_prefill
+    pre.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, i64, vp, vp, vp, vp, vp,
+                    ctypes.c_size_t, vp]
+    dec = lib.fm_mamba2_layer_decode
+    dec.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    big = 1 << 40
+    prefill = lambda o: pre(ctypes.byref(d), weights, None, fake, 1, 16, 2 * fake, None, fake,
+                            ctypes.cast(ctypes.byref(o), vp), fake, big, None)
+    decode = lambda o: dec(ctypes.byref(d), weights, None, fake, 4, ctypes.cast(
+        ctypes.byref(cache), vp), 2 * fake, fake, ctypes.cast(ctypes.byref(o), vp), fake, big,
+        None)
+    assert prefill(Opts(2, 0, None, None)) == FM_ERR_MODE
+    assert "keep_intermediates" in _last_error(lib)
+    assert prefill(Opts(0, 1, None, None)) == FM_ERR_MODE
+    assert prefill(Opts(0, 0, fake + 4, None)) == FM_ERR_SHAPE        # 8-byte alignment
+    assert decode(Opts(0, 0, fake, None)) == FM_ERR_MODE               # decode does not collect
+    assert "do not collect" in _last_error(lib)
+    assert decode(Opts(3, 0, None, None)) == FM_ERR_MODE
+    # nothing of a failed call is remembered: the message is the call's own
+    assert prefill(Opts(0, 1, None, None)) == FM_ERR_MODE
+    assert "reserved" in _last_error(lib)
+
+
+def test_state_shift_for_on_host(lib):
+    """The narrow-state shift helper agrees with the oracle's rule on every
+    bit length, at both widths and several headrooms; bad arguments are refused."""
+    import oracle as O
+    f = lib.fm_state_shift_for
+    f.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    out = ctypes.c_int32()
+    amaxes = [0, 1, 2, 3] + [(1 << k) + d for k in range(2, 32) for d in (-1, 0, 1)
+                              if 0 <= (1 << k) + d < (1 << 32)] + [(1 << 32) - 1]
+    for bits in (16, 24):
+        for headroom in (0, 1, 2, 5):
+            for a in amaxes:
+                assert f(a, bits, headroom, ctypes.byref(out)) == FM_OK
+                assert out.value == O.state_shift_for(a, bits, headroom), (a, bits, headroom)
+    assert f(100, 8, 1, ctypes.byref(out)) == FM_ERR_SHAPE
+    assert f(100, 16, -1, ctypes.byref(out)) == FM_ERR_SHAPE
+    assert f(100, 16, 1, None) == FM_ERR_NULL

@@ -138,14 +138,10 @@ def test_m2p7b_layer0_full_size_whole(B):
     h = layer.prefill(dev(u))  # as the stack runs it: no intermediates kept
     assert_same_float(host(h), want, "layer 0 output")
     check_caches_and_record(layer, cache_o, r, st_o)
-    B.keep_intermediates(True)
-    try:
-        layer.reset_stats()
-        h = layer.prefill(dev(u))
-        check_intermediates(layer, r, T, s)
-        assert_same_float(host(h), want, "layer 0 output (intermediates kept)")
-    finally:
-        B.keep_intermediates(False)
+    layer.reset_stats()
+    h = layer.prefill(dev(u), opts=B.layer_opts(keep=True))
+    check_intermediates(layer, r, T, s)
+    assert_same_float(host(h), want, "layer 0 output (intermediates kept)")
 
 
 def test_m2p7b_stack_full_size_batch_permutation(B):

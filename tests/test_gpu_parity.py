@@ -363,29 +363,25 @@ def test_layer_prefill_dynamic(B, wname, batch, seqlen):
     s = w.shape
     prep = O.prepare_layer(params)
     out_o, r, cache_o, st_o = O.layer_prefill(prep, s, u)
-    B.keep_intermediates(True)
-    try:
-        layer = Mamba2Layer(s, params)
-        assert_exact(host(layer.t["w_in_q"]), prep["w_in_q"], "W_in codes")
-        assert host(layer.t["s_w_in"])[0] == prep["s_w_in"]
-        assert_exact(host(layer.t["w_out_q"]), prep["w_out_q"], "W_out codes")
-        assert_exact(host(layer.t["a_q16"]), prep["A_q16"], "A_q16")
-        out = layer.prefill(dev(u))
-        torch.cuda.synchronize()
-        T = w.batch * w.seqlen
-        _check_layer_intermediates(layer, r, T, s)
-        assert np.array_equal(host(out), out_o), "layer output"
-        assert_exact(host(layer.cache_t["ssm_state"]), cache_o["ssm_state"], "ssm state")
-        assert_exact(host(layer.cache_t["conv_state"]), cache_o["conv_state"], "conv state")
-        assert_exact(host(layer.cache_t["p"]), cache_o["p"], "cached exponents")
-        qp = layer.qparams()
-        assert qp.scale[0] == r["s_u"] and qp.scale[1] == r["s_g"]
-        assert tuple(qp.p) == tuple(r["p"])
-        assert qp.stat_amax[0] == np.float32(st_o.amax_u)
-        assert qp.stat_amax[2] == np.float32(st_o.amax_xbc)
-        assert list(qp.stat_amax_q16) == list(st_o.amax_q16)
-    finally:
-        B.keep_intermediates(False)
+    layer = Mamba2Layer(s, params)
+    assert_exact(host(layer.t["w_in_q"]), prep["w_in_q"], "W_in codes")
+    assert host(layer.t["s_w_in"])[0] == prep["s_w_in"]
+    assert_exact(host(layer.t["w_out_q"]), prep["w_out_q"], "W_out codes")
+    assert_exact(host(layer.t["a_q16"]), prep["A_q16"], "A_q16")
+    out = layer.prefill(dev(u), opts=B.layer_opts(keep=True))
+    torch.cuda.synchronize()
+    T = w.batch * w.seqlen
+    _check_layer_intermediates(layer, r, T, s)
+    assert np.array_equal(host(out), out_o), "layer output"
+    assert_exact(host(layer.cache_t["ssm_state"]), cache_o["ssm_state"], "ssm state")
+    assert_exact(host(layer.cache_t["conv_state"]), cache_o["conv_state"], "conv state")
+    assert_exact(host(layer.cache_t["p"]), cache_o["p"], "cached exponents")
+    qp = layer.qparams()
+    assert qp.scale[0] == r["s_u"] and qp.scale[1] == r["s_g"]
+    assert tuple(qp.p) == tuple(r["p"])
+    assert qp.stat_amax[0] == np.float32(st_o.amax_u)
+    assert qp.stat_amax[2] == np.float32(st_o.amax_xbc)
+    assert list(qp.stat_amax_q16) == list(st_o.amax_q16)
 
 
 # 64 rows: the largest one-token step of the fused five-kernel form; 65: the
@@ -455,3 +451,32 @@ def test_nau_other_knot_tables(B, fn, fit):
             "softplus": lambda: O.softplus_q16(xi, knots),
             "silu": lambda: O.silu_q16(xi, knots)}[fn]()
     assert_exact(host(t_y), want, f"{fn} {fit}")
+
+
+def test_ssm_scan_positive_a_is_decay_one(B):
+    """A > 0 lies outside the method (A = -exp(.)): the exponential takes a
+    positive argument as 0, so a positive a_q16 gives decay 2^16 and the same
+    results as a_q16 = 0 (the oracle's reading of the unit on its domain)."""
+    batch, length, H, P, N = 2, 70, 3, 8, 64
+    rng = np.random.default_rng(77)
+    x = rng.integers(-127, 128, size=(batch, length, H, P)).astype(np.int8)
+    bm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    cm = rng.integers(-127, 128, size=(batch, length, N)).astype(np.int8)
+    dt_raw = (rng.standard_normal((batch * length, H)) - 3).astype(np.float32)
+    dt_bias = np.zeros(H, np.float32)
+    d_q16 = np.full(H, 65536, np.int64)
+    p = np.array([0, 0, 8, 8], np.int32)
+    dt, dA = O.dt_dA(dt_raw.reshape(batch, length, H), dt_bias, np.zeros(H, np.int64))
+    assert np.all(dA == 65536)
+    y, st = O.ssm_scan_pot(x, bm, cm, dt, dA, d_q16, p[2], p[3])
+    for a_pos in ([1, 65536, 1 << 30], [0, 0, 0]):
+        t_y = torch.empty((batch, length, H, P), dtype=torch.int32, device="cuda")
+        t_st = torch.empty((batch, H, P, N), dtype=torch.int32, device="cuda")
+        t_dt = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+        t_da = torch.empty((batch, length, H), dtype=torch.int32, device="cuda")
+        B.fm_ssm_scan_pot(dev(x), dev(bm), dev(cm), dev(dt_raw), H, dev(dt_bias),
+                          dev(np.array(a_pos), torch.int32), dev(d_q16, torch.int32), dev(p),
+                          batch, length, H, P, N, None, t_st, t_y, t_dt, t_da)
+        assert_exact(host(t_da), dA, f"dA, a_q16 {a_pos}")
+        assert_exact(host(t_y), y, f"y, a_q16 {a_pos}")
+        assert_exact(host(t_st), st, f"state, a_q16 {a_pos}")

@@ -3,7 +3,7 @@
 The library adds, for each of a layer's six activation quantization points,
 the number of elements, how many codes were clamped, the sum of squared
 dequantization errors and the sum of squared values into a device record
-(fm_quant_stats, enabled by fm_layer_collect_quant_stats).  Counts must equal
+(fm_quant_stats, requested per call through fm_layer_opts.quant_stats).  Counts must equal
 the oracle's exactly; the float64 sums are added atomically in a varying
 order, so they are compared within 1e-9 relative.
 """
@@ -43,12 +43,8 @@ def test_layer_stats_dynamic(wl, batch, seqlen):
     _, r, _, _ = O.layer_prefill(O.prepare_layer(params), w.shape, u, collect=True)
     layer = Mamba2Layer(w.shape, params)
     buf = B.quant_stats_buffer()
-    B.collect_quant_stats(buf)
-    try:
-        layer.prefill(dev(u))
-        torch.cuda.synchronize()
-    finally:
-        B.collect_quant_stats(None)
+    layer.prefill(dev(u), opts=B.layer_opts(quant_stats=buf))
+    torch.cuda.synchronize()
     got = B.quant_stats_from_device(buf)
     check_point_stats(got, r["qstats"], wl)
     assert sum(got.clipped) == 0  # dynamic scales never clip
@@ -93,11 +89,7 @@ def test_collection_off_by_default_and_outputs_unchanged():
     layer = Mamba2Layer(w.shape, params)
     ref = layer.prefill(u).clone()
     buf = B.quant_stats_buffer()
-    B.collect_quant_stats(buf)
-    try:
-        got = layer.prefill(u).clone()
-    finally:
-        B.collect_quant_stats(None)
+    got = layer.prefill(u, opts=B.layer_opts(quant_stats=buf)).clone()
     again = layer.prefill(u).clone()
     torch.cuda.synchronize()
     assert torch.equal(ref, got) and torch.equal(ref, again)
