@@ -268,6 +268,9 @@ fm_status scale_columns_run(const float* x, int64_t rows, int64_t k, const float
 // layer pipeline (fm_layer.hip)
 size_t layer_ws_bytes(const fm_layer_desc* d, int64_t batch, int64_t len);
 void layer_taps(const fm_layer_desc* d, int64_t batch, int64_t len, fm_layer_taps* t);
+// compute units of the current device (queried once per device)
+int device_cus();
+
 // the per-call options of a layer call (fm_layer_opts, validated)
 struct LayerOpts {
     bool keep = false;               // also write the intermediates the taps name

@@ -25,12 +25,17 @@
 // scan_kernel: a workgroup of 4 waves owns (b, head, 8 consecutive p).  Lane l
 // of wave w owns the states (p, n) for p in {p0, p0+1} = {8g + 2w, 8g + 2w + 1}
 // and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time runs in chunks of 16
-// steps, one barrier per chunk:
+// steps, two barriers per chunk:
 //  - the per-step wave-uniform scalars (da, u of p0, u of p0+1) of a chunk sit
 //    one step per lane in each 16-lane row and are broadcast with DPP
 //    row_newbcast, so they cost no memory traffic inside the step loop;
 //  - B/C codes (int8) of the next chunk are loaded while a chunk runs and
-//    written to the other LDS buffer, widened to float64, after it;
+//    written to LDS widened to float64.  With more workgroups than CUs one
+//    buffer is used: once every wave has finished reading the chunk's B/C
+//    (first barrier) the next chunk's are written over them (visible after
+//    the second barrier); the workgroup then needs about 66 KB of LDS, so two
+//    share a CU and each hides the other's barrier and dependency stalls.
+//    With a workgroup per CU at most, two buffers save the extra barrier;
 //  - the two partial sums of C*h of each lane (one per p) are paired across
 //    the wave halves by a lane swap and stored, one per lane per step; after
 //    the chunk they are added per (step, p) and y is written.
@@ -112,9 +117,9 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 typedef double dpair __attribute__((ext_vector_type(2)));
 
-template <int NN>
+template <int NN, int NBUF>
 struct alignas(16) ScanSmem {
-    double bc[2][kTC][2 * 64 * NN];           // [chunk parity][step][B row, C row]
+    double bc[NBUF][kTC][2 * 64 * NN];        // [buffer][step][B row, C row]
     double ypart[kScanWaves][kTC][kYRow];     // [wave][step][lane]
 };
 
@@ -124,10 +129,10 @@ __device__ __forceinline__ void unroll_steps(std::integer_sequence<int, Ts...>, 
 }
 
 // ---------------------------------------------------------------- scan
-template <int NN>
+template <int NN, int NBUF>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     constexpr int N = 64 * NN;
-    __shared__ ScanSmem<NN> sm;
+    __shared__ ScanSmem<NN, NBUF> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
     __syncthreads();
 
     for (int64_t c = 0; c < nchunks; ++c) {
-        const int par = (int)(c & 1);
+        const int par = NBUF == 2 ? (int)(c & 1) : 0;
         const int tc = (int)(L - c * kTC < kTC ? L - c * kTC : kTC);
         setup();  // this chunk's scalars
         const bool more = c + 1 < nchunks;
@@ -349,10 +354,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
                 unroll_steps(steps, [&](auto Tc) { step(Tc, std::false_type{}, std::true_type{}); });
         }
         write_y(c, reduce());
-        // the next chunk's B/C go to the other buffer (last read a chunk ago,
-        // before the previous barrier) and must be visible before anyone reads them
-        if (more) stage_store(par ^ 1);
-        __syncthreads();
+        if constexpr (NBUF == 2) {
+            // the next chunk's B/C go to the other buffer (last read a chunk ago,
+            // before the previous barrier) and must be visible before anyone reads them
+            if (more) stage_store(par ^ 1);
+            __syncthreads();
+        } else if (more) {
+            // every wave is done with this chunk's B/C before they are overwritten,
+            // and the next chunk's are visible before anyone reads them
+            __syncthreads();
+            stage_store(0);
+            __syncthreads();
+        }
     }
     if (A.state_out) {
 #pragma unroll
@@ -646,8 +659,15 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
     if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
         return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
     const unsigned grid = (unsigned)(a.headdim / kScanP * a.nheads * a.batch);
-    if (a.dstate == 64) scan_kernel<1><<<grid, kScanThreads, 0, s>>>(a);
-    else scan_kernel<2><<<grid, kScanThreads, 0, s>>>(a);
+    // one buffer (two workgroups per CU) once the grid outnumbers the CUs
+    const bool one_buf = grid > (unsigned)device_cus();
+    if (a.dstate == 64) {
+        if (one_buf) scan_kernel<1, 1><<<grid, kScanThreads, 0, s>>>(a);
+        else scan_kernel<1, 2><<<grid, kScanThreads, 0, s>>>(a);
+    } else {
+        if (one_buf) scan_kernel<2, 1><<<grid, kScanThreads, 0, s>>>(a);
+        else scan_kernel<2, 2><<<grid, kScanThreads, 0, s>>>(a);
+    }
     if ((st = check_launch("scan_kernel")) != FM_OK) return st;
     if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess)
         return fail(FM_ERR_HIP, "hipEventRecord(stop) failed");
