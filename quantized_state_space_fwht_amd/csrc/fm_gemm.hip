@@ -33,6 +33,102 @@ __device__ __forceinline__ void for_slots(std::integer_sequence<int, Ss...>, F&&
     (f(std::integral_constant<int, Ss>{}), ...);
 }
 
+// The epilogue of a wave's TM x TN tiles of 16 x 16 (rows from row0, columns from
+// col0; lane l holds rows 4*(l/16)+r, column l % 16 of each tile): int32 and / or
+// dequantized float32 with the optional residual, and the column-range maximum
+// (into a slot region under `slot_key`, or one word).
+template <int TM, int TN>
+__device__ __forceinline__ void tile_epilogue(const GemmParams& P, const v4i (&acc)[TM][TN],
+                                              int64_t row0, int64_t col0, int lane,
+                                              int64_t slot_key) {
+    const GemmEpilogue& ep = P.ep;
+    float sab = 0.0f;
+    if (ep.out) sab = (*ep.s_a) * (*ep.s_b);
+    float amax = 0.0f;
+    // Whole tiles with float output only (almost every tile of a large product):
+    // straight-line code, so the compiler counts the loads and stores in flight
+    // exactly and never waits for a store's acknowledgement (on this chip stores
+    // share the load counter); the residual, if any, never aliases the output.
+    const bool whole = row0 + TM * 16 <= P.m && col0 + TN * 16 <= P.n && ep.out && !ep.acc;
+    auto straight = [&](auto with_resid) {
+        constexpr bool kRes = decltype(with_resid)::value;
+        float* __restrict__ out = ep.out;
+        const float* __restrict__ resid = ep.resid;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            float res[TN][4];
+            if constexpr (kRes) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        res[j][r] = resid[(row0 + i * 16 + (lane >> 4) * 4 + r) * ep.ld_resid +
+                                          col0 + j * 16 + (lane & 15)];
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = col0 + j * 16 + (lane & 15);
+                const bool in_max = col >= ep.amax_c0 && col < ep.amax_c1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = row0 + i * 16 + (lane >> 4) * 4 + r;
+                    float o = (float)acc[i][j][r] * sab;
+                    if constexpr (kRes) o = res[j][r] + o;
+                    out[row * ep.ld_out + col] = o;
+                    amax = in_max ? fmaxf(amax, fabsf(o)) : amax;
+                }
+            }
+        }
+    };
+    if (whole && ep.resid) straight(std::true_type{});
+    else if (whole) straight(std::false_type{});
+    else
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        // the residual of this tile row, loaded as one batch before any store (the
+        // output never aliases it; elements past the edge read a valid one, unused)
+        float res[TN][4];
+        if (ep.out && ep.resid) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                int64_t col = col0 + j * 16 + (lane & 15);
+                col = col < P.n ? col : P.n - 1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int64_t row = row0 + i * 16 + (lane >> 4) * 4 + r;
+                    row = row < P.m ? row : P.m - 1;
+                    res[j][r] = ep.resid[row * ep.ld_resid + col];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = col0 + j * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = row0 + i * 16 + (lane >> 4) * 4 + r;
+                if (row < P.m && col < P.n) {
+                    int32_t v = acc[i][j][r];
+                    if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
+                    if (ep.out) {
+                        float o = (float)v * sab;
+                        if (ep.resid) o = res[j][r] + o;
+                        ep.out[row * ep.ld_out + col] = o;
+                        if (col >= ep.amax_c0 && col < ep.amax_c1) amax = fmaxf(amax, fabsf(o));
+                    }
+                }
+            }
+        }
+    }
+    if (ep.amax_slots) {
+        amax = wave_max_f32(amax);
+        if (lane == 0) slot_max(ep.amax_slots, slot_key, (int32_t)__float_as_uint(amax));
+    } else if (ep.amax) {
+        amax = wave_max_f32(amax);
+        if (lane == 0 && amax > 0.0f) atomic_max_nonneg_f32(ep.amax, amax);
+    }
+}
+
 // BM x BN x BK tiles (BK 64 or 128), 4 waves as 2 x 2, each (BM/2) x (BN/2) =
 // TM x TN tiles of 16 x 16.  The global loads of k-steps kt+1 .. kt+kD are in
 // flight (in a register ring) while step kt is multiplied from LDS; a 128-wide
@@ -158,41 +254,160 @@ void gemm_i8_kernel(GemmParams P) {
                   [&](auto S) { step(kt + decltype(S)::value, S); });
     }
 
-    // epilogue
-    const GemmEpilogue& ep = P.ep;
-    float sab = 0.0f;
-    if (ep.out) sab = (*ep.s_a) * (*ep.s_b);
-    float amax = 0.0f;
+    tile_epilogue<TM, TN>(P, acc, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane,
+                          ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave);
+}
+
+// ---------------------------------------------------------------- large products
+// M and N large (prefill over many tokens): 256 x 128 workgroup tiles, 4 waves
+// as 2 x 2 of 128 x 64 (8 x 4 tiles of 16 x 16), 64-wide k-steps.  A and B move
+// from global memory straight into LDS (16-byte direct loads: no registers, no
+// LDS store instructions) through three stages, so the loads of steps kt+1 and
+// kt+2 are in flight while step kt is multiplied; one barrier per step.  Each
+// wave instruction fills 1 KB = 16 rows of 64 bytes, lane i taking row i / 4
+// and the granule that the XOR swizzle puts at slot i % 4.  The swizzle
+// (granule g of row r at slot g ^ h(r), h from bits 1-3 of r) keeps a fragment
+// read free of bank conflicts whether the 16-byte reads of 8 or of 16 lanes are
+// served together: rows r and r + 2 (8 lanes) and rows r and r + 4, r + 8,
+// r + 12 (16 lanes) fall on different 16-byte bank groups.
+// 72 KB of LDS and at most 128 accumulator registers per lane: two workgroups
+// per CU, so one's epilogue stores overlap the other's products.
+//
+// Tile order: workgroup id i runs on XCD i % 8; tile q = (i % 8) * n8 + i / 8
+// gives each XCD a contiguous range of q, and q runs through groups of 8 tile
+// rows column by column, so the workgroups an XCD holds at once share the A
+// rows and B columns they stream through its L2.
+constexpr int kLdsStages = 3;
+
+__device__ __forceinline__ int lds_swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land at
+// dst + 16 i (dst wave-uniform)
+__device__ __forceinline__ void lds_dma16(const int8_t* src, int8_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_lds_kernel(GemmParams P) {
+    constexpr int BK = 64;
+    constexpr int TM = BM / 32, TN = BN / 32;
+    static_assert(TM == 8 && TN == 4, "the fragment read block below is written for 8 x 4 tiles");
+    constexpr int A_LD = BM * BK / 1024 / 4, B_LD = BN * BK / 1024 / 4;  // per wave and step
+    constexpr int kA = BM * BK, kB = BN * BK;                             // bytes per stage
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kLdsStages * (kA + kB)];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t ntm = (P.m + BM - 1) / BM, ntn = (P.n + BN - 1) / BN;
+    const int64_t ntiles = ntm * ntn, n8 = (ntiles + 7) / 8;
+    const int64_t q = (int64_t)(blockIdx.x % 8) * n8 + blockIdx.x / 8;
+    if (q >= ntiles) return;  // padding of the last XCD's range
+    constexpr int64_t GM = 8;
+    const int64_t grp = q / (GM * ntn), first = grp * GM;
+    const int64_t rows_g = ntm - first < GM ? ntm - first : GM;
+    const int64_t inner = q - grp * GM * ntn;
+    const int64_t m0 = (first + inner % rows_g) * BM, n0 = (inner / rows_g) * BN;
+    if (P.ep.pub_small && q == 0 && tid == 0)
+        layer_publish(P.ep.pub_small, P.ep.pub_qp, P.ep.pub_cache_p);
+    const int64_t K = P.k, KT = K / BK;
+
+    // 64-byte rows, granule slot s of row r holds global granule s ^ lds_swz(r)
+    const int ld_r = lane >> 2, ld_s = lane & 3;
+    const int8_t* ga[A_LD];
+    const int8_t* gb[B_LD];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < A_LD; ++i) {
+        const int r = (i * 4 + wave) * 16 + ld_r;  // row of the tile this lane fills
+        int64_t gr = m0 + r;
+        gr = gr < P.m ? gr : P.m - 1;  // rows past the edge: computed, never stored
+        ga[i] = P.a + gr * K + ((ld_s ^ lds_swz(r)) << 4);
+    }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+    for (int i = 0; i < B_LD; ++i) {
+        const int r = (i * 4 + wave) * 16 + ld_r;
+        int64_t gr = n0 + r;
+        gr = gr < P.n ? gr : P.n - 1;
+        gb[i] = P.b + gr * K + ((ld_s ^ lds_swz(r)) << 4);
+    }
+    // step s into stage st: A_LD + B_LD wave instructions of 1 KB
+    auto issue = [&](int64_t s, int st) {
+        const int64_t k0 = s * BK;
+        int8_t* la = lds + st * (kA + kB);
+        int8_t* lb = la + kA;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
-                if (row < P.m && col < P.n) {
-                    int32_t v = acc[i][j][r];
-                    if (ep.acc) ep.acc[row * ep.ld_acc + col] = v;
-                    if (ep.out) {
-                        float o = (float)v * sab;
-                        if (ep.resid) o = ep.resid[row * ep.ld_resid + col] + o;
-                        ep.out[row * ep.ld_out + col] = o;
-                        if (col >= ep.amax_c0 && col < ep.amax_c1) amax = fmaxf(amax, fabsf(o));
-                    }
-                }
+        for (int i = 0; i < A_LD; ++i) lds_dma16(ga[i] + k0, la + (i * 4 + wave) * 1024);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) lds_dma16(gb[i] + k0, lb + (i * 4 + wave) * 1024);
+    };
+    v4i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    // this lane's fragment row: tile i of A sits 1 KB after tile i - 1 (the swizzle
+    // term depends on r % 16 only), likewise for B
+    const int frag_row = lane & 15, frag_g = lane >> 4;
+    const uint32_t lane_off = (uint32_t)(frag_row * BK + ((frag_g ^ lds_swz(frag_row)) << 4));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds;
+    const uint32_t a_off = lds0 + (uint32_t)(wm * (BM / 2) * BK) + lane_off;
+    const uint32_t b_off = lds0 + (uint32_t)kA + (uint32_t)(wn * (BN / 2) * BK) + lane_off;
+    // The fragments of a step are read in one block that waits for them itself:
+    // the compiler cannot tell these reads from the stages the direct loads are
+    // still filling and would otherwise wait for every load in flight.
+    auto compute = [&](int st) {
+        const uint32_t sa = a_off + (uint32_t)(st * (kA + kB)), sb = b_off + (uint32_t)(st * (kA + kB));
+        v4i a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3;
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:1024\n\t"
+            "ds_read_b128 %2, %12 offset:2048\n\t"
+            "ds_read_b128 %3, %12 offset:3072\n\t"
+            "ds_read_b128 %4, %12 offset:4096\n\t"
+            "ds_read_b128 %5, %12 offset:5120\n\t"
+            "ds_read_b128 %6, %12 offset:6144\n\t"
+            "ds_read_b128 %7, %12 offset:7168\n\t"
+            "ds_read_b128 %8, %13\n\t"
+            "ds_read_b128 %9, %13 offset:1024\n\t"
+            "ds_read_b128 %10, %13 offset:2048\n\t"
+            "ds_read_b128 %11, %13 offset:3072\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6),
+              "=&v"(a7), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+            : "v"(sa), "v"(sb)
+            : "memory");
+        const v4i af[TM] = {a0, a1, a2, a3, a4, a5, a6, a7};
+        const v4i bf[TN] = {b0, b1, b2, b3};
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+    // vmcnt immediates: at most one step's loads (this wave's part) pending, or none
+    constexpr int kPer = A_LD + B_LD;
+    static_assert(kPer <= 15, "vmcnt immediate");
+    constexpr int kWaitOne = kPer | (0x7 << 4) | (0xF << 8);
+    constexpr int kWaitAll = 0 | (0x7 << 4) | (0xF << 8);
+    issue(0, 0);
+    if (KT > 1) issue(1, 1);
+    for (int64_t kt = 0; kt < KT; kt += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int64_t s = kt + u;
+            if (s < KT) {
+                // step s landed (this wave's part), then every wave's; stage (s+2)%3 was
+                // last read at step s-1.  A plain barrier: the fence of __syncthreads
+                // would also wait for the later steps' loads, which write LDS.
+                if (s + 1 < KT) __builtin_amdgcn_s_waitcnt(kWaitOne);
+                else __builtin_amdgcn_s_waitcnt(kWaitAll);
+                asm volatile("s_barrier" ::: "memory");
+                if (s + 2 < KT) issue(s + 2, (u + 2) % 3);
+                compute(u);
             }
         }
     }
-    if (ep.amax_slots) {
-        amax = wave_max_f32(amax);
-        if (lane == 0)
-            slot_max(ep.amax_slots, ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 4 + wave,
-                     (int32_t)__float_as_uint(amax));
-    } else if (ep.amax) {
-        amax = wave_max_f32(amax);
-        if (lane == 0 && amax > 0.0f) atomic_max_nonneg_f32(ep.amax, amax);
-    }
+    tile_epilogue<TM, TN>(P, acc, m0 + wm * (BM / 2), n0 + wn * (BN / 2), lane, q * 4 + wave);
 }
 
 // ---------------------------------------------------------------- few rows (decode)
@@ -566,8 +781,17 @@ fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64
         return check_launch("gemm_i8_few_rows_kernel");
     }
     if (af) return fail(FM_ERR_SHAPE, "gemm: float A needs m <= 64, k %% 256 == 0");
-    // the largest tiles that still give the chip's 256 CUs a workgroup each
     auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+    // large products: 256 x 128 tiles with direct-to-LDS loads, two per CU, as long
+    // as every CU gets at least four of them
+    const int64_t big = tiles(256, 128);
+    if (big >= 4 * (int64_t)device_cus()) {
+        const int64_t nwg = (big + 7) / 8 * 8;
+        if (nwg >= ((int64_t)1 << 31)) return fail(FM_ERR_SHAPE, "gemm: %lld tiles", (long long)big);
+        gemm_i8_lds_kernel<256, 128><<<(unsigned)nwg, kGemmThreads, 0, s>>>(P);
+        return check_launch("gemm_i8_lds_kernel");
+    }
+    // the largest tiles that still give the chip's 256 CUs a workgroup each
     // 128-wide k-steps when k allows (half the barriers and waits per product)
     const bool k128 = k % 128 == 0;
     if (tiles(128, 128) >= 256) {

@@ -80,6 +80,10 @@ def test_hadamard_quant(B, rows, k, mode):
                                    # below, at and past the depth of the load ring
                                    (200, 300, 128), (130, 1100, 192), (2048, 1536, 256),
                                    (1000, 4100, 448), (70, 90, 320),
+                                   # large products (256 x 128 tiles, direct-to-LDS stages):
+                                   # 1 and 2 k-steps, a ragged edge with 5, and 40
+                                   (4096, 8192, 64), (4096, 8192, 128), (4100, 8200, 320),
+                                   (4096, 8192, 2560),
                                    # few-row path (m <= 64, k % 256 == 0): decode shapes, ragged n
                                    (16, 10576, 2560), (16, 2560, 5120), (1, 33, 256),
                                    (3, 1160, 256), (40, 300, 768), (64, 777, 1536)])
