@@ -397,6 +397,25 @@ fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights*
                                  const fm_layer_opts* opts, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* fm_mamba2_layer_decode_noalloc — fm_mamba2_layer_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): no workspace argument and no
+ * allocation of any kind.  The temporary memory is the library's own scratch,
+ * a static device array of FM_DECODE_SCRATCH_BYTES per GPU (held by each GPU
+ * the library runs on until the process ends); a step whose workspace
+ * (fm_mamba2_layer_workspace_size(d, batch, 1)) exceeds it returns
+ * FM_ERR_WORKSPACE before anything is launched (the 2.7B-shaped layer fits up
+ * to batch 64).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialized by the caller.  Results, caches and errors otherwise as
+ * fm_mamba2_layer_decode. */
+#define FM_DECODE_SCRATCH_BYTES (16u << 20)
+fm_status fm_mamba2_layer_decode_noalloc(const fm_layer_desc* d, const fm_layer_weights* w,
+                                         const fm_static_params* sp, const float* u_t,
+                                         int64_t batch, const fm_cache* cache, float* out_t,
+                                         fm_qparams* qp, const fm_layer_opts* opts,
+                                         hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Narrow state caches.  The decode step reads and writes the whole SSM state
  * once per token, so the state's width sets that step's memory traffic; in

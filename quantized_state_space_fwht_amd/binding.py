@@ -140,6 +140,11 @@ _SIGS = {
                                               ctypes.POINTER(StaticParams), _vp, _c_i64,
                                               ctypes.POINTER(Cache), _vp, _vp,
                                               ctypes.POINTER(LayerOpts), _vp, _c_sz, _vp]),
+    "fm_mamba2_layer_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(LayerDesc),
+                                                      ctypes.POINTER(LayerWeights),
+                                                      ctypes.POINTER(StaticParams), _vp, _c_i64,
+                                                      ctypes.POINTER(Cache), _vp, _vp,
+                                                      ctypes.POINTER(LayerOpts), _vp]),
     "fm_mamba2_layer_taps": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _c_i64, _c_i64,
                                             ctypes.POINTER(LayerTaps)]),
     "fm_nau_eval_knots": (ctypes.c_int, [_c_i32, _vp, _vp, _vp, _c_i64, _vp]),

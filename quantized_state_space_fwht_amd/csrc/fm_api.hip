@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "fm_internal.hpp"
 
@@ -474,10 +475,11 @@ size_t fm_mamba2_layer_workspace_size(const fm_layer_desc* d, int64_t batch, int
     return layer_ws_bytes(d, batch, len);
 }
 
-static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights* w,
+// every argument of a layer call but the workspace
+static fm_status check_layer_args(const fm_layer_desc* d, const fm_layer_weights* w,
                                   const fm_static_params* sp, const float* u, int64_t batch,
-                                  int64_t len, const float* out, fm_qparams* qp, void* ws,
-                                  size_t ws_bytes, const char* who, bool ssd = false) {
+                                  int64_t len, const float* out, fm_qparams* qp, const char* who,
+                                  bool ssd) {
     fm_status st;
     if ((st = check_layer_desc(d, who)) != FM_OK) return st;
     if ((st = check_weights(w, who)) != FM_OK) return st;
@@ -493,6 +495,15 @@ static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights
         return fail(FM_ERR_SHAPE, "%s: batch=%lld len=%lld out of range", who, (long long)batch,
                     (long long)len);
     if (ssd && d->headdim != 64) return fail(FM_ERR_SHAPE, "%s: headdim must be 64", who);
+    return FM_OK;
+}
+
+static fm_status check_layer_call(const fm_layer_desc* d, const fm_layer_weights* w,
+                                  const fm_static_params* sp, const float* u, int64_t batch,
+                                  int64_t len, const float* out, fm_qparams* qp, void* ws,
+                                  size_t ws_bytes, const char* who, bool ssd = false) {
+    fm_status st = check_layer_args(d, w, sp, u, batch, len, out, qp, who, ssd);
+    if (st != FM_OK) return st;
     return check_ws(ws, ws_bytes,
                     ssd ? fm_mamba2_layer_workspace_size_ssd(d, batch, len)
                         : fm_mamba2_layer_workspace_size(d, batch, len),
@@ -576,6 +587,58 @@ fm_status fm_mamba2_layer_decode(const fm_layer_desc* d, const fm_layer_weights*
     LayerOpts lo;
     if ((st = check_opts(opts, true, &lo, who)) != FM_OK) return st;
     return layer_run(d, w, sp, u_t, batch, 1, out_t, cache, qp, workspace, true, stream, lo);
+}
+
+// ---------------------------------------------------------------- no-allocation decode
+// The scratch of fm_mamba2_layer_decode_noalloc: one static array per GPU.  In host
+// code its name is only a stand-in: the device address of each GPU's copy is taken
+// once per device with hipGetSymbolAddress and used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[FM_DECODE_SCRATCH_BYTES];
+
+static fm_status scratch_ptr(void** out, const char* who) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FM_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(FM_ERR_HIP, "%s: device %d beyond the %d the scratch table holds", who, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FM_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                        hipGetErrorString(e));
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return FM_OK;
+}
+
+fm_status fm_mamba2_layer_decode_noalloc(const fm_layer_desc* d, const fm_layer_weights* w,
+                                         const fm_static_params* sp, const float* u_t,
+                                         int64_t batch, const fm_cache* cache, float* out_t,
+                                         fm_qparams* qp, const fm_layer_opts* opts,
+                                         hipStream_t stream) {
+    const char* who = "fm_mamba2_layer_decode_noalloc";
+    g_err[0] = 0;
+    fm_status st = check_layer_args(d, w, sp, u_t, batch, 1, out_t, qp, who, false);
+    if (st != FM_OK) return st;
+    const size_t need = fm_mamba2_layer_workspace_size(d, batch, 1);
+    if (need > FM_DECODE_SCRATCH_BYTES)
+        return fail(FM_ERR_WORKSPACE, "%s: batch %lld needs %zu bytes of scratch, more than the "
+                    "%u bytes this entry point holds", who, (long long)batch, need,
+                    FM_DECODE_SCRATCH_BYTES);
+    if (!cache || !cache->conv_state || !cache->ssm_state || !cache->p)
+        return fail(FM_ERR_NULL, "%s: decode needs a complete cache", who);
+    LayerOpts lo;
+    if ((st = check_opts(opts, true, &lo, who)) != FM_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_ptr(&ws, who)) != FM_OK) return st;
+    return layer_run(d, w, sp, u_t, batch, 1, out_t, cache, qp, ws, true, stream, lo);
 }
 
 static fm_status check_state_fmt(int32_t bits, int32_t shift, const char* who) {

@@ -287,3 +287,33 @@ def test_state_shift_for_on_host(lib):
     assert f(100, 8, 1, ctypes.byref(out)) == FM_ERR_SHAPE
     assert f(100, 16, -1, ctypes.byref(out)) == FM_ERR_SHAPE
     assert f(100, 16, 1, None) == FM_ERR_NULL
+
+
+def test_decode_noalloc_refuses_oversize_steps(lib):
+    """The no-allocation decode takes its temporary memory from a fixed scratch:
+    a step whose workspace would exceed it is refused before anything is launched,
+    and so are the arguments fm_mamba2_layer_decode refuses."""
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    fake = 1 << 20
+    f = lib.fm_mamba2_layer_decode_noalloc
+    f.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i64, vp, vp, vp, vp, vp]
+    weights = ctypes.cast((vp * 11)(*([fake] * 11)), vp)
+
+    class Cache(ctypes.Structure):
+        _fields_ = [("conv_state", vp), ("ssm_state", vp), ("p", vp)]
+    cache = ctypes.cast(ctypes.byref(Cache(fake, fake, fake)), vp)
+    lib.fm_mamba2_layer_workspace_size.restype = ctypes.c_size_t
+    lib.fm_mamba2_layer_workspace_size.argtypes = [ctypes.POINTER(Desc), i64, i64]
+    big = Desc(16384, 8192, 128, 64, 128, 4, 0, 1)
+    assert lib.fm_mamba2_layer_workspace_size(ctypes.byref(big), 64, 1) > 16 << 20
+    assert f(ctypes.byref(big), weights, None, fake, 64, cache, 2 * fake, fake, None, None) \
+        == FM_ERR_WORKSPACE
+    assert "scratch" in _last_error(lib)
+    d = Desc(2560, 5120, 80, 64, 128, 4, 0, 1)
+    assert lib.fm_mamba2_layer_workspace_size(ctypes.byref(d), 64, 1) <= 16 << 20
+    assert f(ctypes.byref(d), weights, None, fake, 16, None, 2 * fake, fake, None, None) \
+        == FM_ERR_NULL                                            # no cache
+    assert f(ctypes.byref(d), weights, None, fake, 0, cache, 2 * fake, fake, None, None) \
+        == FM_ERR_SHAPE                                           # empty batch
+    assert f(ctypes.byref(d), weights, None, fake, 16, cache, 2 * fake, fake,
+             ctypes.cast(ctypes.byref(Opts(0, 0, fake, None)), vp), None) == FM_ERR_MODE
