@@ -169,12 +169,12 @@ def layer_decode(prep, shape, u_t, cache, mode="dynamic", qp=None, state_fmt=Non
     return out.reshape(Bsz, dm), r, new_cache, st
 
 
-def stack_prefill(preps, shape, u, mode="dynamic", qps=None, qstats=None):
+def stack_prefill(preps, shape, u, mode="dynamic", qps=None, qstats=None, scan=None):
     """Pre-norm residual stack over u [Bsz, L, d_model].
 
     Returns (h float32 [Bsz, L, d_model], caches, stats per layer).  ``qstats``
     (a list, one oracle.quant_stats dict per layer) receives each layer's
-    quantization statistics added in.
+    quantization statistics added in; ``scan`` as in layer_prefill.
     """
     h = np.asarray(u, dtype=np.float32)
     Bsz, L, dm = h.shape
@@ -183,7 +183,7 @@ def stack_prefill(preps, shape, u, mode="dynamic", qps=None, qstats=None):
     for li, prep in enumerate(preps):
         xin = rmsnorm_fixed_order(h.reshape(Bsz * L, dm), ones).reshape(Bsz, L, dm)
         out, r, cache, st = layer_prefill(prep, shape, xin, mode, None if qps is None else qps[li],
-                                          collect=qstats is not None)
+                                          collect=qstats is not None, scan=scan)
         if qstats is not None:
             for pt in QS.POINTS:
                 QS.accumulate(qstats[li], pt, r["qstats"][pt])
@@ -225,11 +225,12 @@ def qparams_from_stats(st: Stats) -> QParams:
     return QParams(scoe=(s0, s1), sshift=(h0, h1), p=p)
 
 
-def calibrate_stack(preps, shape, calib_inputs):
-    """Dynamic-mode passes over the calibration inputs; returns per-layer QParams."""
+def calibrate_stack(preps, shape, calib_inputs, scan=None):
+    """Dynamic-mode passes over the calibration inputs; returns per-layer QParams
+    and the maxima they come from.  ``scan`` as in layer_prefill."""
     acc = [Stats() for _ in preps]
     for u in calib_inputs:
-        _, _, stats = stack_prefill(preps, shape, u, "dynamic")
+        _, _, stats = stack_prefill(preps, shape, u, "dynamic", scan=scan)
         for a, st in zip(acc, stats):
             a.update(st)
     return [qparams_from_stats(a) for a in acc], acc

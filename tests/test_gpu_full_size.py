@@ -10,21 +10,23 @@ and the rest is checked by properties that hold at any size.
   intermediates kept), the whole layer in the oracle: output, state, conv
   window, scales and exponents bit for bit.  (The parity file compares every
   intermediate of the same layer as well.)
-* m2p7b_stack (batch 4, L 4096, dynamic): layer 0 whole in the oracle, every
-  intermediate; the 64-layer stack under batch-permutation equivariance
-  (per-tensor maxima do not depend on the order of the rows, everything else
-  is row- or sequence-local, so reversing the batch reverses the output bit
-  for bit).
-* m130m_stack_static (batch 8, L 2048): the 24-layer stack calibrated on its
-  64 sequences, then two properties on the evaluation batch (a sequence alone
+* m2p7b_stack (batch 4, L 4096, dynamic): the first three layers chained, every
+  layer's output, caches and record bit for bit and every intermediate of
+  layer 0; the 64-layer stack under batch-permutation equivariance (per-tensor
+  maxima do not depend on the order of the rows, everything else is row- or
+  sequence-local, so reversing the batch reverses the output bit for bit).
+* m130m_stack_static (batch 8, L 2048): all 24 layers calibrated on the first
+  four calibration sequences by both sides, every layer's maxima and static
+  parameters equal; then one whole evaluation sequence through the 24 static
+  layers, the stack output and every layer's caches bit for bit.  The stack
+  calibrated on all 64 sequences: layer 0's maxima equal the oracle's over the
+  64 sequences, and two properties on the evaluation batch (a sequence alone
   gives its row of the batch; a prefill continued by decode steps gives the
-  longer prefill); the calibrated maxima of layer 0 cover the oracle's over
-  one calibration sequence; layers 0, 11 and 23 as static layers whose
-  parameters the oracle calibrates itself, run on the whole batch, one whole
-  sequence recomputed by the oracle.
+  longer prefill).
 * m2p7b_decode (batch 16): layers 0 and 63 as one-layer graph-replayed decode
-  stacks from an 8-token prefill that the oracle runs too, every step bit for
-  bit; the 64-layer stack's graph replays equal its eager steps.
+  stacks seeded by the workload's 1024-token prefill, which the oracle runs
+  too; every step bit for bit with the int32 state and with 24- and 16-bit
+  state codes; the 64-layer stack's graph replays equal its eager steps.
 """
 import numpy as np
 import pytest
@@ -123,25 +125,29 @@ def test_m130m_layer_full_size_as_benchmarked(B):
 
 
 # ----------------------------------------------------------------- m2p7b_stack
-def test_m2p7b_layer0_full_size_whole(B):
-    """Layer 0 of the 2.7B stack at 4 x 4096: the oracle recomputes all of it."""
+def test_m2p7b_stack_first_layers_chained_full_size(B):
+    """Layers 0, 1, 2 of the 2.7B stack at 4 x 4096, chained: the oracle runs the
+    three layers itself (layer 0 on the input, each next layer on its own output)."""
     from quantized_state_space_fwht_amd.runtime import Mamba2Layer
     w = configs.get("m2p7b_stack")
     s = w.shape
-    params = synth.workload_params(w, 0)
     u = synth.workload_activations(w)
     T = w.batch * w.seqlen
-    out_o, r, cache_o, st_o = O.layer_prefill(O.prepare_layer(params), s, prenorm(u),
-                                              scan=ssm_scan_pot_c)
-    want = u + out_o
-    layer = Mamba2Layer(s, params, prenorm_residual=True)
-    h = layer.prefill(dev(u))  # as the stack runs it: no intermediates kept
-    assert_same_float(host(h), want, "layer 0 output")
-    check_caches_and_record(layer, cache_o, r, st_o)
-    layer.reset_stats()
-    h = layer.prefill(dev(u), opts=B.layer_opts(keep=True))
-    check_intermediates(layer, r, T, s)
-    assert_same_float(host(h), want, "layer 0 output (intermediates kept)")
+    h_o = u
+    h = dev(u)
+    for l in range(3):
+        params = synth.workload_params(w, l)
+        out_o, r, cache_o, st_o = O.layer_prefill(O.prepare_layer(params), s, prenorm(h_o),
+                                                  scan=ssm_scan_pot_c)
+        h_o = h_o + out_o
+        layer = Mamba2Layer(s, params, prenorm_residual=True)
+        h = layer.prefill(h, opts=B.layer_opts(keep=(l == 0)))
+        if l == 0:
+            check_intermediates(layer, r, T, s)
+        assert_same_float(host(h), h_o, f"layer {l} output")
+        check_caches_and_record(layer, cache_o, r, st_o)
+        del layer, r
+        torch.cuda.empty_cache()
 
 
 def test_m2p7b_stack_full_size_batch_permutation(B):
@@ -157,22 +163,59 @@ def test_m2p7b_stack_full_size_batch_permutation(B):
 
 
 # ----------------------------------------------------------------- m130m_stack_static
-def test_m130m_static_stack_full_size(B):
-    from quantized_state_space_fwht_amd.runtime import Mamba2Layer, Mamba2Stack
+def test_m130m_static_stack_calibrated_and_chained_full_size(B):
+    """All 24 layers calibrated on the first four calibration sequences by both
+    sides (each sequence whole, 1 x 2048), then one evaluation sequence through
+    the 24 static layers."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Stack
+    w = configs.get("m130m_stack_static")
+    s = w.shape
+    params = [synth.workload_params(w, l) for l in range(w.nlayers)]
+    preps = [O.prepare_layer(p) for p in params]
+    calib = synth.calibration_sequences(w)[:4]
+    qps_o, acc_o = O.calibrate_stack(preps, s, calib, scan=ssm_scan_pot_c)
+    stack = Mamba2Stack(s, params)
+    stack.calibrate([dev(c) for c in calib])
+    for l, (layer, qo, ao) in enumerate(zip(stack.layers, qps_o, acc_o)):
+        qp = layer.qparams()
+        assert tuple(qp.stat_amax) == (np.float32(ao.amax_u), np.float32(ao.amax_g),
+                                       np.float32(ao.amax_xbc)), f"layer {l} maxima"
+        assert list(qp.stat_amax_q16) == list(ao.amax_q16), f"layer {l} Q.16 maxima"
+        sp = layer.static
+        assert (tuple(sp.scoe), tuple(sp.sshift), tuple(sp.p)) == (qo.scoe, qo.sshift, qo.p), \
+            f"layer {l} static parameters"
+    u = synth.eval_batch(w)
+    h = host(stack.prefill(dev(u)))
+    bsel = 5
+    h_o, caches_o, _ = O.stack_prefill(preps, s, u[bsel:bsel + 1], "static", qps_o,
+                                       scan=ssm_scan_pot_c)
+    assert_same_float(h[bsel:bsel + 1], h_o, "stack output, one evaluation sequence")
+    for l, (layer, co) in enumerate(zip(stack.layers, caches_o)):
+        assert_exact(host(layer.cache_t["ssm_state"])[bsel], co["ssm_state"][0], f"layer {l} state")
+        assert_exact(host(layer.cache_t["conv_state"])[bsel], co["conv_state"][0],
+                     f"layer {l} conv window")
+
+
+def test_m130m_static_stack_64_sequence_calibration_full_size(B):
+    """The stack calibrated on all 64 sequences: layer 0's maxima equal the oracle's
+    maximum over the 64 sequences (layer 0's input does not depend on the other
+    layers); then properties of the static stack on the evaluation batch."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Stack
     w = configs.get("m130m_stack_static")
     s = w.shape
     params = [synth.workload_params(w, l) for l in range(w.nlayers)]
     stack = Mamba2Stack(s, params)
     calib = synth.calibration_sequences(w)
     stack.calibrate([dev(c) for c in calib])
-    # the layer-0 maxima cover the oracle's over calibration sequence 0
-    _, _, _, st0 = O.layer_prefill(O.prepare_layer(params[0]), s, prenorm(calib[0]),
-                                   scan=ssm_scan_pot_c)
+    prep0 = O.prepare_layer(params[0])
+    acc = O.Stats()
+    for c in calib:
+        _, _, _, st = O.layer_prefill(prep0, s, prenorm(c), scan=ssm_scan_pot_c)
+        acc.update(st)
     qp0 = stack.layers[0].qparams()
-    assert np.float32(qp0.stat_amax[0]) >= np.float32(st0.amax_u)
-    assert np.float32(qp0.stat_amax[1]) >= np.float32(st0.amax_g)
-    assert np.float32(qp0.stat_amax[2]) >= np.float32(st0.amax_xbc)
-    assert all(int(a) >= int(b) for a, b in zip(qp0.stat_amax_q16, st0.amax_q16))
+    assert tuple(qp0.stat_amax) == (np.float32(acc.amax_u), np.float32(acc.amax_g),
+                                    np.float32(acc.amax_xbc))
+    assert list(qp0.stat_amax_q16) == list(acc.amax_q16)
     # properties of the static stack on the evaluation batch
     u = synth.eval_batch(w)
     h = host(stack.prefill(dev(u)))
@@ -184,49 +227,49 @@ def test_m130m_static_stack_full_size(B):
     stack.prefill(dev(u[:, :L0]))
     steps = [host(stack.decode(dev(u[:, t]))) for t in range(L0, w.seqlen)]
     assert_same_float(np.stack(steps, axis=1), h[:, L0:], "prefill continued by decode")
-    # static layers with parameters the oracle calibrates, on the whole batch
-    cal_short = [c[:, :256] for c in calib[:2]]
-    for l in (0, 11, w.nlayers - 1):
-        prep = O.prepare_layer(params[l])
-        qps, _ = O.calibrate_stack([prep], s, cal_short)
-        qp = qps[0]
-        layer = Mamba2Layer(s, params[l], mode="static", prenorm_residual=True)
-        layer.set_static(B.StaticParams(tuple(qp.scoe), tuple(qp.sshift), tuple(qp.p)))
-        hl = host(layer.prefill(dev(u)))
-        out_o, _, cache_o, _ = O.layer_prefill(prep, s, prenorm(u[bsel:bsel + 1]), "static", qp,
-                                               scan=ssm_scan_pot_c)
-        assert_same_float(hl[bsel:bsel + 1], u[bsel:bsel + 1] + out_o, f"layer {l} sequence")
-        assert_exact(host(layer.cache_t["ssm_state"])[bsel], cache_o["ssm_state"][0],
-                     f"layer {l} state")
-        assert_exact(host(layer.cache_t["conv_state"])[bsel], cache_o["conv_state"][0],
-                     f"layer {l} conv window")
 
 
 # ----------------------------------------------------------------- m2p7b_decode
 @pytest.mark.parametrize("layer_idx", [0, 63])
 def test_m2p7b_decode_layer_full_size(B, layer_idx):
     """One 2.7B layer at batch 16, graph-replayed as the decode benchmark runs its
-    layers, from an 8-token prefill that the oracle runs too."""
+    layers, seeded by the workload's 1024-token prefill (which the oracle runs
+    too), then four decode steps on the workload's step inputs: with the int32
+    state, and with 24- and 16-bit state codes on the shift the oracle picks."""
     from quantized_state_space_fwht_amd.runtime import DecodeGraph, Mamba2Stack
     w = configs.get("m2p7b_decode")
     s = w.shape
-    L0, K = 8, 4
-    wl = configs.with_len(w, w.batch, L0 + K)
+    K = 4
     params = synth.workload_params(w, layer_idx)
-    u = synth.workload_activations(wl)
+    u = synth.workload_activations(w)
+    xs = [synth.decode_step_input(w, t) for t in range(K)]
     prep = O.prepare_layer(params)
-    _, _, cache, _ = O.layer_prefill(prep, s, prenorm(u[:, :L0]))
+    _, _, cache0, _ = O.layer_prefill(prep, s, prenorm(u), scan=ssm_scan_pot_c)
     stack = Mamba2Stack(s, [params])
-    stack.prefill(dev(u[:, :L0]))
     layer = stack.layers[0]
-    assert_exact(host(layer.cache_t["ssm_state"]), cache["ssm_state"], "state after prefill")
-    g = DecodeGraph(stack, w.batch)
-    for t in range(L0, L0 + K):
-        out_o, _, cache, _ = O.layer_decode(prep, s, prenorm(u[:, t]), cache)
-        got = host(g.step(dev(u[:, t])))
-        assert_same_float(got, u[:, t] + out_o, f"layer {layer_idx} step {t}")
-        assert_exact(host(layer.cache_t["ssm_state"]), cache["ssm_state"], f"state step {t}")
-        assert_exact(host(layer.cache_t["conv_state"]), cache["conv_state"], f"conv step {t}")
+    for bits in (32, 24, 16):
+        stack.prefill(dev(u))
+        assert_exact(host(layer.cache_t["ssm_state"]), cache0["ssm_state"], "state after prefill")
+        cache = dict(cache0)
+        fmt = None
+        if bits != 32:
+            shift = O.state_shift_for(int(np.max(np.abs(cache0["ssm_state"]))), bits)
+            assert layer.narrow_state(bits) == shift, f"{bits}-bit shift"
+            fmt = (bits, shift)
+            cache["ssm_state"] = O.narrow_state(cache0["ssm_state"], bits, shift)
+        with DecodeGraph(stack, w.batch) as g:
+            for t, x in enumerate(xs):
+                out_o, _, cache, _ = O.layer_decode(prep, s, prenorm(x), cache, state_fmt=fmt)
+                got = host(g.step(dev(x)))
+                assert_same_float(got, x + out_o, f"layer {layer_idx} {bits}-bit step {t}")
+                if bits == 32:
+                    assert_exact(host(layer.cache_t["ssm_state"]), cache["ssm_state"],
+                                 f"state step {t}")
+                else:
+                    assert_exact(host(layer.cache_t["ssm_codes"]),
+                                 O.pack_state(cache["ssm_state"], bits), f"codes step {t}")
+                assert_exact(host(layer.cache_t["conv_state"]), cache["conv_state"],
+                             f"conv step {t}")
 
 
 def test_m2p7b_decode_stack_graph_equals_eager(B):

@@ -167,18 +167,24 @@ def test_layer_prefill_ssd(B, wname, batch, seqlen):
     prep = O.prepare_layer(params)
     out_o, r, cache_o, _ = O.layer_prefill(prep, s, u, scan=lambda *a: O.ssm_scan_real(*a)[:2])
     T = w.batch * w.seqlen
-    if True:
-        layer = Mamba2Layer(s, params)
-        out = host(layer.prefill(dev(u), scan="ssd", opts=B.layer_opts(keep=True)))
-        g = lambda name, dt, shp: layer.tap(name, dt, shp).cpu().numpy()
-        assert_exact(g("x_q", torch.int8, (T, s.d_inner)), r["x_q"].reshape(T, -1), "x_q")
-        assert_exact(g("b_q", torch.int8, (T, s.dstate)), r["B_q"].reshape(T, -1), "B_q")
-        assert_exact(g("c_q", torch.int8, (T, s.dstate)), r["C_q"].reshape(T, -1), "C_q")
-        assert_exact(g("da", torch.int32, (T, s.nheads)), r["dA"].reshape(T, -1), "dA")
-        y = g("y", torch.int32, (T, s.d_inner))
-        assert_within_one(y, r["y"].reshape(T, -1), "y")
-        assert_within_one(host(layer.cache_t["ssm_state"]), cache_o["ssm_state"], "state")
-        rel = np.linalg.norm(out - out_o) / np.linalg.norm(out_o)
-        assert rel <= 1e-3, rel
-        rows = np.all(y == r["y"].reshape(T, -1), axis=1)
-        assert np.mean(rows) > 0.5
+    layer = Mamba2Layer(s, params)
+    out = host(layer.prefill(dev(u), scan="ssd", opts=B.layer_opts(keep=True)))
+    g = lambda name, dt, shp: layer.tap(name, dt, shp).cpu().numpy()
+    assert_exact(g("x_q", torch.int8, (T, s.d_inner)), r["x_q"].reshape(T, -1), "x_q")
+    assert_exact(g("b_q", torch.int8, (T, s.dstate)), r["B_q"].reshape(T, -1), "B_q")
+    assert_exact(g("c_q", torch.int8, (T, s.dstate)), r["C_q"].reshape(T, -1), "C_q")
+    assert_exact(g("da", torch.int32, (T, s.nheads)), r["dA"].reshape(T, -1), "dA")
+    y = g("y", torch.int32, (T, s.d_inner))
+    assert_within_one(y, r["y"].reshape(T, -1), "y")
+    assert_within_one(host(layer.cache_t["ssm_state"]), cache_o["ssm_state"], "state")
+    # floats: max |gpu - oracle| / max |oracle| <= 1e-3, element by element
+    err = np.max(np.abs(out.astype(np.float64) - out_o)) / np.max(np.abs(out_o))
+    assert err <= 1e-3, err
+    rows = np.all(y == r["y"].reshape(T, -1), axis=1)
+    assert np.mean(rows) > 0.5
+    # a token whose y row agrees has the same out_proj input codes whenever the
+    # call's tensor scale agrees (every other step is row-local): its output row
+    # is bit for bit the oracle's
+    if layer.qparams().scale[1] == r["s_g"]:
+        o2, w2 = out.reshape(T, -1), out_o.reshape(T, -1)
+        assert np.array_equal(o2[rows], w2[rows]), "output rows where y agrees"
