@@ -145,38 +145,4 @@ fm_status gate_run(const GateArgs& g, hipStream_t s) {
     return FM_OK;
 }
 
-// RMSNorm of the residual stream with unit weight (pre-norm stacks): one
-// workgroup of 4 waves per row; the row is staged in LDS by all waves, wave 0
-// forms the fixed-order sum of squares, all waves write the normed row.
-__global__ __launch_bounds__(64 * kGateWaves) void rmsnorm_rows_kernel(
-    const float* __restrict__ h, int d, float* __restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) float hrow[];  // d floats
-    __shared__ float rs_r;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t row = blockIdx.x;
-    const float* hr = h + row * d;
-    for (int i = tid; i < d; i += 64 * kGateWaves) hrow[i] = hr[i];
-    __syncthreads();
-    if (tid < 64) {
-        float a = 0.0f;
-        for (int i = lane; i < d; i += 64) {
-            const float v = hrow[i];
-            const float v2 = v * v;
-            a = a + v2;
-        }
-        const float ss = wave_sum_fixed(a);
-        if (lane == 0) rs_r = 1.0f / sqrtf(ss / (float)d + 1e-5f);
-    }
-    __syncthreads();
-    const float r = rs_r;
-    for (int i = tid; i < d; i += 64 * kGateWaves) out[row * d + i] = (hrow[i] * r) * 1.0f;
-}
-
-fm_status rmsnorm_rows_run(const float* h, int64_t rows, int64_t d, float* out, hipStream_t s) {
-    if (rows == 0) return FM_OK;
-    rmsnorm_rows_kernel<<<(unsigned)rows, 64 * kGateWaves, (size_t)d * sizeof(float), s>>>(
-        h, (int)d, out);
-    return check_launch("rmsnorm_rows_kernel");
-}
-
 }  // namespace fm

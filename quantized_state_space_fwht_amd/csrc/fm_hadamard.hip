@@ -171,6 +171,125 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
     return check_launch("hq_quant_kernel");
 }
 
+// ---------------------------------------------------------------- pre-norm + rotation
+// A stack feeds each layer RMSNorm(h) (weight 1; the fixed summation order of
+// the gate's RMSNorm: 64 lane-strided partial sums in ascending order, then the
+// xor butterfly), rotated and quantized like any in_proj input.  Fused here so
+// the normalized rows never go to memory: one workgroup per row stages the row
+// in LDS, wave 0 forms r = 1 / sqrt(ss / d + 1e-5) (or reads the r that pass 1
+// stored), and the waves rotate the row's 256-blocks of (h_i * r) * 1.
+// Dynamic mode: pass 1 takes the rotated maximum into a slot region and stores
+// r per row; pass 2 reads h again and writes the codes (9 bytes per element in
+// all, against 17 for a separate normalization followed by the two passes).
+// Static mode: one pass.
+constexpr int kNormThreads = 256;
+
+template <bool kQuant>
+__global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
+    const float* __restrict__ h, int dm, float* __restrict__ rs, fm_scale_mode mode,
+    int32_t scoe, int32_t sshift, float* amax_ws, int32_t* amax_slots, char4* __restrict__ q,
+    float* scale_out, float* amax_stats, fm_quant_stats* qs, int qpt) {
+    extern __shared__ __attribute__((aligned(16))) float row[];  // dm floats
+    __shared__ float r_s, c_s, wmax[kNormThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t r0 = blockIdx.x;
+    const float* hr = h + r0 * dm;
+    for (int i0 = tid * 4; i0 < dm; i0 += 4 * 4 * kNormThreads) {  // 4 loads in flight
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * 4 * kNormThreads;
+            v[k] = i < dm ? *reinterpret_cast<const float4*>(hr + i) : make_float4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * 4 * kNormThreads;
+            if (i < dm) *reinterpret_cast<float4*>(row + i) = v[k];
+        }
+    }
+    const bool have_r = kQuant && mode == FM_SCALE_DYNAMIC;  // pass 2 reads pass 1's r
+    __syncthreads();
+    if (wave == 0) {
+        float r;
+        if (have_r) {
+            r = rs[r0];
+        } else {
+            float a = 0.0f;
+            for (int i = lane; i < dm; i += 64) {
+                const float v = row[i];
+                const float v2 = v * v;
+                a = a + v2;  // ascending i within this lane: the fixed order
+            }
+            const float ss = wave_sum_fixed(a);
+            r = 1.0f / sqrtf(ss / (float)dm + 1e-5f);
+            if (!kQuant && lane == 0) rs[r0] = r;
+        }
+        float c = 0.0f;
+        if constexpr (kQuant) {
+            float amax = 0.0f;
+            if (mode == FM_SCALE_DYNAMIC) amax = __int_as_float(slots_wave_max(amax_slots));
+            c = mode == FM_SCALE_DYNAMIC ? (amax == 0.0f ? 1.0f : 127.0f / amax)
+                                         : ldexpf((float)scoe, -sshift);
+            if (blockIdx.x == 0 && lane == 0) {
+                *scale_out = 1.0f / c;
+                if (mode == FM_SCALE_DYNAMIC) *amax_ws = amax;
+            }
+        }
+        if (lane == 0) {
+            r_s = r;
+            c_s = c;
+        }
+    }
+    __syncthreads();
+    const float r = r_s, c = c_s, s_dq = 1.0f / c;
+    float m = 0.0f;
+    QStat st;
+    for (int blk = wave; blk < dm / 256; blk += kNormThreads / 64) {
+        float4 v = *reinterpret_cast<const float4*>(row + blk * 256 + lane * 4);
+        v.x = (v.x * r) * 1.0f;
+        v.y = (v.y * r) * 1.0f;
+        v.z = (v.z * r) * 1.0f;
+        v.w = (v.w * r) * 1.0f;
+        v = fwht256_lane(v, lane);
+        m = fmaxf(m, absmax4(v));
+        if constexpr (kQuant) {
+            q[(r0 * dm + blk * 256) / 4 + lane] = quant4(v, c);
+            if (qs) quant_stat4(st, v, c, s_dq);
+        }
+    }
+    if (kQuant && qs) qstat_flush(st, qs, qpt);
+    if (!kQuant || amax_stats) {
+        m = wave_max_f32(m);
+        if (lane == 0) wmax[wave] = m;
+        __syncthreads();
+        if (tid == 0) {
+            for (int k = 1; k < kNormThreads / 64; ++k) m = fmaxf(m, wmax[k]);
+            if constexpr (!kQuant) slot_max(amax_slots, blockIdx.x, (int32_t)__float_as_uint(m));
+            else atomic_max_nonneg_f32(amax_stats, m);
+        }
+    }
+}
+
+fm_status norm_hq_run(const float* h, int64_t rows, int64_t dm, fm_scale_mode mode, int32_t scoe,
+                      int32_t sshift, int8_t* q, float* scale_out, float* amax_stats,
+                      float* amax_ws, int32_t* amax_slots, float* rs, hipStream_t s,
+                      fm_quant_stats* qs, int qpt) {
+    if (rows == 0) return FM_OK;
+    const size_t lds = (size_t)dm * sizeof(float);
+    fm_status st;
+    if (mode == FM_SCALE_DYNAMIC) {  // amax_slots must hold 0 (zeroed by the caller)
+        norm_hq_kernel<false><<<(unsigned)rows, kNormThreads, lds, s>>>(
+            h, (int)dm, rs, mode, scoe, sshift, amax_ws, amax_slots, nullptr, nullptr, nullptr,
+            nullptr, qpt);
+        if ((st = check_launch("norm_hq_kernel(max)")) != FM_OK) return st;
+    }
+    norm_hq_kernel<true><<<(unsigned)rows, kNormThreads, lds, s>>>(
+        h, (int)dm, mode == FM_SCALE_DYNAMIC ? rs : nullptr, mode, scoe, sshift, amax_ws,
+        amax_slots, (char4*)q, scale_out, amax_stats, qs, qpt);
+    return check_launch("norm_hq_kernel(codes)");
+}
+
 fm_status hq_quant_rotated(const float* r, int64_t rows, int64_t k, fm_scale_mode mode,
                            int32_t scoe, int32_t sshift, float* amax_ws,
                            const int32_t* amax_slots, int8_t* q, float* scale_out,

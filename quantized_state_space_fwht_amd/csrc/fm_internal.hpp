@@ -297,7 +297,11 @@ fm_status prepare_run(const fm_layer_desc* d, const float* w_in, const float* w_
                       int8_t* conv_w_q, int32_t* conv_p_w, int32_t* conv_b_q16, int32_t* a_q16,
                       int32_t* d_q16, void* ws, hipStream_t s);
 
-// pre-norm of the residual stream: n = RMSNorm(h) (weight 1, fixed order)
-fm_status rmsnorm_rows_run(const float* h, int64_t rows, int64_t d, float* out, hipStream_t s);
+// pre-norm of the residual stream fused with the in_proj input rotation and
+// quantization (hq_run's arguments; rs: [rows] floats of scratch for 1/rms)
+fm_status norm_hq_run(const float* h, int64_t rows, int64_t dm, fm_scale_mode mode, int32_t scoe,
+                      int32_t sshift, int8_t* q, float* scale_out, float* amax_stats,
+                      float* amax_ws, int32_t* amax_slots, float* rs, hipStream_t s,
+                      fm_quant_stats* qs, int qpt);
 
 }  // namespace fm

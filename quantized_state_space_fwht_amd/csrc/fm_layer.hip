@@ -29,6 +29,7 @@ struct LayerWs {
     void* scan_ws;   // scan prologue scalars
     float* rowmax;   // one-token step: [2, 64] row maxima (in_proj input, out_proj input)
     float* sz;       // one-token step: [T, di] SiLU(z) from the in_proj epilogue
+    float* rs;       // stacks: [T] 1/rms of the pre-norm, from the dynamic maximum pass
     size_t bytes;
 };
 
@@ -57,6 +58,7 @@ static LayerWs layer_ws(const fm_layer_desc* d, int64_t batch, int64_t len, void
     w.scan_ws = ar.take<char>(scan_ws_bytes(batch, len, d->dstate));
     w.rowmax = ar.take<float>(T <= 64 ? 128 : 0);
     w.sz = ar.take<float>(T <= 64 ? (size_t)T * di : 0);
+    w.rs = ar.take<float>((size_t)T);
     w.bytes = ar.used;
     return w;
 }
@@ -106,7 +108,7 @@ __global__ void layer_setup_kernel(uint32_t* small, int32_t* slots, const int32_
 // ---------------------------------------------------------------- one-token step input
 // A decode step has few rows (T = batch <= 64).  One workgroup per row stages
 // the row in LDS, forms the pre-norm (wave 0: the fixed-order sum of squares as
-// in rmsnorm_rows_kernel), rotates the 256-blocks and stores the rotated row
+// in norm_hq_kernel), rotates the 256-blocks and stores the rotated row
 // and its maximum; the in_proj product turns them into codes with the tensor
 // scale.  Workgroup 0 also zeroes the call's small block and loads the frozen
 // exponents (nothing in this kernel reads the block).
@@ -243,18 +245,20 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             layer_setup_kernel<<<1, 64, 0, s>>>(w.small, w.slots, nullptr, 0, 0, 0, 0, 0);
         if ((st = check_launch("layer_setup_kernel")) != FM_OK) return st;
 
-        // 1. (stacks) pre-norm of the residual stream
-        const float* xin = u;
+        // 1-2. rotate + quantize the in_proj input (stacks: of the residual stream's
+        // pre-norm, formed on the fly)
         if (d->prenorm_residual) {
-            if ((st = rmsnorm_rows_run(u, T, dm, w.un, s)) != FM_OK) return st;
-            xin = w.un;
-        }
-        // 2. rotate + quantize the in_proj input
-        if ((st = hq_run(xin, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0,
-                         w.u_q, small_f + kScaleU, stat ? small_f + kAmaxU : nullptr,
-                         small_f + kAmaxU, w.slots + kRegionU * kSlotRegionWords, s, qs,
-                         FM_QP_U)) != FM_OK)
+            if ((st = norm_hq_run(u, T, dm, mode, stat ? sp->scoe[0] : 0, stat ? sp->sshift[0] : 0,
+                                  w.u_q, small_f + kScaleU, stat ? small_f + kAmaxU : nullptr,
+                                  small_f + kAmaxU, w.slots + kRegionU * kSlotRegionWords, w.rs,
+                                  s, qs, FM_QP_U)) != FM_OK)
+                return st;
+        } else if ((st = hq_run(u, T, dm, mode, stat ? sp->scoe[0] : 0,
+                                stat ? sp->sshift[0] : 0, w.u_q, small_f + kScaleU,
+                                stat ? small_f + kAmaxU : nullptr, small_f + kAmaxU,
+                                w.slots + kRegionU * kSlotRegionWords, s, qs, FM_QP_U)) != FM_OK) {
             return st;
+        }
     }
     if ((st = mark(1)) != FM_OK) return st;
     // 3. in_proj W8A8, dequant, max |xBC| for the conv exponent
