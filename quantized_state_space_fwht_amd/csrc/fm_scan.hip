@@ -312,27 +312,67 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
             if constexpr (decltype(guard)::value)
                 if (T >= tc) return;
             const double da = row_bcast<T>(uda);
-            const double u0 = row_bcast<T>(uu0), u1 = row_bcast<T>(uu1);
             const double* bv = ring[T % (kAhead + 1)];
             const double* cv = bv + NN;
             double y[2];
+            if constexpr (kClamp) {
+                const double u0 = row_bcast<T>(uu0), u1 = row_bcast<T>(uu1);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const double u = r ? u1 : u0;
+                for (int r = 0; r < 2; ++r) {
+                    const double u = r ? u1 : u0;
 #pragma unroll
-                for (int j = 0; j < NN; ++j) {
-                    if constexpr (kClamp) {
+                    for (int j = 0; j < NN; ++j) {
                         // h + 2^31 floored and clamped to [0, 2^32 - 1] by the conversion
                         const double sv =
                             __builtin_fma(da, h[r][j], __builtin_fma(u, bv[j], 2147483648.5));
                         uint32_t hu;
                         asm("v_cvt_u32_f64 %0, %1" : "=v"(hu) : "v"(sv));
                         h[r][j] = (double)hu - 2147483648.0;
-                    } else {
-                        h[r][j] = __builtin_floor(
-                            __builtin_fma(da, h[r][j], __builtin_fma(u, bv[j], 0.5)));
                     }
                 }
+            } else {
+                // t = da * h + 1/2 (exact), then t += u * B with u read from lane T of
+                // the row by the multiply-add itself (DPP row_newbcast: no separate
+                // broadcast), rounded once: the same sum as the clamped form's, and
+                // floor(t) the same integer.  uu0 / uu1 are written once per chunk;
+                // the chunk's first step waits the two cycles a DPP source needs
+                // after a vector write.
+                double t[2][NN];
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int j = 0; j < NN; ++j) t[r][j] = __builtin_fma(da, h[r][j], 0.5);
+                // the four (or two) multiply-adds; the chunk's first step is preceded
+                // by two wait cycles (s_nop 1) in the same block
+#define FM_SCAN_DPP(NOP)                                                                       \
+    if constexpr (NN == 2) {                                                                   \
+        asm volatile(NOP                                                                       \
+                     "v_fmac_f64_dpp %0, %4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t" \
+                     "v_fmac_f64_dpp %1, %4, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t" \
+                     "v_fmac_f64_dpp %2, %5, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t" \
+                     "v_fmac_f64_dpp %3, %5, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf"     \
+                     : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1])              \
+                     : "v"(uu0), "v"(uu1), "v"(bv[0]), "v"(bv[1]), "i"(T));                    \
+    } else {                                                                                   \
+        asm volatile(NOP                                                                       \
+                     "v_fmac_f64_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t" \
+                     "v_fmac_f64_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"     \
+                     : "+v"(t[0][0]), "+v"(t[1][0])                                            \
+                     : "v"(uu0), "v"(uu1), "v"(bv[0]), "i"(T));                                \
+    }
+                if constexpr (T == 0) {
+                    FM_SCAN_DPP("s_nop 1\n\t")
+                } else {
+                    FM_SCAN_DPP("")
+                }
+#undef FM_SCAN_DPP
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int j = 0; j < NN; ++j) h[r][j] = __builtin_floor(t[r][j]);
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
                 y[r] = cv[0] * h[r][0];
 #pragma unroll
                 for (int j = 1; j < NN; ++j) y[r] = __builtin_fma(cv[j], h[r][j], y[r]);
