@@ -98,7 +98,7 @@ def host_cpu():
     return {"nproc": os.cpu_count(), "usable": usable, "model": model, "blas_threads": blas}
 
 
-def cpu_baseline(w, sample_layers=2, sample_batch=1, sample_len=1024):
+def cpu_baseline(w, sample_layers=2, sample_batch=1, sample_len=4096):
     """The oracle as it stands (numpy) on a bounded sample of the workload.
 
     Stacks: the first `sample_layers` layers over `sample_batch` x `sample_len`
@@ -769,6 +769,10 @@ def main():
     ap.add_argument("--workload", default=HEADLINE_WORKLOAD,
                     help="prefill workload timed for the headline (default: the 64-layer "
                          "2.7B-shaped stack, batch 4, L 4096)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="run only the first N layers of a stack workload (every layer runs the "
+                         "same kernels at the same shapes: for profiler runs); config.layers "
+                         "then says N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the headline workload (no 130M layer / static stack / "
@@ -820,6 +824,9 @@ def main():
         return
 
     w = configs.get(args.workload)
+    if args.layers is not None:
+        import dataclasses
+        w = dataclasses.replace(w, nlayers=max(1, min(args.layers, w.nlayers)))
     if w.decode_steps:
         print("bench.py times prefill workloads (decode is an extra key)", file=sys.stderr)
         sys.exit(2)
@@ -836,7 +843,8 @@ def main():
         "stage_ms_sum_per_layer": r["stage_ms_sum_per_layer"],
     }
     extras = not args.no_extras
-    if extras and not args.no_decode and w.name == HEADLINE_WORKLOAD:
+    if (extras and not args.no_decode and w.name == HEADLINE_WORKLOAD
+            and w.nlayers == configs.get(DECODE_WORKLOAD).nlayers):
         # the decode workload has the same layer shapes and weights
         model.u = model.bufs = None
         torch.cuda.empty_cache()
