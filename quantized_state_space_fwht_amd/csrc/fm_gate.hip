@@ -30,12 +30,17 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     __shared__ NauLds tab;
     __shared__ float rs_r;
     __shared__ float wmax[W];
-    nau_lds_init(tab);
-    __syncthreads();
+    if (!G.sz) {  // SiLU(z) formed here
+        nau_lds_init(tab);
+        __syncthreads();
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row = blockIdx.x;
     const int D = (int)G.d_inner;
+    // the norm weights of this wave's first 256-block, loaded ahead of phase 1
+    const float4 w_first = wave < D / 256 ? reinterpret_cast<const float4*>(G.norm_w)[wave * 64 + lane]
+                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     const float ysc = ldexpf(1.0f, -(G.p[1] + 8));
     const int32_t* yr = G.y + row * D;
     const float* zr = G.sz ? G.sz + row * D : G.z + row * G.z_stride;
@@ -61,6 +66,20 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
         }
     }
     __syncthreads();
+    if (G.step_small && row == 0 && wave == W - 1) {
+        // while wave 0 sums: the in_proj epilogue's slotted maxima into the call's
+        // block (that kernel has completed; the out_proj product publishes it)
+        const int32_t xbc = slots_wave_max(G.step_slots + kRegionXbc * kSlotRegionWords);
+        int32_t pm[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            pm[i] = slots_wave_max(G.step_slots + (kRegionConvX + i) * kSlotRegionWords);
+        if (lane == 0) {
+            G.step_small[kAmaxXbc] = (uint32_t)xbc;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) G.step_small[kAmaxQ + i] = (uint32_t)pm[i];
+        }
+    }
     // phase 2: the fixed-order sum of squares
     if (wave == 0) {
         float a = 0.0f;
@@ -90,7 +109,8 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     for (int blk = wave; blk < D / 256; blk += W) {
         const int base = blk * 256 + lane * 4;
         float4 g = *reinterpret_cast<const float4*>(&row_buf[base]);
-        const float4 w = *reinterpret_cast<const float4*>(&G.norm_w[base]);
+        const float4 w =
+            blk == wave ? w_first : *reinterpret_cast<const float4*>(&G.norm_w[base]);
         float4 n;
         n.x = (g.x * r) * w.x;
         n.y = (g.y * r) * w.y;

@@ -690,9 +690,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
             for (int i = 0; i < 3; ++i) pmax[i] = wg_pmax[w][i] > pmax[i] ? wg_pmax[w][i] : pmax[i];
         }
         if (kConv) {
-            if (xmax > 0.0f) atomicMax(reinterpret_cast<unsigned int*>(ep.amax), __float_as_uint(xmax));
+            // slotted: hundreds of workgroups on one word each would serialize
+            slot_max(ep.amax_slots, blockIdx.x, (int32_t)__float_as_uint(xmax));
             for (int i = 0; i < 3; ++i)
-                if (pmax[i] > 0) atomicMax(&ep.conv_amax_q16[i], pmax[i]);
+                slot_max(ep.conv_amax_slots + i * kSlotRegionWords, blockIdx.x, pmax[i]);
         } else if (ep.amax_slots) {
             slot_max(ep.amax_slots, blockIdx.x, (int32_t)__float_as_uint(amax));
         } else if (amax > 0.0f) {

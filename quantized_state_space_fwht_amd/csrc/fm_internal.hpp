@@ -118,7 +118,8 @@ struct GemmEpilogue {
     int8_t* b_out = nullptr;            // [rows, dstate]
     int8_t* c_out = nullptr;
     int8_t* xbc_q = nullptr;            // nullable: [rows, ch] quantized conv input
-    int32_t* conv_amax_q16 = nullptr;   // int[3]: max |SiLU| of x, B, C (Q.16)
+    int32_t* conv_amax_slots = nullptr; // three slot regions: max |SiLU| of x, B, C (Q.16);
+                                        // max |xBC| goes to amax_slots
     int64_t d_inner = 0, dstate = 0;
     float* sz_out = nullptr;            // [rows, d_inner]: SiLU(z) of the z columns [0, amax_c0)
     // dt columns [amax_c1, n): also dt = SoftPlus(dt_in) and dA = e^(dt * A) in Q.16
@@ -250,6 +251,10 @@ struct GateArgs {
     fm_quant_stats* qs;  // nullable: statistics of the out_proj input point
     float* rowmax;     // nullable: one-token form, rotated rows to rot_ws and their maxima
                        // here (the out_proj product quantizes them); q, scale_out unused
+    // one-token form: workgroup 0 also reduces the in_proj epilogue's slotted
+    // maxima (max |xBC|, max |SiLU| of x, B, C) into the call's small block
+    const int32_t* step_slots;
+    uint32_t* step_small;
 };
 fm_status gate_run(const GateArgs& a, hipStream_t s);
 

@@ -110,8 +110,9 @@ __global__ void layer_setup_kernel(uint32_t* small, int32_t* slots, const int32_
 // the row in LDS, forms the pre-norm (wave 0: the fixed-order sum of squares as
 // in norm_hq_kernel), rotates the 256-blocks and stores the rotated row
 // and its maximum; the in_proj product turns them into codes with the tensor
-// scale.  Workgroup 0 also zeroes the call's small block and loads the frozen
-// exponents (nothing in this kernel reads the block).
+// scale.  Workgroup 0 also zeroes the call's small block and the slot regions
+// of the in_proj epilogue's maxima and loads the frozen exponents (nothing in
+// this kernel reads them).
 constexpr int kStepRowThreads = 256;
 static_assert(kSmallWords <= kStepRowThreads, "workgroup 0 zeroes the small block in one pass");
 
@@ -121,6 +122,7 @@ struct StepRowsArgs {
     int prenorm;
     const int32_t* p_src;  // frozen exponents [4]
     uint32_t* small;
+    int32_t* slots;        // the layer's slot regions
     float* rot;            // [rows, dm]
     float* rowmax;         // [rows]
 };
@@ -131,8 +133,15 @@ __global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs
     __shared__ float wmax[kStepRowThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (blockIdx.x == 0 && tid < kSmallWords)
-        A.small[tid] = (tid >= kP && tid < kP + 4) ? (uint32_t)A.p_src[tid - kP] : 0u;
+    if (blockIdx.x == 0) {
+        if (tid < kSmallWords)
+            A.small[tid] = (tid >= kP && tid < kP + 4) ? (uint32_t)A.p_src[tid - kP] : 0u;
+        // slots of max |SiLU| of x, B, C (three regions) and of max |xBC|
+        if (tid < 4 * kSlots) {
+            const int reg = tid / kSlots < 3 ? kRegionConvX + tid / kSlots : kRegionXbc;
+            A.slots[reg * kSlotRegionWords + (tid % kSlots) * kSlotStride] = 0;
+        }
+    }
     const int dm = A.dm;
     const int64_t r = blockIdx.x;
     const float* ur = A.u + r * dm;
@@ -230,6 +239,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         a.prenorm = d->prenorm_residual ? 1 : 0;
         a.p_src = cache->p;
         a.small = w.small;
+        a.slots = w.slots;
         a.rot = w.un;
         a.rowmax = w.rowmax;
         step_rows_kernel<<<(unsigned)T, kStepRowThreads, (size_t)dm * sizeof(float), s>>>(a);
@@ -270,8 +280,8 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         ep.s_b = W->s_w_in;
         // the conv pass reduces max |xBC| from a slot region when its exponents are
         // dynamic; the fused step and fixed exponents keep the one word
-        if (step || stat || decode) ep.amax = small_f + kAmaxXbc;
-        else ep.amax_slots = w.slots + kRegionXbc * kSlotRegionWords;
+        if (step || !(stat || decode)) ep.amax_slots = w.slots + kRegionXbc * kSlotRegionWords;
+        else ep.amax = small_f + kAmaxXbc;
         ep.amax_c0 = di;
         ep.amax_c1 = di + ch;
         if (step) {  // 2 fused: codes of the rotated rows with the tensor scale
@@ -294,7 +304,7 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
             ep.b_out = w.b_q;
             ep.c_out = w.c_q;
             ep.xbc_q = keep ? w.xbc_q : nullptr;
-            ep.conv_amax_q16 = small_i + kAmaxQ;
+            ep.conv_amax_slots = w.slots + kRegionConvX * kSlotRegionWords;
             ep.d_inner = di;
             ep.dstate = N;
             ep.sz_out = w.sz;
@@ -399,6 +409,8 @@ fm_status layer_run(const fm_layer_desc* d, const fm_layer_weights* W, const fm_
         g.amax_ws = small_f + kAmaxG;
         g.amax_slots = w.slots + kRegionG * kSlotRegionWords;
         g.rowmax = step ? w.rowmax + 64 : nullptr;
+        g.step_slots = step ? w.slots : nullptr;
+        g.step_small = step ? w.small : nullptr;
         g.sz = step ? w.sz : nullptr;
         g.qs = qs;
         if ((st = gate_run(g, s)) != FM_OK) return st;
