@@ -9,6 +9,17 @@
 // registers, so each input is read once; a wave covers 64 consecutive
 // channels, so every load and store is coalesced.  d_inner and d_state are
 // multiples of 64, so a wave never straddles the x | B | C split.
+//
+// Dynamic exponents need the maximum of each part over the whole tensor
+// before any code is formed, so a second pass writes the codes.  Between the
+// passes each wave's 64 x 16 SiLU values s (Q.16) are held as 16-bit words
+// T = floor(s * 2^(e - 15)) at the wave's own exponent e (the exponent rule
+// applied to the wave's maximum, 24 for an all-zero wave), so |T| <= 255.
+// The tensor's exponent p is never above e, and with k = e - p + 1 >= 1,
+// rshr(T, k) = floor(s * 2^(p - 16) + 1/2) = rshr(s, 16 - p) exactly (the
+// discarded low bits of s are a fraction below one step of T, which cannot
+// carry the half-up rounding across an integer).  Runs that record
+// quantization statistics keep the 32-bit values, which the statistics need.
 #include "fm_internal.hpp"
 
 namespace fm {
@@ -22,13 +33,23 @@ struct ConvKParams {
     int dynamic;
 };
 
+// The per-wave exponents of the 16-bit form, after its [T, ch] words in s16.
+// Wave blocks are numbered (batch, 16-step block of the sequence, 64-channel
+// group), with ceil(len / 64) * 4 step blocks per sequence.
+__device__ __forceinline__ int8_t* conv_pblk(const ConvArgs& A, int ch) {
+    return reinterpret_cast<int8_t*>(A.s16) + 2 * A.batch * A.len * (int64_t)ch;
+}
+
 // One thread: channel c, steps t0 .. t0+n-1 (n = kConvTL unless kTail).
 // Dynamic: writes Q.16 SiLU outputs + per-part maxima.  Static: writes codes.
+// Dynamic without statistics: the values are held in sv for the wave's
+// exponent instead of being written.
 template <bool kTail, bool kDyn, bool kXq, bool kStats>
 __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLds& tab, int c,
                                                int64_t row0, int64_t t0, int n, int p_c,
                                                int part, int32_t& amax, float& xmax,
-                                               QStat& sx, QStat& sp) {
+                                               QStat& sx, QStat& sp, int32_t (&sv_hold)[kConvTL]) {
+    constexpr bool kHold = kDyn && !kStats;
     const ConvArgs& A = K.a;
     const int di = (int)A.d_inner, N = (int)A.dstate;
     const float qscale = ldexpf(1.0f, p_c);
@@ -64,7 +85,7 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
     // outputs of this thread: element (row0 + i, c) of [rows, ch] / of the part
     const int p_part = kDyn ? 0 : A.p_fixed[1 + part];
     const double oscale = __builtin_ldexp(1.0, p_part - 16);
-    int32_t* s16 = kDyn ? A.s16 + row0 * K.ch + c : nullptr;
+    int32_t* s16 = kDyn && !kHold ? A.s16 + row0 * K.ch + c : nullptr;
     int8_t* code = nullptr;
     uint32_t cstride = 0;
     if (!kDyn) {
@@ -89,7 +110,9 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
         const int32_t sv = nau_silu_f(a, tab);
         const int32_t sa = sv < 0 ? -sv : sv;
         amax = sa > amax ? sa : amax;
-        if constexpr (kDyn) {
+        if constexpr (kHold) {
+            sv_hold[i] = sv;
+        } else if constexpr (kDyn) {
             s16[(uint32_t)i * (uint32_t)K.ch] = sv;
         } else {
             // sat8(rshr(sv, 16 - p_part)): sv * 2^(p_part-16) is exact in float64
@@ -179,12 +202,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     int32_t amax = 0;
     float xmax = 0.0f;
     QStat sx, sp;
+    int32_t sv[kConvTL];
     if (A.xbc_q) {
-        if (n == kConvTL) conv_run_steps<false, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
-        else conv_run_steps<true, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
+        if (n == kConvTL) conv_run_steps<false, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp, sv);
+        else conv_run_steps<true, kDyn, true, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp, sv);
     } else {
-        if (n == kConvTL) conv_run_steps<false, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
-        else conv_run_steps<true, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp);
+        if (n == kConvTL) conv_run_steps<false, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp, sv);
+        else conv_run_steps<true, kDyn, false, kStats>(K, tab, c, row0, t0, n, p_c, part, amax, xmax, sx, sp, sv);
     }
     if constexpr (kStats) {  // every lane of the wave is here (one part per wave)
         qstat_flush(sx, A.qs, FM_QP_XBC);
@@ -194,10 +218,28 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     // of the part's region, by the wave's time block
     amax = wave_max_i32(amax);
     xmax = wave_max_f32(xmax);
+    const int64_t tb = (int64_t)blockIdx.z * gridDim.y * (kConvThreads / 64) +
+                       (int64_t)blockIdx.y * (kConvThreads / 64) + wave;
+    if constexpr (kDyn && !kStats) {
+        // the wave's values as 16-bit words at the wave's exponent, the exponent
+        // in the table after them (one byte per wave block: 16 steps x 64 channels)
+        const int e = amax == 0 ? kPMax : pot_from_q16(amax);
+        int16_t* out = reinterpret_cast<int16_t*>(A.s16) + row0 * K.ch + c;
+#pragma unroll
+        for (int i = 0; i < kConvTL; ++i) {
+            if (i < n) {
+                const int32_t v = sv[i];
+                // floor(v * 2^(e - 15)): e <= 24, so a left shift moves at most 9
+                // bits (|result| <= 255); right shifts floor, 31 places at most
+                const int32_t t = e >= 15 ? v << (e - 15) : v >> (15 - e < 31 ? 15 - e : 31);
+                out[(uint32_t)i * (uint32_t)K.ch] = (int16_t)t;
+            }
+        }
+        if (lane == 0)
+            conv_pblk(A, K.ch)[tb * (K.ch / 64) + blockIdx.x] = (int8_t)e;
+    }
     if (lane == 0) {
         if (kDyn) {
-            const int64_t tb = (int64_t)blockIdx.z * gridDim.y * (kConvThreads / 64) +
-                               (int64_t)blockIdx.y * (kConvThreads / 64) + wave;
             slot_max(A.amax_slots + part * kSlotRegionWords, tb, amax);
         } else if (A.amax_stats) {
             if (amax > 0) atomic_max_i32(&A.amax_stats[1 + part], amax);
@@ -206,24 +248,53 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
     }
 }
 
-// Dynamic second pass: exponents from the maxima, Q.16 -> int8 codes.
-// grid.y = token row, threads over groups of 4 channels.
+// Dynamic second pass: exponents from the maxima, SiLU values -> int8 codes
+// (k16: from the 16-bit words and their wave exponents; otherwise from the
+// 32-bit Q.16 values, with statistics).
+// grid.y = token row, threads over groups of kRqCh channels (one 16-byte load
+// per row: 8 16-bit words, or 4 32-bit values).
 constexpr int kRqRows = 4;  // rows per thread in the requantization pass
+template <bool k16> constexpr int kRqCh = k16 ? 8 : 4;
 
+template <bool k16>
 __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
     const ConvArgs& A = K.a;
     const int di = (int)A.d_inner, N = (int)A.dstate;
-    const int c = (blockIdx.x * kConvThreads + threadIdx.x) * 4;
+    const int c = (blockIdx.x * kConvThreads + threadIdx.x) * kRqCh<k16>;
     const bool active = c < K.ch;  // idle lanes stay for the statistics' wave sums
     const int64_t rows = A.batch * A.len;
+    // 16-bit form: the wave block of (row, c) in the exponent table
+    const int64_t L = A.len, sblocks = (L + 63) / 64 * (kConvThreads / 64);
+    const int8_t* pblk = k16 ? conv_pblk(A, K.ch) + c / 64 : nullptr;
     // kRqRows rows per thread and round, their loads issued before any use (the
     // first round's before the maxima are known)
     int4 sr[kRqRows];
+    int32_t eb[kRqRows];
     auto load_round = [&](int64_t r0) {
+        // (sequence, step) of row r0, then stepped along the round's rows
+        int64_t b = 0, t = 0;
+        if constexpr (k16) {
+            b = r0 / L;
+            t = r0 - b * L;
+        }
 #pragma unroll
-        for (int k = 0; k < kRqRows; ++k)
-            sr[k] = r0 + k < rows ? *reinterpret_cast<const int4*>(A.s16 + (r0 + k) * K.ch + c)
-                                  : make_int4(0, 0, 0, 0);
+        for (int k = 0; k < kRqRows; ++k) {
+            if constexpr (k16) {
+                while (t >= L) {
+                    t -= L;
+                    ++b;
+                }
+                const bool ok = r0 + k < rows;
+                sr[k] = ok ? *reinterpret_cast<const int4*>(
+                                 reinterpret_cast<const int16_t*>(A.s16) + (r0 + k) * K.ch + c)
+                           : make_int4(0, 0, 0, 0);
+                eb[k] = ok ? pblk[(b * sblocks + t / kConvTL) * (K.ch / 64)] : kPMax;
+                ++t;
+            } else {
+                sr[k] = r0 + k < rows ? *reinterpret_cast<const int4*>(A.s16 + (r0 + k) * K.ch + c)
+                                      : make_int4(0, 0, 0, 0);
+            }
+        }
     };
     const int64_t rfirst = (int64_t)blockIdx.y * kRqRows;
     if (active) load_round(rfirst);
@@ -258,6 +329,14 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
         const double q = __builtin_floor(__builtin_fma((double)v, sc, 0.5));
         return (signed char)__builtin_fmin(__builtin_fmax(q, -127.0), 127.0);
     };
+    // 16-bit words T at the wave exponent e: code = sat8(rshr(T, e - p + 1)), where
+    // e - p + 1 >= 1 and shifts past 16 leave 0 (|T| <= 255)
+    const int p_part = pot_from_q16(amax_part);
+    auto q8w = [&](int32_t t, int32_t e) {
+        const int k = e - p_part + 1;
+        const int32_t r = k > 16 ? 0 : (t + (1 << (k - 1))) >> k;
+        return (signed char)(r < -127 ? -127 : (r > 127 ? 127 : r));
+    };
     QStat st;
     const double step = __builtin_ldexp(1.0, 16 - pot_from_q16(amax_part));
     for (int64_t r0 = rfirst; active && r0 < rows; r0 += (int64_t)gridDim.y * kRqRows) {
@@ -268,11 +347,32 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
             if (row >= rows) break;
             const int4 s = sr[k];
             char4 q;
-            q.x = q8(s.x);
-            q.y = q8(s.y);
-            q.z = q8(s.z);
-            q.w = q8(s.w);
-            if (A.qs) {
+            if constexpr (k16) {
+                // eight words -> eight codes, stored as one 8-byte word
+                const int32_t e = eb[k];
+                const int32_t wd[4] = {s.x, s.y, s.z, s.w};
+                uint32_t out[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    char4 o;
+                    o.x = q8w((int16_t)(wd[2 * h] & 0xFFFF), e);
+                    o.y = q8w((int16_t)(wd[2 * h] >> 16), e);
+                    o.z = q8w((int16_t)(wd[2 * h + 1] & 0xFFFF), e);
+                    o.w = q8w((int16_t)(wd[2 * h + 1] >> 16), e);
+                    out[h] = __builtin_bit_cast(uint32_t, o);
+                }
+                const uint2 o8 = make_uint2(out[0], out[1]);
+                if (part == 0) *reinterpret_cast<uint2*>(A.x_out + row * di + c) = o8;
+                else if (part == 1) *reinterpret_cast<uint2*>(A.b_out + row * N + (c - di)) = o8;
+                else *reinterpret_cast<uint2*>(A.c_out + row * N + (c - di - N)) = o8;
+                continue;
+            } else {
+                q.x = q8(s.x);
+                q.y = q8(s.y);
+                q.z = q8(s.z);
+                q.w = q8(s.w);
+            }
+            if (!k16 && A.qs) {
                 const int32_t sv[4] = {s.x, s.y, s.z, s.w};
                 const signed char qc[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -287,7 +387,7 @@ __global__ __launch_bounds__(kConvThreads) void requant_kernel(ConvKParams K) {
             else *reinterpret_cast<char4*>(A.c_out + row * N + (c - di - N)) = q;
         }
     }
-    if (A.qs)  // a wave may span two parts: one wave sum per part
+    if (!k16 && A.qs)  // a wave may span two parts: one wave sum per part
         for (int pt = 0; pt < 3; ++pt)
             qstat_flush(part == pt && active ? st : QStat{}, A.qs, FM_QP_X + pt);
 }
@@ -332,9 +432,12 @@ fm_status conv_run(const ConvArgs& a, hipStream_t s) {
     fm_status st = check_launch("conv_silu_kernel");
     if (st != FM_OK || !K.dynamic) return st;
     const int64_t rows = a.batch * a.len, rblocks = (rows + kRqRows - 1) / kRqRows;
-    dim3 rgrid((unsigned)((K.ch / 4 + kConvThreads - 1) / kConvThreads),
-               (unsigned)(rblocks < 65535 ? rblocks : 65535));
-    requant_kernel<<<rgrid, kConvThreads, 0, s>>>(K);
+    auto rgrid = [&](int per) {
+        return dim3((unsigned)((K.ch / per + kConvThreads - 1) / kConvThreads),
+                    (unsigned)(rblocks < 65535 ? rblocks : 65535));
+    };
+    if (a.qs) requant_kernel<false><<<rgrid(kRqCh<false>), kConvThreads, 0, s>>>(K);
+    else requant_kernel<true><<<rgrid(kRqCh<true>), kConvThreads, 0, s>>>(K);
     return check_launch("requant_kernel");
 }
 

@@ -170,7 +170,8 @@ struct ConvArgs {
     const int8_t* state_in;
     int8_t* state_out;
     int8_t* xbc_q;
-    int32_t* s16;              // dynamic: [T, ch] Q.16 SiLU outputs
+    int32_t* s16;              // dynamic: [T, ch] SiLU outputs between the passes (Q.16, or
+                               // 16-bit words at per-wave exponents and their table)
     int32_t* amax_q16;         // dynamic: [3] the part maxima (written by the requant pass)
     int32_t* amax_slots;       // dynamic: three slot regions (x, B, C) zeroed before
     int8_t* x_out;
