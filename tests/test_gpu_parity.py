@@ -178,6 +178,67 @@ def test_conv1d_pot(B, wname, batch, length, mode, with_state):
     assert_exact(stats[1:], amaxes, "Q.16 maxima")
 
 
+def test_conv1d_pot_wave_exponents_far_apart(B):
+    """Dynamic conv whose 64-channel groups and 16-step runs differ by many
+    octaves: silent groups (zero weights and bias: all-zero SiLU values), groups
+    with a tiny bias and tiny inputs, ordinary ones and large ones, and a run of
+    silent steps across every group.  Between its two passes the kernel holds
+    each wave's values as 16-bit words at the wave's own power-of-two exponent;
+    these inputs spread those exponents from the top of the exponent range (24,
+    silent waves) to the tensor's own, so the words are formed by left and by
+    right shifts and brought back onto the tensor's grid by rounding shifts from
+    1 to past 16 places.  Ragged length, two sequences, a carried window: codes
+    and exponents equal the oracle's."""
+    s = configs.get("m130m_layer").shape
+    di, N, ch = s.d_inner, s.dstate, s.conv_ch
+    batch, length = 2, 83
+    params, _, _, _, _ = _conv_case(s, batch, length, 7)
+    groups = ch // 64
+    kind = np.arange(groups) % 4            # 0 silent, 1 tiny, 2 ordinary, 3 large
+    w = np.asarray(params["conv_w"], np.float32).copy()
+    b = np.asarray(params["conv_b"], np.float32).copy()
+    gsel = np.repeat(kind, 64)
+    w[gsel == 0] = 0.0
+    b[gsel == 0] = 0.0
+    b[gsel == 1] = 2e-4
+    b[gsel == 3] *= 500.0
+    params = dict(params, conv_w=w, conv_b=b)
+    w_q, p_w, b_q16 = O.conv_weight_prep(params["conv_w"], params["conv_b"])
+    rng = np.random.default_rng(13)
+    gain = np.array([0.0, 1e-5, 1.0, 400.0], np.float32)[gsel]
+    xbc = (rng.standard_normal((batch * length, ch)) * gain[None, :]).astype(np.float32)
+    xbc[16:48] = 0.0
+    t_wq = torch.empty((ch, 4), dtype=torch.int8, device="cuda")
+    t_pw = torch.empty(ch, dtype=torch.int32, device="cuda")
+    t_bq = torch.empty(ch, dtype=torch.int32, device="cuda")
+    _device_conv_prep(B, s, params, t_wq, t_pw, t_bq)
+    assert_exact(host(t_bq), b_q16, "conv b_q16")
+    state = np.zeros((batch, ch, 3), np.int8)
+    state[:, gsel == 3] = 100
+    xbc_q, p_c, amax = O.xbc_pot_quant(xbc, None)
+    a, _, st_out = O.conv1d_pot(xbc_q.reshape(batch, length, ch), w_q, p_w, b_q16, p_c, state)
+    xq, bq, cq, ps, amaxes, _ = O.silu_requant(a, di, N, None)
+    T = batch * length
+    out = {k: torch.empty(shp, dtype=torch.int8, device="cuda") for k, shp in
+           (("xbc_q", (T, ch)), ("x", (T, di)), ("b", (T, N)), ("c", (T, N)))}
+    t_st_out = torch.zeros((batch, ch, 3), dtype=torch.int8, device="cuda")
+    t_p = torch.zeros(4, dtype=torch.int32, device="cuda")
+    t_stats = torch.zeros(4, dtype=torch.int32, device="cuda")
+    B.fm_conv1d_pot(dev(xbc), ch, batch, length, di, N, t_wq, t_pw, t_bq, B.DYNAMIC, None,
+                    dev(state), t_st_out, out["xbc_q"], out["x"], out["b"], out["c"], t_p,
+                    t_stats)
+    assert_exact(host(t_p), (p_c,) + tuple(ps), "exponents")
+    assert_exact(host(out["x"]), xq.reshape(T, di), "x codes")
+    assert_exact(host(out["b"]), bq.reshape(T, N), "B codes")
+    assert_exact(host(out["c"]), cq.reshape(T, N), "C codes")
+    assert_exact(host(t_st_out), st_out, "conv state")
+    assert_exact(host(t_stats)[1:], amaxes, "Q.16 maxima")
+    # the case spans the intended range: the B part holds only silent and tiny
+    # groups (a high tensor exponent), x and C large ones next to silent groups
+    assert ps[1] >= 16 and ps[0] <= 0 and ps[2] <= 0
+    assert np.abs(xq).max() > 60 and (xq == 0).mean() > 0.2
+
+
 def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
     desc = B.LayerDesc(s.d_model, s.d_inner, s.nheads, s.headdim, s.dstate, 4, 0, 0)
     # keep every input tensor referenced until the asynchronous kernels have run
