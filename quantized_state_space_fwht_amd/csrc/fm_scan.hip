@@ -22,20 +22,21 @@
 // scan_prep_kernel: dt and the decay for every (token, head) through the 2^v
 // unit, before the scan reads them.
 //
-// scan_kernel: a workgroup of 4 waves owns (b, head, 8 consecutive p).  Lane l
-// of wave w owns the states (p, n) for p in {p0, p0+1} = {8g + 2w, 8g + 2w + 1}
-// and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time runs in chunks of 16
-// steps, two barriers per chunk:
+// scan_kernel: a workgroup of W waves (4 or 8) owns (b, head, 2W consecutive p).
+// Lane l of wave w owns the states (p, n) for p in {p0, p0+1} =
+// {2Wg + 2w, 2Wg + 2w + 1} and n = NN*l .. NN*l+NN-1 (d_state = 64*NN).  Time
+// runs in chunks of 16 steps:
 //  - the per-step wave-uniform scalars (da, u of p0, u of p0+1) of a chunk sit
 //    one step per lane in each 16-lane row and are broadcast with DPP
 //    row_newbcast, so they cost no memory traffic inside the step loop;
 //  - B/C codes (int8) of the next chunk are loaded while a chunk runs and
-//    written to LDS widened to float64.  With more workgroups than CUs one
-//    buffer is used: once every wave has finished reading the chunk's B/C
-//    (first barrier) the next chunk's are written over them (visible after
-//    the second barrier); the workgroup then needs about 66 KB of LDS, so two
-//    share a CU and each hides the other's barrier and dependency stalls.
-//    With a workgroup per CU at most, two buffers save the extra barrier;
+//    written to LDS widened to float64, into the second of two buffers (one
+//    barrier per chunk), or over the chunk's own once every wave has read
+//    them (two barriers, a buffer less).  With more 4-wave workgroups than
+//    CUs, 8-wave workgroups with two buffers (132 KB of LDS, one per CU)
+//    share each chunk's B/C among twice the waves; at head dims that are not
+//    a multiple of 16, 4-wave workgroups with one buffer (66 KB, two per CU).
+//    With a workgroup per CU at most, 4 waves and two buffers;
 //  - the two partial sums of C*h of each lane (one per p) are paired across
 //    the wave halves by a lane swap and stored, one per lane per step; after
 //    the chunk they are added per (step, p) and y is written.
@@ -45,9 +46,6 @@
 
 namespace fm {
 
-constexpr int kScanWaves = 4;
-constexpr int kScanThreads = 64 * kScanWaves;
-constexpr int kScanP = 2 * kScanWaves;  // p per workgroup
 constexpr int kTC = 16;                 // steps per chunk (= lanes per DPP row)
 constexpr int kYRow = 66;               // doubles per partial-sum row (64 + pad)
 
@@ -117,10 +115,10 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 typedef double dpair __attribute__((ext_vector_type(2)));
 
-template <int NN, int NBUF>
+template <int NN, int NBUF, int W>
 struct alignas(16) ScanSmem {
     double bc[NBUF][kTC][2 * 64 * NN];        // [buffer][step][B row, C row]
-    double ypart[kScanWaves][kTC][kYRow];     // [wave][step][lane]
+    double ypart[W][kTC][kYRow];              // [wave][step][lane]
 };
 
 template <int... Ts, class F>
@@ -129,10 +127,11 @@ __device__ __forceinline__ void unroll_steps(std::integer_sequence<int, Ts...>, 
 }
 
 // ---------------------------------------------------------------- scan
-template <int NN, int NBUF>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs A) {
+template <int NN, int NBUF, int W>
+__global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
     constexpr int N = 64 * NN;
-    __shared__ ScanSmem<NN, NBUF> sm;
+    constexpr int kScanP = 2 * W;  // p per workgroup
+    __shared__ ScanSmem<NN, NBUF, W> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -698,15 +697,20 @@ fm_status scan_run(const ScanArgs& a, void*, hipStream_t s, hipEvent_t ev_start,
     if (!a.dt_ready && (st = scan_prep_run(a, s)) != FM_OK) return st;
     if (ev_start && hipEventRecord(ev_start, s) != hipSuccess)
         return fail(FM_ERR_HIP, "hipEventRecord(start) failed");
-    const unsigned grid = (unsigned)(a.headdim / kScanP * a.nheads * a.batch);
-    // one buffer (two workgroups per CU) once the grid outnumbers the CUs
-    const bool one_buf = grid > (unsigned)device_cus();
+    const unsigned grid4 = (unsigned)(a.headdim / 8 * a.nheads * a.batch);  // 4-wave groups
+    // once the 4-wave grid outnumbers the CUs: 4-wave workgroups with one B/C
+    // buffer (two per CU), or, with at least as many 8-wave workgroups as CUs,
+    // those with two buffers (one per CU)
+    const bool many = grid4 > (unsigned)device_cus();
+    const bool wide = grid4 >= 2u * (unsigned)device_cus() && a.headdim % 16 == 0;
     if (a.dstate == 64) {
-        if (one_buf) scan_kernel<1, 1><<<grid, kScanThreads, 0, s>>>(a);
-        else scan_kernel<1, 2><<<grid, kScanThreads, 0, s>>>(a);
+        if (wide) scan_kernel<1, 2, 8><<<grid4 / 2, 512, 0, s>>>(a);
+        else if (many) scan_kernel<1, 1, 4><<<grid4, 256, 0, s>>>(a);
+        else scan_kernel<1, 2, 4><<<grid4, 256, 0, s>>>(a);
     } else {
-        if (one_buf) scan_kernel<2, 1><<<grid, kScanThreads, 0, s>>>(a);
-        else scan_kernel<2, 2><<<grid, kScanThreads, 0, s>>>(a);
+        if (wide) scan_kernel<2, 2, 8><<<grid4 / 2, 512, 0, s>>>(a);
+        else if (many) scan_kernel<2, 1, 4><<<grid4, 256, 0, s>>>(a);
+        else scan_kernel<2, 2, 4><<<grid4, 256, 0, s>>>(a);
     }
     if ((st = check_launch("scan_kernel")) != FM_OK) return st;
     if (ev_stop && hipEventRecord(ev_stop, s) != hipSuccess)

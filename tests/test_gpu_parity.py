@@ -268,7 +268,14 @@ def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
                                                       ("m130m_layer", 2, 33, 3),
                                                       ("m130m_layer", 3, 1, 4),
                                                       ("tiny_layer", 2, 1, None),
-                                                      ("m2p7b_stack", 1, 300, 4)])
+                                                      ("m2p7b_stack", 1, 300, 4),
+                                                      # grids past the CU count: 4-wave
+                                                      # workgroups with one B/C buffer, and
+                                                      # 8-wave ones with two (d_state 128, 64)
+                                                      ("m130m_layer", 2, 37, None),
+                                                      ("m130m_layer", 16, 40, None),
+                                                      ("tiny_layer", 5, 20, None),
+                                                      ("tiny_layer", 64, 20, None)])
 @pytest.mark.parametrize("with_state", [False, True])
 def test_ssm_scan_pot(B, wname, batch, length, heads, with_state):
     s = configs.get(wname).shape
