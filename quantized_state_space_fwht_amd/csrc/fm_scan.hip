@@ -161,24 +161,36 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
         for (int j = 0; j < NN; ++j)
             h[r][j] = A.state_in ? (double)A.state_in[sbase + r * N + j] : 0.0;
 
-    // ---- B/C staging.  Thread k < kLoaders owns 16 consecutive codes (B or C,
-    //      one step of a chunk, n = 16g .. 16g+15): a 16-byte load while the
-    //      previous chunk runs, eight 16-byte LDS stores of float64 pairs after it.
-    //      d_state 128: the pair of lane l sits in slot bc_slot(l) of its row,
-    //      which keeps both the stores (writers of one step hit 8 different
-    //      16-byte columns per instruction) and the step reads conflict-free.
-    constexpr int kGroups = N / 16;              // 16-code groups per row
-    constexpr int kLoaders = 2 * kTC * kGroups;  // 256 (d_state 128) or 128
-    const int ld_which = tid / (kTC * kGroups);  // 0: B, 1: C
-    const int ld_step = (tid / kGroups) % kTC;
-    const int ld_g = tid % kGroups;
-    const int8_t* __restrict__ ld_src = (ld_which ? A.cm : A.bm) + (int64_t)b * L * N + ld_g * 16;
+    // ---- B/C staging.  A loader owns kCodes = 16 (4 waves) or 8 (8 waves, so
+    //      that every thread takes a share) consecutive codes of B or C, one step
+    //      of a chunk, n = 16g + 8h ..: one load while the previous chunk runs,
+    //      kCodes/2 16-byte LDS stores of float64 pairs after it.  d_state 128:
+    //      the pair of lane l sits in slot bc_slot(l) of its row, which keeps
+    //      both the stores (writers of one step hit 8 different 16-byte columns
+    //      per instruction) and the step reads conflict-free.
+    constexpr int kGroups = N / 16;                 // 16-code groups per row
+    constexpr int kHalves = W == 8 ? 2 : 1;         // loaders per group
+    constexpr int kCodes = 16 / kHalves;
+    constexpr int kLoaders = 2 * kTC * kGroups * kHalves;  // <= 64 W
+    static_assert(kLoaders <= 64 * W, "one loader per thread at most");
+    const int ld_h = tid % kHalves;
+    const int ld_which = tid / (kTC * kGroups * kHalves);  // 0: B, 1: C
+    const int ld_step = (tid / (kGroups * kHalves)) % kTC;
+    const int ld_g = (tid / kHalves) % kGroups;
+    const int8_t* __restrict__ ld_src =
+        (ld_which ? A.cm : A.bm) + (int64_t)b * L * N + ld_g * 16 + ld_h * kCodes;
     int4 stg = make_int4(0, 0, 0, 0);
     // chunk c's codes into stg (rows past the end repeat the last row: unused)
     auto stage_load = [&](int64_t c) __attribute__((always_inline)) {
         if (tid < kLoaders) {
             const int64_t t = c * kTC + ld_step < L ? c * kTC + ld_step : L - 1;
-            stg = *reinterpret_cast<const int4*>(ld_src + (uint32_t)t * (uint32_t)N);
+            const int8_t* src = ld_src + (uint32_t)t * (uint32_t)N;
+            if constexpr (kCodes == 16) {
+                stg = *reinterpret_cast<const int4*>(src);
+            } else {
+                const int2 v = *reinterpret_cast<const int2*>(src);
+                stg = make_int4(v.x, v.y, 0, 0);
+            }
         }
     };
     // stg into LDS buffer `par`
@@ -187,9 +199,10 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
             double* row = &sm.bc[par][ld_step][ld_which * N];
             const int32_t wv[4] = {stg.x, stg.y, stg.z, stg.w};
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int32_t word = wv[q >> 1];
-                const int sh = (q & 1) * 16;
+            for (int k = 0; k < kCodes / 2; ++k) {
+                const int q = ld_h * (kCodes / 2) + k;  // pair q of the group
+                const int32_t word = wv[k >> 1];
+                const int sh = (k & 1) * 16;
                 const dpair v = {(double)(int8_t)(word >> sh), (double)(int8_t)(word >> (sh + 8))};
                 // codes 16g + 2q, +1: the pair of lane 8g + q (d_state 128)
                 const int slot = NN == 2 ? 8 * ld_g + ((q + ld_g) & 7) : 8 * ld_g + q;
