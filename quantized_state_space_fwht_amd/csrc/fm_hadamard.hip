@@ -175,45 +175,54 @@ fm_status hq_run(const float* x, int64_t rows, int64_t k, fm_scale_mode mode, in
 // A stack feeds each layer RMSNorm(h) (weight 1; the fixed summation order of
 // the gate's RMSNorm: 64 lane-strided partial sums in ascending order, then the
 // xor butterfly), rotated and quantized like any in_proj input.  Fused here so
-// the normalized rows never go to memory: one workgroup per row stages the row
-// in LDS, wave 0 forms r = 1 / sqrt(ss / d + 1e-5) (or reads the r that pass 1
-// stored), and the waves rotate the row's 256-blocks of (h_i * r) * 1.
+// the normalized rows never go to memory: a workgroup takes kNormRows rows,
+// two waves each; a row is staged in LDS, its first wave forms
+// r = 1 / sqrt(ss / d + 1e-5) (or reads the r that pass 1 stored), and the
+// row's two waves rotate its 256-blocks of (h_i * r) * 1.  Two rows per
+// workgroup keep twice the bytes in flight per CU for the same wave count.
 // Dynamic mode: pass 1 takes the rotated maximum into a slot region and stores
 // r per row; pass 2 reads h again and writes the codes (9 bytes per element in
 // all, against 17 for a separate normalization followed by the two passes).
 // Static mode: one pass.
-constexpr int kNormThreads = 256;
+constexpr int kNormRows = 2;
+constexpr int kNormWaves = 2;  // per row
+constexpr int kNormThreads = 64 * kNormWaves * kNormRows;
 
 template <bool kQuant>
 __global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
-    const float* __restrict__ h, int dm, float* __restrict__ rs, fm_scale_mode mode,
+    const float* __restrict__ h, int64_t rows, int dm, float* __restrict__ rs, fm_scale_mode mode,
     int32_t scoe, int32_t sshift, float* amax_ws, int32_t* amax_slots, char4* __restrict__ q,
     float* scale_out, float* amax_stats, fm_quant_stats* qs, int qpt) {
-    extern __shared__ __attribute__((aligned(16))) float row[];  // dm floats
-    __shared__ float r_s, c_s, wmax[kNormThreads / 64];
+    extern __shared__ __attribute__((aligned(16))) float rows_buf[];  // kNormRows x dm floats
+    __shared__ float r_s[kNormRows], c_s, wmax[kNormThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t r0 = blockIdx.x;
-    const float* hr = h + r0 * dm;
-    for (int i0 = tid * 4; i0 < dm; i0 += 4 * 4 * kNormThreads) {  // 4 loads in flight
+    const int sub = wave / kNormWaves, wv = wave % kNormWaves;  // row of the workgroup, wave in it
+    const int st = tid % (64 * kNormWaves);                     // thread within the row's waves
+    const int64_t r0 = blockIdx.x * (int64_t)kNormRows + sub;
+    const bool live = r0 < rows;  // the last workgroup's second row may lie past the end
+    float* row = rows_buf + sub * dm;
+    const float* hr = h + (live ? r0 : rows - 1) * dm;
+    constexpr int kRowThreads = 64 * kNormWaves;
+    for (int i0 = st * 4; i0 < dm; i0 += 4 * 4 * kRowThreads) {  // 4 loads in flight
         float4 v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int i = i0 + k * 4 * kNormThreads;
+            const int i = i0 + k * 4 * kRowThreads;
             v[k] = i < dm ? *reinterpret_cast<const float4*>(hr + i) : make_float4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int i = i0 + k * 4 * kNormThreads;
+            const int i = i0 + k * 4 * kRowThreads;
             if (i < dm) *reinterpret_cast<float4*>(row + i) = v[k];
         }
     }
     const bool have_r = kQuant && mode == FM_SCALE_DYNAMIC;  // pass 2 reads pass 1's r
     __syncthreads();
-    if (wave == 0) {
+    if (wv == 0) {
         float r;
         if (have_r) {
-            r = rs[r0];
+            r = live ? rs[r0] : 1.0f;
         } else {
             float a = 0.0f;
             for (int i = lane; i < dm; i += 64) {
@@ -223,29 +232,30 @@ __global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
             }
             const float ss = wave_sum_fixed(a);
             r = 1.0f / sqrtf(ss / (float)dm + 1e-5f);
-            if (!kQuant && lane == 0) rs[r0] = r;
+            if (!kQuant && live && lane == 0) rs[r0] = r;
         }
-        float c = 0.0f;
-        if constexpr (kQuant) {
+        if (lane == 0) r_s[sub] = r;
+    }
+    if constexpr (kQuant) {
+        if (wave == 0) {
             float amax = 0.0f;
             if (mode == FM_SCALE_DYNAMIC) amax = __int_as_float(slots_wave_max(amax_slots));
-            c = mode == FM_SCALE_DYNAMIC ? (amax == 0.0f ? 1.0f : 127.0f / amax)
-                                         : ldexpf((float)scoe, -sshift);
-            if (blockIdx.x == 0 && lane == 0) {
-                *scale_out = 1.0f / c;
-                if (mode == FM_SCALE_DYNAMIC) *amax_ws = amax;
+            const float c = mode == FM_SCALE_DYNAMIC ? (amax == 0.0f ? 1.0f : 127.0f / amax)
+                                                     : ldexpf((float)scoe, -sshift);
+            if (lane == 0) {
+                c_s = c;
+                if (blockIdx.x == 0) {
+                    *scale_out = 1.0f / c;
+                    if (mode == FM_SCALE_DYNAMIC) *amax_ws = amax;
+                }
             }
-        }
-        if (lane == 0) {
-            r_s = r;
-            c_s = c;
         }
     }
     __syncthreads();
-    const float r = r_s, c = c_s, s_dq = 1.0f / c;
+    const float r = r_s[sub], c = kQuant ? c_s : 0.0f, s_dq = kQuant ? 1.0f / c : 0.0f;
     float m = 0.0f;
-    QStat st;
-    for (int blk = wave; blk < dm / 256; blk += kNormThreads / 64) {
+    QStat stt;
+    for (int blk = wv; live && blk < dm / 256; blk += kNormWaves) {
         float4 v = *reinterpret_cast<const float4*>(row + blk * 256 + lane * 4);
         v.x = (v.x * r) * 1.0f;
         v.y = (v.y * r) * 1.0f;
@@ -255,15 +265,16 @@ __global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
         m = fmaxf(m, absmax4(v));
         if constexpr (kQuant) {
             q[(r0 * dm + blk * 256) / 4 + lane] = quant4(v, c);
-            if (qs) quant_stat4(st, v, c, s_dq);
+            if (qs) quant_stat4(stt, v, c, s_dq);
         }
     }
-    if (kQuant && qs) qstat_flush(st, qs, qpt);
+    if (kQuant && qs) qstat_flush(stt, qs, qpt);
     if (!kQuant || amax_stats) {
         m = wave_max_f32(m);
         if (lane == 0) wmax[wave] = m;
         __syncthreads();
         if (tid == 0) {
+            // rows past the end contribute 0; maxima are exact in any order
             for (int k = 1; k < kNormThreads / 64; ++k) m = fmaxf(m, wmax[k]);
             if constexpr (!kQuant) slot_max(amax_slots, blockIdx.x, (int32_t)__float_as_uint(m));
             else atomic_max_nonneg_f32(amax_stats, m);
@@ -276,16 +287,17 @@ fm_status norm_hq_run(const float* h, int64_t rows, int64_t dm, fm_scale_mode mo
                       float* amax_ws, int32_t* amax_slots, float* rs, hipStream_t s,
                       fm_quant_stats* qs, int qpt) {
     if (rows == 0) return FM_OK;
-    const size_t lds = (size_t)dm * sizeof(float);
+    const size_t lds = (size_t)kNormRows * dm * sizeof(float);
+    const unsigned grid = (unsigned)((rows + kNormRows - 1) / kNormRows);
     fm_status st;
     if (mode == FM_SCALE_DYNAMIC) {  // amax_slots must hold 0 (zeroed by the caller)
-        norm_hq_kernel<false><<<(unsigned)rows, kNormThreads, lds, s>>>(
-            h, (int)dm, rs, mode, scoe, sshift, amax_ws, amax_slots, nullptr, nullptr, nullptr,
-            nullptr, qpt);
+        norm_hq_kernel<false><<<grid, kNormThreads, lds, s>>>(
+            h, rows, (int)dm, rs, mode, scoe, sshift, amax_ws, amax_slots, nullptr, nullptr,
+            nullptr, nullptr, qpt);
         if ((st = check_launch("norm_hq_kernel(max)")) != FM_OK) return st;
     }
-    norm_hq_kernel<true><<<(unsigned)rows, kNormThreads, lds, s>>>(
-        h, (int)dm, mode == FM_SCALE_DYNAMIC ? rs : nullptr, mode, scoe, sshift, amax_ws,
+    norm_hq_kernel<true><<<grid, kNormThreads, lds, s>>>(
+        h, rows, (int)dm, mode == FM_SCALE_DYNAMIC ? rs : nullptr, mode, scoe, sshift, amax_ws,
         amax_slots, (char4*)q, scale_out, amax_stats, qs, qpt);
     return check_launch("norm_hq_kernel(codes)");
 }
