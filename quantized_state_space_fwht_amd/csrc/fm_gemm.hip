@@ -670,7 +670,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
             }
         }
     }
-    // the workgroup's maxima, then one atomic per quantity
+    // the workgroup's maxima, then one atomic per quantity (into a slot region
+    // where many workgroups would otherwise meet on one word)
     if (!kConv && !ep.amax && !ep.amax_slots) return;
     amax = wave_max_f32(amax);
     xmax = wave_max_f32(xmax);

@@ -155,8 +155,9 @@ fm_status quant_rows_run(const float* x, const float* rowmax, int64_t m, int64_t
 fm_status gemm_run(const int8_t* a, const int8_t* b, int64_t m, int64_t n, int64_t k,
                    const GemmEpilogue& ep, hipStream_t s);
 
-// conv: quantize xBC, conv, SiLU.  Dynamic: writes Q.16 activations to s16 and
-// accumulates part maxima into amax_q16[3]; static (p given): writes codes directly.
+// conv: quantize xBC, conv, SiLU.  Dynamic: hands the SiLU values to the requant
+// pass through s16 and the part maxima through slot regions (the requant pass
+// writes amax_q16[3] and the codes); static (p given): writes codes directly.
 struct ConvArgs {
     const float* xbc;
     int64_t xbc_stride;
