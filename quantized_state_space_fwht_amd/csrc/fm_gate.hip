@@ -38,9 +38,12 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row = blockIdx.x;
     const int D = (int)G.d_inner;
-    // the norm weights of this wave's first 256-block, loaded ahead of phase 1
-    const float4 w_first = wave < D / 256 ? reinterpret_cast<const float4*>(G.norm_w)[wave * 64 + lane]
-                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    // one-token form (few rows, latency-bound): the norm weights of this wave's
+    // first 256-block, loaded ahead of phase 1.  With many rows the workgroups
+    // fill the wave slots and the longer-held registers cost more than this hides.
+    constexpr bool kAhead = W == kGateStepWaves;
+    float4 w_first = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (kAhead && wave < D / 256) w_first = reinterpret_cast<const float4*>(G.norm_w)[wave * 64 + lane];
     const float ysc = ldexpf(1.0f, -(G.p[1] + 8));
     const int32_t* yr = G.y + row * D;
     const float* zr = G.sz ? G.sz + row * D : G.z + row * G.z_stride;
@@ -109,8 +112,8 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     for (int blk = wave; blk < D / 256; blk += W) {
         const int base = blk * 256 + lane * 4;
         float4 g = *reinterpret_cast<const float4*>(&row_buf[base]);
-        const float4 w =
-            blk == wave ? w_first : *reinterpret_cast<const float4*>(&G.norm_w[base]);
+        const float4 w = kAhead && blk == wave ? w_first
+                                                : *reinterpret_cast<const float4*>(&G.norm_w[base]);
         float4 n;
         n.x = (g.x * r) * w.x;
         n.y = (g.y * r) * w.y;
