@@ -150,7 +150,15 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
     const int ky = A.p[2] + A.p[3];
     const double dq = (double)A.d_q16[head];
     const int i16 = lane & 15;
-    const int64_t nchunks = (L + kTC - 1) / kTC;
+    // 32-bit positions: the host keeps batch*len*nheads*headdim and batch*len*dstate
+    // below 2^31
+    const int L32 = (int)L;
+    const int nchunks = (L32 + kTC - 1) / kTC;
+    // index of (b, t = 0, head) in [B, L, H] and of (b, 0, head, p0) in [B, L, H, P];
+    // step t adds t*H, t*H*P
+    const uint32_t qb = ((uint32_t)b * (uint32_t)L32) * (uint32_t)H + (uint32_t)head;
+    const uint32_t xb = qb * (uint32_t)P + (uint32_t)p0;
+    const uint32_t HP = (uint32_t)H * (uint32_t)P;
 
     // states h of (p0 + r, NN*lane + j)
     double h[2][NN];
@@ -181,9 +189,9 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
         (ld_which ? A.cm : A.bm) + (int64_t)b * L * N + ld_g * 16 + ld_h * kCodes;
     int4 stg = make_int4(0, 0, 0, 0);
     // chunk c's codes into stg (rows past the end repeat the last row: unused)
-    auto stage_load = [&](int64_t c) __attribute__((always_inline)) {
+    auto stage_load = [&](int c) __attribute__((always_inline)) {
         if (tid < kLoaders) {
-            const int64_t t = c * kTC + ld_step < L ? c * kTC + ld_step : L - 1;
+            const int t = c * kTC + ld_step < L32 ? c * kTC + ld_step : L32 - 1;
             const int8_t* src = ld_src + (uint32_t)t * (uint32_t)N;
             if constexpr (kCodes == 16) {
                 stg = *reinterpret_cast<const int4*>(src);
@@ -215,12 +223,12 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
     // ---- per-step scalars: lane i of every row holds step 16c + i of chunk c
     int32_t pf_dt = 0, pf_da = 0;
     uint32_t pf_x = 0;
-    auto prefetch = [&](int64_t c) __attribute__((always_inline)) {
-        const int64_t t = c * kTC + i16 < L ? c * kTC + i16 : L - 1;  // past the end: unused
-        const uint32_t q = ((uint32_t)b * (uint32_t)L + (uint32_t)t) * (uint32_t)H + head;
+    auto prefetch = [&](int c) __attribute__((always_inline)) {
+        const int t = c * kTC + i16 < L32 ? c * kTC + i16 : L32 - 1;  // past the end: unused
+        const uint32_t q = qb + (uint32_t)t * (uint32_t)H;
         pf_dt = A.dt_out[q];
         pf_da = A.da_out[q];
-        pf_x = *reinterpret_cast<const uint16_t*>(A.x + (q * (uint32_t)P + p0));
+        pf_x = *reinterpret_cast<const uint16_t*>(A.x + (xb + (uint32_t)t * HP));
     };
     // scalars of the chunk about to run
     double uda = 0.0, uu0 = 0.0, uu1 = 0.0;
@@ -237,12 +245,14 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
     auto needs_clamp = [&]() __attribute__((always_inline)) {
         const float e = (float)__builtin_fma(
             __builtin_fmax(__builtin_fabs(uu0), __builtin_fabs(uu1)), 127.0, 1.5);
-        const double S = (double)row_sum16(e) * (1.0 + 0x1p-16) + 16.0;
-        double hm = 0.0;
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int j = 0; j < NN; ++j) hm = __builtin_fmax(hm, __builtin_fabs(h[r][j]));
+        // the float sum's rounding covered by the factor, the floors' 1 per step by 16
+        const double S = __builtin_fma((double)row_sum16(e), 1.0 + 0x1p-16, 16.0);
+        double hm;
+        if constexpr (NN == 2)
+            hm = __builtin_fmax(__builtin_fmax(__builtin_fabs(h[0][0]), __builtin_fabs(h[0][1])),
+                                __builtin_fmax(__builtin_fabs(h[1][0]), __builtin_fabs(h[1][1])));
+        else
+            hm = __builtin_fmax(__builtin_fabs(h[0][0]), __builtin_fabs(h[1][0]));
         return __any(hm + S > 2147483646.0);
     };
     // partial sums of the chunk just run -> y codes; lane l < 16 returns (y of
@@ -269,13 +279,9 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
         return make_int2(yi, (int32_t)sw[1]);
     };
     // y of chunk c from reduce(): lanes 0..15, one step each
-    auto write_y = [&](int64_t c, int2 yy) __attribute__((always_inline)) {
-        const int tcc = (int)(L - c * kTC < kTC ? L - c * kTC : kTC);
-        if (lane < tcc) {
-            int32_t* dst = A.y + (((uint32_t)b * (uint32_t)L + (uint32_t)(c * kTC + lane)) *
-                                      (uint32_t)H + head) * (uint32_t)P + p0;
-            *reinterpret_cast<int2*>(dst) = yy;
-        }
+    auto write_y = [&](int c, int2 yy) __attribute__((always_inline)) {
+        if (lane < kTC && c * kTC + lane < L32)
+            *reinterpret_cast<int2*>(A.y + (xb + (uint32_t)(c * kTC + lane) * HP)) = yy;
     };
 
     stage_load(0);
@@ -283,9 +289,9 @@ __global__ __launch_bounds__(64 * W) void scan_kernel(ScanArgs A) {
     stage_store(0);
     __syncthreads();
 
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int par = NBUF == 2 ? (int)(c & 1) : 0;
-        const int tc = (int)(L - c * kTC < kTC ? L - c * kTC : kTC);
+    for (int c = 0; c < nchunks; ++c) {
+        const int par = NBUF == 2 ? (c & 1) : 0;
+        const int tc = L32 - c * kTC < kTC ? L32 - c * kTC : kTC;
         setup();  // this chunk's scalars
         const bool more = c + 1 < nchunks;
         if (more) {  // next chunk in flight
