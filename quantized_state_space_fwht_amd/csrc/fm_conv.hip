@@ -106,8 +106,8 @@ __device__ __forceinline__ void conv_run_steps(const ConvKParams& K, const NauLd
         if constexpr (kXq) xq_out[(uint32_t)i * (uint32_t)K.ch] = (int8_t)xq;
         // int8 x int8 products: 24-bit multiplies (full rate; 32-bit ones are not)
         const int32_t acc = __mul24(w0, xm3) + __mul24(w1, xm2) + __mul24(w2, xm1) + __mul24(w3, xq);
-        const int32_t a = round_sat32(__builtin_fma((double)acc, ascale, bias));
-        const int32_t sv = nau_silu_f(a, tab);
+        const double a = round_sat_d(__builtin_fma((double)acc, ascale, bias));
+        const int32_t sv = (int32_t)nau_silu_d(a, tab);
         const int32_t sa = sv < 0 ? -sv : sv;
         amax = sa > amax ? sa : amax;
         if constexpr (kHold) {

@@ -77,11 +77,13 @@ __device__ __forceinline__ int32_t quant_xbc(float v, float scale) {
     return (int32_t)fminf(fmaxf(rintf(v * scale), -127.0f), 127.0f);
 }
 
-// clamp(floor(v + 1/2)) to int32 for an integer-valued or half-step v
-__device__ __forceinline__ int32_t round_sat32(double v) {
-    return (int32_t)__builtin_fmin(__builtin_fmax(__builtin_floor(v + 0.5), -2147483648.0),
-                                   2147483647.0);
+// clamp(floor(v + 1/2)) to the int32 range for an integer-valued or half-step
+// v, as float64 and as int32
+__device__ __forceinline__ double round_sat_d(double v) {
+    return __builtin_fmin(__builtin_fmax(__builtin_floor(v + 0.5), -2147483648.0), 2147483647.0);
 }
+
+__device__ __forceinline__ int32_t round_sat32(double v) { return (int32_t)round_sat_d(v); }
 
 // ---------------------------------------------------------------- NAU
 // Chord endpoints Y_i = rint(2^(i/8) * 2^30), i = 0..8.
@@ -109,57 +111,85 @@ constexpr int64_t kLog2eQ30 = 1549082005LL;  // rint(log2(e) * 2^30)
 // vector rate on MI355X, where 64-bit integer multiplies and shifts are not).
 // Every product below stays under 2^53 wherever the result is not already
 // known to be 0, so each floor() sees the exact rational value and the results
-// equal the integer definitions.  The 9 chord endpoints live in LDS
-// (nau_lds_init, then a barrier before first use).
+// equal the integer definitions.  The chords live in LDS as pairs
+// (Y[i], (Y[i+1] - Y[i]) * 2^-13), one 16-byte read per evaluation
+// (nau_lds_init or nau_lds_set, then a barrier before first use).
 struct NauLds {
-    double y[9];
+    struct alignas(16) Chord {
+        double y, d;
+    } c[8];
 };
 
-__device__ __forceinline__ void nau_lds_init(NauLds& t) {
-    if (threadIdx.x < 9) t.y[threadIdx.x] = (double)exp2_knot(threadIdx.x);
+__device__ __forceinline__ void nau_lds_set(NauLds& t, int i, int64_t y0, int64_t y1) {
+    t.c[i].y = (double)y0;
+    t.c[i].d = (double)(y1 - y0) * 0x1p-13;  // exact: |y1 - y0| < 2^53
 }
 
-// e^(x/2^16) in Q.16 for -2^31 <= x <= 0.  Branch-free: below v = -18*2^16
-// the Q.30 mantissa is shifted right by >= 32 and rounds to 0, so v is clamped
-// there (the product is exact wherever v >= -17*2^16, |x * log2e| < 2^51).
-__device__ __forceinline__ int32_t nau_exp_f(int32_t x, const NauLds& t) {
-    double vf = __builtin_floor(__builtin_fma((double)x, (double)kLog2eQ30, 0x1p29) * 0x1p-30);
-    // arguments > 0 (outside the unit's domain) are taken as 0
-    vf = __builtin_fmin(__builtin_fmax(vf, -1179648.0), 0.0);
+__device__ __forceinline__ void nau_lds_init(NauLds& t) {
+    if (threadIdx.x < 8) nau_lds_set(t, threadIdx.x, exp2_knot(threadIdx.x), exp2_knot(threadIdx.x + 1));
+}
+
+// 2^(v/2^16) in Q.16 for an integer-valued vf in [-18*2^16, 0].  Below
+// v = -18*2^16 the Q.30 mantissa is shifted right by >= 32 and rounds to 0.
+__device__ __forceinline__ double nau_exp2_d(double vf, const NauLds& t) {
     const int v = (int)vf;
     const int n = v >> 16;  // -18..0
-    const int f = v & 0xFFFF;
-    const int seg = f >> 13;
-    const double r = (double)(f & 0x1FFF);
-    const double y0 = t.y[seg], y1 = t.y[seg + 1];
+    const int seg = (v >> 13) & 7;
+    const double r = (double)(v & 0x1FFF);
+    const NauLds::Chord ch = t.c[seg];
     // m = Y[seg] + rshr((Y[seg+1] - Y[seg]) * r, 13): the product is below 2^41
-    const double m = y0 + __builtin_floor(__builtin_fma(y1 - y0, r, 0x1p12) * 0x1p-13);
+    const double m = ch.y + __builtin_floor(__builtin_fma(ch.d, r, 0.5));
     // rshr(m, 14 - n): m * 2^(n-14) + 1/2 spans at most 50 bits
-    return (int)__builtin_floor(__builtin_fma(m, __builtin_ldexp(1.0, n - 14), 0.5));
+    return __builtin_floor(__builtin_ldexp(m, n - 14) + 0.5);
+}
+
+// e^(x/2^16) in Q.16 for an integer-valued xd in [-2^31, 0].  The argument
+// v = rshr(x * kLog2eQ30, 30) is exact while |x| < 2^22 (x * kLog2eQ30 < 2^53);
+// beyond, v lies far below the clamp at -18*2^16 whatever the rounding.
+__device__ __forceinline__ double nau_exp_d(double xd, const NauLds& t) {
+    constexpr double kL = (double)kLog2eQ30 * 0x1p-30;  // exact
+    const double vf = __builtin_fmax(__builtin_floor(__builtin_fma(xd, kL, 0.5)), -1179648.0);
+    return nau_exp2_d(vf, t);
+}
+
+// e^(x/2^16) in Q.16; arguments > 0 (outside the unit's domain) are taken as 0.
+__device__ __forceinline__ int32_t nau_exp_f(int32_t x, const NauLds& t) {
+    return (int32_t)nau_exp_d(__builtin_fmin((double)x, 0.0), t);
 }
 
 // SoftPlus in Q.16: e^-|x| + max(x, 0) (Eq. (5) for x <= 0, the symmetry above).
 __device__ __forceinline__ int32_t nau_softplus_f(int32_t x, const NauLds& t) {
-    const int32_t xn = x < 0 ? x : -x;  // -|x| (no overflow for INT32_MIN)
-    const int64_t e = nau_exp_f(xn, t);
-    return sat32(e + (x > 0 ? (int64_t)x : 0));
+    const double xd = (double)x;
+    const double e = nau_exp_d(-__builtin_fabs(xd), t);
+    return (int32_t)__builtin_fmin(e + __builtin_fmax(xd, 0.0), 2147483647.0);  // sat32
 }
 
-// SiLU in Q.16: for x <= 0, sigma = floor(E*2^16 / (2^16 + E)), E = e^x,
-// SiLU = rshr(x * sigma, 16); for x > 0, x + SiLU(-x).  Branch-free (E = 2^16
-// gives sigma = 2^15 through the same division).
-__device__ __forceinline__ int32_t nau_silu_f(int32_t x, const NauLds& t) {
-    const int32_t xn = x < 0 ? x : -x;
-    const int32_t e = nau_exp_f(xn, t);  // [0, 2^16]
-    // quotient <= 2^15: a float32 reciprocal puts floor() within 1 of it, and
-    // the exact remainder a - q*b (integers below 2^34) corrects it
-    const double a = (double)e * 65536.0, b = 65536.0 + (double)e;
-    double q = __builtin_floor(a * (double)__builtin_amdgcn_rcpf((float)b));
-    const double rem = __builtin_fma(-q, b, a);
-    q = rem < 0.0 ? q - 1.0 : (rem >= b ? q + 1.0 : q);
+// SiLU in Q.16 of an integer-valued xd in [-2^31, 2^31) (as float64): for
+// x <= 0, sigma = floor(E*2^16 / (2^16 + E)), E = e^x, SiLU = rshr(x * sigma, 16);
+// for x > 0, x + SiLU(-x).  The quotient is E / b with b = 1 + E*2^-16 in
+// [1, 2]: the hardware reciprocal of b (relative error near 2^-23) refined by
+// one Newton step is within 2^-44 of 1/b, so E / b + 2^-20 lies at or above the
+// quotient and below the next integer, whose distance from it is at least
+// 1 / (2^16 + E) >= 2^-17; floor() gives sigma.  E = 2^16 gives 2^15.
+__device__ __forceinline__ double nau_silu_d(double xd, const NauLds& t) {
+    const double xn = -__builtin_fabs(xd);
+    const double e = nau_exp_d(xn, t);  // [0, 2^16]
+    const double b = __builtin_fma(e, 0x1p-16, 1.0);
+    const double r0 = __builtin_amdgcn_rcp(b);
+    const double r1 = __builtin_fma(r0, __builtin_fma(-b, r0, 1.0), r0);
+    const double sig = __builtin_floor(__builtin_fma(e, r1, 0x1p-20));
     // rshr(xn * sigma, 16): |xn * sigma| < 2^46
-    const int32_t sn = (int32_t)__builtin_floor(__builtin_fma((double)xn, q * 0x1p-16, 0.5));
-    return x > 0 ? x + sn : sn;
+    const double sn = __builtin_floor(__builtin_fma(xn * 0x1p-16, sig, 0.5));
+    return sn + __builtin_fmax(xd, 0.0);
+}
+
+__device__ __forceinline__ int32_t nau_silu_f(int32_t x, const NauLds& t) {
+    return (int32_t)nau_silu_d((double)x, t);
+}
+
+// rint()ed float32 -> int32 with saturation, as an integer-valued float64
+__device__ __forceinline__ double f2d_sat(float f) {
+    return __builtin_fmin(__builtin_fmax((double)f, -2147483648.0), 2147483647.0);
 }
 
 // ---------------------------------------------------------------- 256-point FWHT

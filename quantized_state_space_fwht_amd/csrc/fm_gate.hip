@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
             if (i < D) {
                 const float yf = (float)yv[k] * ysc;
                 float sz = zv[k];
-                if (!G.sz) sz = (float)nau_silu_f(f2i_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
+                if (!G.sz) sz = (float)nau_silu_d(f2d_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
                 row_buf[i] = yf * sz;
             }
         }

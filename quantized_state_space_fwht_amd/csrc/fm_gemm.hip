@@ -621,8 +621,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
                 if (ep.xbc_q) ep.xbc_q[row * ch + cx] = (int8_t)xq;
                 const int32_t acc4 = __mul24(w0, xm3) + __mul24(w1, xm2) + __mul24(w2, xm1) +
                                      __mul24(w3, xq);  // int8 products: 24-bit multiplies
-                const int32_t a = round_sat32(__builtin_fma((double)acc4, ascale, (double)xb[k]));
-                const int32_t sv = nau_silu_f(a, tab);
+                const double a = round_sat_d(__builtin_fma((double)acc4, ascale, (double)xb[k]));
+                const int32_t sv = (int32_t)nau_silu_d(a, tab);
                 const int32_t sa = sv < 0 ? -sv : sv;
                 pmax[part_i] = sa > pmax[part_i] ? sa : pmax[part_i];
                 // sat8(rshr(sv, 16 - p_part)): sv * 2^(p_part-16) is exact in float64
@@ -642,8 +642,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_i8_few_rows_kernel(GemmParams P)
             if (ok) {
                 const float o = (float)v * sab;
                 if (ep.write_xbc) ep.out[row * ep.ld_out + col] = o;
-                const int32_t zq = f2i_sat(rintf(o * 65536.0f));
-                ep.sz_out[row * di + col] = (float)nau_silu_f(zq, tab) * 0x1p-16f;
+                const double zq = f2d_sat(rintf(o * 65536.0f));
+                ep.sz_out[row * di + col] = (float)nau_silu_d(zq, tab) * 0x1p-16f;
             }
             continue;
         }

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void nau_eval_kernel(int fn, const int32_t* __
                                                        NauKnots kn) {
     __shared__ NauLds tab;
     if (kn.use) {
-        if (threadIdx.x < 9) tab.y[threadIdx.x] = (double)kn.y[threadIdx.x];
+        if (threadIdx.x < 8) nau_lds_set(tab, threadIdx.x, kn.y[threadIdx.x], kn.y[threadIdx.x + 1]);
     } else {
         nau_lds_init(tab);
     }
