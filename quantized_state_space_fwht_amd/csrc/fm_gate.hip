@@ -8,6 +8,8 @@
 // k = 32..1), because the normed values become int8 codes and a different
 // rounding could flip one.  The row is staged in LDS and re-read in the
 // 4-per-lane layout of the 256-point transform.
+#include <type_traits>
+
 #include "fm_internal.hpp"
 
 namespace fm {
@@ -15,7 +17,7 @@ namespace fm {
 constexpr int kGateMaxD = 8192;
 constexpr int kGateWaves = 4;     // many rows: a workgroup of 4 waves per row
 constexpr int kGateStepWaves = 16;  // one-token step (few rows): 16 waves per row
-constexpr int kGatePer = 8;       // gate values per thread whose loads go out together
+constexpr int kGatePer = 10;      // gate values per thread whose loads go out together
 
 // One workgroup of W waves per row.  Phase 1: every thread computes gate
 // values g_i (any split: each is independent) into LDS.  Phase 2: wave 0
@@ -47,27 +49,34 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     const float ysc = ldexpf(1.0f, -(G.p[1] + 8));
     const int32_t* yr = G.y + row * D;
     const float* zr = G.sz ? G.sz + row * D : G.z + row * G.z_stride;
-    // phase 1: kGatePer elements per thread per round, loads of a round issued together
-    for (int i0 = tid; i0 < D; i0 += kGatePer * 64 * W) {
+    // phase 1: kGatePer elements per thread per round, loads of a round issued
+    // together; rounds wholly inside the row (D is a multiple of 256, so a round
+    // is whole for every thread or for none) run without per-element guards
+    auto gate_round = [&](int i0, auto guarded) __attribute__((always_inline)) {
+        constexpr bool kG = decltype(guarded)::value;
         int32_t yv[kGatePer];
         float zv[kGatePer];
 #pragma unroll
         for (int k = 0; k < kGatePer; ++k) {
             const int i = i0 + 64 * W * k;
-            yv[k] = i < D ? yr[i] : 0;
-            zv[k] = i < D ? zr[i] : 0.0f;
+            yv[k] = !kG || i < D ? yr[i] : 0;
+            zv[k] = !kG || i < D ? zr[i] : 0.0f;
         }
 #pragma unroll
         for (int k = 0; k < kGatePer; ++k) {
             const int i = i0 + 64 * W * k;
-            if (i < D) {
+            if (!kG || i < D) {
                 const float yf = (float)yv[k] * ysc;
                 float sz = zv[k];
                 if (!G.sz) sz = (float)nau_silu_d(f2d_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
                 row_buf[i] = yf * sz;
             }
         }
-    }
+    };
+    constexpr int kRound = kGatePer * 64 * W;
+    int i0 = tid;
+    for (; i0 - tid + kRound <= D; i0 += kRound) gate_round(i0, std::false_type{});
+    if (i0 < D) gate_round(i0, std::true_type{});
     __syncthreads();
     if (G.step_small && row == 0 && wave == W - 1) {
         // while wave 0 sums: the in_proj epilogue's slotted maxima into the call's

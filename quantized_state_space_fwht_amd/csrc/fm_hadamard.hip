@@ -204,15 +204,16 @@ __global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
     float* row = rows_buf + sub * dm;
     const float* hr = h + (live ? r0 : rows - 1) * dm;
     constexpr int kRowThreads = 64 * kNormWaves;
-    for (int i0 = st * 4; i0 < dm; i0 += 4 * 4 * kRowThreads) {  // 4 loads in flight
-        float4 v[4];
+    constexpr int kLd = 8;  // loads in flight per thread: rows up to 4096 floats in one round
+    for (int i0 = st * 4; i0 < dm; i0 += 4 * kLd * kRowThreads) {
+        float4 v[kLd];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kLd; ++k) {
             const int i = i0 + k * 4 * kRowThreads;
             v[k] = i < dm ? *reinterpret_cast<const float4*>(hr + i) : make_float4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kLd; ++k) {
             const int i = i0 + k * 4 * kRowThreads;
             if (i < dm) *reinterpret_cast<float4*>(row + i) = v[k];
         }
