@@ -225,15 +225,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(ConvKParams K) 
         // in the table after them (one byte per wave block: 16 steps x 64 channels)
         const int e = amax == 0 ? kPMax : pot_from_q16(amax);
         int16_t* out = reinterpret_cast<int16_t*>(A.s16) + row0 * K.ch + c;
+        // floor(v * 2^(e - 15)): e <= 24, so a left shift moves at most 9 bits
+        // (|result| <= 255); right shifts floor, 31 places at most
+        const int ls = e >= 15 ? e - 15 : 0, rs = e >= 15 ? 0 : (15 - e < 31 ? 15 - e : 31);
+        auto word = [&](int i) { return (int16_t)((sv[i] << ls) >> rs); };
+        if (n == kConvTL) {
 #pragma unroll
-        for (int i = 0; i < kConvTL; ++i) {
-            if (i < n) {
-                const int32_t v = sv[i];
-                // floor(v * 2^(e - 15)): e <= 24, so a left shift moves at most 9
-                // bits (|result| <= 255); right shifts floor, 31 places at most
-                const int32_t t = e >= 15 ? v << (e - 15) : v >> (15 - e < 31 ? 15 - e : 31);
-                out[(uint32_t)i * (uint32_t)K.ch] = (int16_t)t;
-            }
+            for (int i = 0; i < kConvTL; ++i) out[(uint32_t)i * (uint32_t)K.ch] = word(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kConvTL; ++i)
+                if (i < n) out[(uint32_t)i * (uint32_t)K.ch] = word(i);
         }
         if (lane == 0)
             conv_pblk(A, K.ch)[tb * (K.ch / 64) + blockIdx.x] = (int8_t)e;

@@ -94,17 +94,28 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     }
     // phase 2: the fixed-order sum of squares
     if (wave == 0) {
+        // ascending i within this lane (the fixed order): groups of 16 steps of
+        // 64, then the rest in groups of 4 (D % 256 == 0), no per-element guards
         float a = 0.0f;
-        for (int i0 = lane; i0 < D; i0 += 16 * 64) {  // D % 256 == 0: 4 steps at least
+        int i0 = lane;
+        for (; i0 - lane + 16 * 64 <= D; i0 += 16 * 64) {
             float g[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) g[k] = i0 + 64 * k < D ? row_buf[i0 + 64 * k] : 0.0f;
+            for (int k = 0; k < 16; ++k) g[k] = row_buf[i0 + 64 * k];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                if (i0 + 64 * k < D) {
-                    const float g2 = g[k] * g[k];
-                    a = a + g2;  // ascending i within this lane: the fixed order
-                }
+                const float g2 = g[k] * g[k];
+                a = a + g2;
+            }
+        }
+        for (; i0 < D; i0 += 4 * 64) {
+            float g[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) g[k] = row_buf[i0 + 64 * k];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float g2 = g[k] * g[k];
+                a = a + g2;
             }
         }
         const float ss = wave_sum_fixed(a);
