@@ -51,9 +51,11 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     const float* zr = G.sz ? G.sz + row * D : G.z + row * G.z_stride;
     // phase 1: kGatePer elements per thread per round, loads of a round issued
     // together; rounds wholly inside the row (D is a multiple of 256, so a round
-    // is whole for every thread or for none) run without per-element guards
-    auto gate_round = [&](int i0, auto guarded) __attribute__((always_inline)) {
-        constexpr bool kG = decltype(guarded)::value;
+    // is whole for every thread or for none) run without per-element guards, and
+    // whether SiLU(z) is formed here is decided once, so a round is straight-line
+    // code whose independent SiLU chains interleave
+    auto gate_round = [&](int i0, auto guarded, auto silu) __attribute__((always_inline)) {
+        constexpr bool kG = decltype(guarded)::value, kSilu = decltype(silu)::value;
         int32_t yv[kGatePer];
         float zv[kGatePer];
 #pragma unroll
@@ -68,15 +70,19 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
             if (!kG || i < D) {
                 const float yf = (float)yv[k] * ysc;
                 float sz = zv[k];
-                if (!G.sz) sz = (float)nau_silu_d(f2d_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
+                if constexpr (kSilu) sz = (float)nau_silu_d(f2d_sat(rintf(sz * 65536.0f)), tab) * 0x1p-16f;
                 row_buf[i] = yf * sz;
             }
         }
     };
     constexpr int kRound = kGatePer * 64 * W;
-    int i0 = tid;
-    for (; i0 - tid + kRound <= D; i0 += kRound) gate_round(i0, std::false_type{});
-    if (i0 < D) gate_round(i0, std::true_type{});
+    auto phase1 = [&](auto silu) __attribute__((always_inline)) {
+        int i0 = tid;
+        for (; i0 - tid + kRound <= D; i0 += kRound) gate_round(i0, std::false_type{}, silu);
+        if (i0 < D) gate_round(i0, std::true_type{}, silu);
+    };
+    if (G.sz) phase1(std::false_type{});
+    else phase1(std::true_type{});
     __syncthreads();
     if (G.step_small && row == 0 && wave == W - 1) {
         // while wave 0 sums: the in_proj epilogue's slotted maxima into the call's
