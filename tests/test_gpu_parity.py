@@ -504,6 +504,25 @@ def test_static_stack_calibration_and_prefill(B):
     assert np.array_equal(np.stack(outs, axis=1), h_o[:, L0:]), "continuation"
 
 
+@pytest.mark.parametrize("batch,seqlen", [(1, 37), (1, 2201)])
+def test_dynamic_stack_prenorm_rows(B, batch, seqlen):
+    """Dynamic-mode stack whose pre-norm passes see an odd row count (the last
+    row pair half empty) and, at 2201 rows, more row pairs than resident
+    workgroups (each workgroup loops over pairs): bit-exact against the oracle."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Stack
+    w = configs.with_len(configs.get("tiny_layer"), batch=batch, seqlen=seqlen)
+    s = w.shape
+    params = [synth.workload_params(w, l) for l in range(2)]
+    u = synth.workload_activations(w, seed=300)
+    preps = [O.prepare_layer(p) for p in params]
+    h_o, caches_o, _ = O.stack_prefill(preps, s, u, "dynamic")
+    stack = Mamba2Stack(s, params)
+    h = stack.prefill(dev(u))
+    assert np.array_equal(host(h), h_o), "dynamic stack output"
+    for layer, c in zip(stack.layers, caches_o):
+        assert_exact(host(layer.cache_t["ssm_state"]), c["ssm_state"], "stack state")
+
+
 @pytest.mark.parametrize("fit", ["lsq", "minimax"])
 @pytest.mark.parametrize("fn", ["exp", "softplus", "silu"])
 def test_nau_other_knot_tables(B, fn, fit):
