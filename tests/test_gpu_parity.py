@@ -275,7 +275,10 @@ def _device_conv_prep(B, s, params, t_wq, t_pw, t_bq):
                                                       ("m130m_layer", 2, 37, None),
                                                       ("m130m_layer", 16, 40, None),
                                                       ("tiny_layer", 5, 20, None),
-                                                      ("tiny_layer", 64, 20, None)])
+                                                      ("tiny_layer", 64, 20, None),
+                                                      # one row per wave at up to two
+                                                      # workgroups per CU, d_state 64
+                                                      ("tiny_layer", 3, 45, None)])
 @pytest.mark.parametrize("with_state", [False, True])
 def test_ssm_scan_pot(B, wname, batch, length, heads, with_state):
     s = configs.get(wname).shape
@@ -337,11 +340,13 @@ def test_ssm_scan_saturates_like_the_oracle(B):
     assert_exact(host(t_st), st, "state (saturating)")
 
 
-def test_ssm_scan_mixed_saturation(B):
+@pytest.mark.parametrize("batch", [1, 80, 160])
+def test_ssm_scan_mixed_saturation(B, batch):
     """Some states reach the int32 clamp part-way through a long sequence (decay
     exactly 1, B and x of one sign) while others stay small: chunks before and
-    after the crossing, and workgroups that never get near it, must all agree."""
-    batch, length, H, P, N = 1, 181, 2, 16, 128
+    after the crossing, and workgroups that never get near it, must all agree.
+    Batches 1, 80 and 160 take the one-row, the 4-wave and the 8-wave layouts."""
+    length, H, P, N = 181, 2, 16, 128
     rng = np.random.default_rng(11)
     x = rng.integers(-127, 128, size=(batch, length, H, P)).astype(np.int8)
     x[:, :, 1, :8] = 127                        # head 1, first 8 p: one sign
