@@ -125,6 +125,24 @@ def test_m130m_layer_full_size_as_benchmarked(B):
 
 
 # ----------------------------------------------------------------- m2p7b_stack
+def test_m2p7b_layer_ragged_rows_large_product(B):
+    """A 2.7B pre-norm layer over 1 x 3228 rows: the in_proj product takes the
+    large-product kernel (13 x 83 tiles of 256 x 128, over four per CU) with a
+    partial last row tile, whose z columns go through the epilogue's SiLU one
+    element at a time; bit-exact against the oracle."""
+    from quantized_state_space_fwht_amd.runtime import Mamba2Layer
+    w = configs.with_len(configs.get("m2p7b_stack"), batch=1, seqlen=3228)
+    s = w.shape
+    params = synth.workload_params(w, 0)
+    u = synth.workload_activations(w)
+    out_o, r, cache_o, st_o = O.layer_prefill(O.prepare_layer(params), s, prenorm(u),
+                                              scan=ssm_scan_pot_c)
+    layer = Mamba2Layer(s, params, prenorm_residual=True)
+    h = layer.prefill(dev(u))
+    assert_same_float(host(h), u + out_o, "layer output")
+    check_caches_and_record(layer, cache_o, r, st_o)
+
+
 def test_m2p7b_stack_first_layers_chained_full_size(B):
     """Layers 0, 1, 2 of the 2.7B stack at 4 x 4096, chained: the oracle runs the
     three layers itself (layer 0 on the input, each next layer on its own output)."""
