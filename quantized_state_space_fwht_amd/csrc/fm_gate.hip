@@ -17,7 +17,9 @@ namespace fm {
 constexpr int kGateMaxD = 8192;
 constexpr int kGateWaves = 4;     // many rows: a workgroup of 4 waves per row
 constexpr int kGateStepWaves = 16;  // one-token step (few rows): 16 waves per row
-constexpr int kGatePer = 10;      // gate values per thread whose loads go out together
+// gate values per thread whose loads go out together: a round of 4 waves covers
+// 2560 values, one of 16 waves 5120 (whole rounds at d_inner 5120 either way)
+template <int W> constexpr int kGatePer = W == kGateStepWaves ? 5 : 10;
 
 // One workgroup of W waves per row.  Phase 1: every thread computes gate
 // values g_i (any split: each is independent) into LDS.  Phase 2: wave 0
@@ -56,16 +58,16 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     // code whose independent SiLU chains interleave
     auto gate_round = [&](int i0, auto guarded, auto silu) __attribute__((always_inline)) {
         constexpr bool kG = decltype(guarded)::value, kSilu = decltype(silu)::value;
-        int32_t yv[kGatePer];
-        float zv[kGatePer];
+        int32_t yv[kGatePer<W>];
+        float zv[kGatePer<W>];
 #pragma unroll
-        for (int k = 0; k < kGatePer; ++k) {
+        for (int k = 0; k < kGatePer<W>; ++k) {
             const int i = i0 + 64 * W * k;
             yv[k] = !kG || i < D ? yr[i] : 0;
             zv[k] = !kG || i < D ? zr[i] : 0.0f;
         }
 #pragma unroll
-        for (int k = 0; k < kGatePer; ++k) {
+        for (int k = 0; k < kGatePer<W>; ++k) {
             const int i = i0 + 64 * W * k;
             if (!kG || i < D) {
                 const float yf = (float)yv[k] * ysc;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
             }
         }
     };
-    constexpr int kRound = kGatePer * 64 * W;
+    constexpr int kRound = kGatePer<W> * 64 * W;
     auto phase1 = [&](auto silu) __attribute__((always_inline)) {
         int i0 = tid;
         for (; i0 - tid + kRound <= D; i0 += kRound) gate_round(i0, std::false_type{}, silu);

@@ -162,17 +162,28 @@ __global__ __launch_bounds__(kStepRowThreads) void step_rows_kernel(StepRowsArgs
     float rs = 1.0f;
     if (A.prenorm) {
         if (wave == 0) {
+            // ascending i within this lane (the fixed order): groups of 16 steps of
+            // 64, then the rest in groups of 4 (dm % 256 == 0), no per-element guards
             float a = 0.0f;
-            for (int i0 = lane; i0 < dm; i0 += 16 * 64) {
+            int i0 = lane;
+            for (; i0 - lane + 16 * 64 <= dm; i0 += 16 * 64) {
                 float v[16];
 #pragma unroll
-                for (int k = 0; k < 16; ++k) v[k] = i0 + 64 * k < dm ? row[i0 + 64 * k] : 0.0f;
+                for (int k = 0; k < 16; ++k) v[k] = row[i0 + 64 * k];
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    if (i0 + 64 * k < dm) {
-                        const float v2 = v[k] * v[k];
-                        a = a + v2;  // ascending i within this lane: the fixed order
-                    }
+                    const float v2 = v[k] * v[k];
+                    a = a + v2;
+                }
+            }
+            for (; i0 < dm; i0 += 4 * 64) {
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = row[i0 + 64 * k];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float v2 = v[k] * v[k];
+                    a = a + v2;
                 }
             }
             const float ss = wave_sum_fixed(a);
