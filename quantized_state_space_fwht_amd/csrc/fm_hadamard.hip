@@ -225,11 +225,30 @@ __global__ __launch_bounds__(kNormThreads) void norm_hq_kernel(
         if (have_r) {
             r = live ? rs[r0] : 1.0f;
         } else {
+            // ascending i within this lane (the fixed order): groups of 16 steps
+            // of 64 whose reads go out together, then the rest in groups of 4
+            // (dm % 256 == 0)
             float a = 0.0f;
-            for (int i = lane; i < dm; i += 64) {
-                const float v = row[i];
-                const float v2 = v * v;
-                a = a + v2;  // ascending i within this lane: the fixed order
+            int i0 = lane;
+            for (; i0 - lane + 16 * 64 <= dm; i0 += 16 * 64) {
+                float v[16];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) v[k] = row[i0 + 64 * k];
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const float v2 = v[k] * v[k];
+                    a = a + v2;
+                }
+            }
+            for (; i0 < dm; i0 += 4 * 64) {
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = row[i0 + 64 * k];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float v2 = v[k] * v[k];
+                    a = a + v2;
+                }
             }
             const float ss = wave_sum_fixed(a);
             r = 1.0f / sqrtf(ss / (float)dm + 1e-5f);
