@@ -27,7 +27,8 @@ template <int W> constexpr int kGatePer = W == kGateStepWaves ? 5 : 10;
 // i = l, l+64, ... ascending, then the xor tree).  Phase 3: the 256-blocks
 // are normalized, rotated and quantized, block b by wave b % W.  With
 // `rowmax` set (one-token step), the rotated row goes to rot_ws and its
-// maximum to rowmax[row]; the out_proj product quantizes.
+// maximum to rowmax[row]; one pass over all rows then forms the codes with the
+// tensor scale from those maxima.
 template <int W>
 __global__ __launch_bounds__(64 * W) void gate_norm_kernel(GateArgs G) {
     extern __shared__ __attribute__((aligned(16))) float row_buf[];  // d_inner floats
